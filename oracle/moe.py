@@ -1,0 +1,342 @@
+"""Float64 CPU oracle for the forward pass of a top-k routed MoE FFN layer.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+baseline may import this module. The GPU library never calls it and shares no
+code with it; the only thing both sides share is the seeded input generator.
+
+Everything here is the plain definition of each stage, in float64, written
+from the pages (cited by page title and section):
+
+* [CME295] "Week 2 Day 2: Mixture of Experts" course notes (semidirectx.com),
+  §1.3 formalism, §3.2 balance loss, §3.3 capacity, §4.2 selection bias,
+  §A.2 implementation pitfalls.
+* [FANDEX] "Mixture-of-Experts models" (fanquanpp.github.io), "Step 1: the
+  router" code.
+* [CS336] "Stanford CS336 Lecture 04: MoE architecture" (devpress.csdn.net),
+  §2.1.2 top-K routing, §2.3.3 balancing loss.
+* [15-779] "Lecture 21: Mixture-of-Experts" notes for CMU 15-779
+  (semidirectx.com), §2.1 gating, §2.5 top-1 pitfall, §3.2 four steps,
+  §3.3 permutation by prefix sum, §3.5 capacity, §10 exercises.
+* [W11] "W11: MoE routing and parallel cost" (botof.cn), §2 toy MoE, §3
+  capacity factor.
+
+Readings where the pages are silent or disagree:
+* SwiGLU expert: f(x) = W2 (silu(W1 x) * (W3 x)), silu(u) = u / (1 + e^-u),
+  no biases ([CME295] §2.1 counts 3·d·d_ff weights, no bias).
+* The selection bias is added to the logits z ([CME295] §4.2, [FANDEX]
+  step 1), not to the softmax probabilities ([CS336] §2.3.3 c).
+* Ties in top-k go to the lower expert index (a stable descending sort, as in
+  [FANDEX] step 1; [CME295] §A.2 warns that an unstable top-k is not
+  reproducible).
+* Capacity C = ceil(cf·T·k/E) ([15-779] §3.5, [W11] §3); within one expert all
+  first choices are served before any second choice, tokens in order (the
+  GShard rule described in [15-779] §3.5). A dropped assignment contributes 0
+  and the surviving gates are not renormalised ([CME295] §3.3: the token only
+  takes the residual path).
+* f_i counts the router's choices before any drop, all k of them
+  ([CME295] §3.2 and §A.2).
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Optional, Sequence, Tuple
+
+import numpy as np
+
+GATE_SELECTED = "selected"
+GATE_ALL = "all"
+NEAR_TIE = 1e-3
+
+
+# ------------------------------------------------------------------ routing
+
+def router_logits(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """z = W_r^T x for every token ([CME295] §1.3; [15-779] §2.1).
+
+    ``w_router`` is stored [E, d]: row e is expert e's score vector ([FANDEX]
+    step 1 writes one d-vector ``W_router[e]`` per expert), i.e. the columns of
+    the pages' W_r in R^{d x E}.  Returns z[T, E].
+    """
+    return np.asarray(x, np.float64) @ np.asarray(w_router, np.float64).T
+
+
+def select_topk(s: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Greedy top-k of each row of s, highest first, ties to the lower index
+    ([CME295] §1.3 TopK; [FANDEX] step 1's stable ``sorted``).
+
+    Returns (idx[T, k] int64 in rank order, margin[T]) where the margin is the
+    k-th minus the (k+1)-th largest score (inf when k == E): tokens with a small
+    margin have a selection that rounding can flip.
+    """
+    s = np.asarray(s, np.float64)
+    T, E = s.shape
+    order = np.argsort(-s, axis=1, kind="stable")
+    idx = order[:, :k]
+    if k < E:
+        kth = np.take_along_axis(s, order[:, k - 1:k], 1)[:, 0]
+        nxt = np.take_along_axis(s, order[:, k:k + 1], 1)[:, 0]
+        margin = kth - nxt
+    else:
+        margin = np.full(T, np.inf)
+    return idx, margin
+
+
+def softmax(z: np.ndarray) -> np.ndarray:
+    """Row softmax p = e^z / sum e^z, shifted by the row max."""
+    z = np.asarray(z, np.float64)
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def gates_selected(z: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """g_i = e^{z_i} / sum_{j in T} e^{z_j} over the selected set
+    ([CME295] §1.3; [FANDEX] step 1 shifts by the max of the chosen raw scores)."""
+    zs = np.take_along_axis(np.asarray(z, np.float64), idx, 1)
+    e = np.exp(zs - zs.max(axis=1, keepdims=True))
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def gates_all(z: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """g_i = softmax(z)_i of the chosen experts, not renormalised
+    (Switch top-1, [CME295] §1.3 and [15-779] §2.5; [CS336] §2.1.2)."""
+    return np.take_along_axis(softmax(z), idx, 1)
+
+
+def route(x, w_router, k: int, gate: str = GATE_SELECTED, bias=None):
+    """Router scores, selection on z + b, gates on the unbiased z
+    ([CME295] §4.2: the bias only changes which experts are chosen).
+
+    Returns dict(z, idx, margin, gates, probs)."""
+    z = router_logits(x, w_router)
+    s = z if bias is None else z + np.asarray(bias, np.float64)[None, :]
+    idx, margin = select_topk(s, k)
+    g = gates_selected(z, idx) if gate == GATE_SELECTED else gates_all(z, idx)
+    return dict(z=z, idx=idx, margin=margin, gates=g, probs=softmax(z))
+
+
+# ------------------------------------------------------------------ stats
+
+def load_fractions(idx: np.ndarray, E: int) -> np.ndarray:
+    """f_i = (1/T) #{(t, j): token t chose i}, all k choices counted
+    ([CME295] §3.2 and §A.2)."""
+    T = idx.shape[0]
+    return np.bincount(np.asarray(idx).ravel(), minlength=E).astype(np.float64) / T
+
+
+def mean_probs(probs: np.ndarray) -> np.ndarray:
+    """P_i = (1/T) sum_t p_{t,i} ([CME295] §3.2)."""
+    return np.asarray(probs, np.float64).mean(axis=0)
+
+
+def aux_loss(f: np.ndarray, P: np.ndarray, alpha: float) -> float:
+    """L_aux = alpha · E · sum_i f_i P_i ([CME295] §3.2; [CS336] §2.3.3 a;
+    [15-779] §2.4)."""
+    f = np.asarray(f, np.float64)
+    return float(alpha * f.shape[0] * np.dot(f, np.asarray(P, np.float64)))
+
+
+def coverage_fraction(k: int, E: int, B: int) -> float:
+    """Expected fraction of experts chosen by at least one of B tokens that
+    each pick a uniformly random k-subset: 1 - (1 - k/E)^B ([CME295] §2.3;
+    [15-779] §3.1)."""
+    return 1.0 - (1.0 - k / E) ** B
+
+
+def touched_experts(idx: np.ndarray, E: int) -> int:
+    """Number of distinct experts chosen by a batch."""
+    return int(np.count_nonzero(np.bincount(np.asarray(idx).ravel(), minlength=E)))
+
+
+# ------------------------------------------------------------------ permutation
+
+def capacity(cf: float, T: int, k: int, E: int) -> Optional[int]:
+    """C = ceil(k·T/E · cf) ([15-779] §3.5; [W11] §3); None when cf <= 0."""
+    if cf is None or cf <= 0:
+        return None
+    return int(math.ceil(k * T / E * cf))
+
+
+def assign_rows(idx: np.ndarray, E: int, cf: float = 0.0):
+    """Histogram, capacity and permutation of the (token, slot) assignments.
+
+    Without capacity every assignment gets a row: rows are grouped by expert
+    (expert-major) and ordered by token inside a group, which is the row that
+    the prefix sum over the transposed 0/1 selection mask gives
+    ([15-779] §3.3, worked examples there and in §10 exercise 2). The group
+    boundaries are the CSR indptr ("offsets", length E+1).
+
+    With capacity C, assignment (t, j) to expert e has priority position
+    (#first..(j-1)-th choices of e over all tokens) + (#tokens t' < t whose j-th
+    choice is e); it is kept iff that position < C ([15-779] §3.5 GShard rule).
+    Kept assignments are then laid out as above; dropped ones get dest = -1.
+
+    Returns dict(counts[E], kept[E], offsets[E+1], dest[T,k], src[R], n_dropped, C).
+    """
+    idx = np.asarray(idx, np.int64)
+    T, k = idx.shape
+    counts = np.bincount(idx.ravel(), minlength=E)
+    C = capacity(cf, T, k, E)
+    keep = np.ones((T, k), bool)
+    if C is not None:
+        used = np.zeros(E, np.int64)        # positions handed out so far per expert
+        for j in range(k):                   # all j-th choices before any (j+1)-th
+            for t in range(T):
+                e = idx[t, j]
+                keep[t, j] = used[e] < C
+                used[e] += 1
+    kept = np.zeros(E, np.int64)
+    for t in range(T):
+        for j in range(k):
+            if keep[t, j]:
+                kept[idx[t, j]] += 1
+    offsets = np.zeros(E + 1, np.int64)
+    offsets[1:] = np.cumsum(kept)
+    dest = np.full((T, k), -1, np.int64)
+    src = np.zeros(int(offsets[E]), np.int64)
+    nxt = offsets[:E].copy()
+    for t in range(T):                       # token order inside each expert's group
+        for j in range(k):
+            if keep[t, j]:
+                e = idx[t, j]
+                dest[t, j] = nxt[e]
+                src[nxt[e]] = t
+                nxt[e] += 1
+    return dict(counts=counts, kept=kept, offsets=offsets, dest=dest, src=src,
+                n_dropped=int(T * k - offsets[E]), C=C)
+
+
+def permutation_by_prefix_sum(idx: np.ndarray, E: int):
+    """The prefix-sum formulation of [15-779] §3.3, kept separate from
+    ``assign_rows`` so the two can be checked against each other: flatten the
+    transposed (T x E) 0/1 mask expert-major, take the inclusive cumulative sum,
+    read it back at the mask's ones and subtract 1; indptr is 0 followed by the
+    running total at the end of each expert's column."""
+    idx = np.asarray(idx, np.int64)
+    T, k = idx.shape
+    mask = np.zeros((T, E), np.int64)
+    for t in range(T):
+        mask[t, idx[t]] = 1
+    cs = np.cumsum(mask.T.reshape(-1)).reshape(E, T).T     # [T, E]
+    dest = np.take_along_axis(cs, idx, 1) - 1
+    indptr = np.concatenate([[0], cs[T - 1, :]]) if T > 0 else np.zeros(E + 1, np.int64)
+    return dest, indptr, cs
+
+
+# ------------------------------------------------------------------ experts
+
+def silu(u: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return u / (1.0 + np.exp(-u))
+
+
+def swiglu(X: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """One SwiGLU expert on rows X[n, d]: (silu(X W1^T) * (X W3^T)) W2^T,
+    with W1, W3 stored [d_ff, d] and W2 stored [d, d_ff]."""
+    X = np.asarray(X, np.float64)
+    a = silu(X @ np.asarray(w1, np.float64).T) * (X @ np.asarray(w3, np.float64).T)
+    return a @ np.asarray(w2, np.float64).T
+
+
+def swiglu_hidden(X, w1, w3) -> np.ndarray:
+    """The SwiGLU hidden activation a = silu(X W1^T) * (X W3^T)."""
+    X = np.asarray(X, np.float64)
+    return silu(X @ np.asarray(w1, np.float64).T) * (X @ np.asarray(w3, np.float64).T)
+
+
+ExpertFn = Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]
+
+
+def expert_ffn(rows: np.ndarray, offsets: np.ndarray, experts: ExpertFn) -> np.ndarray:
+    """Z = GroupGemm(data, indptr, weights) of [15-779] §3.3: rows
+    [offsets[e], offsets[e+1]) go through expert e. ``experts(e)`` returns that
+    expert's (W1, W3, W2); it is called once per non-empty group so large
+    layers can be streamed one expert at a time."""
+    rows = np.asarray(rows, np.float64)
+    out = np.zeros((rows.shape[0], rows.shape[1]), np.float64)
+    E = len(offsets) - 1
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            w1, w3, w2 = experts(e)
+            out[lo:hi] = swiglu(rows[lo:hi], w1, w3, w2)
+    return out
+
+
+def combine(yp: np.ndarray, dest: np.ndarray, gates: np.ndarray, d: int,
+            shared: Optional[np.ndarray] = None) -> np.ndarray:
+    """Unpermute and mix: y_t = sum_{j kept} g_{t,j} yp[dest[t,j]] (+ shared_t)
+    ([CME295] §1.3 y = sum g_i f_i(x); [15-779] §3.2 step 4)."""
+    T, k = dest.shape
+    y = np.zeros((T, d), np.float64)
+    for j in range(k):
+        ok = dest[:, j] >= 0
+        y[ok] += gates[ok, j][:, None] * yp[dest[ok, j]]
+    if shared is not None:
+        y += shared
+    return y
+
+
+def forward(x, w_router, experts: ExpertFn, k: int, gate: str = GATE_SELECTED,
+            bias=None, cf: float = 0.0, shared=None, alpha: float = 0.0,
+            idx_override: Optional[np.ndarray] = None):
+    """The whole layer: route -> permute -> grouped experts -> combine
+    ([15-779] §3.2). ``shared`` is (W1, W3, W2) of an always-on expert whose
+    output is added with weight 1 ([CME295] §4.1). ``idx_override`` replaces
+    the selection (gates are recomputed from z for it), which lets a caller
+    evaluate the layer under another implementation's routing.
+
+    Returns a dict with every intermediate and the stats."""
+    x = np.asarray(x, np.float64)
+    T, d = x.shape
+    r = route(x, w_router, k, gate, bias)
+    idx = r["idx"] if idx_override is None else np.asarray(idx_override, np.int64)
+    if idx_override is not None:
+        r["gates"] = (gates_selected(r["z"], idx) if gate == GATE_SELECTED
+                      else gates_all(r["z"], idx))
+    E = np.asarray(w_router).shape[0]
+    p = assign_rows(idx, E, cf)
+    xp = x[p["src"]]
+    yp = expert_ffn(xp, p["offsets"], experts)
+    sh = swiglu(x, *shared) if shared is not None else None
+    y = combine(yp, p["dest"], r["gates"], d, sh)
+    f = load_fractions(idx, E)
+    P = mean_probs(r["probs"])
+    return dict(y=y, idx=idx, gates=r["gates"], z=r["z"], margin=r["margin"],
+                probs=r["probs"], f=f, P=P, aux=aux_loss(f, P, alpha),
+                yp=yp, shared_out=sh, **p)
+
+
+def dense_all_experts(x, experts: ExpertFn, G: np.ndarray) -> np.ndarray:
+    """Every expert on every token, weighted by a dense [T, E] gate matrix:
+    y = sum_e G[:, e] f_e(x) ([15-779] §3.4 formulation 0; with G zero outside
+    the selected set it equals the top-k layer, [15-779] §2.1 demo)."""
+    x = np.asarray(x, np.float64)
+    y = np.zeros_like(x)
+    for e in range(G.shape[1]):
+        if np.any(G[:, e] != 0):
+            y += G[:, e:e + 1] * swiglu(x, *experts(e))
+    return y
+
+
+def scatter_gates(idx: np.ndarray, gates: np.ndarray, E: int) -> np.ndarray:
+    """Dense [T, E] gate matrix with zeros outside each token's selection."""
+    T = idx.shape[0]
+    G = np.zeros((T, E), np.float64)
+    np.put_along_axis(G, np.asarray(idx, np.int64), np.asarray(gates, np.float64), 1)
+    return G
+
+
+def token_output(x_t: np.ndarray, idx_t: Sequence[int], gates_t: Sequence[float],
+                 experts: ExpertFn, keep_t: Optional[Sequence[bool]] = None,
+                 shared=None) -> np.ndarray:
+    """y for one token, straight from y = sum_i g_i f_i(x) (+ shared): the
+    one-token-at-a-time form used to sample outputs of full-size runs."""
+    x_t = np.asarray(x_t, np.float64)[None, :]
+    y = np.zeros(x_t.shape[1])
+    for j, e in enumerate(idx_t):
+        if keep_t is None or keep_t[j]:
+            y += gates_t[j] * swiglu(x_t, *experts(int(e)))[0]
+    if shared is not None:
+        y += swiglu(x_t, *shared)[0]
+    return y

@@ -1,0 +1,461 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+Each test names the page passage it checks. None of them compares the oracle
+with itself: they use printed numbers (tests/golden/), closed forms, brute
+force on tiny inputs, or a second formulation the pages give.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import moe as om
+from oracle import params as op
+import workloads as wk
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------- permutation
+
+def test_permutation_worked_examples():
+    """CMU 15-779 L21 §3.3 worked example and §10 exercise 2: dest and indptr."""
+    for ex in _gold("permutation_examples.json")["examples"]:
+        idx = np.array(ex["choices"])
+        p = om.assign_rows(idx, ex["E"])
+        assert p["dest"].tolist() == ex["dest"], ex["cite"]
+        assert p["offsets"].tolist() == ex["indptr"], ex["cite"]
+        dest2, indptr2, cs = om.permutation_by_prefix_sum(idx, ex["E"])
+        assert dest2.tolist() == ex["dest"]
+        assert indptr2.tolist() == ex["indptr"]
+        if "cumsum_matrix" in ex:
+            assert cs.tolist() == ex["cumsum_matrix"]
+        # src is the inverse of dest
+        for t in range(idx.shape[0]):
+            for j in range(idx.shape[1]):
+                assert p["src"][p["dest"][t, j]] == t
+
+
+def _random_choices(rng, T, E, k):
+    return np.stack([rng.permutation(E)[:k] for _ in range(T)]) if T else np.zeros((0, k), int)
+
+
+def test_permutation_brute_force_and_prefix_sum_agree():
+    """Rows are expert-major, token order inside a group (15-779 §3.3): compare the
+    oracle with a brute-force sort of (expert, token) pairs and with the prefix-sum
+    formulation on random tiny inputs, including empty experts."""
+    rng = np.random.default_rng(7)
+    for T, E, k in [(1, 1, 1), (5, 4, 2), (9, 3, 3), (17, 8, 2), (33, 6, 1), (12, 16, 4)]:
+        idx = _random_choices(rng, T, E, k)
+        p = om.assign_rows(idx, E)
+        pairs = sorted((int(idx[t, j]), t, j) for t in range(T) for j in range(k))
+        dest_bf = np.full((T, k), -1)
+        for r, (e, t, j) in enumerate(pairs):
+            dest_bf[t, j] = r
+        assert (p["dest"] == dest_bf).all()
+        cnt = [sum(1 for e, _, _ in pairs if e == ee) for ee in range(E)]
+        assert p["counts"].tolist() == cnt
+        assert p["offsets"].tolist() == [0] + list(np.cumsum(cnt))
+        dest2, indptr2, _ = om.permutation_by_prefix_sum(idx, E)
+        assert (dest2 == p["dest"]).all() and (indptr2 == p["offsets"]).all()
+        # bijection onto [0, T*k)
+        assert sorted(p["dest"].ravel().tolist()) == list(range(T * k))
+        assert p["n_dropped"] == 0
+
+
+def test_capacity_exercise3():
+    """15-779 §10 exercise 3: C = ceil(2*4096/16*1.25) = 640; a 900-token expert drops 260;
+    dynamic capacity computes 16*900 = 14,400 rows for 8,192 needed (1.76x)."""
+    g = _gold("printed_numbers.json")["capacity_ex3"]
+    C = om.capacity(g["cf"], g["N"], g["k"], g["E"])
+    assert C == g["C"]
+    N, E, k = g["N"], g["E"], g["k"]
+    t = np.arange(N)
+    first = np.where(t < g["busiest_load"], 0, 1 + t % 15)
+    second = np.where(t < g["busiest_load"], 1 + t % 15, 1 + (t + 7) % 15)
+    idx = np.stack([first, second], 1)
+    assert (idx[:, 0] != idx[:, 1]).all()
+    p = om.assign_rows(idx, E, g["cf"])
+    assert p["counts"][0] == g["busiest_load"]
+    assert p["counts"][0] - p["kept"][0] == g["busiest_dropped"]
+    assert p["n_dropped"] == g["busiest_dropped"]
+    assert E * g["busiest_load"] == g["dynamic_rows"] and N * k == g["needed_rows"]
+    assert round(g["dynamic_rows"] / g["needed_rows"], 2) == g["dynamic_ratio"]
+    # the kept first choices are the first 640 tokens in order
+    kept_tokens = p["src"][p["offsets"][0]:p["offsets"][1]]
+    assert kept_tokens.tolist() == list(range(C))
+
+
+def test_capacity_first_choices_before_second():
+    """GShard rule (15-779 §3.5): every first choice gets a slot before any second choice."""
+    idx = np.array([[0, 1], [1, 0], [0, 1], [1, 0]])
+    p = om.assign_rows(idx, 2, cf=0.5)          # C = ceil(0.5*4*2/2) = 2
+    assert p["C"] == 2
+    keep = p["dest"] >= 0
+    assert keep[:, 0].all() and not keep[:, 1].any()
+    assert p["kept"].tolist() == [2, 2] and p["n_dropped"] == 4
+    assert p["dest"].tolist() == [[0, -1], [2, -1], [1, -1], [3, -1]]
+
+
+def test_capacity_none_and_large():
+    """cf <= 0 means no limit; a capacity above every load drops nothing."""
+    rng = np.random.default_rng(3)
+    idx = _random_choices(rng, 40, 5, 2)
+    a = om.assign_rows(idx, 5, 0.0)
+    b = om.assign_rows(idx, 5, 100.0)
+    assert a["C"] is None and b["C"] == math.ceil(100 * 40 * 2 / 5)
+    assert (a["dest"] == b["dest"]).all() and b["n_dropped"] == 0
+
+
+def test_average_load_and_expert_calls():
+    """W11 §3/§9: N=1024, E=8, top-2 -> 256 tokens per expert on average;
+    CME295 §1.3: 6 tokens at top-2 of 8 make 12 expert calls, not 48."""
+    g = _gold("printed_numbers.json")
+    al = g["average_load"]
+    rng = np.random.default_rng(11)
+    idx = _random_choices(rng, al["N"], al["E"], al["k"])
+    p = om.assign_rows(idx, al["E"])
+    assert p["counts"].mean() == al["per_expert"]
+    ec = g["expert_calls"]
+    idx = _random_choices(rng, ec["T"], ec["E"], ec["k"])
+    assert om.assign_rows(idx, ec["E"])["offsets"][-1] == ec["calls"]
+    assert ec["T"] * ec["E"] == 48
+
+
+# --------------------------------------------------------------- selection
+
+def test_topk_brute_force():
+    """TopK = the k-subset with the largest score sum (distinct scores), listed by rank."""
+    rng = np.random.default_rng(5)
+    for E, k in [(4, 2), (8, 2), (8, 3), (6, 6), (7, 1)]:
+        s = rng.standard_normal((25, E))
+        idx, margin = om.select_topk(s, k)
+        for t in range(25):
+            best = max(itertools.combinations(range(E), k), key=lambda c: sum(s[t, list(c)]))
+            assert set(idx[t].tolist()) == set(best)
+            vals = s[t, idx[t]]
+            assert (np.diff(vals) <= 0).all()
+            if k < E:
+                rest = [s[t, e] for e in range(E) if e not in best]
+                assert margin[t] == pytest.approx(min(vals) - max(rest))
+            else:
+                assert margin[t] == np.inf
+
+
+def test_topk_ties_go_to_lower_index():
+    """Equal scores: the lower expert index wins (stable sort of FANDEX step 1)."""
+    idx, m = om.select_topk(np.array([[1.0, 3.0, 3.0, 2.0], [3.0, 1.0, 3.0, 3.0]]), 2)
+    assert idx.tolist() == [[1, 2], [0, 2]]
+    assert m.tolist() == [1.0, 0.0]
+
+
+def test_gate_values_by_hand():
+    """CME295 §1.3 softmax over the selected logits; CS336 §2.1.2 / Switch: full softmax."""
+    z = np.array([[0.0, math.log(3.0), -5.0]])
+    idx = np.array([[1, 0]])
+    g = om.gates_selected(z, idx)
+    assert g[0].tolist() == pytest.approx([0.75, 0.25], abs=1e-15)
+    ga = om.gates_all(z, idx)
+    denom = 1 + 3 + math.exp(-5)
+    assert ga[0].tolist() == pytest.approx([3 / denom, 1 / denom], abs=1e-15)
+
+
+def test_selected_gate_is_renormalised_full_softmax():
+    """15-779 §2.1 writes s_i = g_{e_i} / (g_{e_0} + g_{e_1}) with g = softmax(W_g x); CME295
+    §1.3 writes the softmax over the selected logits. The two must agree."""
+    rng = np.random.default_rng(9)
+    z = rng.standard_normal((50, 8)) * 3
+    idx, _ = om.select_topk(z, 2)
+    p = om.softmax(z)
+    ps = np.take_along_axis(p, idx, 1)
+    assert np.allclose(om.gates_selected(z, idx), ps / ps.sum(1, keepdims=True), rtol=0, atol=1e-15)
+
+
+def test_gate_invariants():
+    """Selected gates sum to 1; k = 1 selected gating gives g = 1 (15-779 §2.5 pitfall)."""
+    rng = np.random.default_rng(1)
+    z = rng.standard_normal((30, 6))
+    for k in (1, 2, 3, 6):
+        idx, _ = om.select_topk(z, k)
+        g = om.gates_selected(z, idx)
+        assert np.allclose(g.sum(1), 1.0, atol=1e-15)
+        if k == 1:
+            assert (g == 1.0).all()
+
+
+def test_bias_changes_selection_not_gates():
+    """CME295 §4.2 / FANDEX step 1: TopK on z + b, gates from the unbiased z."""
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((200, 16))
+    w = rng.standard_normal((8, 16)) / 4
+    b = rng.uniform(-0.5, 0.5, 8)
+    r0 = om.route(x, w, 2, om.GATE_SELECTED, None)
+    r1 = om.route(x, w, 2, om.GATE_SELECTED, b)
+    same = (r0["idx"] == r1["idx"]).all(1)
+    assert same.any() and (~same).any()          # the bias did move some tokens
+    assert np.array_equal(r0["gates"][same], r1["gates"][same])
+    # and the gates of moved tokens are still softmaxes of unbiased z over the new set
+    assert np.allclose(r1["gates"], om.gates_selected(r0["z"], r1["idx"]), atol=0)
+    # the bias enters selection exactly as z + b
+    idx_b, _ = om.select_topk(r0["z"] + b[None, :], 2)
+    assert (idx_b == r1["idx"]).all()
+
+
+def test_router_logits_by_hand():
+    """z = W_r^T x with W_r stored one row per expert."""
+    x = np.array([[1.0, 2.0, 3.0]])
+    w = np.array([[1.0, 0.0, 0.0], [0.0, 1.0, -1.0]])
+    assert om.router_logits(x, w).tolist() == [[1.0, -1.0]]
+
+
+# --------------------------------------------------------------- statistics
+
+def test_aux_loss_printed_values():
+    """CME295 §3.2: uniform routing gives exactly alpha (0.0100 at alpha=0.01);
+    15-779 §10 ex. 5: E*sum(fP) = 1.84 and d/dP_1 = E*f_1 = 2.8 (others 0.4)."""
+    g = _gold("printed_numbers.json")["aux_loss"]
+    for E in (2, 8, 64):
+        u = np.full(E, 1.0 / E)
+        assert om.aux_loss(u, u, g["alpha"]) == pytest.approx(g["uniform_value"], abs=1e-15)
+    f, P = np.array(g["ex5_f"]), np.array(g["ex5_P"])
+    assert om.aux_loss(f, P, 1.0) == pytest.approx(g["ex5_E_sum_fP"], abs=1e-12)
+    h = 1e-6
+    grads = []
+    for i in range(4):
+        dp = P.copy(); dp[i] += h
+        dm = P.copy(); dm[i] -= h
+        grads.append((om.aux_loss(f, dp, 1.0) - om.aux_loss(f, dm, 1.0)) / (2 * h))
+    assert grads[0] == pytest.approx(g["ex5_dP1"], abs=1e-6)
+    assert grads[1:] == pytest.approx([g["ex5_dP_other"]] * 3, abs=1e-6)
+
+
+def test_aux_loss_through_router():
+    """Routing that is balanced in both counts and probabilities gives L_aux = alpha; full
+    collapse onto one expert approaches alpha*E (15-779 §2.4)."""
+    E, alpha = 8, 0.01
+    x = np.eye(E) * 4.0                     # token t prefers expert t; cyclic symmetry
+    w = np.eye(E)
+    r = om.route(x, w, 1, om.GATE_ALL)
+    f = om.load_fractions(r["idx"], E)
+    P = om.mean_probs(r["probs"])
+    assert np.allclose(f, 1 / E) and np.allclose(P, 1 / E, atol=1e-15)
+    assert om.aux_loss(f, P, alpha) == pytest.approx(alpha, abs=1e-15)
+    xc = np.tile(np.eye(E)[:1] * 60.0, (E, 1))   # every token: expert 0 with p ~ 1
+    r = om.route(xc, w, 1, om.GATE_ALL)
+    L = om.aux_loss(om.load_fractions(r["idx"], E), om.mean_probs(r["probs"]), alpha)
+    assert L == pytest.approx(alpha * E, rel=1e-12)
+
+
+def test_coverage_closed_form_table():
+    """CME295 §2.3 table (top-2 of 8): 25.0/43.8/68.4/90.0/99.0/100.0 %;
+    15-779 §3.1: 7.9 experts at B=16; §10 ex. 4: ~163 of 256 at top-8, B=32."""
+    g = _gold("printed_numbers.json")
+    cov = g["coverage_top2_of_8"]
+    for B, pct in zip(cov["B"], cov["percent"]):
+        assert round(100 * om.coverage_fraction(2, 8, B), 1) == pct
+    cc = g["coverage_counts"]
+    assert round(8 * om.coverage_fraction(2, 8, 16), 1) == cc["mixtral_B16"]
+    assert round(256 * om.coverage_fraction(8, 256, 32)) == cc["deepseek_B32"]
+
+
+def test_coverage_exact_enumeration_small_batches():
+    """With i.i.d. symmetric scores every top-2 subset is equally likely, so B=1 and B=2 can be
+    enumerated exactly: the oracle's selection + touched count must give 0.25 and 0.4375."""
+    subsets = list(itertools.combinations(range(8), 2))
+    def frac(batch):
+        idx = np.array(batch)
+        return om.touched_experts(idx, 8) / 8
+    assert np.mean([frac([s]) for s in subsets]) == 0.25
+    assert np.mean([frac([a, b]) for a in subsets for b in subsets]) == pytest.approx(0.4375, abs=1e-15)
+    # and the oracle's selection reproduces those subsets from scores that rank them
+    for s in subsets:
+        z = np.zeros((1, 8)); z[0, list(s)] = [2.0, 1.0]
+        assert set(om.select_topk(z, 2)[0][0].tolist()) == set(s)
+
+
+def test_coverage_monte_carlo_on_generated_router():
+    """The Mixtral-shaped recipe (orthonormal router, x ~ N(0, I)) gives z ~ N(0, I_8); the
+    oracle's routing then touches 1 - 0.75^B of the experts (CME295 §2.3) within 4 SE."""
+    wl = wk.get("mixtral_t32")
+    inp = wk.make_inputs(wl, T=2016)                 # 63 batches of 32 tokens
+    z = om.router_logits(wk.to_f64(inp.x, wl.dtype), wk.to_f64(inp.w_router, wl.dtype))
+    assert abs(z.mean()) < 0.05 and abs(z.std() - 1.0) < 0.05
+    rng = np.random.default_rng(2024)
+    zz = rng.standard_normal((4000 * 32, 8))
+    for B in (1, 2, 4, 8, 16, 32):
+        n = 4000
+        idx, _ = om.select_topk(zz[: n * B], 2)
+        fr = np.array([om.touched_experts(idx[i * B:(i + 1) * B], 8) / 8 for i in range(n)])
+        se = fr.std(ddof=1) / math.sqrt(n) + 1e-12
+        assert abs(fr.mean() - om.coverage_fraction(2, 8, B)) < 4 * se + 1e-9, B
+    # generated batches of 32 touch (almost) all experts
+    idx, _ = om.select_topk(z, 2)
+    per = [om.touched_experts(idx[i * 32:(i + 1) * 32], 8) for i in range(63)]
+    assert np.mean(per) > 7.5
+
+
+# --------------------------------------------------------------- experts and combine
+
+def test_silu_values():
+    u = np.array([0.0, 1.0, -1.0, 40.0, -800.0])
+    s = om.silu(u)
+    assert s[0] == 0.0
+    assert s[1] == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), abs=1e-16)
+    assert s[2] == pytest.approx(-1.0 / (1.0 + math.e), abs=1e-16)
+    assert s[3] == pytest.approx(40.0, rel=1e-15)
+    assert s[4] == 0.0
+
+
+def test_swiglu_triple_loop():
+    """The BLAS path equals a pure-Python triple loop on a tiny case."""
+    rng = np.random.default_rng(8)
+    n, d, f = 3, 4, 5
+    X = rng.standard_normal((n, d)); w1 = rng.standard_normal((f, d))
+    w3 = rng.standard_normal((f, d)); w2 = rng.standard_normal((d, f))
+    ref = np.zeros((n, d))
+    for r in range(n):
+        a = []
+        for i in range(f):
+            g = sum(X[r, c] * w1[i, c] for c in range(d))
+            u = sum(X[r, c] * w3[i, c] for c in range(d))
+            a.append(g / (1 + math.exp(-g)) * u)
+        for o in range(d):
+            ref[r, o] = sum(a[i] * w2[o, i] for i in range(f))
+    assert np.allclose(om.swiglu(X, w1, w3, w2), ref, rtol=1e-13, atol=1e-13)
+
+
+def _toy(T=64):
+    wl = wk.get("toy_t64")
+    inp = wk.make_inputs(wl, T=T)
+    cache = {}
+    def experts(e):
+        if e not in cache:
+            cache[e] = tuple(wk.to_f64(a, wl.dtype) for a in inp.expert(e))
+        return cache[e]
+    return wl, inp, experts
+
+
+def test_forward_equals_dense_all_experts():
+    """15-779 §2.1 demo / §3.4 formulation 0: every expert on every token with the unselected
+    gates set to 0 gives the same output as the routed layer."""
+    wl, inp, experts = _toy()
+    x = wk.to_f64(inp.x, wl.dtype)
+    wr = wk.to_f64(inp.w_router, wl.dtype)
+    out = om.forward(x, wr, experts, wl.k, wl.gate)
+    G = om.scatter_gates(out["idx"], out["gates"], wl.E)
+    yd = om.dense_all_experts(x, experts, G)
+    scale = np.sqrt(np.mean(out["y"] ** 2))
+    assert np.max(np.abs(out["y"] - yd)) <= 1e-12 * scale
+    # one token at a time, straight from y = sum g f(x)
+    for t in (0, 17, 63):
+        yt = om.token_output(x[t], out["idx"][t], out["gates"][t], experts)
+        assert np.allclose(yt, out["y"][t], rtol=0, atol=1e-12 * scale)
+    # the dense full-softmax mixture is a different function (CME295 §1.3: relative gap 0.30)
+    yfull = om.dense_all_experts(x, experts, om.softmax(out["z"]))
+    assert np.linalg.norm(yfull - out["y"]) > 0.05 * np.linalg.norm(out["y"])
+    # T*k expert rows
+    assert out["offsets"][-1] == wl.T * wl.k
+
+
+def test_single_expert_is_dense_swiglu():
+    """CME295 §B: with E = 1 and k = 1 the layer is exactly the dense SwiGLU FFN."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((10, 8))
+    w = (rng.standard_normal((16, 8)), rng.standard_normal((16, 8)), rng.standard_normal((8, 16)))
+    wr = rng.standard_normal((1, 8))
+    for gate in (om.GATE_SELECTED,):
+        out = om.forward(x, wr, lambda e: w, 1, gate)
+        assert np.array_equal(out["gates"], np.ones((10, 1)))
+        assert np.allclose(out["y"], om.swiglu(x, *w), rtol=1e-14, atol=1e-14)
+
+
+def test_shared_expert_adds_with_weight_one():
+    """CME295 §4.1: a shared expert runs on every token and adds to the routed output."""
+    wl, inp, experts = _toy(T=20)
+    x = wk.to_f64(inp.x, wl.dtype)
+    wr = wk.to_f64(inp.w_router, wl.dtype)
+    sh = experts(3)
+    a = om.forward(x, wr, experts, 2, shared=sh)
+    b = om.forward(x, wr, experts, 2)
+    assert np.allclose(a["y"] - b["y"], om.swiglu(x, *sh), rtol=1e-13, atol=1e-13)
+
+
+def test_dropped_assignment_contributes_zero():
+    """A token that overflows its only expert skips the layer (CME295 §3.3): y_t = 0 for k = 1."""
+    wl, inp, experts = _toy(T=16)
+    x = wk.to_f64(inp.x, wl.dtype)
+    wr = wk.to_f64(inp.w_router, wl.dtype)
+    out = om.forward(x, wr, experts, 1, om.GATE_ALL, cf=0.5)   # C = ceil(0.5*16/4) = 2
+    assert out["C"] == 2
+    dropped = out["dest"][:, 0] < 0
+    assert dropped.sum() == out["n_dropped"] == 16 - out["kept"].sum()
+    assert (out["y"][dropped] == 0).all()
+    assert (np.abs(out["y"][~dropped]).sum(1) > 0).all()
+    # the kept ones are the first C tokens of each expert in token order
+    for e in range(4):
+        toks = np.nonzero(out["idx"][:, 0] == e)[0]
+        assert (out["dest"][toks[:2], 0] >= 0).all() and (out["dest"][toks[2:], 0] < 0).all()
+
+
+# --------------------------------------------------------------- parameter counts
+
+def test_mixtral_parameter_counts():
+    """CME295 §2.1: 46,702,792,704 total and 12,879,925,248 active; 41.9M attention, 176.2M per
+    expert, 32,768 router per layer; §2.2: experts are 96.6% of the total, ~87 GiB in bf16."""
+    g = _gold("printed_numbers.json")["mixtral_counts"]
+    m = op.MIXTRAL_8X7B
+    total, active = op.counts(m)
+    assert (total, active) == (g["total"], g["active"])
+    assert round(op.attention_params(m) / 1e6, 1) == g["attention_per_layer_M"]
+    assert round(op.expert_params(m) / 1e6, 1) == g["expert_per_layer_M"]
+    assert op.router_params(m) == g["router_per_layer"]
+    share = m.layers * m.E * op.expert_params(m) / total
+    assert round(100 * share, 1) == g["expert_share_percent"]
+    assert round(total * 2 / 2 ** 30) == g["bf16_GiB_approx"]
+    # the Mixtral-shaped workload uses exactly these layer shapes
+    wl = wk.get("mixtral_t4096")
+    assert (wl.d, wl.E, wl.k, wl.d_ff) == (m.d, m.E, m.k, m.d_ff)
+
+
+def test_exercise1_parameter_counts():
+    """15-779 §10 ex. 1: 64 fine-grained experts (f=1408) top-6 + 2 shared -> ~38.1B / ~6.04B."""
+    g = _gold("printed_numbers.json")["exercise1_counts"]
+    m = op.ModelShape(layers=32, d=4096, q_heads=32, kv_heads=8, head_dim=128, E=64, k=6,
+                      d_ff=1408, vocab=32000, n_shared=2)
+    total, active = op.counts(m, with_norms=False)
+    # the page sums rounded per-layer figures (41.9M + 1142M), so its total is "about 38.1B";
+    # the exact count is 38.153B
+    assert abs(total / 1e9 - g["total_B"]) < 0.1
+    assert round(active / 1e9, 2) == g["active_B"]
+
+
+# --------------------------------------------------------------- workload recipes
+
+def test_skew_recipe_puts_expert0_everywhere():
+    """Stress config reading: expert 0 in every token's top-2, experts 6 and 7 never chosen,
+    max/mean load = 4 (the maximum for top-2 of 8)."""
+    wl = wk.get("skew_t16384")
+    inp = wk.make_inputs(wl, T=2048)
+    r = om.route(wk.to_f64(inp.x, wl.dtype), wk.to_f64(inp.w_router, wl.dtype), wl.k)
+    counts = np.bincount(r["idx"].ravel(), minlength=8)
+    assert counts[0] == 2048 and counts[6] == 0 and counts[7] == 0
+    assert counts.max() / (2048 * 2 / 8) == 4.0
+
+
+def test_switch_recipe_overflows():
+    """Switch config: skewed logits make the busiest experts overflow at every cf."""
+    wl = wk.get("switch_t8192_cf1.25")
+    inp = wk.make_inputs(wl, T=1024)
+    r = om.route(wk.to_f64(inp.x, wl.dtype), wk.to_f64(inp.w_router, wl.dtype), 1, om.GATE_ALL)
+    for cf in (1.0, 1.25, 2.0):
+        p = om.assign_rows(r["idx"], wl.E, cf)
+        assert p["n_dropped"] > 0
+    assert np.bincount(r["idx"].ravel(), minlength=64).max() > 4 * 1024 / 64
