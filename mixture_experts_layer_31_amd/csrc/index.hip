@@ -1,0 +1,202 @@
+// Per-expert histogram, capacity and the token permutation.
+//
+// The CMU 15-779 Lecture 21 notes, §3.3: the destination row of every
+// (token, expert) assignment is the prefix sum of the transposed 0/1 selection
+// mask taken expert-major, so rows are grouped by expert, tokens in order inside
+// a group, and the group boundaries (CSR indptr) come out of the same scan.
+// §3.5: with a capacity C an expert keeps at most C assignments, every first
+// choice before any second choice, tokens in order; the rest are dropped.
+//
+// GPU formulation. Tokens are cut into blocks of 256. Each block builds, in LDS,
+// one 256-bit token bitmap per key (key = expert, or (slot, expert) with
+// capacity) with LDS atomics; counts are popcounts. A single-workgroup scan
+// turns the per-block counts into per-block bases (exclusive prefix over
+// blocks, in block order) and the expert offsets. The rank of a token among the
+// earlier tokens of its key is then base + popcount of the bitmap bits below it.
+// Atomics only ever set bits, so every output is deterministic and equal to the
+// sequential definition.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kTB = kIndexTokensPerBlock;   // tokens per block = threads per block
+constexpr int kWords = kTB / 32;            // 32-bit bitmap words per key
+
+int index_blocks(int T) { return (T + kTB - 1) / kTB; }
+
+__device__ __forceinline__ void build_bitmaps(uint32_t* bm, const int32_t* idx, int T, int k,
+                                              int E, int nkeys, bool cap) {
+  for (int i = threadIdx.x; i < nkeys * kWords; i += kTB) bm[i] = 0u;
+  __syncthreads();
+  const int t = blockIdx.x * kTB + threadIdx.x;
+  if (t < T) {
+    const uint32_t bit = 1u << (threadIdx.x & 31);
+    const int w = threadIdx.x >> 5;
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[static_cast<size_t>(t) * k + j];
+      if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) continue;  // not an expert
+      const int key = cap ? j * E + e : e;
+      atomicOr(&bm[key * kWords + w], bit);
+    }
+  }
+  __syncthreads();
+}
+
+// number of set bits of key's bitmap strictly below local token position p
+__device__ __forceinline__ int bits_below(const uint32_t* bm, int key, int p) {
+  const uint32_t* b = bm + key * kWords;
+  int r = 0;
+  const int w = p >> 5;
+  for (int i = 0; i < w; ++i) r += __popc(b[i]);
+  return r + __popc(b[w] & ((1u << (p & 31)) - 1u));
+}
+
+__global__ __launch_bounds__(kTB) void index_count_kernel(const int32_t* __restrict__ idx, int T,
+                                                          int k, int E, int cap,
+                                                          int32_t* __restrict__ blk) {
+  extern __shared__ uint32_t bm[];
+  const int nkeys = cap ? E * k : E;
+  build_bitmaps(bm, idx, T, k, E, nkeys, cap);
+  for (int key = threadIdx.x; key < nkeys; key += kTB) {
+    int c = 0;
+    for (int w = 0; w < kWords; ++w) c += __popc(bm[key * kWords + w]);
+    blk[static_cast<size_t>(blockIdx.x) * nkeys + key] = c;
+  }
+}
+
+// One workgroup. blk[b][key] (counts) becomes the exclusive prefix over blocks.
+__global__ __launch_bounds__(1024) void index_scan_kernel(
+    int32_t* __restrict__ blk, int nb, int T, int k, int E, long long C,
+    int32_t* __restrict__ slot_base, int32_t* __restrict__ slot_keep,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ counts_out,
+    int32_t* __restrict__ kept_out, int32_t* __restrict__ n_dropped) {
+  __shared__ int32_t part[1024];
+  const int cap = C >= 0;
+  const int nkeys = cap ? E * k : E;
+  int32_t* tot = blk + static_cast<size_t>(nb) * nkeys;   // row nb holds the key totals
+  for (int key = threadIdx.x; key < nkeys; key += blockDim.x) {
+    int run = 0;
+    for (int b = 0; b < nb; ++b) {
+      const size_t o = static_cast<size_t>(b) * nkeys + key;
+      const int c = blk[o];
+      blk[o] = run;
+      run += c;
+    }
+    tot[key] = run;
+  }
+  __threadfence_block();
+  __syncthreads();
+  // per expert: count before drops and kept after capacity
+  const int e = threadIdx.x;
+  int keep_e = 0;
+  if (e < E) {
+    int cnt = 0;
+    if (cap) {
+      // all j-th choices are served before any (j+1)-th choice
+      for (int j = 0; j < k; ++j) {
+        const int tj = tot[j * E + e];
+        long long room = C - cnt;
+        room = room < 0 ? 0 : room;
+        const int keep_j = static_cast<int>(room < tj ? room : tj);
+        slot_base[j * E + e] = cnt;
+        slot_keep[j * E + e] = keep_j;
+        keep_e += keep_j;
+        cnt += tj;
+      }
+    } else {
+      cnt = tot[e];
+      keep_e = cnt;
+    }
+    if (counts_out) counts_out[e] = cnt;
+    if (kept_out) kept_out[e] = keep_e;
+  }
+  // exclusive scan of kept over experts (E <= 1024 = blockDim.x)
+  part[threadIdx.x] = (e < E) ? keep_e : 0;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  if (e < E) offsets[e + 1] = part[e];
+  if (threadIdx.x == 0) {
+    offsets[0] = 0;
+    if (n_dropped) n_dropped[0] = T * k - part[E - 1];
+  }
+}
+
+__global__ __launch_bounds__(kTB) void index_rank_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int E, long long C,
+    const int32_t* __restrict__ blk, const int32_t* __restrict__ slot_base,
+    const int32_t* __restrict__ slot_keep, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ dest, int32_t* __restrict__ src) {
+  extern __shared__ uint32_t bm[];
+  const int cap = C >= 0;
+  const int nkeys = cap ? E * k : E;
+  build_bitmaps(bm, idx, T, k, E, nkeys, cap);
+  const int t = blockIdx.x * kTB + threadIdx.x;
+  if (t >= T) return;
+  const int p = threadIdx.x;
+  const int32_t* base = blk + static_cast<size_t>(blockIdx.x) * nkeys;
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[static_cast<size_t>(t) * k + j];
+    int row;
+    if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) {
+      row = -1;   // an out-of-range index is never given a row
+    } else if (!cap) {
+      row = offsets[e] + base[e] + bits_below(bm, e, p);
+    } else {
+      const int key = j * E + e;
+      const int rank_j = base[key] + bits_below(bm, key, p);
+      if (static_cast<long long>(slot_base[key]) + rank_j >= C) {
+        row = -1;
+      } else {
+        // kept rows of e held by earlier tokens: in each slot j', the kept ones
+        // are the first slot_keep[j'][e] tokens of that slot (token order)
+        int before = 0;
+        for (int j2 = 0; j2 < k; ++j2) {
+          const int key2 = j2 * E + e;
+          const int r2 = base[key2] + bits_below(bm, key2, p);
+          const int kk = slot_keep[key2];
+          before += r2 < kk ? r2 : kk;
+        }
+        row = offsets[e] + before;
+      }
+    }
+    dest[static_cast<size_t>(t) * k + j] = row;
+    if (row >= 0) src[row] = t;
+  }
+}
+
+hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capacity,
+                        int32_t* blk, int32_t* slot_base, int32_t* slot_keep, int32_t* offsets,
+                        int32_t* dest, int32_t* src, int32_t* counts, int32_t* kept,
+                        int32_t* n_dropped, hipStream_t s) {
+  const bool cap = capacity >= 0;
+  const int nb = index_blocks(T);
+  const int nkeys = index_keys(E, k, cap);
+  const size_t lds = static_cast<size_t>(nkeys) * kWords * sizeof(uint32_t);
+  if (lds > 65536) {
+    hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(index_count_kernel),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(index_rank_kernel),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e1 != hipSuccess) return e1;
+    if (e2 != hipSuccess) return e2;
+  }
+  index_count_kernel<<<dim3(nb), dim3(kTB), lds, s>>>(idx, T, k, E, cap ? 1 : 0, blk);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  index_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(blk, nb, T, k, E, cap ? capacity : -1,
+                                                   slot_base, slot_keep, offsets, counts, kept,
+                                                   n_dropped);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  index_rank_kernel<<<dim3(nb), dim3(kTB), lds, s>>>(idx, T, k, E, cap ? capacity : -1, blk,
+                                                     slot_base, slot_keep, offsets, dest, src);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,87 @@
+// Internal launchers of the MoE kernels. Every launcher enqueues on `s` and
+// returns hipGetLastError() of its launch(es); shapes are validated by the
+// C-ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- router (router.hip)
+constexpr int kSelectTokensPerBlock = 64;
+int router_select_blocks(int T);
+hipError_t launch_router_scores(int dtype_bf16, const void* x, const void* w, int T, int d, int E,
+                                float* z, hipStream_t s);
+hipError_t launch_router_select(const float* z, const float* bias, int T, int E, int k,
+                                int gate_all, int32_t* idx, float* gates, float* p_part,
+                                int32_t* c_part, hipStream_t s);
+hipError_t launch_router_stats(const float* p_part, const int32_t* c_part, int nblocks, int T,
+                               int E, float alpha, float* f, float* P, float* aux,
+                               hipStream_t s);
+
+// ---- index: histogram, scan, rank (index.hip)
+constexpr int kIndexTokensPerBlock = 256;
+int index_blocks(int T);
+// number of histogram keys: E without capacity, k*E with capacity
+inline int index_keys(int E, int k, bool cap) { return cap ? E * k : E; }
+constexpr int kIndexMaxKeys = 4096;   // LDS bitmaps: 32 bytes per key
+hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capacity,
+                        int32_t* blk /*[nb+1][keys]*/, int32_t* slot_base /*[k][E]*/,
+                        int32_t* slot_keep /*[k][E]*/, int32_t* offsets, int32_t* dest,
+                        int32_t* src, int32_t* counts, int32_t* kept, int32_t* n_dropped,
+                        hipStream_t s);
+
+// ---- row movement (rows.hip)
+hipError_t launch_gather_rows(int elt_bytes, const void* x, const int32_t* src,
+                              const int32_t* offsets, int E, int R_max, int d, void* x_perm,
+                              hipStream_t s);
+hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* gates, int T,
+                          int k, int d, int shared_row0 /* -1: none */, float* y,
+                          hipStream_t s);
+
+// ---- grouped GEMMs (gemm_bf16.hip, gemm_f32.hip)
+//
+// Tile table entry: {group, first row, rows, 0}. An entry with rows == 0 ends
+// the work of its workgroup.
+struct GemmTileMap {
+  const int32_t* tiles;   // [max_tiles][4], or nullptr for one group of n_single rows
+  int max_tiles;
+  int n_single;
+};
+
+// BM of the grouped GEMMs; n128_ok: every GEMM N (d, d_ff, d_ff_shared) is a multiple of 128
+int gemm_tile_rows(int dtype_bf16, int R_max, bool n128_ok);
+int gemm_max_tiles(int BM, int R_max, int E);
+hipError_t launch_tile_map(const int32_t* offsets, int E, int BM, int max_tiles,
+                           int32_t* tiles, hipStream_t s);
+
+struct GateUpArgs {
+  const void* x;          // activation rows source
+  const int32_t* src;     // row -> x row (nullable: identity)
+  const void* w1;         // [G][N][K]
+  const void* w3;
+  long long w_stride;     // elements between groups' weight matrices
+  void* act;              // [rows][act_stride]
+  int act_stride;
+  int out_row0;           // output row = out_row0 + grouped row
+  int K, N;               // K = d, N = d_ff
+};
+struct DownArgs {
+  const void* act;        // [rows][act_stride]
+  int act_stride;
+  int in_row0;            // input row = in_row0 + grouped row
+  const void* w2;         // [G][N][K]
+  long long w_stride;
+  float* y;               // [rows][N]
+  int out_row0;
+  int K, N;               // K = d_ff, N = d
+};
+hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, int BM,
+                                   hipStream_t s);
+hipError_t launch_gemm_down_bf16(const GemmTileMap& map, const DownArgs& a, int BM,
+                                 hipStream_t s);
+hipError_t launch_gemm_gateup_f32(const GemmTileMap& map, const GateUpArgs& a, hipStream_t s);
+hipError_t launch_gemm_down_f32(const GemmTileMap& map, const DownArgs& a, hipStream_t s);
+
+}  // namespace moe

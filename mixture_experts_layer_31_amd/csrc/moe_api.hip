@@ -1,0 +1,433 @@
+// C ABI of the MoE layer: validation, workspace layout and launch sequences.
+// Every entry point validates its arguments completely before it enqueues
+// anything, so a rejected call leaves the stream and all outputs untouched.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernels.h"
+#include "moe.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+moe_status hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define MOE_HIP(call, where)                          \
+  do {                                                \
+    hipError_t e_ = (call);                           \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t al(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+// Validated shape and the sizes derived from it.
+struct Shape {
+  int T, d, E, k, dff, nsh, dffs;
+  int gate_all, bf16, elt;
+  long long C;          // capacity, -1 when it cannot bind
+  int R;                // T*k routed rows (buffer size)
+  int rows_total;       // R + n_shared*T
+  int act_stride;
+  int BM, max_tiles;
+  bool n128;            // every GEMM N is a multiple of 128
+  int nb_sel, nb_idx, nkeys;
+};
+
+moe_status validate(const moe_config* c, Shape* s) {
+  if (c == nullptr) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->reserved != 0 || c->reserved2 != 0.0f)
+    return fail(MOE_ERR_INVALID_ARG, "reserved fields must be 0");
+  if (c->T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d < 0", c->T);
+  if (c->E < 1 || c->E > 1024) return fail(MOE_ERR_INVALID_ARG, "E=%d not in [1, 1024]", c->E);
+  if (c->k < 1 || c->k > c->E || c->k > 16)
+    return fail(MOE_ERR_INVALID_ARG, "k=%d not in [1, min(E, 16)]", c->k);
+  if (c->d < 1 || c->d_ff < 1) return fail(MOE_ERR_INVALID_ARG, "d=%d, d_ff=%d must be > 0", c->d, c->d_ff);
+  if (c->n_shared != 0 && c->n_shared != 1)
+    return fail(MOE_ERR_INVALID_ARG, "n_shared=%d must be 0 or 1", c->n_shared);
+  if (c->n_shared == 1 && c->d_ff_shared < 1)
+    return fail(MOE_ERR_INVALID_ARG, "d_ff_shared=%d must be > 0", c->d_ff_shared);
+  if (c->gate_mode != MOE_GATE_SOFTMAX_SELECTED && c->gate_mode != MOE_GATE_SOFTMAX_ALL)
+    return fail(MOE_ERR_INVALID_ARG, "gate_mode=%d unknown", c->gate_mode);
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "dtype=%d unknown", c->dtype);
+  if (std::isnan(c->capacity_factor) || std::isinf(c->capacity_factor))
+    return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be finite");
+  if (!std::isfinite(c->aux_alpha)) return fail(MOE_ERR_INVALID_ARG, "aux_alpha must be finite");
+  const int dffs = c->n_shared ? c->d_ff_shared : 0;
+  if (c->d % 64 || c->d_ff % 64 || dffs % 64)
+    return fail(MOE_ERR_UNSUPPORTED, "d=%d, d_ff=%d, d_ff_shared=%d must be multiples of 64",
+                c->d, c->d_ff, dffs);
+  const long long R = static_cast<long long>(c->T) * c->k;
+  const long long rows = R + static_cast<long long>(c->n_shared) * c->T;
+  if (rows > (1LL << 30)) return fail(MOE_ERR_INVALID_ARG, "T*k + n_shared*T = %lld too large", rows);
+
+  s->T = c->T; s->d = c->d; s->E = c->E; s->k = c->k; s->dff = c->d_ff;
+  s->nsh = c->n_shared; s->dffs = dffs;
+  s->gate_all = c->gate_mode == MOE_GATE_SOFTMAX_ALL;
+  s->bf16 = c->dtype == MOE_BF16;
+  s->elt = s->bf16 ? 2 : 4;
+  s->R = static_cast<int>(R);
+  s->rows_total = static_cast<int>(rows);
+  s->act_stride = c->d_ff > dffs ? c->d_ff : dffs;
+  // C = ceil(k*T/E * cf) in double; it cannot bind when C >= T (a token picks an
+  // expert at most once), so that case runs the capacity-free path.
+  s->C = -1;
+  if (c->capacity_factor > 0) {
+    const double cd = std::ceil(static_cast<double>(R) / c->E * c->capacity_factor);
+    if (cd < static_cast<double>(c->T)) s->C = static_cast<long long>(cd);
+  }
+  s->nkeys = moe::index_keys(s->E, s->k, s->C >= 0);
+  if (s->nkeys > moe::kIndexMaxKeys)
+    return fail(MOE_ERR_UNSUPPORTED, "capacity with E*k=%d > %d is not supported", s->nkeys,
+                moe::kIndexMaxKeys);
+  s->n128 = (s->d % 128 == 0) && (s->dff % 128 == 0) && (s->dffs % 128 == 0);
+  s->BM = moe::gemm_tile_rows(s->bf16, s->R, s->n128);
+  s->max_tiles = moe::gemm_max_tiles(s->BM, s->R, s->E);
+  s->nb_sel = moe::router_select_blocks(s->T);
+  s->nb_idx = moe::index_blocks(s->T);
+  return MOE_OK;
+}
+
+// workspace sizes per stage
+size_t route_bytes(const Shape& s) {
+  return al(static_cast<size_t>(s.T) * s.E * 4) + 2 * al(static_cast<size_t>(s.nb_sel) * s.E * 4);
+}
+size_t permute_bytes(const Shape& s) {
+  return al(static_cast<size_t>(s.nb_idx + 1) * s.nkeys * 4) + 2 * al(static_cast<size_t>(s.k) * s.E * 4);
+}
+size_t tiles_bytes(const Shape& s) { return al(static_cast<size_t>(s.max_tiles) * 16); }
+size_t act_bytes(const Shape& s) {
+  return al(static_cast<size_t>(s.rows_total) * s.act_stride * s.elt);
+}
+size_t yperm_bytes(const Shape& s) { return al(static_cast<size_t>(s.rows_total) * s.d * 4); }
+size_t forward_fixed_bytes(const Shape& s) {
+  const size_t R4 = al(static_cast<size_t>(s.R) * 4);
+  return 4 * R4 + al(static_cast<size_t>(s.E + 1) * 4) + yperm_bytes(s) + act_bytes(s);
+}
+
+size_t stage_bytes(const Shape& s, moe_stage st) {
+  size_t b = 0;
+  switch (st) {
+    case MOE_STAGE_ROUTE: b = route_bytes(s); break;
+    case MOE_STAGE_PERMUTE: b = permute_bytes(s); break;
+    case MOE_STAGE_EXPERT_GATEUP:
+    case MOE_STAGE_EXPERT_DOWN: b = tiles_bytes(s); break;
+    case MOE_STAGE_EXPERT_FFN: b = act_bytes(s) + tiles_bytes(s); break;
+    case MOE_STAGE_COMBINE: b = 0; break;
+    case MOE_STAGE_FORWARD: {
+      size_t scratch = route_bytes(s);
+      if (permute_bytes(s) > scratch) scratch = permute_bytes(s);
+      if (tiles_bytes(s) > scratch) scratch = tiles_bytes(s);
+      b = forward_fixed_bytes(s) + scratch;
+      break;
+    }
+  }
+  return b < kAlign ? kAlign : b;
+}
+
+struct Carver {
+  char* p;
+  template <typename T>
+  T* take(size_t bytes) {
+    T* r = reinterpret_cast<T*>(p);
+    p += al(bytes);
+    return r;
+  }
+};
+
+moe_status check_ws(const Shape& s, moe_stage st, const void* ws, size_t ws_bytes) {
+  const size_t need = stage_bytes(s, st);
+  if (ws == nullptr) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+#define REQUIRE(ptr)                                                            \
+  do {                                                                          \
+    if ((ptr) == nullptr) return fail(MOE_ERR_INVALID_ARG, #ptr " is NULL");    \
+    if (!aligned16(ptr)) return fail(MOE_ERR_INVALID_ARG, #ptr " not 16-byte aligned"); \
+  } while (0)
+
+bool want_route_stats(const moe_stats* st) {
+  return st != nullptr && (st->f != nullptr || st->P != nullptr || st->aux != nullptr);
+}
+
+// ---- stage bodies (arguments already validated)
+
+moe_status do_route(const Shape& s, float alpha, const void* x, const void* wr, const float* bias,
+                    int32_t* idx, float* gates, const moe_stats* st, void* ws, hipStream_t stream) {
+  Carver cv{static_cast<char*>(ws)};
+  float* z = cv.take<float>(static_cast<size_t>(s.T) * s.E * 4);
+  float* p_part = cv.take<float>(static_cast<size_t>(s.nb_sel) * s.E * 4);
+  int32_t* c_part = cv.take<int32_t>(static_cast<size_t>(s.nb_sel) * s.E * 4);
+  const bool stats = want_route_stats(st);
+  MOE_HIP(moe::launch_router_scores(s.bf16, x, wr, s.T, s.d, s.E, z, stream), "router_scores");
+  MOE_HIP(moe::launch_router_select(z, bias, s.T, s.E, s.k, s.gate_all, idx, gates,
+                                    stats ? p_part : nullptr, stats ? c_part : nullptr, stream),
+          "router_select");
+  if (stats)
+    MOE_HIP(moe::launch_router_stats(p_part, c_part, s.nb_sel, s.T, s.E, alpha, st->f, st->P,
+                                     st->aux, stream),
+            "router_stats");
+  return MOE_OK;
+}
+
+moe_status do_permute(const Shape& s, const int32_t* idx, const void* x, int32_t* offsets,
+                      int32_t* dest, int32_t* src, void* x_perm, const moe_stats* st, void* ws,
+                      hipStream_t stream) {
+  Carver cv{static_cast<char*>(ws)};
+  int32_t* blk = cv.take<int32_t>(static_cast<size_t>(s.nb_idx + 1) * s.nkeys * 4);
+  int32_t* slot_base = cv.take<int32_t>(static_cast<size_t>(s.k) * s.E * 4);
+  int32_t* slot_keep = cv.take<int32_t>(static_cast<size_t>(s.k) * s.E * 4);
+  MOE_HIP(moe::launch_index(idx, s.T, s.k, s.E, s.C, blk, slot_base, slot_keep, offsets, dest, src,
+                            st ? st->counts : nullptr, st ? st->kept : nullptr,
+                            st ? st->n_dropped : nullptr, stream),
+          "index");
+  if (x_perm != nullptr)
+    MOE_HIP(moe::launch_gather_rows(s.elt, x, src, offsets, s.E, s.R, s.d, x_perm, stream),
+            "gather_rows");
+  return MOE_OK;
+}
+
+moe_status do_gateup(const Shape& s, const void* x, const int32_t* src, const int32_t* tiles,
+                     const void* w1, const void* w3, const void* ws1, const void* ws3, void* act,
+                     hipStream_t stream) {
+  moe::GemmTileMap map{tiles, s.max_tiles, 0};
+  moe::GateUpArgs a{x, src, w1, w3, static_cast<long long>(s.dff) * s.d, act, s.act_stride, 0,
+                    s.d, s.dff};
+  if (s.bf16) MOE_HIP(moe::launch_gemm_gateup_bf16(map, a, s.BM, stream), "gemm_gateup");
+  else MOE_HIP(moe::launch_gemm_gateup_f32(map, a, stream), "gemm_gateup");
+  if (s.nsh) {
+    moe::GemmTileMap m1{nullptr, 0, s.T};
+    moe::GateUpArgs b{x, nullptr, ws1, ws3, 0, act, s.act_stride, s.R, s.d, s.dffs};
+    const int bm = moe::gemm_tile_rows(1, s.T, s.n128);
+    if (s.bf16) MOE_HIP(moe::launch_gemm_gateup_bf16(m1, b, bm, stream), "gemm_gateup_shared");
+    else MOE_HIP(moe::launch_gemm_gateup_f32(m1, b, stream), "gemm_gateup_shared");
+  }
+  return MOE_OK;
+}
+
+moe_status do_down(const Shape& s, const void* act, const int32_t* tiles, const void* w2,
+                   const void* ws2, float* y_perm, hipStream_t stream) {
+  moe::GemmTileMap map{tiles, s.max_tiles, 0};
+  moe::DownArgs a{act, s.act_stride, 0, w2, static_cast<long long>(s.d) * s.dff, y_perm, 0, s.dff, s.d};
+  if (s.bf16) MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, stream), "gemm_down");
+  else MOE_HIP(moe::launch_gemm_down_f32(map, a, stream), "gemm_down");
+  if (s.nsh) {
+    moe::GemmTileMap m1{nullptr, 0, s.T};
+    moe::DownArgs b{act, s.act_stride, s.R, ws2, 0, y_perm, s.R, s.dffs, s.d};
+    const int bm = moe::gemm_tile_rows(1, s.T, s.n128);
+    if (s.bf16) MOE_HIP(moe::launch_gemm_down_bf16(m1, b, bm, stream), "gemm_down_shared");
+    else MOE_HIP(moe::launch_gemm_down_f32(m1, b, stream), "gemm_down_shared");
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_workspace_size(const moe_config* cfg, moe_stage stage, size_t* bytes) {
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  if (stage < MOE_STAGE_ROUTE || stage > MOE_STAGE_EXPERT_DOWN)
+    return fail(MOE_ERR_INVALID_ARG, "unknown stage %d", static_cast<int>(stage));
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  *bytes = stage_bytes(s, stage);
+  return MOE_OK;
+}
+
+int32_t moe_act_stride(const moe_config* cfg) {
+  Shape s;
+  if (validate(cfg, &s) != MOE_OK) return -1;
+  return s.act_stride;
+}
+
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
+                     const float* sel_bias, int32_t* idx, float* gates, const moe_stats* stats,
+                     void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  REQUIRE(x); REQUIRE(w_router); REQUIRE(idx); REQUIRE(gates);
+  st = check_ws(s, MOE_STAGE_ROUTE, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  return do_route(s, cfg->aux_alpha, x, w_router, sel_bias, idx, gates, stats, ws,
+                  static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_permute(const moe_config* cfg, const int32_t* idx, const void* x, int32_t* offsets,
+                       int32_t* dest, int32_t* src, void* x_perm, const moe_stats* stats, void* ws,
+                       size_t ws_bytes, void* stream) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  REQUIRE(idx); REQUIRE(offsets); REQUIRE(dest); REQUIRE(src);
+  if (x_perm != nullptr) { REQUIRE(x); REQUIRE(x_perm); }
+  st = check_ws(s, MOE_STAGE_PERMUTE, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  return do_permute(s, idx, x, offsets, dest, src, x_perm, stats, ws,
+                    static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_expert_gateup(const moe_config* cfg, const void* x, const int32_t* src,
+                             const int32_t* offsets, const void* w1, const void* w3,
+                             const void* ws1, const void* ws3, void* act, void* ws,
+                             size_t ws_bytes, void* stream) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  REQUIRE(x); REQUIRE(offsets); REQUIRE(w1); REQUIRE(w3); REQUIRE(act);
+  if (s.nsh) {
+    REQUIRE(ws1); REQUIRE(ws3);
+    if (src == nullptr) return fail(MOE_ERR_INVALID_ARG, "a shared expert needs src (x unpermuted)");
+  }
+  st = check_ws(s, MOE_STAGE_EXPERT_GATEUP, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  int32_t* tiles = static_cast<int32_t*>(ws);
+  MOE_HIP(moe::launch_tile_map(offsets, s.E, s.BM, s.max_tiles, tiles, strm), "tile_map");
+  return do_gateup(s, x, src, tiles, w1, w3, ws1, ws3, act, strm);
+}
+
+moe_status moe_expert_down(const moe_config* cfg, const void* act, const int32_t* offsets,
+                           const void* w2, const void* ws2, float* y_perm, void* ws,
+                           size_t ws_bytes, void* stream) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  REQUIRE(act); REQUIRE(offsets); REQUIRE(w2); REQUIRE(y_perm);
+  if (s.nsh) REQUIRE(ws2);
+  st = check_ws(s, MOE_STAGE_EXPERT_DOWN, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  int32_t* tiles = static_cast<int32_t*>(ws);
+  MOE_HIP(moe::launch_tile_map(offsets, s.E, s.BM, s.max_tiles, tiles, strm), "tile_map");
+  return do_down(s, act, tiles, w2, ws2, y_perm, strm);
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* src,
+                          const int32_t* offsets, const void* w1, const void* w3, const void* w2,
+                          const void* ws1, const void* ws3, const void* ws2, float* y_perm,
+                          void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  REQUIRE(x); REQUIRE(offsets); REQUIRE(w1); REQUIRE(w3); REQUIRE(w2); REQUIRE(y_perm);
+  if (s.nsh) {
+    REQUIRE(ws1); REQUIRE(ws3); REQUIRE(ws2);
+    if (src == nullptr) return fail(MOE_ERR_INVALID_ARG, "a shared expert needs src (x unpermuted)");
+  }
+  st = check_ws(s, MOE_STAGE_EXPERT_FFN, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  Carver cv{static_cast<char*>(ws)};
+  void* act = cv.take<char>(static_cast<size_t>(s.rows_total) * s.act_stride * s.elt);
+  int32_t* tiles = cv.take<int32_t>(static_cast<size_t>(s.max_tiles) * 16);
+  MOE_HIP(moe::launch_tile_map(offsets, s.E, s.BM, s.max_tiles, tiles, strm), "tile_map");
+  st = do_gateup(s, x, src, tiles, w1, w3, ws1, ws3, act, strm);
+  if (st != MOE_OK) return st;
+  return do_down(s, act, tiles, w2, ws2, y_perm, strm);
+}
+
+moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* dest,
+                       const float* gates, float* y, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  REQUIRE(y_perm); REQUIRE(dest); REQUIRE(gates); REQUIRE(y);
+  st = check_ws(s, MOE_STAGE_COMBINE, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  MOE_HIP(moe::launch_combine(y_perm, dest, gates, s.T, s.k, s.d, s.nsh ? s.R : -1, y,
+                              static_cast<hipStream_t>(stream)),
+          "combine");
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
+                       const float* sel_bias, const void* w1, const void* w3, const void* w2,
+                       const void* ws1, const void* ws3, const void* ws2, float* y,
+                       int32_t* idx_out, float* gates_out, const moe_stats* stats, void* ws,
+                       size_t ws_bytes, void* stream) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  REQUIRE(x); REQUIRE(w_router); REQUIRE(w1); REQUIRE(w3); REQUIRE(w2); REQUIRE(y);
+  if (s.nsh) { REQUIRE(ws1); REQUIRE(ws3); REQUIRE(ws2); }
+  if (idx_out != nullptr) REQUIRE(idx_out);
+  if (gates_out != nullptr) REQUIRE(gates_out);
+  st = check_ws(s, MOE_STAGE_FORWARD, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  Carver cv{static_cast<char*>(ws)};
+  const size_t R4 = static_cast<size_t>(s.R) * 4;
+  int32_t* idx = cv.take<int32_t>(R4);
+  float* gates = cv.take<float>(R4);
+  int32_t* dest = cv.take<int32_t>(R4);
+  int32_t* src = cv.take<int32_t>(R4);
+  int32_t* offsets = cv.take<int32_t>(static_cast<size_t>(s.E + 1) * 4);
+  float* y_perm = cv.take<float>(static_cast<size_t>(s.rows_total) * s.d * 4);
+  void* act = cv.take<char>(static_cast<size_t>(s.rows_total) * s.act_stride * s.elt);
+  void* scratch = cv.p;   // shared by the stages in turn (stream order)
+  if (idx_out) idx = idx_out;
+  if (gates_out) gates = gates_out;
+
+  st = do_route(s, cfg->aux_alpha, x, w_router, sel_bias, idx, gates, stats, scratch, strm);
+  if (st != MOE_OK) return st;
+  st = do_permute(s, idx, x, offsets, dest, src, nullptr, stats, scratch, strm);
+  if (st != MOE_OK) return st;
+  int32_t* tiles = static_cast<int32_t*>(scratch);
+  MOE_HIP(moe::launch_tile_map(offsets, s.E, s.BM, s.max_tiles, tiles, strm), "tile_map");
+  st = do_gateup(s, x, src, tiles, w1, w3, ws1, ws3, act, strm);
+  if (st != MOE_OK) return st;
+  st = do_down(s, act, tiles, w2, ws2, y_perm, strm);
+  if (st != MOE_OK) return st;
+  MOE_HIP(moe::launch_combine(y_perm, dest, gates, s.T, s.k, s.d, s.nsh ? s.R : -1, y, strm),
+          "combine");
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -107,12 +107,13 @@ def route(x, w_router, k: int, gate: str = GATE_SELECTED, bias=None):
     """Router scores, selection on z + b, gates on the unbiased z
     ([CME295] §4.2: the bias only changes which experts are chosen).
 
-    Returns dict(z, idx, margin, gates, probs)."""
+    Returns dict(z, s, idx, margin, gates, probs); s = z + b is the score the
+    selection ranks."""
     z = router_logits(x, w_router)
     s = z if bias is None else z + np.asarray(bias, np.float64)[None, :]
     idx, margin = select_topk(s, k)
     g = gates_selected(z, idx) if gate == GATE_SELECTED else gates_all(z, idx)
-    return dict(z=z, idx=idx, margin=margin, gates=g, probs=softmax(z))
+    return dict(z=z, s=s, idx=idx, margin=margin, gates=g, probs=softmax(z))
 
 
 # ------------------------------------------------------------------ stats
