@@ -35,9 +35,10 @@
  *     ([15-779] §3.3). Rows [offsets[E], T*k) are unused.
  *   - Expert outputs y_perm are fp32 [T*k + n_shared*T, d]; the shared expert's
  *     output for token t is row T*k + t. The layer output y[T, d] is fp32.
- *   - `ws` is caller-provided device scratch of at least the size that
- *     moe_workspace_size() returns for that entry point; its contents on entry
- *     do not matter and on return are undefined.
+ *   - `ws` is caller-provided device scratch, 256-byte aligned, of at least the
+ *     size that moe_workspace_size() returns for that entry point; its contents
+ *     on entry do not matter and on return are undefined. moe_combine uses no
+ *     scratch and accepts ws == NULL.
  *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *     asynchronously; the call never synchronises the host and never reads
  *     device data back.
