@@ -277,7 +277,7 @@ def cpu_baseline(wl, inp, host, sample):
     except Exception:
         cores = os.cpu_count() or 1
     if sample <= 0:
-        sample = {4096: 1024, 16384: 1024, 8192: 2048, 512: 512}.get(wl.T, min(wl.T, 32))
+        sample = {4096: 4096, 16384: 4096, 8192: 8192, 512: 512}.get(wl.T, min(wl.T, 32))
         if wl.E >= 64 and wl.k >= 8:
             sample = min(sample, 64)
     S = min(sample, wl.T)

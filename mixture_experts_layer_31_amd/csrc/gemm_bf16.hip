@@ -13,10 +13,15 @@
 // * v_mfma_f32_32x32x16_bf16 with the weight tile as the A operand and the
 //   token tile as B, so each lane's accumulators hold 4 consecutive output
 //   columns of one token row: the epilogue stores 8 (bf16) or 16 (fp32) bytes.
-// * BK = 64 tiles of both operands double-buffered in LDS with a 16-byte row
-//   pad (no bank conflicts for the 16-byte fragment reads); global loads of
-//   tile k+1 are in flight while tile k is multiplied.
-// * A device-side tile table (one entry per 128-row tile of each group) lets
+// * Large tiles (gemm_bf16_lds_kernel, 128 or 256 token rows): operands go
+//   straight from global memory into LDS with the 16-byte global->LDS loads of
+//   gfx950 (no staging registers, no LDS store instructions), double-buffered,
+//   into 128-byte LDS rows whose 16-byte chunks are XOR-swizzled by row so the
+//   MFMA fragment reads are free of bank conflicts. Eight waves per workgroup
+//   (two per SIMD) let one wave's LDS waits overlap the other's MFMAs.
+// * Small tiles (gemm_bf16_kernel, 32 token rows, decode-sized groups): the
+//   operands are staged through registers into padded LDS rows.
+// * A device-side tile table (one entry per BM-row tile of each group) lets
 //   one launch cover every group with no host sync; grid slots past the last
 //   real tile exit at once.
 // * Workgroups are dispatched round-robin over the 8 XCDs; the launch index is
@@ -208,6 +213,166 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------- large tiles
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// s_waitcnt with vmcnt = n and the other counters not waited on (gfx9 encoding)
+#define MOE_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+// 16 bytes per lane from global memory to LDS at lds_base + 16 * lane
+#define MOE_LDS_DMA16(g, l) __builtin_amdgcn_global_load_lds((g), (l), 16, 0, 0)
+#else
+#define MOE_WAIT_VMCNT(n) ((void)0)
+#define MOE_LDS_DMA16(g, l) ((void)(g), (void)(l))
+#endif
+
+constexpr int kRowBytes = 128;   // one LDS row holds 64 bf16 of K
+
+template <int BM, int BN, int WM, int WN, bool GATEUP>
+__global__ __launch_bounds__(64 * WM * WN)
+__attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_lds_kernel(
+    const int32_t* __restrict__ tiles, int max_tiles, int n_single, int n_logical,
+    const uint16_t* __restrict__ xa, const int32_t* __restrict__ src, int a_stride, int a_row0,
+    const uint16_t* __restrict__ w_a, const uint16_t* __restrict__ w_b, long long w_stride,
+    void* __restrict__ out, int out_stride, int out_row0, int K, int N) {
+  constexpr int NW = WM * WN;
+  constexpr int WR = GATEUP ? 2 * BN : BN;     // weight rows per tile
+  constexpr int XD = BM / 8 / NW;              // LDS-DMA instructions per wave per stage
+  constexpr int WD = WR / 8 / NW;
+  constexpr int MT = BM / WM / 32;             // 32-row blocks per wave
+  constexpr int NT = BN / WN / 32;             // 32-col output blocks per wave
+  constexpr int NTW = GATEUP ? 2 * NT : NT;
+  constexpr int XBYTES = BM * kRowBytes;
+  constexpr int STAGE = (BM + WR) * kRowBytes;
+  static_assert(XD * 8 * NW == BM && WD * 8 * NW == WR, "tile/wave mismatch");
+
+  extern __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[];
+
+  int m_tile, n_tile;
+  xcd_tile(n_logical, max_tiles, m_tile, n_tile);
+  if (m_tile < 0) return;
+  const TileCoord tc = lookup_tile(tiles, n_single, BM, m_tile);
+  if (tc.rows <= 0) return;
+  const int n0 = n_tile * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // DMA instruction i of this wave fills LDS rows 8*(i*NW + wave) .. +7 (1 KB);
+  // lane l writes row +l/8, physical chunk l%8, which holds logical K-chunk
+  // (l%8) ^ (l/8): the row's chunks are XOR-swizzled by the row index.
+  const int lrow8 = lane >> 3;
+  const int lchunk = (lane & 7) ^ lrow8;
+  const uint16_t* xg[XD];
+#pragma unroll
+  for (int i = 0; i < XD; ++i) {
+    const int r = 8 * (i * NW + wave) + lrow8;
+    int grow = tc.row0 + min(r, tc.rows - 1);
+    if (src != nullptr) grow = src[grow];
+    xg[i] = xa + (static_cast<size_t>(a_row0) + grow) * a_stride + lchunk * 8;
+  }
+  const uint16_t* wg[WD];
+  const size_t wbase = static_cast<size_t>(tc.group) * w_stride;
+#pragma unroll
+  for (int i = 0; i < WD; ++i) {
+    const int r = 8 * (i * NW + wave) + lrow8;
+    const uint16_t* wsrc = (!GATEUP || r < BN) ? w_a : w_b;
+    const int n = n0 + ((GATEUP && r >= BN) ? r - BN : r);
+    wg[i] = wsrc + wbase + static_cast<size_t>(n) * K + lchunk * 8;
+  }
+  auto dma = [&](int kt, int buf) {
+    const int ko = kt * kBK;
+    unsigned char* xs = lds_raw + buf * STAGE;
+    unsigned char* ws = xs + XBYTES;
+#pragma unroll
+    for (int i = 0; i < XD; ++i) MOE_LDS_DMA16(xg[i] + ko, xs + (i * NW + wave) * 1024);
+#pragma unroll
+    for (int i = 0; i < WD; ++i) MOE_LDS_DMA16(wg[i] + ko, ws + (i * NW + wave) * 1024);
+  };
+
+  f32x16 acc[MT][NTW];
+#pragma unroll
+  for (int a = 0; a < MT; ++a)
+#pragma unroll
+    for (int b = 0; b < NTW; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  // fragment reads: row lane%32 of a 32-row block, logical K-chunk 2*kk + lane/32
+  const int frow = lane & 31, fhi = lane >> 5;
+  int koff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) koff[kk] = frow * kRowBytes + (((2 * kk + fhi) ^ (frow & 7)) << 4);
+  const int xblk0 = wm * (BM / WM) * kRowBytes;
+  bf16x8 fa[4][NTW], fb[4][MT];
+  auto rfrag = [&](int buf, int kk) {
+    const unsigned char* xs = lds_raw + buf * STAGE;
+    const unsigned char* ws = xs + XBYTES;
+#pragma unroll
+    for (int b = 0; b < NTW; ++b) {
+      const int wrow = (b < NT) ? wn * (BN / WN) + b * 32 : BN + wn * (BN / WN) + (b - NT) * 32;
+      fa[kk][b] = *reinterpret_cast<const bf16x8*>(ws + wrow * kRowBytes + koff[kk]);
+    }
+#pragma unroll
+    for (int a = 0; a < MT; ++a)
+      fb[kk][a] = *reinterpret_cast<const bf16x8*>(xs + xblk0 + a * 32 * kRowBytes + koff[kk]);
+  };
+  auto mfmas = [&](int kk) {
+#pragma unroll
+    for (int a = 0; a < MT; ++a)
+#pragma unroll
+      for (int b = 0; b < NTW; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][b], fb[kk][a], acc[a][b], 0, 0, 0);
+  };
+
+  // one barrier per K-step: it publishes stage kt (every thread waited for its
+  // own LDS-DMA loads) and retires all reads of the buffer the next loads fill
+  const int nk = K / kBK;
+  dma(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    MOE_WAIT_VMCNT(0);
+    __syncthreads();
+    if (kt + 1 < nk) dma(kt + 1, cur ^ 1);
+    rfrag(cur, 0);
+    rfrag(cur, 1);
+    mfmas(0);
+    rfrag(cur, 2);
+    mfmas(1);
+    rfrag(cur, 3);
+    mfmas(2);
+    mfmas(3);
+  }
+
+#pragma unroll
+  for (int a = 0; a < MT; ++a) {
+    const int m = wm * (BM / WM) + a * 32 + frow;
+    if (m >= tc.rows) continue;
+    const size_t orow = static_cast<size_t>(out_row0) + tc.row0 + m;
+#pragma unroll
+    for (int b = 0; b < NT; ++b) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int n = n0 + wn * (BN / WN) + b * 32 + 8 * rq + 4 * fhi;
+        if (GATEUP) {
+          float h[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            h[q] = silu(acc[a][b][4 * rq + q]) * acc[a][NT + b][4 * rq + q];
+          u32x2 pk;
+          pk[0] = pack_bf16x2(h[0], h[1]);
+          pk[1] = pack_bf16x2(h[2], h[3]);
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow * out_stride + n) = pk;
+        } else {
+          f32x4 v;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = acc[a][b][4 * rq + q];
+          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow * out_stride + n) = v;
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- tile table
 
 __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restrict__ offsets,
@@ -235,9 +400,16 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
   for (int i = total + e; i < max_tiles; i += 1024) tiles[i] = make_int4(0, 0, 0, 0);
 }
 
-int gemm_tile_rows(int dtype_bf16, int R_max, bool n128_ok) {
+int gemm_tile_rows(int dtype_bf16, int R_max, int groups, bool n256_ok) {
   if (!dtype_bf16) return 64;
-  return (R_max >= 2048 && n128_ok) ? 128 : 32;
+  if (!n256_ok) return 32;
+  // average rows per non-empty group decides how tall a tile can be without
+  // mostly computing padding
+  const int g = groups < R_max ? groups : R_max;
+  const int avg = g > 0 ? R_max / g : 0;
+  if (avg >= 768) return 256;
+  if (avg >= 96) return 128;
+  return 32;
 }
 
 int gemm_max_tiles(int BM, int R_max, int E) {
@@ -254,14 +426,12 @@ hipError_t launch_tile_map(const int32_t* offsets, int E, int BM, int max_tiles,
 
 // ---------------------------------------------------------------- launchers
 
-template <int BM, int BN, int WM, int WN, bool GATEUP>
-static hipError_t run_bf16(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
-                           int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
-                           long long w_stride, void* out, int out_stride, int out_row0, int K,
-                           int N, hipStream_t s) {
-  constexpr int WR = GATEUP ? 2 * BN : BN;
-  const size_t lds = static_cast<size_t>(2) * (BM + WR) * kPitch * sizeof(uint16_t);
-  auto kern = gemm_bf16_kernel<BM, BN, WM, WN, GATEUP>;
+template <typename Kern>
+static hipError_t launch_tiled(Kern kern, int BM, int BN, int threads, size_t lds,
+                               const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
+                               int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
+                               long long w_stride, void* out, int out_stride, int out_row0, int K,
+                               int N, hipStream_t s) {
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -270,34 +440,69 @@ static hipError_t run_bf16(const GemmTileMap& map, const uint16_t* xa, const int
   const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + BM - 1) / BM;
   const long long n_logical = static_cast<long long>(m_tiles) * (N / BN);
   const long long grid = ((n_logical + 7) / 8) * 8;
-  kern<<<dim3(static_cast<unsigned>(grid)), dim3(64 * WM * WN), lds, s>>>(
+  kern<<<dim3(static_cast<unsigned>(grid)), dim3(threads), lds, s>>>(
       map.tiles, m_tiles, map.n_single, static_cast<int>(n_logical), xa, src, a_stride, a_row0,
       wa, wb, w_stride, out, out_stride, out_row0, K, N);
   return hipGetLastError();
 }
 
+// register-staged small tiles
+template <int BM, int BN, int WM, int WN, bool GATEUP>
+static hipError_t run_small(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
+                            int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
+                            long long w_stride, void* out, int out_stride, int out_row0, int K,
+                            int N, hipStream_t s) {
+  constexpr int WR = GATEUP ? 2 * BN : BN;
+  const size_t lds = static_cast<size_t>(2) * (BM + WR) * kPitch * sizeof(uint16_t);
+  return launch_tiled(gemm_bf16_kernel<BM, BN, WM, WN, GATEUP>, BM, BN, 64 * WM * WN, lds, map,
+                      xa, src, a_stride, a_row0, wa, wb, w_stride, out, out_stride, out_row0, K,
+                      N, s);
+}
+
+// LDS-DMA large tiles
+template <int BM, int BN, int WM, int WN, bool GATEUP>
+static hipError_t run_lds(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
+                          int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
+                          long long w_stride, void* out, int out_stride, int out_row0, int K,
+                          int N, hipStream_t s) {
+  constexpr int WR = GATEUP ? 2 * BN : BN;
+  const size_t lds = static_cast<size_t>(2) * (BM + WR) * kRowBytes;
+  return launch_tiled(gemm_bf16_lds_kernel<BM, BN, WM, WN, GATEUP>, BM, BN, 64 * WM * WN, lds,
+                      map, xa, src, a_stride, a_row0, wa, wb, w_stride, out, out_stride,
+                      out_row0, K, N, s);
+}
+
+// BM = 256 or 128 needs N % 256 == 0 (down) / N % 128 == 0 (gate/up); the
+// caller picks BM with gemm_tile_rows(), which checks that.
 hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, int BM,
                                    hipStream_t s) {
   const auto* x = static_cast<const uint16_t*>(a.x);
   const auto* w1 = static_cast<const uint16_t*>(a.w1);
   const auto* w3 = static_cast<const uint16_t*>(a.w3);
+  if (BM == 256)
+    return run_lds<256, 128, 2, 4, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
+                                         a.act_stride, a.out_row0, a.K, a.N, s);
   if (BM == 128)
-    return run_bf16<128, 128, 2, 2, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
-                                          a.act_stride, a.out_row0, a.K, a.N, s);
-  return run_bf16<32, 64, 1, 2, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
-                                      a.act_stride, a.out_row0, a.K, a.N, s);
+    return run_lds<128, 128, 2, 4, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
+                                         a.act_stride, a.out_row0, a.K, a.N, s);
+  return run_small<32, 64, 1, 2, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
+                                       a.act_stride, a.out_row0, a.K, a.N, s);
 }
 
 hipError_t launch_gemm_down_bf16(const GemmTileMap& map, const DownArgs& a, int BM,
                                  hipStream_t s) {
   const auto* act = static_cast<const uint16_t*>(a.act);
   const auto* w2 = static_cast<const uint16_t*>(a.w2);
+  if (BM == 256)
+    return run_lds<256, 256, 2, 4, false>(map, act, nullptr, a.act_stride, a.in_row0, w2,
+                                          nullptr, a.w_stride, a.y, a.N, a.out_row0, a.K, a.N,
+                                          s);
   if (BM == 128)
-    return run_bf16<128, 128, 2, 2, false>(map, act, nullptr, a.act_stride, a.in_row0, w2,
-                                           nullptr, a.w_stride, a.y, a.N, a.out_row0, a.K, a.N,
-                                           s);
-  return run_bf16<32, 64, 1, 2, false>(map, act, nullptr, a.act_stride, a.in_row0, w2, nullptr,
-                                       a.w_stride, a.y, a.N, a.out_row0, a.K, a.N, s);
+    return run_lds<128, 256, 2, 4, false>(map, act, nullptr, a.act_stride, a.in_row0, w2,
+                                          nullptr, a.w_stride, a.y, a.N, a.out_row0, a.K, a.N,
+                                          s);
+  return run_small<32, 64, 1, 2, false>(map, act, nullptr, a.act_stride, a.in_row0, w2, nullptr,
+                                        a.w_stride, a.y, a.N, a.out_row0, a.K, a.N, s);
 }
 
 }  // namespace moe

@@ -50,8 +50,9 @@ struct GemmTileMap {
   int n_single;
 };
 
-// BM of the grouped GEMMs; n128_ok: every GEMM N (d, d_ff, d_ff_shared) is a multiple of 128
-int gemm_tile_rows(int dtype_bf16, int R_max, bool n128_ok);
+// BM of the grouped GEMMs for R_max rows in `groups` groups; n256_ok: d is a
+// multiple of 256 and d_ff (and d_ff_shared) of 128, as the large tiles need
+int gemm_tile_rows(int dtype_bf16, int R_max, int groups, bool n256_ok);
 int gemm_max_tiles(int BM, int R_max, int E);
 hipError_t launch_tile_map(const int32_t* offsets, int E, int BM, int max_tiles,
                            int32_t* tiles, hipStream_t s);

@@ -46,7 +46,7 @@ struct Shape {
   int rows_total;       // R + n_shared*T
   int act_stride;
   int BM, max_tiles;
-  bool n128;            // every GEMM N is a multiple of 128
+  bool n256;            // d % 256 == 0 and d_ff, d_ff_shared % 128 == 0 (large tiles)
   int nb_sel, nb_idx, nkeys;
 };
 
@@ -97,8 +97,8 @@ moe_status validate(const moe_config* c, Shape* s) {
   if (s->nkeys > moe::kIndexMaxKeys)
     return fail(MOE_ERR_UNSUPPORTED, "capacity with E*k=%d > %d is not supported", s->nkeys,
                 moe::kIndexMaxKeys);
-  s->n128 = (s->d % 128 == 0) && (s->dff % 128 == 0) && (s->dffs % 128 == 0);
-  s->BM = moe::gemm_tile_rows(s->bf16, s->R, s->n128);
+  s->n256 = (s->d % 256 == 0) && (s->dff % 128 == 0) && (s->dffs % 128 == 0);
+  s->BM = moe::gemm_tile_rows(s->bf16, s->R, s->E, s->n256);
   s->max_tiles = moe::gemm_max_tiles(s->BM, s->R, s->E);
   s->nb_sel = moe::router_select_blocks(s->T);
   s->nb_idx = moe::index_blocks(s->T);
@@ -223,7 +223,7 @@ moe_status do_gateup(const Shape& s, const void* x, const int32_t* src, const in
   if (s.nsh) {
     moe::GemmTileMap m1{nullptr, 0, s.T};
     moe::GateUpArgs b{x, nullptr, ws1, ws3, 0, act, s.act_stride, s.R, s.d, s.dffs};
-    const int bm = moe::gemm_tile_rows(1, s.T, s.n128);
+    const int bm = moe::gemm_tile_rows(1, s.T, 1, s.n256);
     if (s.bf16) MOE_HIP(moe::launch_gemm_gateup_bf16(m1, b, bm, stream), "gemm_gateup_shared");
     else MOE_HIP(moe::launch_gemm_gateup_f32(m1, b, stream), "gemm_gateup_shared");
   }
@@ -239,7 +239,7 @@ moe_status do_down(const Shape& s, const void* act, const int32_t* tiles, const 
   if (s.nsh) {
     moe::GemmTileMap m1{nullptr, 0, s.T};
     moe::DownArgs b{act, s.act_stride, s.R, ws2, 0, y_perm, s.R, s.dffs, s.d};
-    const int bm = moe::gemm_tile_rows(1, s.T, s.n128);
+    const int bm = moe::gemm_tile_rows(1, s.T, 1, s.n256);
     if (s.bf16) MOE_HIP(moe::launch_gemm_down_bf16(m1, b, bm, stream), "gemm_down_shared");
     else MOE_HIP(moe::launch_gemm_down_f32(m1, b, stream), "gemm_down_shared");
   }
