@@ -373,6 +373,149 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
   }
 }
 
+// ---------------------------------------------------------------- decode tiles
+//
+// Groups of at most a few rows (decode): the time is reading the experts'
+// weights, which are streamed exactly once. A work item is 16 weight rows
+// (output columns) of one 16-row token tile; KS waves of a workgroup split
+// its K range and their partial sums are added in LDS in a fixed order. Each
+// wave walks its K range with v_mfma_f32_16x16x32_bf16: lane l loads 16 bytes
+// of weight row l%16 and 16 bytes of token row l%16, both at K-chunk l/16 of
+// the current 32-wide step, straight from global memory into registers (the
+// token rows are tiny and stay in cache). Batches of U steps are double-
+// buffered in registers, so the next batch's loads are in flight while the
+// current batch is multiplied. The accumulators then hold token l%16 and four
+// consecutive output columns 4*(l/16)..+3. Items with the same n-slice and
+// consecutive token tiles run in the same workgroup (KS < 4) so they share the
+// weight rows in cache.
+template <bool GATEUP, int U, int KS>
+__global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
+    const int32_t* __restrict__ tiles, int max_tiles, int n_single,
+    const uint16_t* __restrict__ xa, const int32_t* __restrict__ src, int a_stride, int a_row0,
+    const uint16_t* __restrict__ w_a, const uint16_t* __restrict__ w_b, long long w_stride,
+    void* __restrict__ out, int out_stride, int out_row0, int K, int N) {
+  typedef __attribute__((ext_vector_type(8))) __bf16 bf8;
+  constexpr int IPB = 4 / KS;                  // items per workgroup
+  __shared__ f32x4 red[KS > 1 ? 3 : 1][GATEUP ? 2 : 1][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kpart = wave % KS;
+  const long long item = static_cast<long long>(blockIdx.x) * IPB + wave / KS;
+  const int n_slices = N >> 4;
+  const bool live = item < static_cast<long long>(max_tiles) * n_slices;
+  const int m_tile = live ? static_cast<int>(item % max_tiles) : 0;
+  const int n0 = live ? static_cast<int>(item / max_tiles) * 16 : 0;
+  const TileCoord tc = lookup_tile(tiles, n_single, 16, m_tile);
+  const bool active = live && tc.rows > 0;
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+  const int r16 = lane & 15, ck = (lane >> 4) * 8;
+  if (active) {
+    int grow = tc.row0 + min(r16, tc.rows - 1);
+    if (src != nullptr) grow = src[grow];
+    const uint16_t* xp = xa + (static_cast<size_t>(a_row0) + grow) * a_stride + ck;
+    const size_t wrow = static_cast<size_t>(tc.group) * w_stride + static_cast<size_t>(n0 + r16) * K + ck;
+    const uint16_t* wp = w_a + wrow;
+    const uint16_t* wq = GATEUP ? w_b + wrow : nullptr;
+    // this wave's K range: whole 32-wide steps, split as evenly as possible
+    const int steps = K >> 5;
+    const int s_lo = steps * kpart / KS, s_hi = steps * (kpart + 1) / KS;
+    bf8 wv[2][U], xv[2][U], qv[2][U];
+    auto load = [&](int s0, int b) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = (s0 + u) << 5;
+        wv[b][u] = *reinterpret_cast<const bf8*>(wp + k);
+        if (GATEUP) qv[b][u] = *reinterpret_cast<const bf8*>(wq + k);
+        xv[b][u] = *reinterpret_cast<const bf8*>(xp + k);
+      }
+    };
+    auto comp = [&](int b) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[b][u], xv[b][u], acc, 0, 0, 0);
+        if (GATEUP) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qv[b][u], xv[b][u], acc2, 0, 0, 0);
+      }
+    };
+    const int nb = (s_hi - s_lo) / U;
+    if (nb > 0) {
+      load(s_lo, 0);
+      int i = 0;
+      for (; i + 2 <= nb; i += 2) {
+        load(s_lo + (i + 1) * U, 1);
+        comp(0);
+        if (i + 2 < nb) load(s_lo + (i + 2) * U, 0);
+        comp(1);
+      }
+      if (i < nb) comp(0);
+    }
+    for (int st = s_lo + nb * U; st < s_hi; ++st) {
+      const int k = st << 5;
+      const bf8 w1v = *reinterpret_cast<const bf8*>(wp + k);
+      const bf8 x1v = *reinterpret_cast<const bf8*>(xp + k);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1v, x1v, acc, 0, 0, 0);
+      if (GATEUP) {
+        const bf8 q1v = *reinterpret_cast<const bf8*>(wq + k);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q1v, x1v, acc2, 0, 0, 0);
+      }
+    }
+  }
+  if (KS > 1) {
+    // partial sums of waves 1..KS-1 of this item, added by wave 0 in wave order
+    const int slot = wave / KS;   // KS > 1 => IPB <= 2
+    if (kpart > 0) {
+      red[(kpart - 1) + slot * (KS - 1)][0][lane] = acc;
+      if (GATEUP) red[(kpart - 1) + slot * (KS - 1)][GATEUP ? 1 : 0][lane] = acc2;
+    }
+    __syncthreads();
+    if (kpart > 0) return;
+#pragma unroll
+    for (int p = 0; p < KS - 1; ++p) {
+      const f32x4 v = red[p + slot * (KS - 1)][0][lane];
+      acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
+      if (GATEUP) {
+        const f32x4 v2 = red[p + slot * (KS - 1)][GATEUP ? 1 : 0][lane];
+        acc2[0] += v2[0]; acc2[1] += v2[1]; acc2[2] += v2[2]; acc2[3] += v2[3];
+      }
+    }
+  }
+  if (!active || r16 >= tc.rows) return;
+  const size_t orow = static_cast<size_t>(out_row0) + tc.row0 + r16;
+  const int n = n0 + (lane >> 4) * 4;
+  if (GATEUP) {
+    u32x2 pk;
+    pk[0] = pack_bf16x2(silu(acc[0]) * acc2[0], silu(acc[1]) * acc2[1]);
+    pk[1] = pack_bf16x2(silu(acc[2]) * acc2[2], silu(acc[3]) * acc2[3]);
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow * out_stride + n) = pk;
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow * out_stride + n) = acc;
+  }
+}
+
+template <bool GATEUP>
+static hipError_t run_stream(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
+                             int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
+                             long long w_stride, void* out, int out_stride, int out_row0, int K,
+                             int N, hipStream_t s) {
+  const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + 15) / 16;
+  const long long items = static_cast<long long>(m_tiles) * (N / 16);
+  // real items (upper bound): split K when there are too few waves to keep
+  // enough weight bytes in flight across the 1024 SIMDs
+  if (items < 2048) {
+    gemm_bf16_stream_kernel<GATEUP, 8, 4><<<dim3(static_cast<unsigned>(items)), dim3(256), 0, s>>>(
+        map.tiles, m_tiles, map.n_single, xa, src, a_stride, a_row0, wa, wb, w_stride, out,
+        out_stride, out_row0, K, N);
+  } else if (items < 8192) {
+    gemm_bf16_stream_kernel<GATEUP, 8, 2><<<dim3(static_cast<unsigned>((items + 1) / 2)), dim3(256), 0, s>>>(
+        map.tiles, m_tiles, map.n_single, xa, src, a_stride, a_row0, wa, wb, w_stride, out,
+        out_stride, out_row0, K, N);
+  } else {
+    gemm_bf16_stream_kernel<GATEUP, 8, 1><<<dim3(static_cast<unsigned>((items + 3) / 4)), dim3(256), 0, s>>>(
+        map.tiles, m_tiles, map.n_single, xa, src, a_stride, a_row0, wa, wb, w_stride, out,
+        out_stride, out_row0, K, N);
+  }
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- tile table
 
 __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restrict__ offsets,
@@ -402,14 +545,14 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
 
 int gemm_tile_rows(int dtype_bf16, int R_max, int groups, bool n256_ok) {
   if (!dtype_bf16) return 64;
-  if (!n256_ok) return 32;
   // average rows per non-empty group decides how tall a tile can be without
   // mostly computing padding
   const int g = groups < R_max ? groups : R_max;
   const int avg = g > 0 ? R_max / g : 0;
+  if (avg <= 16) return 16;          // decode: stream the weights
+  if (!n256_ok || avg < 96) return 32;
   if (avg >= 768) return 256;
-  if (avg >= 96) return 128;
-  return 32;
+  return 128;
 }
 
 int gemm_max_tiles(int BM, int R_max, int E) {
@@ -485,6 +628,9 @@ hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, 
   if (BM == 128)
     return run_lds<128, 128, 2, 4, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
                                          a.act_stride, a.out_row0, a.K, a.N, s);
+  if (BM == 16)
+    return run_stream<true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act, a.act_stride,
+                            a.out_row0, a.K, a.N, s);
   return run_small<32, 64, 1, 2, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
                                        a.act_stride, a.out_row0, a.K, a.N, s);
 }
@@ -501,6 +647,9 @@ hipError_t launch_gemm_down_bf16(const GemmTileMap& map, const DownArgs& a, int 
     return run_lds<128, 256, 2, 4, false>(map, act, nullptr, a.act_stride, a.in_row0, w2,
                                           nullptr, a.w_stride, a.y, a.N, a.out_row0, a.K, a.N,
                                           s);
+  if (BM == 16)
+    return run_stream<false>(map, act, nullptr, a.act_stride, a.in_row0, w2, nullptr, a.w_stride,
+                             a.y, a.N, a.out_row0, a.K, a.N, s);
   return run_small<32, 64, 1, 2, false>(map, act, nullptr, a.act_stride, a.in_row0, w2, nullptr,
                                         a.w_stride, a.y, a.N, a.out_row0, a.K, a.N, s);
 }

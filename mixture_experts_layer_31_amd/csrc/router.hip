@@ -228,7 +228,8 @@ static hipError_t launch_scores_t(const void* x, const void* w, int T, int d, in
     const long items = static_cast<long>((T + TT - 1) / TT) * ((E + EC - 1) / EC);
     router_scores_kernel<Tin, TT, EC><<<dim3((items + 3) / 4), dim3(256), 0, s>>>(xp, wp, T, d, E, z);
   } else {
-    constexpr int TT = 1, EC = 16;
+    // few tokens: one wave per (token, expert) so the router rows stream in parallel
+    constexpr int TT = 1, EC = 1;
     const long items = static_cast<long>(T) * ((E + EC - 1) / EC);
     router_scores_kernel<Tin, TT, EC><<<dim3((items + 3) / 4), dim3(256), 0, s>>>(xp, wp, T, d, E, z);
   }

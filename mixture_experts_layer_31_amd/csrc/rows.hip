@@ -24,34 +24,34 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restric
 }
 
 // y[t] = sum_{j: dest[t,j] >= 0} gates[t,j] * y_perm[dest[t,j]] (+ y_perm[shared_row0 + t]),
-// summed in slot order. One workgroup per token, 4 floats per lane.
+// summed in slot order. Workgroup (t, c) covers 1024 columns of token t, 4 per lane.
 __global__ __launch_bounds__(256) void combine_kernel(const f32x4* __restrict__ yp,
                                                       const int32_t* __restrict__ dest,
                                                       const float* __restrict__ gates, int k,
                                                       int row_vecs, int shared_row0,
                                                       f32x4* __restrict__ y) {
   const int t = blockIdx.x;
+  const int v = blockIdx.y * 256 + threadIdx.x;
+  if (v >= row_vecs) return;
   const int32_t* dt = dest + static_cast<size_t>(t) * k;
   const float* gt = gates + static_cast<size_t>(t) * k;
-  for (int v = threadIdx.x; v < row_vecs; v += 256) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int r = dt[j];
-      if (r >= 0) {
-        const float g = gt[j];
-        const f32x4 a = yp[static_cast<size_t>(r) * row_vecs + v];
-        acc[0] = fmaf(g, a[0], acc[0]);
-        acc[1] = fmaf(g, a[1], acc[1]);
-        acc[2] = fmaf(g, a[2], acc[2]);
-        acc[3] = fmaf(g, a[3], acc[3]);
-      }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const int r = dt[j];
+    if (r >= 0) {
+      const float g = gt[j];
+      const f32x4 a = yp[static_cast<size_t>(r) * row_vecs + v];
+      acc[0] = fmaf(g, a[0], acc[0]);
+      acc[1] = fmaf(g, a[1], acc[1]);
+      acc[2] = fmaf(g, a[2], acc[2]);
+      acc[3] = fmaf(g, a[3], acc[3]);
     }
-    if (shared_row0 >= 0) {
-      const f32x4 a = yp[static_cast<size_t>(shared_row0 + t) * row_vecs + v];
-      acc[0] += a[0]; acc[1] += a[1]; acc[2] += a[2]; acc[3] += a[3];
-    }
-    y[static_cast<size_t>(t) * row_vecs + v] = acc;
   }
+  if (shared_row0 >= 0) {
+    const f32x4 a = yp[static_cast<size_t>(shared_row0 + t) * row_vecs + v];
+    acc[0] += a[0]; acc[1] += a[1]; acc[2] += a[2]; acc[3] += a[3];
+  }
+  y[static_cast<size_t>(t) * row_vecs + v] = acc;
 }
 
 hipError_t launch_gather_rows(int elt_bytes, const void* x, const int32_t* src,
@@ -67,7 +67,7 @@ hipError_t launch_gather_rows(int elt_bytes, const void* x, const int32_t* src,
 hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* gates, int T,
                           int k, int d, int shared_row0, float* y, hipStream_t s) {
   const int row_vecs = d / 4;
-  combine_kernel<<<dim3(T), dim3(256), 0, s>>>(reinterpret_cast<const f32x4*>(y_perm), dest,
+  combine_kernel<<<dim3(T, (row_vecs + 255) / 256), dim3(256), 0, s>>>(reinterpret_cast<const f32x4*>(y_perm), dest,
                                                gates, k, row_vecs, shared_row0,
                                                reinterpret_cast<f32x4*>(y));
   return hipGetLastError();
