@@ -52,17 +52,17 @@ def parse():
 
 
 def calibrate_copy():
-    """Plain device-to-device copies of a known size (1 GiB), so that rocprofv3's
-    FETCH_SIZE / WRITE_SIZE can be scaled to bytes."""
+    """A plain elementwise kernel of known traffic (reads 1 GiB, writes 1 GiB, five
+    launches), so that rocprofv3's FETCH_SIZE / WRITE_SIZE can be scaled to bytes."""
     import torch
-    n = 1 << 30
-    a = torch.empty(n, dtype=torch.uint8, device="cuda")
-    b = torch.empty(n, dtype=torch.uint8, device="cuda")
-    a.fill_(1)
+    n = 1 << 28                      # 2^28 fp32 = 1 GiB
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty(n, dtype=torch.float32, device="cuda")
     for _ in range(5):
-        b.copy_(a)
+        torch.add(a, 1.0, out=b)
     torch.cuda.synchronize()
-    print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
+    print(json.dumps({"calibration": "elementwise add", "bytes_read": 4 * n,
+                      "bytes_written": 4 * n, "launches": 5}))
 
 
 def kernel_source_hash():
