@@ -576,8 +576,7 @@ static hipError_t launch_tiled(Kern kern, int BM, int BN, int threads, size_t ld
                                long long w_stride, void* out, int out_stride, int out_row0, int K,
                                int N, hipStream_t s) {
   if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = allow_large_lds(reinterpret_cast<const void*>(kern), lds);
     if (e != hipSuccess) return e;
   }
   const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + BM - 1) / BM;

@@ -179,11 +179,9 @@ hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capac
   const int nkeys = index_keys(E, k, cap);
   const size_t lds = static_cast<size_t>(nkeys) * kWords * sizeof(uint32_t);
   if (lds > 65536) {
-    hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(index_count_kernel),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(index_rank_kernel),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e1 = allow_large_lds(reinterpret_cast<const void*>(index_count_kernel), lds);
     if (e1 != hipSuccess) return e1;
+    hipError_t e2 = allow_large_lds(reinterpret_cast<const void*>(index_rank_kernel), lds);
     if (e2 != hipSuccess) return e2;
   }
   index_count_kernel<<<dim3(nb), dim3(kTB), lds, s>>>(idx, T, k, E, cap ? 1 : 0, blk);

@@ -8,6 +8,10 @@
 
 namespace moe {
 
+// Raise a kernel's dynamic-LDS limit above 64 KiB, once per (kernel, device):
+// setting the attribute before every launch measurably slows the launches.
+hipError_t allow_large_lds(const void* kernel, size_t bytes);
+
 // ---- router (router.hip)
 constexpr int kSelectTokensPerBlock = 64;
 int router_select_blocks(int T);

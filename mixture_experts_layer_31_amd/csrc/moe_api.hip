@@ -5,7 +5,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <set>
 #include <string>
+#include <tuple>
 
 #include "kernels.h"
 #include "moe.h"
@@ -247,6 +250,25 @@ moe_status do_down(const Shape& s, const void* act, const int32_t* tiles, const 
 }
 
 }  // namespace
+
+namespace moe {
+
+hipError_t allow_large_lds(const void* kernel, size_t bytes) {
+  static std::mutex mu;
+  static std::set<std::tuple<const void*, int, size_t>> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_tuple(kernel, dev, bytes);
+  if (done.count(key)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(bytes));
+  if (e == hipSuccess) done.insert(key);
+  return e;
+}
+
+}  // namespace moe
 
 extern "C" {
 
