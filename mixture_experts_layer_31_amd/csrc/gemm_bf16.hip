@@ -27,6 +27,8 @@
 // * Workgroups are dispatched round-robin over the 8 XCDs; the launch index is
 //   remapped so each XCD works on a contiguous range of (n-tile, m-tile) pairs
 //   with m fastest, so the tiles that share a weight panel share an L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -221,12 +223,38 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(
   __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 // 16 bytes per lane from global memory to LDS at lds_base + 16 * lane
 #define MOE_LDS_DMA16(g, l) __builtin_amdgcn_global_load_lds((g), (l), 16, 0, 0)
+// keeps vector-memory instructions on their side of this point; every other
+// instruction kind may still be scheduled across it
+#define MOE_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0x78F)
 #else
+#define MOE_SCHED_FENCE() ((void)0)
 #define MOE_WAIT_VMCNT(n) ((void)0)
 #define MOE_LDS_DMA16(g, l) ((void)(g), (void)(l))
 #endif
 
 constexpr int kRowBytes = 128;   // one LDS row holds 64 bf16 of K
+
+// The next stage's LDS-DMA loads are spread over this many points of the
+// K-step instead of issued in one burst after the barrier: a burst of 1 KB
+// loads from every wave fills the CU's vector-memory queue, and the waves
+// then stall at their later loads instead of issuing MFMAs.
+#ifndef MOE_DMA_SLICES
+#define MOE_DMA_SLICES 2
+#endif
+constexpr int kDmaSlices = MOE_DMA_SLICES;
+static_assert(kDmaSlices == 1 || kDmaSlices == 2 || kDmaSlices == 4, "1, 2 or 4 slices");
+
+// f(integral_constant<int, min(n, N)>) for 0 <= n: a runtime count turned into
+// a compile-time one, so each count gets its own fully unrolled code.
+template <int N, class F>
+__device__ __forceinline__ void with_count(int n, F&& f) {
+  if constexpr (N == 0) {
+    f(std::integral_constant<int, 0>{});
+  } else {
+    if (n >= N) f(std::integral_constant<int, N>{});
+    else with_count<N - 1>(n, f);
+  }
+}
 
 template <int BM, int BN, int WM, int WN, bool GATEUP>
 __global__ __launch_bounds__(64 * WM * WN)
@@ -279,14 +307,26 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
     const int n = n0 + ((GATEUP && r >= BN) ? r - BN : r);
     wg[i] = wsrc + wbase + static_cast<size_t>(n) * K + lchunk * 8;
   }
-  auto dma = [&](int kt, int buf) {
+  // the stage's XD + WD LDS-DMA instructions, issued in slices: instruction j
+  // goes out in slice j * kDmaSlices / (XD + WD)
+  constexpr int ND = XD + WD;
+  auto dma_slice = [&](int kt, int buf, auto slice_c) {
+    constexpr int S = decltype(slice_c)::value;
     const int ko = kt * kBK;
     unsigned char* xs = lds_raw + buf * STAGE;
     unsigned char* ws = xs + XBYTES;
 #pragma unroll
-    for (int i = 0; i < XD; ++i) MOE_LDS_DMA16(xg[i] + ko, xs + (i * NW + wave) * 1024);
-#pragma unroll
-    for (int i = 0; i < WD; ++i) MOE_LDS_DMA16(wg[i] + ko, ws + (i * NW + wave) * 1024);
+    for (int j = 0; j < ND; ++j) {
+      if (j * kDmaSlices / ND != S) continue;
+      if (j < XD) MOE_LDS_DMA16(xg[j] + ko, xs + (j * NW + wave) * 1024);
+      else MOE_LDS_DMA16(wg[j - XD] + ko, ws + ((j - XD) * NW + wave) * 1024);
+    }
+  };
+  auto dma = [&](int kt, int buf) {
+    dma_slice(kt, buf, std::integral_constant<int, 0>{});
+    dma_slice(kt, buf, std::integral_constant<int, 1>{});
+    dma_slice(kt, buf, std::integral_constant<int, 2>{});
+    dma_slice(kt, buf, std::integral_constant<int, 3>{});
   };
 
   f32x16 acc[MT][NTW];
@@ -302,9 +342,11 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
   int koff[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) koff[kk] = frow * kRowBytes + (((2 * kk + fhi) ^ (frow & 7)) << 4);
-  const int xblk0 = wm * (BM / WM) * kRowBytes;
+  // token block a of wave row wm is the tile's 32-row block a*WM + wm: the
+  // blocks of a short (ragged-tail) tile are shared by all wave rows
   bf16x8 fa[4][NTW], fb[4][MT];
-  auto rfrag = [&](int buf, int kk) {
+  auto rfrag = [&](int buf, int kk, auto na_c) {
+    constexpr int NA = decltype(na_c)::value;
     const unsigned char* xs = lds_raw + buf * STAGE;
     const unsigned char* ws = xs + XBYTES;
 #pragma unroll
@@ -313,39 +355,55 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
       fa[kk][b] = *reinterpret_cast<const bf16x8*>(ws + wrow * kRowBytes + koff[kk]);
     }
 #pragma unroll
-    for (int a = 0; a < MT; ++a)
-      fb[kk][a] = *reinterpret_cast<const bf16x8*>(xs + xblk0 + a * 32 * kRowBytes + koff[kk]);
+    for (int a = 0; a < NA; ++a)
+      fb[kk][a] = *reinterpret_cast<const bf16x8*>(xs + (a * WM + wm) * 32 * kRowBytes + koff[kk]);
   };
-  auto mfmas = [&](int kk) {
+  auto mfmas = [&](int kk, auto na_c) {
+    constexpr int NA = decltype(na_c)::value;
 #pragma unroll
-    for (int a = 0; a < MT; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int b = 0; b < NTW; ++b)
         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][b], fb[kk][a], acc[a][b], 0, 0, 0);
   };
 
   // one barrier per K-step: it publishes stage kt (every thread waited for its
-  // own LDS-DMA loads) and retires all reads of the buffer the next loads fill
+  // own LDS-DMA loads) and retires all reads of the buffer the next loads fill.
+  // The loop is specialised on the number of this wave's token blocks that
+  // hold rows (NA): a full tile runs NA = MT, a ragged tail only the MFMAs of
+  // its rows, so it costs about its share of a full tile.
   const int nk = K / kBK;
-  dma(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    MOE_WAIT_VMCNT(0);
-    __syncthreads();
-    if (kt + 1 < nk) dma(kt + 1, cur ^ 1);
-    rfrag(cur, 0);
-    rfrag(cur, 1);
-    mfmas(0);
-    rfrag(cur, 2);
-    mfmas(1);
-    rfrag(cur, 3);
-    mfmas(2);
-    mfmas(3);
-  }
+  auto kloop = [&](auto na_c) {
+    dma(0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      MOE_WAIT_VMCNT(0);
+      __syncthreads();
+      const bool more = kt + 1 < nk;
+      if (more) dma_slice(kt + 1, cur ^ 1, std::integral_constant<int, 0>{});
+      MOE_SCHED_FENCE();
+      rfrag(cur, 0, na_c);
+      rfrag(cur, 1, na_c);
+      mfmas(0, na_c);
+      if (more && kDmaSlices > 1) dma_slice(kt + 1, cur ^ 1, std::integral_constant<int, 1>{});
+      MOE_SCHED_FENCE();
+      rfrag(cur, 2, na_c);
+      mfmas(1, na_c);
+      if (more && kDmaSlices > 2) dma_slice(kt + 1, cur ^ 1, std::integral_constant<int, 2>{});
+      MOE_SCHED_FENCE();
+      rfrag(cur, 3, na_c);
+      mfmas(2, na_c);
+      if (more && kDmaSlices > 3) dma_slice(kt + 1, cur ^ 1, std::integral_constant<int, 3>{});
+      MOE_SCHED_FENCE();
+      mfmas(3, na_c);
+    }
+  };
+  const int nb = (min(tc.rows, BM) + 31) / 32;
+  with_count<MT>((nb - wm + WM - 1) / WM, kloop);
 
 #pragma unroll
   for (int a = 0; a < MT; ++a) {
-    const int m = wm * (BM / WM) + a * 32 + frow;
+    const int m = (a * WM + wm) * 32 + frow;
     if (m >= tc.rows) continue;
     const size_t orow = static_cast<size_t>(out_row0) + tc.row0 + m;
 #pragma unroll
