@@ -13,7 +13,8 @@ namespace moe {
 hipError_t allow_large_lds(const void* kernel, size_t bytes);
 
 // ---- router (router.hip)
-constexpr int kSelectTokensPerBlock = 64;
+constexpr int kSelectMaxBlocks = 1024;
+int router_select_tokens(int T);   // tokens per router_select workgroup
 int router_select_blocks(int T);
 hipError_t launch_router_scores(int dtype_bf16, const void* x, const void* w, int T, int d, int E,
                                 float* z, hipStream_t s);
@@ -21,7 +22,7 @@ hipError_t launch_router_select(const float* z, const float* bias, int T, int E,
                                 int gate_all, int32_t* idx, float* gates, float* p_part,
                                 int32_t* c_part, hipStream_t s);
 hipError_t launch_router_stats(const float* p_part, const int32_t* c_part, int nblocks, int T,
-                               int E, float alpha, float* f, float* P, float* aux,
+                               int E, float alpha, float* f, float* P, float* aux, float* fp,
                                hipStream_t s);
 
 // ---- index: histogram, scan, rank (index.hip)

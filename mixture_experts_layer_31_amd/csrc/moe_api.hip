@@ -110,7 +110,8 @@ moe_status validate(const moe_config* c, Shape* s) {
 
 // workspace sizes per stage
 size_t route_bytes(const Shape& s) {
-  return al(static_cast<size_t>(s.T) * s.E * 4) + 2 * al(static_cast<size_t>(s.nb_sel) * s.E * 4);
+  return al(static_cast<size_t>(s.T) * s.E * 4) + 2 * al(static_cast<size_t>(s.nb_sel) * s.E * 4) +
+         al(static_cast<size_t>(s.E) * 4);
 }
 size_t permute_bytes(const Shape& s) {
   return al(static_cast<size_t>(s.nb_idx + 1) * s.nkeys * 4) + 2 * al(static_cast<size_t>(s.k) * s.E * 4);
@@ -186,6 +187,7 @@ moe_status do_route(const Shape& s, float alpha, const void* x, const void* wr, 
   float* z = cv.take<float>(static_cast<size_t>(s.T) * s.E * 4);
   float* p_part = cv.take<float>(static_cast<size_t>(s.nb_sel) * s.E * 4);
   int32_t* c_part = cv.take<int32_t>(static_cast<size_t>(s.nb_sel) * s.E * 4);
+  float* fp = cv.take<float>(static_cast<size_t>(s.E) * 4);
   const bool stats = want_route_stats(st);
   MOE_HIP(moe::launch_router_scores(s.bf16, x, wr, s.T, s.d, s.E, z, stream), "router_scores");
   MOE_HIP(moe::launch_router_select(z, bias, s.T, s.E, s.k, s.gate_all, idx, gates,
@@ -193,7 +195,7 @@ moe_status do_route(const Shape& s, float alpha, const void* x, const void* wr, 
           "router_select");
   if (stats)
     MOE_HIP(moe::launch_router_stats(p_part, c_part, s.nb_sel, s.T, s.E, alpha, st->f, st->P,
-                                     st->aux, stream),
+                                     st->aux, fp, stream),
             "router_stats");
   return MOE_OK;
 }

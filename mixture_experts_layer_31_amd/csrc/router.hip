@@ -12,21 +12,50 @@ namespace moe {
 
 // ---------------------------------------------------------------- scores
 //
-// One wave computes z for TT tokens x EC experts. Lanes split d into chunks of 8
-// consecutive elements (chunk c handled by lane c % 64), so the loads of one
-// row are coalesced across the wave; each lane accumulates its chunks in order
-// and a fixed butterfly sums the 64 lane partials. The tree keeps the fp32
-// rounding error of z near log2(64) roundings of the total instead of d/8.
+// Reduce-scatter over a wave: at mask M a lane keeps the upper half of its N
+// remaining values if lane & M, else the lower half, and adds its partner's
+// copy of that half; once one value is left the remaining masks are plain
+// butterfly sums. Lane l ends with the wave's sum of value l / (64 / N0).
+template <int M, int N, int NV>
+__device__ __forceinline__ void reduce_scatter(float (&v)[NV], int lane) {
+  if constexpr (M >= 1) {
+    if constexpr (N > 1) {
+      constexpr int H = N / 2;
+      const bool up = (lane & M) != 0;
+#pragma unroll
+      for (int q = 0; q < H; ++q) {
+        const float send = up ? v[q] : v[q + H];
+        const float keep = up ? v[q + H] : v[q];
+        v[q] = keep + __shfl_xor(send, M, 64);
+      }
+      reduce_scatter<M / 2, H>(v, lane);
+    } else {
+      v[0] += __shfl_xor(v[0], M, 64);
+      reduce_scatter<M / 2, 1>(v, lane);
+    }
+  }
+}
+
+//
+// A workgroup computes z for TT tokens x EC experts (TT * EC = NV values). Its
+// 256 threads split d into chunks of 8 consecutive elements (chunk c handled by
+// thread c % 256), so every load of a row is coalesced across the workgroup and
+// the grid holds ceil(T / TT) * ceil(E / EC) workgroups. Each thread accumulates
+// its chunks in order; a reduce-scatter butterfly then leaves every lane of a
+// wave with the wave's sum of one value (log2(64) shuffle steps in all instead
+// of NV full reductions), and the four waves' sums are added in wave order.
+// Every summation order is fixed, so z is bitwise reproducible.
 template <typename Tin, int TT, int EC>
 __global__ __launch_bounds__(256) void router_scores_kernel(
     const Tin* __restrict__ x, const Tin* __restrict__ w, int T, int d, int E,
     float* __restrict__ z) {
-  const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int NV = TT * EC;
+  static_assert(NV >= 1 && NV <= 64 && (NV & (NV - 1)) == 0, "NV must be a power of 2 <= 64");
+  constexpr int REP = 64 / NV;                 // lanes that end up holding the same value
+  __shared__ float part[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n_ec = (E + EC - 1) / EC;
-  const int n_tg = (T + TT - 1) / TT;
-  if (wave >= n_ec * n_tg) return;
-  const int tg = wave / n_ec, ec = wave % n_ec;
+  const int tg = blockIdx.x / n_ec, ec = blockIdx.x % n_ec;
   const int t0 = tg * TT, e0 = ec * EC;
 
   const Tin* xr[TT];
@@ -36,41 +65,40 @@ __global__ __launch_bounds__(256) void router_scores_kernel(
 #pragma unroll
   for (int j = 0; j < EC; ++j) wr[j] = w + static_cast<size_t>(min(e0 + j, E - 1)) * d;
 
-  float acc[TT][EC];
+  float v[NV];
 #pragma unroll
-  for (int i = 0; i < TT; ++i)
-#pragma unroll
-    for (int j = 0; j < EC; ++j) acc[i][j] = 0.f;
-
+  for (int q = 0; q < NV; ++q) v[q] = 0.f;
   const int nchunk = d >> 3;
-  for (int c = lane; c < nchunk; c += 64) {
+  for (int c = tid; c < nchunk; c += 256) {
     float xv[TT][8];
 #pragma unroll
     for (int i = 0; i < TT; ++i) Elt<Tin>::load8(xr[i] + c * 8, xv[i]);
 #pragma unroll
     for (int j = 0; j < EC; ++j) {
-      float wv[8];
-      Elt<Tin>::load8(wr[j] + c * 8, wv);
+      float wv8[8];
+      Elt<Tin>::load8(wr[j] + c * 8, wv8);
 #pragma unroll
       for (int i = 0; i < TT; ++i)
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[i][j] = fmaf(xv[i][q], wv[q], acc[i][j]);
+        for (int q = 0; q < 8; ++q) v[i * EC + j] = fmaf(xv[i][q], wv8[q], v[i * EC + j]);
     }
   }
-#pragma unroll
-  for (int i = 0; i < TT; ++i)
-#pragma unroll
-    for (int j = 0; j < EC; ++j) {
-      const float s = wave_allsum(acc[i][j]);
-      const int p = i * EC + j;
-      if ((p & 63) == lane && t0 + i < T && e0 + j < E)
-        z[static_cast<size_t>(t0 + i) * E + e0 + j] = s;
-    }
+
+  reduce_scatter<32, NV>(v, lane);
+  part[wv][lane] = v[0];
+  __syncthreads();
+  if (wv == 0 && lane % REP == 0) {
+    const int p = lane / REP, i = p / EC, j = p % EC;
+    if (t0 + i < T && e0 + j < E)
+      z[static_cast<size_t>(t0 + i) * E + e0 + j] =
+          ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+  }
 }
 
 // ---------------------------------------------------------------- selection
 //
 // One wave per token at a time; lane l owns experts l, l+64, ... (NE per lane).
+// A workgroup covers router_select_tokens(T) consecutive tokens (4 waves).
 // Top-k is k rounds of a wave argmax on (score desc, index asc). The full
 // softmax (for the ALL gate and for P_i) is computed on every token. Per-wave
 // sums of p_{t,e} and of the selection counts run in token order and are then
@@ -186,34 +214,55 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   }
 }
 
-// Sum the per-block partials in block order and form f, P and the balance loss
-// L_aux = alpha * E * sum_i f_i P_i (CME295 notes §3.2).
+// f_i and P_i (CME295 notes §3.2): workgroup e sums column e of the per-block
+// partials, thread j taking blocks j, j + 256, ... in order and a fixed tree
+// adding the 256 thread sums, so the result does not depend on scheduling.
+// fp[e] = f_e * P_e feeds the balance loss.
 __global__ __launch_bounds__(256) void router_stats_kernel(
     const float* __restrict__ p_part, const int32_t* __restrict__ c_part, int nblocks,
-    int T, int E, float alpha, float* __restrict__ f_out, float* __restrict__ P_out,
-    float* __restrict__ aux_out) {
-  __shared__ float red[256];
-  float local = 0.f;
-  const float invT = 1.0f / static_cast<float>(T);
-  for (int e = threadIdx.x; e < E; e += 256) {
-    float p = 0.f;
-    int c = 0;
-    for (int b = 0; b < nblocks; ++b) {
-      p += p_part[static_cast<size_t>(b) * E + e];
-      c += c_part[static_cast<size_t>(b) * E + e];
-    }
-    const float P = p * invT, f = static_cast<float>(c) * invT;
-    if (P_out) P_out[e] = P;
-    if (f_out) f_out[e] = f;
-    local += f * P;
+    int T, int E, float* __restrict__ f_out, float* __restrict__ P_out,
+    float* __restrict__ fp) {
+  __shared__ float rp[256];
+  __shared__ int rc[256];
+  const int e = blockIdx.x;
+  float p = 0.f;
+  int c = 0;
+  for (int b = threadIdx.x; b < nblocks; b += 256) {
+    p += p_part[static_cast<size_t>(b) * E + e];
+    c += c_part[static_cast<size_t>(b) * E + e];
   }
-  red[threadIdx.x] = local;
+  rp[threadIdx.x] = p;
+  rc[threadIdx.x] = c;
   __syncthreads();
-  for (int s = 128; s >= 1; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+  for (int h = 128; h >= 1; h >>= 1) {
+    if (threadIdx.x < h) {
+      rp[threadIdx.x] += rp[threadIdx.x + h];
+      rc[threadIdx.x] += rc[threadIdx.x + h];
+    }
     __syncthreads();
   }
-  if (threadIdx.x == 0 && aux_out) aux_out[0] = alpha * static_cast<float>(E) * red[0];
+  if (threadIdx.x == 0) {
+    const float invT = 1.0f / static_cast<float>(T);
+    const float P = rp[0] * invT, f = static_cast<float>(rc[0]) * invT;
+    if (P_out) P_out[e] = P;
+    if (f_out) f_out[e] = f;
+    fp[e] = f * P;
+  }
+}
+
+// L_aux = alpha * E * sum_i f_i P_i, the sum in a fixed order (CME295 notes §3.2).
+__global__ __launch_bounds__(256) void router_aux_kernel(const float* __restrict__ fp, int E,
+                                                         float alpha, float* __restrict__ aux) {
+  __shared__ float red[256];
+  float local = 0.f;
+  for (int e = threadIdx.x; e < E; e += 256) local += fp[e];
+  red[threadIdx.x] = local;
+  __syncthreads();
+  for (int h = 128; h >= 1; h >>= 1) {
+    if (threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) aux[0] = alpha * static_cast<float>(E) * red[0];
 }
 
 // ---------------------------------------------------------------- launchers
@@ -223,15 +272,15 @@ static hipError_t launch_scores_t(const void* x, const void* w, int T, int d, in
                                   hipStream_t s) {
   const Tin* xp = static_cast<const Tin*>(x);
   const Tin* wp = static_cast<const Tin*>(w);
+  constexpr int EC = 8;
+  const long n_ec = (E + EC - 1) / EC;
   if (T >= 8) {
-    constexpr int TT = 8, EC = 8;
-    const long items = static_cast<long>((T + TT - 1) / TT) * ((E + EC - 1) / EC);
-    router_scores_kernel<Tin, TT, EC><<<dim3((items + 3) / 4), dim3(256), 0, s>>>(xp, wp, T, d, E, z);
+    constexpr int TT = 8;
+    const long blocks = static_cast<long>((T + TT - 1) / TT) * n_ec;
+    router_scores_kernel<Tin, TT, EC><<<dim3(blocks), dim3(256), 0, s>>>(xp, wp, T, d, E, z);
   } else {
-    // few tokens: one wave per (token, expert) so the router rows stream in parallel
-    constexpr int TT = 1, EC = 1;
-    const long items = static_cast<long>(T) * ((E + EC - 1) / EC);
-    router_scores_kernel<Tin, TT, EC><<<dim3((items + 3) / 4), dim3(256), 0, s>>>(xp, wp, T, d, E, z);
+    const long blocks = static_cast<long>(T) * n_ec;
+    router_scores_kernel<Tin, 1, EC><<<dim3(blocks), dim3(256), 0, s>>>(xp, wp, T, d, E, z);
   }
   return hipGetLastError();
 }
@@ -242,17 +291,28 @@ hipError_t launch_router_scores(int dtype_bf16, const void* x, const void* w, in
                     : launch_scores_t<float>(x, w, T, d, E, z, s);
 }
 
-int router_select_blocks(int T) { return (T + kSelectTokensPerBlock - 1) / kSelectTokensPerBlock; }
+// 4 tokens per workgroup (one per wave) while that keeps the grid at <= 1024
+// workgroups, else a multiple of 4 that does
+int router_select_tokens(int T) {
+  const int per_wave = (((T + 3) / 4) + kSelectMaxBlocks - 1) / kSelectMaxBlocks;
+  return 4 * (per_wave > 1 ? per_wave : 1);
+}
+
+int router_select_blocks(int T) {
+  const int tpb = router_select_tokens(T);
+  return (T + tpb - 1) / tpb;
+}
 
 hipError_t launch_router_select(const float* z, const float* bias, int T, int E, int k,
                                 int gate_all, int32_t* idx, float* gates, float* p_part,
                                 int32_t* c_part, hipStream_t s) {
   const int nb = router_select_blocks(T);
+  const int tpb = router_select_tokens(T);
   const size_t lds = static_cast<size_t>(8) * E * sizeof(float);
   const int ne = (E + 63) / 64;
 #define MOE_SEL(NE_)                                                                       \
   router_select_kernel<NE_><<<dim3(nb), dim3(256), lds, s>>>(z, bias, T, E, k, gate_all,   \
-                                                             kSelectTokensPerBlock, idx,   \
+                                                             tpb, idx,                     \
                                                              gates, p_part, c_part)
   if (ne <= 1) MOE_SEL(1);
   else if (ne <= 2) MOE_SEL(2);
@@ -263,10 +323,10 @@ hipError_t launch_router_select(const float* z, const float* bias, int T, int E,
 }
 
 hipError_t launch_router_stats(const float* p_part, const int32_t* c_part, int nblocks, int T,
-                               int E, float alpha, float* f, float* P, float* aux,
+                               int E, float alpha, float* f, float* P, float* aux, float* fp,
                                hipStream_t s) {
-  router_stats_kernel<<<dim3(1), dim3(256), 0, s>>>(p_part, c_part, nblocks, T, E, alpha, f, P,
-                                                   aux);
+  router_stats_kernel<<<dim3(E), dim3(256), 0, s>>>(p_part, c_part, nblocks, T, E, f, P, fp);
+  if (aux != nullptr) router_aux_kernel<<<dim3(1), dim3(256), 0, s>>>(fp, E, alpha, aux);
   return hipGetLastError();
 }
 
