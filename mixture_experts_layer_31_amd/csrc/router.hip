@@ -95,6 +95,63 @@ __global__ __launch_bounds__(256) void router_scores_kernel(
   }
 }
 
+// bf16 inputs: z on the matrix cores. A workgroup covers 16 tokens x 16
+// experts with v_mfma_f32_16x16x32_bf16 (A = 16 token rows, B = 16 router
+// rows, both 32 elements of d per step); wave w takes the K-steps w, w+4, ...
+// in order, and the four waves' 16x16 partial sums are added in wave order,
+// so z is bitwise reproducible. Lane l loads 16 bytes of token row l%16 and of
+// router row l%16 at K-offset 8*(l/16) of the step and ends holding expert
+// l%16 of tokens 4*(l/16) .. +3. Products of bf16 values are exact in fp32;
+// sums are fp32. Out-of-range tokens and experts read a clamped row and are
+// not written.
+constexpr int kScoreWaves = 16;
+__global__ __launch_bounds__(64 * kScoreWaves) void router_scores_mfma_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T, int d, int E,
+    float* __restrict__ z) {
+  __shared__ f32x4 part[kScoreWaves][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n_ec = (E + 15) / 16;
+  const int t0 = (blockIdx.x / n_ec) * 16, e0 = (blockIdx.x % n_ec) * 16;
+  const int r = lane & 15, q = lane >> 4;
+  const uint16_t* xp = x + static_cast<size_t>(min(t0 + r, T - 1)) * d + q * 8;
+  const uint16_t* wp = w + static_cast<size_t>(min(e0 + r, E - 1)) * d + q * 8;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int nsteps = d / 32;
+  // wave w takes the step pairs (2j, 2j + 1) for j = w, w + NW, ... (a pair
+  // covers 128 bytes of each row); U steps are loaded per batch, steps past the
+  // end read as zeros, which add nothing
+  constexpr int U = 8, NW = kScoreWaves;
+  const bf16x8 zero = {};
+  for (int base = 2 * wv; base < nsteps; base += NW * U) {
+    bf16x8 a[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int stp = base + 2 * NW * (u >> 1) + (u & 1);
+      const bool ok = stp < nsteps;
+      a[u] = ok ? *reinterpret_cast<const bf16x8*>(xp + stp * 32) : zero;
+      b[u] = ok ? *reinterpret_cast<const bf16x8*>(wp + stp * 32) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u], acc, 0, 0, 0);
+  }
+  part[wv][lane] = acc;
+  __syncthreads();
+  if (wv != 0) return;
+  f32x4 tot = part[0][lane];
+#pragma unroll
+  for (int w2 = 1; w2 < kScoreWaves; ++w2) {
+    const f32x4 o = part[w2][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tot[i] += o[i];
+  }
+  const int e = e0 + r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 4 * q + i;
+    if (t < T && e < E) z[static_cast<size_t>(t) * E + e] = tot[i];
+  }
+}
+
 // ---------------------------------------------------------------- selection
 //
 // One wave per token at a time; lane l owns experts l, l+64, ... (NE per lane).
@@ -287,8 +344,13 @@ static hipError_t launch_scores_t(const void* x, const void* w, int T, int d, in
 
 hipError_t launch_router_scores(int dtype_bf16, const void* x, const void* w, int T, int d, int E,
                                 float* z, hipStream_t s) {
-  return dtype_bf16 ? launch_scores_t<uint16_t>(x, w, T, d, E, z, s)
-                    : launch_scores_t<float>(x, w, T, d, E, z, s);
+  if (dtype_bf16) {
+    const long blocks = static_cast<long>((T + 15) / 16) * ((E + 15) / 16);
+    router_scores_mfma_kernel<<<dim3(blocks), dim3(64 * kScoreWaves), 0, s>>>(
+        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), T, d, E, z);
+    return hipGetLastError();
+  }
+  return launch_scores_t<float>(x, w, T, d, E, z, s);
 }
 
 // 4 tokens per workgroup (one per wave) while that keeps the grid at <= 1024
