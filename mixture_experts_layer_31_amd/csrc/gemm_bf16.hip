@@ -13,7 +13,7 @@
 // * v_mfma_f32_32x32x16_bf16 with the weight tile as the A operand and the
 //   token tile as B, so each lane's accumulators hold 4 consecutive output
 //   columns of one token row: the epilogue stores 8 (bf16) or 16 (fp32) bytes.
-// * Large tiles (gemm_bf16_lds_kernel, 128 or 256 token rows): operands go
+// * Large tiles (gemm_bf16_lds_kernel, 256 token rows): operands go
 //   straight from global memory into LDS with the 16-byte global->LDS loads of
 //   gfx950 (no staging registers, no LDS store instructions), double-buffered,
 //   into 128-byte LDS rows whose 16-byte chunks are XOR-swizzled by row so the
@@ -223,16 +223,30 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(
   __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 // 16 bytes per lane from global memory to LDS at lds_base + 16 * lane
 #define MOE_LDS_DMA16(g, l) __builtin_amdgcn_global_load_lds((g), (l), 16, 0, 0)
+// s_waitcnt vmcnt(n) for a wave-uniform n <= N (the count is an immediate)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_at_most(int n) {
+  if constexpr (N == 0) {
+    MOE_WAIT_VMCNT(0);
+  } else {
+    if (n >= N) MOE_WAIT_VMCNT(N);
+    else wait_vmcnt_at_most<N - 1>(n);
+  }
+}
 // keeps vector-memory instructions on their side of this point; every other
 // instruction kind may still be scheduled across it
 #define MOE_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0x78F)
 #else
 #define MOE_SCHED_FENCE() ((void)0)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_at_most(int) {}
 #define MOE_WAIT_VMCNT(n) ((void)0)
 #define MOE_LDS_DMA16(g, l) ((void)(g), (void)(l))
 #endif
 
 constexpr int kRowBytes = 128;   // one LDS row holds 64 bf16 of K
+constexpr size_t kMaxLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
+constexpr int kNumCUs = 256;                    // MI355X
 
 // The next stage's LDS-DMA loads are spread over this many points of the
 // K-step instead of issued in one burst after the barrier: a burst of 1 KB
@@ -243,6 +257,11 @@ constexpr int kRowBytes = 128;   // one LDS row holds 64 bf16 of K
 #endif
 constexpr int kDmaSlices = MOE_DMA_SLICES;
 static_assert(kDmaSlices == 1 || kDmaSlices == 2 || kDmaSlices == 4, "1, 2 or 4 slices");
+#ifndef MOE_DMA_SLICES3
+#define MOE_DMA_SLICES3 4
+#endif
+constexpr int kDmaSlices3 = MOE_DMA_SLICES3;   // with three LDS stages
+static_assert(kDmaSlices3 == 1 || kDmaSlices3 == 2 || kDmaSlices3 == 4, "1, 2 or 4 slices");
 
 // f(integral_constant<int, min(n, N)>) for 0 <= n: a runtime count turned into
 // a compile-time one, so each count gets its own fully unrolled code.
@@ -256,7 +275,7 @@ __device__ __forceinline__ void with_count(int n, F&& f) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool GATEUP>
+template <int BM, int BN, int WM, int WN, bool GATEUP, int ST>
 __global__ __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_lds_kernel(
     const int32_t* __restrict__ tiles, int max_tiles, int n_single, int n_logical,
@@ -273,6 +292,11 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
   constexpr int XBYTES = BM * kRowBytes;
   constexpr int STAGE = (BM + WR) * kRowBytes;
   static_assert(XD * 8 * NW == BM && WD * 8 * NW == WR, "tile/wave mismatch");
+  static_assert(ST == 2 || ST == 3, "two or three LDS stages");
+  // a stage's loads go out in SL slices over the K-step that precedes its use
+  // by ST - 1 steps (with three stages every slice still has a full step of
+  // latency to hide)
+  constexpr int SL = ST == 3 ? kDmaSlices3 : kDmaSlices;
 
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[];
 
@@ -317,9 +341,13 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
     unsigned char* ws = xs + XBYTES;
 #pragma unroll
     for (int j = 0; j < ND; ++j) {
-      if (j * kDmaSlices / ND != S) continue;
-      if (j < XD) MOE_LDS_DMA16(xg[j] + ko, xs + (j * NW + wave) * 1024);
-      else MOE_LDS_DMA16(wg[j - XD] + ko, ws + ((j - XD) * NW + wave) * 1024);
+      if (j * SL / ND != S) continue;
+      if (j < XD) {
+        // token rows past the tile's last row are never stored: skip their loads
+        if (8 * (j * NW + wave) < tc.rows) MOE_LDS_DMA16(xg[j] + ko, xs + (j * NW + wave) * 1024);
+      } else {
+        MOE_LDS_DMA16(wg[j - XD] + ko, ws + ((j - XD) * NW + wave) * 1024);
+      }
     }
   };
   auto dma = [&](int kt, int buf) {
@@ -368,34 +396,45 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
   };
 
   // one barrier per K-step: it publishes stage kt (every thread waited for its
-  // own LDS-DMA loads) and retires all reads of the buffer the next loads fill.
+  // own LDS-DMA loads of that stage) and retires all reads of the buffer that
+  // this step's loads fill, stage kt + ST - 1 (ST buffers in rotation).
   // The loop is specialised on the number of this wave's token blocks that
   // hold rows (NA): a full tile runs NA = MT, a ragged tail only the MFMAs of
   // its rows, so it costs about its share of a full tile.
   const int nk = K / kBK;
+  int nd_stage = WD;                 // LDS-DMA instructions this wave issues per stage
+#pragma unroll
+  for (int j = 0; j < XD; ++j) nd_stage += 8 * (j * NW + wave) < tc.rows ? 1 : 0;
   auto kloop = [&](auto na_c) {
     dma(0, 0);
+    if (ST == 3 && nk > 1) dma(1, 1);
+    int cur = 0;
     for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      MOE_WAIT_VMCNT(0);
+      // loads complete in issue order: stage kt has landed once no more than
+      // the next stage's nd_stage loads are outstanding
+      if (ST == 3 && kt + 1 < nk) wait_vmcnt_at_most<ND>(nd_stage);
+      else MOE_WAIT_VMCNT(0);
       __syncthreads();
-      const bool more = kt + 1 < nk;
-      if (more) dma_slice(kt + 1, cur ^ 1, std::integral_constant<int, 0>{});
+      const int ahead = kt + ST - 1;
+      const bool more = ahead < nk;
+      const int nbuf = cur == 0 ? ST - 1 : cur - 1;   // (cur + ST - 1) % ST
+      if (more) dma_slice(ahead, nbuf, std::integral_constant<int, 0>{});
       MOE_SCHED_FENCE();
       rfrag(cur, 0, na_c);
       rfrag(cur, 1, na_c);
       mfmas(0, na_c);
-      if (more && kDmaSlices > 1) dma_slice(kt + 1, cur ^ 1, std::integral_constant<int, 1>{});
+      if (more && SL > 1) dma_slice(ahead, nbuf, std::integral_constant<int, 1>{});
       MOE_SCHED_FENCE();
       rfrag(cur, 2, na_c);
       mfmas(1, na_c);
-      if (more && kDmaSlices > 2) dma_slice(kt + 1, cur ^ 1, std::integral_constant<int, 2>{});
+      if (more && SL > 2) dma_slice(ahead, nbuf, std::integral_constant<int, 2>{});
       MOE_SCHED_FENCE();
       rfrag(cur, 3, na_c);
       mfmas(2, na_c);
-      if (more && kDmaSlices > 3) dma_slice(kt + 1, cur ^ 1, std::integral_constant<int, 3>{});
+      if (more && SL > 3) dma_slice(ahead, nbuf, std::integral_constant<int, 3>{});
       MOE_SCHED_FENCE();
       mfmas(3, na_c);
+      cur = cur + 1 == ST ? 0 : cur + 1;
     }
   };
   const int nb = (min(tc.rows, BM) + 31) / 32;
@@ -609,8 +648,9 @@ int gemm_tile_rows(int dtype_bf16, int R_max, int groups, bool n256_ok) {
   const int avg = g > 0 ? R_max / g : 0;
   if (avg <= 16) return 16;          // decode: stream the weights
   if (!n256_ok || avg < 96) return 32;
-  if (avg >= 768) return 256;
-  return 128;
+  // one 256-row tile covers a group of up to 256 rows, so each expert's weight
+  // panel is read once; the MFMAs and loads of a tail's empty rows are skipped
+  return 256;
 }
 
 int gemm_max_tiles(int BM, int R_max, int E) {
@@ -660,19 +700,24 @@ static hipError_t run_small(const GemmTileMap& map, const uint16_t* xa, const in
 }
 
 // LDS-DMA large tiles
+// Three LDS stages where they fit (256 x 128 down tiles: 3 x 48 KB), which
+// keeps two stages of loads in flight per CU; those tiles serve short groups,
+// where the weights stream from HBM and load latency matters most.
 template <int BM, int BN, int WM, int WN, bool GATEUP>
 static hipError_t run_lds(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
                           int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
                           long long w_stride, void* out, int out_stride, int out_row0, int K,
                           int N, hipStream_t s) {
   constexpr int WR = GATEUP ? 2 * BN : BN;
-  const size_t lds = static_cast<size_t>(2) * (BM + WR) * kRowBytes;
-  return launch_tiled(gemm_bf16_lds_kernel<BM, BN, WM, WN, GATEUP>, BM, BN, 64 * WM * WN, lds,
-                      map, xa, src, a_stride, a_row0, wa, wb, w_stride, out, out_stride,
+  constexpr size_t kStage = static_cast<size_t>(BM + WR) * kRowBytes;
+  constexpr int ST = 3 * kStage <= kMaxLdsBytes ? 3 : 2;
+  const size_t lds = ST * kStage;
+  return launch_tiled(gemm_bf16_lds_kernel<BM, BN, WM, WN, GATEUP, ST>, BM, BN, 64 * WM * WN,
+                      lds, map, xa, src, a_stride, a_row0, wa, wb, w_stride, out, out_stride,
                       out_row0, K, N, s);
 }
 
-// BM = 256 or 128 needs N % 256 == 0 (down) / N % 128 == 0 (gate/up); the
+// BM = 256 needs N % 256 == 0 (down) / N % 128 == 0 (gate/up); the
 // caller picks BM with gemm_tile_rows(), which checks that.
 hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, int BM,
                                    hipStream_t s) {
@@ -682,9 +727,6 @@ hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, 
   if (BM == 256)
     return run_lds<256, 128, 2, 4, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
                                          a.act_stride, a.out_row0, a.K, a.N, s);
-  if (BM == 128)
-    return run_lds<128, 128, 2, 4, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
-                                         a.act_stride, a.out_row0, a.K, a.N, s);
   if (BM == 16)
     return run_stream<true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act, a.act_stride,
                             a.out_row0, a.K, a.N, s);
@@ -692,18 +734,28 @@ hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, 
                                        a.act_stride, a.out_row0, a.K, a.N, s);
 }
 
+// Output tiles of 256 columns unless that leaves fewer than two tiles per CU
+// (few, short groups, as in a prefill of a few hundred tokens): then 128
+// columns, which doubles the tiles and, at 3 x 48 KB, runs three LDS stages.
+static int gemm_down_cols(int BM, int m_tiles, int N) {
+  if (BM != 256 || N % 256 != 0) return 256;
+  return static_cast<long long>(m_tiles) * (N / 256) < 2 * kNumCUs ? 128 : 256;
+}
+
 hipError_t launch_gemm_down_bf16(const GemmTileMap& map, const DownArgs& a, int BM,
                                  hipStream_t s) {
   const auto* act = static_cast<const uint16_t*>(a.act);
   const auto* w2 = static_cast<const uint16_t*>(a.w2);
-  if (BM == 256)
+  if (BM == 256) {
+    const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + BM - 1) / BM;
+    if (gemm_down_cols(BM, m_tiles, a.N) == 128)
+      return run_lds<256, 128, 2, 4, false>(map, act, nullptr, a.act_stride, a.in_row0, w2,
+                                            nullptr, a.w_stride, a.y, a.N, a.out_row0, a.K,
+                                            a.N, s);
     return run_lds<256, 256, 2, 4, false>(map, act, nullptr, a.act_stride, a.in_row0, w2,
                                           nullptr, a.w_stride, a.y, a.N, a.out_row0, a.K, a.N,
                                           s);
-  if (BM == 128)
-    return run_lds<128, 256, 2, 4, false>(map, act, nullptr, a.act_stride, a.in_row0, w2,
-                                          nullptr, a.w_stride, a.y, a.N, a.out_row0, a.K, a.N,
-                                          s);
+  }
   if (BM == 16)
     return run_stream<false>(map, act, nullptr, a.act_stride, a.in_row0, w2, nullptr, a.w_stride,
                              a.y, a.N, a.out_row0, a.K, a.N, s);
