@@ -221,7 +221,7 @@ def main():
                     frac=round(achieved / PEAK_HBM_GBPS, 4))
     tr = counters_traffic(wl.name)
     roof["traffic"] = tr
-    roof["kernel"] = "moe::gemm_bf16_kernel gate/up (+SwiGLU)"
+    roof["kernel"] = "moe_expert_gateup: grouped gate/up GEMM + SwiGLU"
     roof["kernel_ms"] = round(gemm_ms, 4)
     roof["algorithmic_bytes"] = B_g
     roof["algorithmic_flops"] = F_g
