@@ -170,11 +170,163 @@ __global__ __launch_bounds__(kTB) void index_rank_kernel(
   }
 }
 
+// ---------------------------------------------------------------- one workgroup
+//
+// T <= 256 tokens and at most kIndexSingleMaxKeys keys (decode and small
+// batches): the three steps above in one 1024-thread workgroup with every
+// intermediate in LDS, so a decode step pays one launch instead of three. The
+// arithmetic and its order are those of the three kernels with one token block
+// (every per-block base is 0). When `tiles` is set it also writes the grouped
+// GEMM tile table of BM-row tiles (group, first row, rows) from the offsets, as
+// tile_map_kernel does, and zero entries up to max_tiles.
+__global__ __launch_bounds__(1024) void index_single_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int E, long long C,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ dest, int32_t* __restrict__ src,
+    int32_t* __restrict__ counts_out, int32_t* __restrict__ kept_out,
+    int32_t* __restrict__ n_dropped, int BM, int max_tiles, int4* __restrict__ tiles) {
+  extern __shared__ uint32_t smem[];
+  const int cap = C >= 0;
+  const int nkeys = cap ? E * k : E;
+  uint32_t* bm = smem;                                              // [nkeys][kWords]
+  int32_t* tot = reinterpret_cast<int32_t*>(bm + nkeys * kWords);   // [nkeys]
+  int32_t* sbase = tot + nkeys;                                     // [nkeys]
+  int32_t* skeep = sbase + nkeys;                                   // [nkeys]
+  int32_t* off = skeep + nkeys;                                     // [E + 1]
+  int32_t* part = off + (E + 1);                                    // [1024]
+  const int tid = threadIdx.x;
+
+  for (int i = tid; i < nkeys * kWords; i += 1024) bm[i] = 0u;
+  __syncthreads();
+  if (tid < T) {
+    const uint32_t bit = 1u << (tid & 31);
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[static_cast<size_t>(tid) * k + j];
+      if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) continue;
+      atomicOr(&bm[(cap ? j * E + e : e) * kWords + (tid >> 5)], bit);
+    }
+  }
+  __syncthreads();
+  for (int key = tid; key < nkeys; key += 1024) {
+    int c = 0;
+    for (int w = 0; w < kWords; ++w) c += __popc(bm[key * kWords + w]);
+    tot[key] = c;
+  }
+  __syncthreads();
+  const int e = tid;
+  int keep_e = 0;
+  if (e < E) {
+    int cnt = 0;
+    if (cap) {
+      for (int j = 0; j < k; ++j) {
+        const int tj = tot[j * E + e];
+        long long room = C - cnt;
+        room = room < 0 ? 0 : room;
+        const int keep_j = static_cast<int>(room < tj ? room : tj);
+        sbase[j * E + e] = cnt;
+        skeep[j * E + e] = keep_j;
+        keep_e += keep_j;
+        cnt += tj;
+      }
+    } else {
+      cnt = tot[e];
+      keep_e = cnt;
+    }
+    if (counts_out) counts_out[e] = cnt;
+    if (kept_out) kept_out[e] = keep_e;
+  }
+  part[tid] = (e < E) ? keep_e : 0;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  if (e < E) { off[e + 1] = part[e]; offsets[e + 1] = part[e]; }
+  if (tid == 0) {
+    off[0] = 0;
+    offsets[0] = 0;
+    if (n_dropped) n_dropped[0] = T * k - part[E - 1];
+  }
+  __syncthreads();
+
+  if (tid < T) {
+    for (int j = 0; j < k; ++j) {
+      const int ej = idx[static_cast<size_t>(tid) * k + j];
+      int row;
+      if (static_cast<unsigned>(ej) >= static_cast<unsigned>(E)) {
+        row = -1;
+      } else if (!cap) {
+        row = off[ej] + bits_below(bm, ej, tid);
+      } else {
+        const int key = j * E + ej;
+        const int rank_j = bits_below(bm, key, tid);
+        if (static_cast<long long>(sbase[key]) + rank_j >= C) {
+          row = -1;
+        } else {
+          int before = 0;
+          for (int j2 = 0; j2 < k; ++j2) {
+            const int key2 = j2 * E + ej;
+            const int r2 = bits_below(bm, key2, tid);
+            const int kk = skeep[key2];
+            before += r2 < kk ? r2 : kk;
+          }
+          row = off[ej] + before;
+        }
+      }
+      dest[static_cast<size_t>(tid) * k + j] = row;
+      if (row >= 0) src[row] = tid;
+    }
+  }
+
+  if (tiles == nullptr) return;
+  // tile table: exclusive scan of ceil(n_e / BM) over the experts
+  int lo = 0, n = 0, nt = 0;
+  if (e < E) {
+    lo = off[e];
+    n = off[e + 1] - lo;
+    nt = (n + BM - 1) / BM;
+  }
+  __syncthreads();            // every thread has read part[] above
+  part[tid] = nt;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  const int start = part[tid] - nt;
+  const int total = part[1023];
+  for (int i = 0; i < nt; ++i) tiles[start + i] = make_int4(e, lo + i * BM, min(BM, n - i * BM), 0);
+  for (int i = total + tid; i < max_tiles; i += 1024) tiles[i] = make_int4(0, 0, 0, 0);
+}
+
+static size_t index_single_lds(int E, int nkeys) {
+  return (static_cast<size_t>(nkeys) * (kWords + 3) + (E + 1) + 1024) * sizeof(uint32_t);
+}
+
+bool index_single_ok(int T, int E, int k, bool cap) {
+  return T <= kTB && E <= 1024 && index_keys(E, k, cap) <= kIndexSingleMaxKeys;
+}
+
 hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capacity,
                         int32_t* blk, int32_t* slot_base, int32_t* slot_keep, int32_t* offsets,
                         int32_t* dest, int32_t* src, int32_t* counts, int32_t* kept,
-                        int32_t* n_dropped, hipStream_t s) {
+                        int32_t* n_dropped, int BM, int max_tiles, int32_t* tiles,
+                        hipStream_t s) {
   const bool cap = capacity >= 0;
+  if (index_single_ok(T, E, k, cap)) {
+    const size_t lds = index_single_lds(E, index_keys(E, k, cap));
+    if (lds > 65536) {
+      hipError_t e1 = allow_large_lds(reinterpret_cast<const void*>(index_single_kernel), lds);
+      if (e1 != hipSuccess) return e1;
+    }
+    index_single_kernel<<<dim3(1), dim3(1024), lds, s>>>(
+        idx, T, k, E, cap ? capacity : -1, offsets, dest, src, counts, kept, n_dropped, BM,
+        max_tiles, reinterpret_cast<int4*>(tiles));
+    return hipGetLastError();
+  }
   const int nb = index_blocks(T);
   const int nkeys = index_keys(E, k, cap);
   const size_t lds = static_cast<size_t>(nkeys) * kWords * sizeof(uint32_t);
@@ -194,7 +346,9 @@ hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capac
   if (err != hipSuccess) return err;
   index_rank_kernel<<<dim3(nb), dim3(kTB), lds, s>>>(idx, T, k, E, cap ? capacity : -1, blk,
                                                      slot_base, slot_keep, offsets, dest, src);
-  return hipGetLastError();
+  err = hipGetLastError();
+  if (err != hipSuccess || tiles == nullptr) return err;
+  return launch_tile_map(offsets, E, BM, max_tiles, tiles, s);
 }
 
 }  // namespace moe

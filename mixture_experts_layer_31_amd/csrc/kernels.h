@@ -31,10 +31,15 @@ int index_blocks(int T);
 // number of histogram keys: E without capacity, k*E with capacity
 inline int index_keys(int E, int k, bool cap) { return cap ? E * k : E; }
 constexpr int kIndexMaxKeys = 4096;   // LDS bitmaps: 32 bytes per key
+// Single-workgroup index (one launch) when T <= 256 and the keys fit in LDS.
+constexpr int kIndexSingleMaxKeys = 1024;
+bool index_single_ok(int T, int E, int k, bool cap);
+// With `tiles` set, also writes the grouped GEMM tile table for BM-row tiles
+// (as launch_tile_map does), in the same launch on the single-workgroup path.
 hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capacity,
-                        int32_t* blk /*[nb+1][keys]*/, int32_t* slot_base /*[k][E]*/,
-                        int32_t* slot_keep /*[k][E]*/, int32_t* offsets, int32_t* dest,
-                        int32_t* src, int32_t* counts, int32_t* kept, int32_t* n_dropped,
+                        int32_t* blk, int32_t* slot_base, int32_t* slot_keep, int32_t* offsets,
+                        int32_t* dest, int32_t* src, int32_t* counts, int32_t* kept,
+                        int32_t* n_dropped, int BM, int max_tiles, int32_t* tiles,
                         hipStream_t s);
 
 // ---- row movement (rows.hip)

@@ -200,16 +200,18 @@ moe_status do_route(const Shape& s, float alpha, const void* x, const void* wr, 
   return MOE_OK;
 }
 
+// tiles (nullable): also build the grouped GEMM tile table there; it may alias
+// the workspace (written after the index kernels are done with it)
 moe_status do_permute(const Shape& s, const int32_t* idx, const void* x, int32_t* offsets,
                       int32_t* dest, int32_t* src, void* x_perm, const moe_stats* st, void* ws,
-                      hipStream_t stream) {
+                      int32_t* tiles, hipStream_t stream) {
   Carver cv{static_cast<char*>(ws)};
   int32_t* blk = cv.take<int32_t>(static_cast<size_t>(s.nb_idx + 1) * s.nkeys * 4);
   int32_t* slot_base = cv.take<int32_t>(static_cast<size_t>(s.k) * s.E * 4);
   int32_t* slot_keep = cv.take<int32_t>(static_cast<size_t>(s.k) * s.E * 4);
   MOE_HIP(moe::launch_index(idx, s.T, s.k, s.E, s.C, blk, slot_base, slot_keep, offsets, dest, src,
                             st ? st->counts : nullptr, st ? st->kept : nullptr,
-                            st ? st->n_dropped : nullptr, stream),
+                            st ? st->n_dropped : nullptr, s.BM, s.max_tiles, tiles, stream),
           "index");
   if (x_perm != nullptr)
     MOE_HIP(moe::launch_gather_rows(s.elt, x, src, offsets, s.E, s.R, s.d, x_perm, stream),
@@ -329,7 +331,7 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* idx, const void* x,
   st = check_ws(s, MOE_STAGE_PERMUTE, ws, ws_bytes);
   if (st != MOE_OK) return st;
   if (s.T == 0) return MOE_OK;
-  return do_permute(s, idx, x, offsets, dest, src, x_perm, stats, ws,
+  return do_permute(s, idx, x, offsets, dest, src, x_perm, stats, ws, nullptr,
                     static_cast<hipStream_t>(stream));
 }
 
@@ -442,10 +444,9 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
 
   st = do_route(s, cfg->aux_alpha, x, w_router, sel_bias, idx, gates, stats, scratch, strm);
   if (st != MOE_OK) return st;
-  st = do_permute(s, idx, x, offsets, dest, src, nullptr, stats, scratch, strm);
-  if (st != MOE_OK) return st;
   int32_t* tiles = static_cast<int32_t*>(scratch);
-  MOE_HIP(moe::launch_tile_map(offsets, s.E, s.BM, s.max_tiles, tiles, strm), "tile_map");
+  st = do_permute(s, idx, x, offsets, dest, src, nullptr, stats, scratch, tiles, strm);
+  if (st != MOE_OK) return st;
   st = do_gateup(s, x, src, tiles, w1, w3, ws1, ws3, act, strm);
   if (st != MOE_OK) return st;
   st = do_down(s, act, tiles, w2, ws2, y_perm, strm);

@@ -151,15 +151,17 @@ def test_single_expert_is_dense_swiglu():
     check_y(wl, g["y"], om.swiglu(x64, *W.expert64(0)), "dense")
 
 
-def test_capacity_with_two_choices():
-    """k = 2 with a binding capacity: first choices before second choices (GShard rule)."""
-    wl = _adhoc("cap_k2", 103, T=300, d=128, E=8, k=2, d_ff=128, dtype=wk.BF16,
+@pytest.mark.parametrize("T", [200, 256, 300])
+def test_capacity_with_two_choices(T):
+    """k = 2 with a binding capacity: first choices before second choices (GShard rule).
+    T <= 256 takes the single-workgroup index path, T = 300 the three-kernel one."""
+    wl = _adhoc("cap_k2", 103, T=T, d=128, E=8, k=2, d_ff=128, dtype=wk.BF16,
                 capacity_factor=0.6, offset_var=1.5)
     W = Weights(wl)
-    g, r, p = full_check(wl, W, 300)
-    assert p["n_dropped"] > 0 and p["C"] == int(np.ceil(2 * 300 / 8 * 0.6))
-    b = run_staged(wl, W, wk.make_inputs(wl, T=300).x, 300)
-    check_permutation(wl, 300, b, b["idx"])
+    g, r, p = full_check(wl, W, T)
+    assert p["n_dropped"] > 0 and p["C"] == int(np.ceil(2 * T / 8 * 0.6))
+    b = run_staged(wl, W, wk.make_inputs(wl, T=T).x, T)
+    check_permutation(wl, T, b, b["idx"])
 
 
 def test_router_many_experts_max_k():
