@@ -8,8 +8,8 @@ Everything here is the plain definition of each stage, in float64, written
 from the pages (cited by page title and section):
 
 * [CME295] "Week 2 Day 2: Mixture of Experts" course notes (semidirectx.com),
-  §1.3 formalism, §3.2 balance loss, §3.3 capacity, §4.2 selection bias,
-  §A.2 implementation pitfalls.
+  §1.3 formalism, §3.2 balance loss, §3.3 capacity, §3.4 z-loss, §4.2
+  selection bias, §A.2 implementation pitfalls.
 * [FANDEX] "Mixture-of-Experts models" (fanquanpp.github.io), "Step 1: the
   router" code.
 * [CS336] "Stanford CS336 Lecture 04: MoE architecture" (devpress.csdn.net),
@@ -18,7 +18,7 @@ from the pages (cited by page title and section):
   (semidirectx.com), §2.1 gating, §2.5 top-1 pitfall, §3.2 four steps,
   §3.3 permutation by prefix sum, §3.5 capacity, §10 exercises.
 * [W11] "W11: MoE routing and parallel cost" (botof.cn), §2 toy MoE, §3
-  capacity factor.
+  capacity factor, §5 balance metrics.
 
 Readings where the pages are silent or disagree:
 * SwiGLU expert: f(x) = W2 (silu(W1 x) * (W3 x)), silu(u) = u / (1 + e^-u),
@@ -135,6 +135,44 @@ def aux_loss(f: np.ndarray, P: np.ndarray, alpha: float) -> float:
     [15-779] §2.4)."""
     f = np.asarray(f, np.float64)
     return float(alpha * f.shape[0] * np.dot(f, np.asarray(P, np.float64)))
+
+
+def logsumexp_rows(z: np.ndarray) -> np.ndarray:
+    """log sum_i e^{z_{t,i}} per token, with the row maximum factored out."""
+    z = np.asarray(z, np.float64)
+    m = z.max(axis=1)
+    return m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+
+
+def z_loss(z: np.ndarray) -> float:
+    """Router z-loss L_z = (1/T) sum_t (log sum_i e^{z_{t,i}})^2 on the
+    unbiased logits ([CME295] §3.4, the ST-MoE penalty on the logits' scale)."""
+    return float(np.mean(logsumexp_rows(z) ** 2))
+
+
+def router_entropy(z: np.ndarray) -> float:
+    """Mean over tokens of the Shannon entropy (natural log) of the full
+    softmax p_t = softmax(z_t). [W11] §5 lists router entropy as a quantity to
+    monitor without a formula; this is its plainest reading."""
+    p = softmax(z)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        h = -np.where(p > 0, p * np.log(p), 0.0).sum(axis=1)
+    return float(np.mean(h))
+
+
+def mean_max_prob(z: np.ndarray) -> float:
+    """Mean over tokens of max_i p_{t,i} ([CME295] §3.4 reports it beside the
+    z-loss)."""
+    return float(np.mean(softmax(z).max(axis=1)))
+
+
+def top_gap(z: np.ndarray) -> float:
+    """Mean over tokens of p_{t,(1)} - p_{t,(2)}, the two largest entries of the
+    full softmax of the unbiased logits (p_{(2)} = 0 when E = 1). [W11] §5 lists
+    the top-1/top-2 gap without a formula; this is its plainest reading."""
+    p = np.sort(softmax(z), axis=1)[:, ::-1]
+    second = p[:, 1] if p.shape[1] > 1 else np.zeros(p.shape[0])
+    return float(np.mean(p[:, 0] - second))
 
 
 def coverage_fraction(k: int, E: int, B: int) -> float:

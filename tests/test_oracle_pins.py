@@ -459,3 +459,67 @@ def test_switch_recipe_overflows():
         p = om.assign_rows(r["idx"], wl.E, cf)
         assert p["n_dropped"] > 0
     assert np.bincount(r["idx"].ravel(), minlength=64).max() > 4 * 1024 / 64
+
+
+# ---------------------------------------------------------------- router scale statistics
+
+def test_z_loss_closed_forms():
+    """All-equal logits c: log sum e^c = c + log E exactly; a constant shift moves
+    every logsumexp by the shift; E = 1 gives mean z^2 ([CME295] §3.4)."""
+    for E in (1, 2, 8, 256):
+        for c in (0.0, -3.5, 2.25):
+            z = np.full((5, E), c)
+            assert om.z_loss(z) == pytest.approx((c + math.log(E)) ** 2, rel=1e-14, abs=1e-14)
+    rng = np.random.default_rng(11)
+    z = rng.standard_normal((40, 6))
+    lse = np.array([math.log(sum(math.exp(v) for v in row)) for row in z])   # plain loop
+    assert om.z_loss(z) == pytest.approx(float(np.mean(lse ** 2)), rel=1e-12)
+    assert om.z_loss(z + 1.5) == pytest.approx(float(np.mean((lse + 1.5) ** 2)), rel=1e-12)
+    zz = rng.standard_normal((30, 1))
+    assert om.z_loss(zz) == pytest.approx(float(np.mean(zz[:, 0] ** 2)), rel=1e-12)
+    # large logits stay finite (the max is factored out)
+    assert math.isfinite(om.z_loss(np.array([[1000.0, 999.0, -5.0]])))
+
+
+def test_z_loss_and_max_prob_printed_values():
+    """[CME295] §3.4 prints z-loss 6.2 / 59.6 / 988.9 and a mean top probability
+    rising from 0.355 to 0.949 for logits of standard deviation 1 / 5 / 20. With
+    E = 8 normal logits per token (the notes' toy router) a 200k-token sample
+    lands within 7 % and 0.01 of those printed figures; the square of the mean
+    logsumexp instead of the mean square would miss by 9-18 % at std 5 and 20."""
+    g = _gold("printed_numbers.json")["z_loss"]
+    rng = np.random.default_rng(2024)
+    maxp = []
+    for s, want in zip(g["logit_std"], g["z_loss"]):
+        z = rng.standard_normal((200_000, 8)) * s
+        assert abs(om.z_loss(z) - want) <= 0.07 * want, (s, om.z_loss(z), want)
+        maxp.append(om.mean_max_prob(z))
+    assert abs(maxp[0] - g["mean_max_prob_first_last"][0]) <= 0.01
+    assert abs(maxp[-1] - g["mean_max_prob_first_last"][1]) <= 0.01
+    assert maxp[0] < maxp[1] < maxp[2]
+
+
+def test_entropy_gap_max_prob_closed_forms():
+    """Uniform logits: entropy log E, top probability 1/E, gap 0. Two experts with
+    logit difference a: p = sigmoid(a), entropy -p ln p - (1-p) ln(1-p), gap
+    |2p - 1| = tanh(|a|/2). A dominant logit: entropy -> 0, top probability and
+    gap -> 1. E = 1: entropy 0, top probability 1, gap 1 (p_(2) = 0)."""
+    for E in (2, 8, 64):
+        z = np.zeros((3, E)) + 0.7
+        assert om.router_entropy(z) == pytest.approx(math.log(E), rel=1e-13)
+        assert om.mean_max_prob(z) == pytest.approx(1.0 / E, rel=1e-13)
+        assert om.top_gap(z) == pytest.approx(0.0, abs=1e-15)
+    for a in (0.3, -1.7, 4.0):
+        p = 1.0 / (1.0 + math.exp(-a))
+        z = np.array([[a, 0.0]])
+        assert om.router_entropy(z) == pytest.approx(-p * math.log(p) - (1 - p) * math.log(1 - p), rel=1e-12)
+        assert om.top_gap(z) == pytest.approx(math.tanh(abs(a) / 2), rel=1e-12)
+        assert om.mean_max_prob(z) == pytest.approx(max(p, 1 - p), rel=1e-12)
+    z = np.array([[60.0, 0.0, 0.0, 0.0]])
+    assert om.router_entropy(z) < 1e-20 and om.top_gap(z) == pytest.approx(1.0)
+    z1 = np.array([[0.4], [-2.0]])
+    assert om.router_entropy(z1) == 0.0 and om.mean_max_prob(z1) == 1.0 and om.top_gap(z1) == 1.0
+    # per-token means: a batch mixing the cases averages them
+    z = np.array([[0.0, 0.0], [50.0, 0.0]])
+    assert om.router_entropy(z) == pytest.approx(math.log(2) / 2, rel=1e-12)
+    assert om.top_gap(z) == pytest.approx(0.5, rel=1e-12)
