@@ -117,14 +117,22 @@ typedef struct {
   float reserved2;          /* must be 0                                        */
 } moe_config;
 
-/* Optional router/load statistics ([CME295] §3.2, [W11] §3 and §5); every
- * pointer is a nullable device pointer.
+/* Optional router/load statistics ([CME295] §3.2 and §3.4, [W11] §3 and §5);
+ * every pointer is a nullable device pointer. Means are over the T tokens;
+ * p_t is the full softmax of the unbiased logits z_t.
  *   counts[E]  assignments per expert before any drop (int32)
  *   kept[E]    assignments per expert after capacity (int32)
  *   n_dropped  dropped assignments, T*k - sum(kept) (int32[1])
  *   f[E]       counts / T (all k choices counted, before drops)
  *   P[E]       mean over tokens of the full softmax probability
- *   aux        alpha * E * sum_i f_i P_i (float[1])                            */
+ *   aux        alpha * E * sum_i f_i P_i (float[1])
+ *   z_loss     mean_t (log sum_i e^{z_{t,i}})^2, the router z-loss (float[1])
+ *   entropy    mean_t of -sum_i p_{t,i} ln p_{t,i} (float[1])
+ *   max_prob   mean_t of max_i p_{t,i} (float[1])
+ *   top_gap    mean_t of p_{t,(1)} - p_{t,(2)}, the two largest probabilities
+ *              (p_{(2)} = 0 when E = 1) (float[1])
+ * The last four are computed by moe_route / moe_forward; all in fp32 with
+ * fixed summation orders (reproducible bit for bit).                          */
 typedef struct {
   int32_t* counts;
   int32_t* kept;
@@ -132,6 +140,10 @@ typedef struct {
   float* f;
   float* P;
   float* aux;
+  float* z_loss;
+  float* entropy;
+  float* max_prob;
+  float* top_gap;
 } moe_stats;
 
 /* Human-readable status name; never NULL. */

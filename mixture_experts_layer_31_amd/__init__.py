@@ -38,7 +38,9 @@ class MoeConfig(ctypes.Structure):
 class MoeStats(ctypes.Structure):
     _fields_ = [("counts", ctypes.c_void_p), ("kept", ctypes.c_void_p),
                 ("n_dropped", ctypes.c_void_p), ("f", ctypes.c_void_p),
-                ("P", ctypes.c_void_p), ("aux", ctypes.c_void_p)]
+                ("P", ctypes.c_void_p), ("aux", ctypes.c_void_p),
+                ("z_loss", ctypes.c_void_p), ("entropy", ctypes.c_void_p),
+                ("max_prob", ctypes.c_void_p), ("top_gap", ctypes.c_void_p)]
 
 
 class MoEError(RuntimeError):
@@ -146,17 +148,23 @@ class Stats:
     f: object = None
     P: object = None
     aux: object = None
+    z_loss: object = None
+    entropy: object = None
+    max_prob: object = None
+    top_gap: object = None
 
     @staticmethod
     def alloc(E: int, device="cuda") -> "Stats":
         import torch
         z = lambda n, dt: torch.zeros(n, dtype=dt, device=device)
+        f1 = lambda: z(1, torch.float32)
         return Stats(z(E, torch.int32), z(E, torch.int32), z(1, torch.int32),
-                     z(E, torch.float32), z(E, torch.float32), z(1, torch.float32))
+                     z(E, torch.float32), z(E, torch.float32), f1(), f1(), f1(), f1(), f1())
 
     def c(self) -> MoeStats:
         return MoeStats(_p(self.counts), _p(self.kept), _p(self.n_dropped), _p(self.f),
-                        _p(self.P), _p(self.aux))
+                        _p(self.P), _p(self.aux), _p(self.z_loss), _p(self.entropy),
+                        _p(self.max_prob), _p(self.top_gap))
 
 
 def _stats_ref(stats: Optional[Stats]):

@@ -18,12 +18,16 @@ int router_select_tokens(int T);   // tokens per router_select workgroup
 int router_select_blocks(int T);
 hipError_t launch_router_scores(int dtype_bf16, const void* x, const void* w, int T, int d, int E,
                                 float* z, hipStream_t s);
+// q_part (nullable): per-block sums of the four scale statistics (z-loss,
+// entropy, top probability, top-2 gap), [blocks][kScaleStats]
+constexpr int kScaleStats = 4;
 hipError_t launch_router_select(const float* z, const float* bias, int T, int E, int k,
                                 int gate_all, int32_t* idx, float* gates, float* p_part,
-                                int32_t* c_part, hipStream_t s);
-hipError_t launch_router_stats(const float* p_part, const int32_t* c_part, int nblocks, int T,
-                               int E, float alpha, float* f, float* P, float* aux, float* fp,
-                               hipStream_t s);
+                                int32_t* c_part, float* q_part, hipStream_t s);
+hipError_t launch_router_stats(const float* p_part, const int32_t* c_part, const float* q_part,
+                               int nblocks, int T, int E, float alpha, float* f, float* P,
+                               float* aux, float* fp, float* z_loss, float* entropy,
+                               float* max_prob, float* top_gap, hipStream_t s);
 
 // ---- index: histogram, scan, rank (index.hip)
 constexpr int kIndexTokensPerBlock = 256;

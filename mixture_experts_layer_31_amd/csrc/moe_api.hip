@@ -111,7 +111,8 @@ moe_status validate(const moe_config* c, Shape* s) {
 // workspace sizes per stage
 size_t route_bytes(const Shape& s) {
   return al(static_cast<size_t>(s.T) * s.E * 4) + 2 * al(static_cast<size_t>(s.nb_sel) * s.E * 4) +
-         al(static_cast<size_t>(s.E) * 4);
+         al(static_cast<size_t>(s.E) * 4) +
+         al(static_cast<size_t>(s.nb_sel) * moe::kScaleStats * 4);
 }
 size_t permute_bytes(const Shape& s) {
   return al(static_cast<size_t>(s.nb_idx + 1) * s.nkeys * 4) + 2 * al(static_cast<size_t>(s.k) * s.E * 4);
@@ -176,7 +177,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
   } while (0)
 
 bool want_route_stats(const moe_stats* st) {
-  return st != nullptr && (st->f != nullptr || st->P != nullptr || st->aux != nullptr);
+  return st != nullptr && (st->f != nullptr || st->P != nullptr || st->aux != nullptr ||
+                           st->z_loss != nullptr || st->entropy != nullptr ||
+                           st->max_prob != nullptr || st->top_gap != nullptr);
 }
 
 // ---- stage bodies (arguments already validated)
@@ -188,14 +191,18 @@ moe_status do_route(const Shape& s, float alpha, const void* x, const void* wr, 
   float* p_part = cv.take<float>(static_cast<size_t>(s.nb_sel) * s.E * 4);
   int32_t* c_part = cv.take<int32_t>(static_cast<size_t>(s.nb_sel) * s.E * 4);
   float* fp = cv.take<float>(static_cast<size_t>(s.E) * 4);
+  float* q_part = cv.take<float>(static_cast<size_t>(s.nb_sel) * moe::kScaleStats * 4);
   const bool stats = want_route_stats(st);
+  const bool scale = stats && (st->z_loss || st->entropy || st->max_prob || st->top_gap);
   MOE_HIP(moe::launch_router_scores(s.bf16, x, wr, s.T, s.d, s.E, z, stream), "router_scores");
   MOE_HIP(moe::launch_router_select(z, bias, s.T, s.E, s.k, s.gate_all, idx, gates,
-                                    stats ? p_part : nullptr, stats ? c_part : nullptr, stream),
+                                    stats ? p_part : nullptr, stats ? c_part : nullptr,
+                                    scale ? q_part : nullptr, stream),
           "router_select");
   if (stats)
-    MOE_HIP(moe::launch_router_stats(p_part, c_part, s.nb_sel, s.T, s.E, alpha, st->f, st->P,
-                                     st->aux, fp, stream),
+    MOE_HIP(moe::launch_router_stats(p_part, c_part, scale ? q_part : nullptr, s.nb_sel, s.T, s.E,
+                                     alpha, st->f, st->P, st->aux, fp, st->z_loss, st->entropy,
+                                     st->max_prob, st->top_gap, stream),
             "router_stats");
   return MOE_OK;
 }

@@ -165,8 +165,10 @@ template <int NE>
 __global__ __launch_bounds__(256) void router_select_kernel(
     const float* __restrict__ z, const float* __restrict__ bias, int T, int E, int k,
     int gate_all, int tokens_per_block, int32_t* __restrict__ idx,
-    float* __restrict__ gates, float* __restrict__ p_part, int32_t* __restrict__ c_part) {
+    float* __restrict__ gates, float* __restrict__ p_part, int32_t* __restrict__ c_part,
+    float* __restrict__ q_part) {
   extern __shared__ unsigned char smem_raw[];
+  __shared__ float sq[4][kScaleStats];
   float* sp = reinterpret_cast<float*>(smem_raw);             // [4][E]
   int32_t* sc = reinterpret_cast<int32_t*>(sp + 4 * E);        // [4][E]
   const int lane = threadIdx.x & 63;
@@ -176,6 +178,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
 
   float b[NE], pacc[NE];
   int cacc[NE];
+  float qacc[kScaleStats] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < NE; ++i) {
     const int e = lane + 64 * i;
@@ -207,6 +210,34 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     const float inv = 1.0f / se;
 #pragma unroll
     for (int i = 0; i < NE; ++i) pacc[i] += ex[i] * inv;
+    if (q_part != nullptr) {
+      // scale statistics of p_t = softmax(z_t): with m the max logit and
+      // se = sum e^{z-m}, log sum e^z = m + ln se, max p = 1/se,
+      // entropy = ln se - sum e^{z-m} (z-m) / se, and the top-2 gap is
+      // (1 - e^{z_(2) - m}) / se with z_(2) the second largest logit
+      float zm = 0.f, t1 = -INFINITY, t2 = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NE; ++i) {
+        if (lane + 64 * i < E) {
+          zm += ex[i] * (zl[i] - m);
+          if (zl[i] > t1) { t2 = t1; t1 = zl[i]; }
+          else if (zl[i] > t2) { t2 = zl[i]; }
+        }
+      }
+      zm = wave_allsum(zm);
+#pragma unroll
+      for (int msk = 32; msk >= 1; msk >>= 1) {
+        const float o1 = __shfl_xor(t1, msk, 64), o2 = __shfl_xor(t2, msk, 64);
+        const float n2 = fmaxf(fminf(t1, o1), fmaxf(t2, o2));
+        t1 = fmaxf(t1, o1);
+        t2 = n2;
+      }
+      const float lse = m + logf(se);
+      qacc[0] += lse * lse;
+      qacc[1] += logf(se) - zm * inv;
+      qacc[2] += inv;
+      qacc[3] += (1.0f - expf(t2 - m)) * inv;
+    }
 
     // k rounds of argmax; lane r keeps the round-r winner and its unbiased logit
     int my_e = 0;
@@ -256,6 +287,10 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   }
 
   if (p_part == nullptr) return;
+  if (q_part != nullptr && lane == 0) {
+#pragma unroll
+    for (int q = 0; q < kScaleStats; ++q) sq[wv][q] = qacc[q];
+  }
 #pragma unroll
   for (int i = 0; i < NE; ++i) {
     const int e = lane + 64 * i;
@@ -268,6 +303,11 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     for (int w2 = 1; w2 < 4; ++w2) { p += sp[w2 * E + e]; c += sc[w2 * E + e]; }
     p_part[static_cast<size_t>(blockIdx.x) * E + e] = p;
     c_part[static_cast<size_t>(blockIdx.x) * E + e] = c;
+  }
+  if (q_part != nullptr && threadIdx.x < kScaleStats) {
+    const int q = threadIdx.x;
+    q_part[static_cast<size_t>(blockIdx.x) * kScaleStats + q] =
+        ((sq[0][q] + sq[1][q]) + sq[2][q]) + sq[3][q];
   }
 }
 
@@ -307,19 +347,39 @@ __global__ __launch_bounds__(256) void router_stats_kernel(
   }
 }
 
-// L_aux = alpha * E * sum_i f_i P_i, the sum in a fixed order (CME295 notes §3.2).
-__global__ __launch_bounds__(256) void router_aux_kernel(const float* __restrict__ fp, int E,
-                                                         float alpha, float* __restrict__ aux) {
-  __shared__ float red[256];
-  float local = 0.f;
-  for (int e = threadIdx.x; e < E; e += 256) local += fp[e];
-  red[threadIdx.x] = local;
+// L_aux = alpha * E * sum_i f_i P_i (CME295 notes §3.2) and the token means of
+// the scale statistics (z-loss, entropy, top probability, top-2 gap) from the
+// per-block partials; every sum in a fixed order.
+__device__ __forceinline__ float block_sum_fixed(float v, float* red) {
+  red[threadIdx.x] = v;
   __syncthreads();
   for (int h = 128; h >= 1; h >>= 1) {
     if (threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
     __syncthreads();
   }
-  if (threadIdx.x == 0) aux[0] = alpha * static_cast<float>(E) * red[0];
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(256) void router_aux_kernel(
+    const float* __restrict__ fp, int E, float alpha, float* __restrict__ aux,
+    const float* __restrict__ q_part, int nblocks, int T, float* __restrict__ z_loss,
+    float* __restrict__ entropy, float* __restrict__ max_prob, float* __restrict__ top_gap) {
+  __shared__ float red[256];
+  float local = 0.f;
+  for (int e = threadIdx.x; e < E; e += 256) local += fp[e];
+  const float s = block_sum_fixed(local, red);
+  if (threadIdx.x == 0 && aux) aux[0] = alpha * static_cast<float>(E) * s;
+  if (q_part == nullptr) return;
+  float* outs[kScaleStats] = {z_loss, entropy, max_prob, top_gap};
+  const float invT = 1.0f / static_cast<float>(T);
+  for (int q = 0; q < kScaleStats; ++q) {
+    float acc = 0.f;
+    for (int b = threadIdx.x; b < nblocks; b += 256) acc += q_part[static_cast<size_t>(b) * kScaleStats + q];
+    const float tot = block_sum_fixed(acc, red);
+    if (threadIdx.x == 0 && outs[q]) outs[q][0] = tot * invT;
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -367,7 +427,7 @@ int router_select_blocks(int T) {
 
 hipError_t launch_router_select(const float* z, const float* bias, int T, int E, int k,
                                 int gate_all, int32_t* idx, float* gates, float* p_part,
-                                int32_t* c_part, hipStream_t s) {
+                                int32_t* c_part, float* q_part, hipStream_t s) {
   const int nb = router_select_blocks(T);
   const int tpb = router_select_tokens(T);
   const size_t lds = static_cast<size_t>(8) * E * sizeof(float);
@@ -375,7 +435,7 @@ hipError_t launch_router_select(const float* z, const float* bias, int T, int E,
 #define MOE_SEL(NE_)                                                                       \
   router_select_kernel<NE_><<<dim3(nb), dim3(256), lds, s>>>(z, bias, T, E, k, gate_all,   \
                                                              tpb, idx,                     \
-                                                             gates, p_part, c_part)
+                                                             gates, p_part, c_part, q_part)
   if (ne <= 1) MOE_SEL(1);
   else if (ne <= 2) MOE_SEL(2);
   else if (ne <= 4) MOE_SEL(4);
@@ -384,11 +444,13 @@ hipError_t launch_router_select(const float* z, const float* bias, int T, int E,
   return hipGetLastError();
 }
 
-hipError_t launch_router_stats(const float* p_part, const int32_t* c_part, int nblocks, int T,
-                               int E, float alpha, float* f, float* P, float* aux, float* fp,
-                               hipStream_t s) {
+hipError_t launch_router_stats(const float* p_part, const int32_t* c_part, const float* q_part,
+                               int nblocks, int T, int E, float alpha, float* f, float* P,
+                               float* aux, float* fp, float* z_loss, float* entropy,
+                               float* max_prob, float* top_gap, hipStream_t s) {
   router_stats_kernel<<<dim3(E), dim3(256), 0, s>>>(p_part, c_part, nblocks, T, E, f, P, fp);
-  if (aux != nullptr) router_aux_kernel<<<dim3(1), dim3(256), 0, s>>>(fp, E, alpha, aux);
+  router_aux_kernel<<<dim3(1), dim3(256), 0, s>>>(fp, E, alpha, aux, q_part, nblocks, T, z_loss,
+                                                  entropy, max_prob, top_gap);
   return hipGetLastError();
 }
 

@@ -94,7 +94,9 @@ def run_forward(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int, bias="d
     return dict(y=y.cpu().numpy(), idx=idx.cpu().numpy().astype(np.int64),
                 gates=gates.cpu().numpy(), counts=st.counts.cpu().numpy(),
                 kept=st.kept.cpu().numpy(), n_dropped=int(st.n_dropped.cpu()[0]),
-                f=st.f.cpu().numpy(), P=st.P.cpu().numpy(), aux=float(st.aux.cpu()[0]))
+                f=st.f.cpu().numpy(), P=st.P.cpu().numpy(), aux=float(st.aux.cpu()[0]),
+                z_loss=float(st.z_loss.cpu()[0]), entropy=float(st.entropy.cpu()[0]),
+                max_prob=float(st.max_prob.cpu()[0]), top_gap=float(st.top_gap.cpu()[0]))
 
 
 def run_staged(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int):

@@ -50,6 +50,14 @@ def weights(name):
     return _W[key]
 
 
+def check_scale_stats(g, z64, what):
+    """z-loss, entropy, top probability and top-2 gap: fp32 token means against the
+    float64 oracle on the same logits, to 2e-5 relative (1e-6 absolute near 0)."""
+    for name, want in (("z_loss", om.z_loss(z64)), ("entropy", om.router_entropy(z64)),
+                       ("max_prob", om.mean_max_prob(z64)), ("top_gap", om.top_gap(z64))):
+        assert abs(g[name] - want) <= 2e-5 * abs(want) + 1e-6, f"{what}: {name} {g[name]} vs {want}"
+
+
 def full_check(wl, W, T, sample=None, seed=0):
     """Run the fused forward on T tokens and compare everything with the oracle."""
     inp = wk.make_inputs(wl, T=T)
@@ -66,6 +74,7 @@ def full_check(wl, W, T, sample=None, seed=0):
     if wl.aux_alpha > 0:
         aux64 = om.aux_loss(om.load_fractions(g["idx"], wl.E), P64, wl.aux_alpha)
         assert abs(g["aux"] - aux64) <= 1e-5 * max(1.0, abs(aux64))
+    check_scale_stats(g, r["z"], f"{wl.name} T={T}")
     keep = p["dest"] >= 0
     if sample is None:
         tokens = np.arange(T)
@@ -179,6 +188,32 @@ def test_router_many_experts_max_k():
     r = om.route(wk.to_f64(inp.x, wl.dtype), wk.to_f64(inp.w_router, wl.dtype), 16)
     check_routing(wl, gi, r)
     check_gates(wl, gi, gates.cpu().numpy(), r["z"])
+
+
+@pytest.mark.parametrize("std", [1, 5, 20])
+def test_router_scale_statistics(std):
+    """z-loss, entropy, top probability and top-2 gap at router logits of standard
+    deviation 1, 5 and 20 (the CME295 notes §3.4 scenario: 8 experts): the orthonormal
+    router scaled by std, so z ~ N(0, std^2); GPU against the oracle on the same bf16
+    operands, and the z-loss within 7 % of the printed 6.2 / 59.6 / 988.9."""
+    T = 4096
+    wl = _adhoc("zscale", 106, T=T, d=256, E=8, k=2, d_ff=64, dtype=wk.BF16, router="orthonormal")
+    inp = wk.make_inputs(wl, T=T)
+    wr_bits = wk.f32_to_bf16_bits(wk.bf16_bits_to_f32(inp.w_router) * np.float32(std))
+    cfg = config_of(wl, T)
+    idx = torch.empty((T, 2), dtype=torch.int32, device=dev())
+    gates = torch.empty((T, 2), dtype=torch.float32, device=dev())
+    st = moe.Stats.alloc(wl.E)
+    moe.route(cfg, to_dev(inp.x, wl.dtype), to_dev(wr_bits, wl.dtype), None, idx, gates, st,
+              moe.alloc_workspace(cfg, moe.STAGE_ROUTE))
+    torch.cuda.synchronize()
+    z64 = om.router_logits(wk.to_f64(inp.x, wl.dtype), wk.to_f64(wr_bits, wl.dtype))
+    g = {n: float(getattr(st, n).cpu()[0]) for n in ("z_loss", "entropy", "max_prob", "top_gap")}
+    check_scale_stats(g, z64, f"std {std}")
+    printed = {1: 6.2, 5: 59.6, 20: 988.9}[std]
+    assert abs(g["z_loss"] - printed) <= 0.07 * printed
+    log(f"[ok] logit std {std}: z_loss {g['z_loss']:.2f} entropy {g['entropy']:.4f} "
+        f"max_prob {g['max_prob']:.4f} gap {g['top_gap']:.4f}")
 
 
 def test_bias_changes_selection_not_gates():
