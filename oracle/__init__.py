@@ -8,6 +8,7 @@ Parity status of each function (the pins are the ``-m "not gpu"`` tests in
   router_logits, select_topk, gates_selected, gates_all, route  - pinned
   load_fractions, mean_probs, aux_loss, coverage_fraction         - pinned
   logsumexp_rows, z_loss, router_entropy, mean_max_prob, top_gap  - pinned
+  bias_update                                                     - pinned
   capacity, assign_rows, permutation_by_prefix_sum                - pinned
   swiglu, expert_ffn, combine, forward, dense_all_experts,
   token_output                                                    - pinned

@@ -175,6 +175,19 @@ def top_gap(z: np.ndarray) -> float:
     return float(np.mean(p[:, 0] - second))
 
 
+def bias_update(bias: np.ndarray, counts: np.ndarray, T: int, k: int, gamma: float) -> np.ndarray:
+    """Auxiliary-loss-free balancing step ([CME295] §4.2; [15-779] §2.4): after a
+    step, every expert loaded above the mean T·k/E has its selection bias lowered
+    by gamma, every expert below it raised by gamma, one exactly at the mean
+    left alone. The bias only enters the top-k selection, never the gates."""
+    b = np.asarray(bias, np.float64)
+    c = np.asarray(counts, np.int64)
+    E = b.shape[0]
+    # c_e > T k / E compared as integers: c_e·E vs T·k
+    direction = np.sign(c * E - T * k).astype(np.float64)
+    return b - gamma * direction
+
+
 def coverage_fraction(k: int, E: int, B: int) -> float:
     """Expected fraction of experts chosen by at least one of B tokens that
     each pick a uniformly random k-subset: 1 - (1 - k/E)^B ([CME295] §2.3;

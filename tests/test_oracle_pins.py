@@ -523,3 +523,41 @@ def test_entropy_gap_max_prob_closed_forms():
     z = np.array([[0.0, 0.0], [50.0, 0.0]])
     assert om.router_entropy(z) == pytest.approx(math.log(2) / 2, rel=1e-12)
     assert om.top_gap(z) == pytest.approx(0.5, rel=1e-12)
+
+
+# ---------------------------------------------------------------- auxiliary-loss-free bias
+
+def test_bias_update_rule_by_hand():
+    """[CME295] §4.2 / [15-779] §2.4: overloaded experts go down by gamma, underloaded
+    up, an expert exactly at the mean T·k/E stays; gamma = 0.001 as printed."""
+    b = np.array([0.0, 0.5, -0.25, 0.1])
+    # T = 10, k = 2, E = 4: mean load 5
+    out = om.bias_update(b, [9, 5, 1, 5], 10, 2, 0.001)
+    assert out.tolist() == [-0.001, 0.5, -0.249, 0.1]
+    # balanced routing leaves every bias unchanged; sum of changes is gamma·(#under - #over)
+    assert (om.bias_update(b, [5, 5, 5, 5], 10, 2, 0.001) == b).all()
+    # a mean that is not an integer: T·k/E = 7/3 for T = 7, k = 1, E = 3
+    out = om.bias_update(np.zeros(3), [3, 2, 2], 7, 1, 0.5)
+    assert out.tolist() == [-0.5, 0.5, 0.5]
+
+
+def test_bias_update_balances_a_skewed_router():
+    """Iterating the rule with the oracle's own selection on a skewed router lowers the
+    busiest expert's load towards the mean and raises the idlest (the behaviour
+    [CME295] §4.2 reports; its exact trajectory depends on an unstated setup, so only
+    the direction and the end state are checked)."""
+    rng = np.random.default_rng(5)
+    T, d, E, k = 2048, 64, 8, 2
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d)) / math.sqrt(d)
+    off = np.array([0.6, 0.3, 0.0, 0.0, 0.0, 0.0, -0.3, -0.6])
+    z = om.router_logits(x, wr) + off
+    b = np.zeros(E)
+    ratios = []
+    for _ in range(400):
+        idx, _ = om.select_topk(z + b, k)
+        c = np.bincount(idx.ravel(), minlength=E)
+        ratios.append((c.max() / (T * k / E), c.min() / (T * k / E)))
+        b = om.bias_update(b, c, T, k, 0.01)
+    assert ratios[0][0] > 1.3 and ratios[0][1] < 0.7
+    assert ratios[-1][0] < 1.06 and ratios[-1][1] > 0.94
