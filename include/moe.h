@@ -164,7 +164,8 @@ moe_status moe_workspace_size(const moe_config* cfg, moe_stage stage, size_t* by
  *   first, ties to the lower expert index; gates from the unbiased z.
  *   x[T,d] elt, w_router[E,d] elt, sel_bias[E] fp32 (nullable)
  *   -> idx[T,k] int32, gates[T,k] fp32 (both required).
- *   stats (nullable): fills f, P and aux when their pointers are set.        */
+ *   stats (nullable): fills f, P, aux, z_loss, entropy, max_prob and top_gap
+ *   when their pointers are set.                                              */
 moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
                      const float* sel_bias, int32_t* idx, float* gates,
                      const moe_stats* stats, void* ws, size_t ws_bytes, void* stream);
@@ -222,6 +223,18 @@ int32_t moe_act_stride(const moe_config* cfg);
 moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* dest,
                        const float* gates, float* y, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* Auxiliary-loss-free balancing step ([CME295] §4.2; [15-779] §2.4): after a
+ * step, bias[e] -= gamma if counts[e] > T*k/E, += gamma if counts[e] < T*k/E,
+ * unchanged at the mean (compared exactly as counts[e]*E vs T*k). The bias is
+ * the sel_bias of moe_route / moe_forward: it moves the top-k selection only,
+ * never the gates.
+ *   counts[E] int32 (e.g. moe_stats.counts of the step; required),
+ *   bias[E] fp32, updated in place (required); gamma finite.
+ * Errors: INVALID_ARG (bad config, NULL or misaligned pointer, non-finite
+ * gamma) before anything is launched.                                        */
+moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float gamma, float* bias,
+                           void* stream);
 
 /* The whole layer in one call: route -> permute -> grouped experts (+shared)
  * -> combine, on one stream, with every intermediate in `ws`.

@@ -23,7 +23,7 @@ GATE_SELECTED, GATE_ALL = 0, 1
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_workspace_size", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_expert_gateup", "moe_expert_down",
-           "moe_act_stride", "moe_combine", "moe_forward")
+           "moe_act_stride", "moe_combine", "moe_forward", "moe_update_bias")
 
 
 class MoeConfig(ctypes.Structure):
@@ -77,6 +77,7 @@ def load(path: str = LIB_PATH):
         "moe_combine": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, sz, vp]),
         "moe_forward": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        stp, vp, sz, vp]),
+        "moe_update_bias": (ctypes.c_int, [cfgp, vp, ctypes.c_float, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -214,6 +215,12 @@ def combine(cfg, y_perm, dest, gates, y, ws=None, stream=None):
     wp, wb = _ws(ws)
     _check(load().moe_combine(ctypes.byref(cfg), _p(y_perm), _p(dest), _p(gates), _p(y), wp, wb,
                               _stream(stream)), "moe_combine")
+
+
+def update_bias(cfg, counts, gamma: float, bias, stream=None):
+    """bias[e] -= gamma above the mean load T*k/E, += gamma below (in place)."""
+    _check(load().moe_update_bias(ctypes.byref(cfg), _p(counts), ctypes.c_float(gamma), _p(bias),
+                                  _stream(stream)), "moe_update_bias")
 
 
 def forward(cfg, x, w_router, sel_bias, w1, w3, w2, ws1, ws3, ws2, y, idx=None, gates=None,

@@ -24,6 +24,8 @@ constexpr int kScaleStats = 4;
 hipError_t launch_router_select(const float* z, const float* bias, int T, int E, int k,
                                 int gate_all, int32_t* idx, float* gates, float* p_part,
                                 int32_t* c_part, float* q_part, hipStream_t s);
+hipError_t launch_bias_update(const int32_t* counts, int T, int k, int E, float gamma, float* bias,
+                              hipStream_t s);
 hipError_t launch_router_stats(const float* p_part, const int32_t* c_part, const float* q_part,
                                int nblocks, int T, int E, float alpha, float* f, float* P,
                                float* aux, float* fp, float* z_loss, float* entropy,

@@ -420,6 +420,20 @@ moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t
   return MOE_OK;
 }
 
+moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float gamma, float* bias,
+                           void* stream) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  REQUIRE(counts); REQUIRE(bias);
+  if (!std::isfinite(gamma)) return fail(MOE_ERR_INVALID_ARG, "gamma must be finite");
+  if (s.T == 0) return MOE_OK;   // no load to balance
+  MOE_HIP(moe::launch_bias_update(counts, s.T, s.k, s.E, gamma, bias,
+                                  static_cast<hipStream_t>(stream)),
+          "bias_update");
+  return MOE_OK;
+}
+
 moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
                        const float* sel_bias, const void* w1, const void* w3, const void* w2,
                        const void* ws1, const void* ws3, const void* ws2, float* y,

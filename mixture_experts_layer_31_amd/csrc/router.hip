@@ -382,6 +382,18 @@ __global__ __launch_bounds__(256) void router_aux_kernel(
   }
 }
 
+// Auxiliary-loss-free balancing (CME295 notes §4.2; CMU 15-779 notes §2.4):
+// bias[e] moves by -gamma above the mean load T*k/E, +gamma below, 0 at it.
+__global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restrict__ counts,
+                                                          long long Tk, int E, float gamma,
+                                                          float* __restrict__ bias) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  const long long c = static_cast<long long>(counts[e]) * E;
+  if (c > Tk) bias[e] -= gamma;
+  else if (c < Tk) bias[e] += gamma;
+}
+
 // ---------------------------------------------------------------- launchers
 
 template <typename Tin>
@@ -451,6 +463,13 @@ hipError_t launch_router_stats(const float* p_part, const int32_t* c_part, const
   router_stats_kernel<<<dim3(E), dim3(256), 0, s>>>(p_part, c_part, nblocks, T, E, f, P, fp);
   router_aux_kernel<<<dim3(1), dim3(256), 0, s>>>(fp, E, alpha, aux, q_part, nblocks, T, z_loss,
                                                   entropy, max_prob, top_gap);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_update(const int32_t* counts, int T, int k, int E, float gamma, float* bias,
+                              hipStream_t s) {
+  bias_update_kernel<<<dim3((E + 255) / 256), dim3(256), 0, s>>>(
+      counts, static_cast<long long>(T) * k, E, gamma, bias);
   return hipGetLastError();
 }
 

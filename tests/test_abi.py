@@ -134,6 +134,24 @@ def test_entry_points_reject_before_launch(lib):
                               None) == moe.ERR_INVALID_ARG
 
 
+def test_update_bias_rejects_before_launch(lib):
+    """moe_update_bias: NULL / misaligned counts or bias, a non-finite gamma and a bad
+    config are rejected on the host; T == 0 is a no-op."""
+    c = _cfg()
+    P = FAKE
+    g = ctypes.c_float(0.001)
+    assert lib.moe_update_bias(ctypes.byref(c), None, g, P, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_update_bias(ctypes.byref(c), P, g, None, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_update_bias(ctypes.byref(c), P + 4, g, P, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_update_bias(ctypes.byref(c), P, ctypes.c_float(float("nan")), P,
+                               None) == moe.ERR_INVALID_ARG
+    assert lib.moe_update_bias(ctypes.byref(c), P, ctypes.c_float(float("inf")), P,
+                               None) == moe.ERR_INVALID_ARG
+    assert lib.moe_update_bias(ctypes.byref(_cfg(E=0)), P, g, P, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_update_bias(None, P, g, P, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_update_bias(ctypes.byref(_cfg(T=0)), P, g, P, None) == moe.OK
+
+
 def test_zero_tokens_is_a_noop(lib):
     """T == 0 validates and returns MOE_OK without touching any pointer."""
     c = _cfg(T=0)

@@ -216,6 +216,65 @@ def test_router_scale_statistics(std):
         f"max_prob {g['max_prob']:.4f} gap {g['top_gap']:.4f}")
 
 
+def _route_counts(cfg, x, wr, bias, T, k, E):
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev())
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev())
+    st = moe.Stats.alloc(E)
+    moe.route(cfg, x, wr, bias, idx, gates, st, moe.alloc_workspace(cfg, moe.STAGE_ROUTE))
+    moe.permute(cfg, idx, None, torch.empty(E + 1, dtype=torch.int32, device=dev()),
+                torch.empty((T, k), dtype=torch.int32, device=dev()),
+                torch.empty(T * k, dtype=torch.int32, device=dev()), None, st,
+                moe.alloc_workspace(cfg, moe.STAGE_PERMUTE))
+    return st.counts
+
+
+def test_update_bias_one_step_matches_oracle():
+    """One auxiliary-loss-free step (CME295 notes §4.2) on the GPU's own counts: the
+    direction is exact (integer comparison with the mean load), the bias moves by gamma
+    in fp32."""
+    T, E, k = 1000, 64, 1
+    wl = _adhoc("bias_step", 107, T=T, d=256, E=E, k=k, d_ff=64, dtype=wk.BF16, offset_var=1.5)
+    inp = wk.make_inputs(wl, T=T)
+    cfg = config_of(wl, T)
+    rng = np.random.default_rng(3)
+    b0 = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    bias = torch.from_numpy(b0.copy()).to(dev())
+    counts = _route_counts(cfg, to_dev(inp.x, wl.dtype), to_dev(inp.w_router, wl.dtype), bias,
+                           T, k, E)
+    moe.update_bias(cfg, counts, 0.001, bias)
+    torch.cuda.synchronize()
+    c = counts.cpu().numpy()
+    want = om.bias_update(b0.astype(np.float64), c, T, k, 0.001)
+    got = bias.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got - want)) <= 1.2e-7 * np.maximum(1.0, np.abs(want)).max()
+    moved = np.sign(got - b0)
+    assert (moved == -np.sign(c * E - T * k)).all()
+
+
+def test_update_bias_balances_on_gpu():
+    """The balancing loop entirely on the GPU (route -> counts -> update, 300 steps,
+    gamma = 0.01) takes a skewed router from max/mean > 1.3 to within 6 % of the mean."""
+    T, E, k = 2048, 8, 2
+    wl = _adhoc("bias_loop", 108, T=T, d=256, E=E, k=k, d_ff=64, dtype=wk.BF16,
+                offsets=(0.6, 0.3, 0.0, 0.0, 0.0, 0.0, -0.3, -0.6))
+    inp = wk.make_inputs(wl, T=T)
+    cfg = config_of(wl, T)
+    x, wr = to_dev(inp.x, wl.dtype), to_dev(inp.w_router, wl.dtype)
+    bias = torch.zeros(E, dtype=torch.float32, device=dev())
+    first = None
+    for _ in range(300):
+        counts = _route_counts(cfg, x, wr, bias, T, k, E)
+        if first is None:
+            first = counts.cpu().numpy()
+        moe.update_bias(cfg, counts, 0.01, bias)
+    last = _route_counts(cfg, x, wr, bias, T, k, E).cpu().numpy()
+    mean = T * k / E
+    log(f"[ok] bias loop: max/mean {first.max() / mean:.3f} -> {last.max() / mean:.3f}, "
+        f"min/mean {first.min() / mean:.3f} -> {last.min() / mean:.3f}")
+    assert first.max() / mean > 1.3
+    assert last.max() / mean < 1.06 and last.min() / mean > 0.94
+
+
 def test_bias_changes_selection_not_gates():
     """DeepSeek-style selection bias on the GPU: tokens whose selection the bias does not move
     get bitwise-identical gates (CME295 notes §4.2)."""
