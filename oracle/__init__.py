@@ -9,6 +9,8 @@ Parity status of each function (the pins are the ``-m "not gpu"`` tests in
   load_fractions, mean_probs, aux_loss, coverage_fraction         - pinned
   logsumexp_rows, z_loss, router_entropy, mean_max_prob, top_gap  - pinned
   bias_update                                                     - pinned
+  ep_group_ids, ep_permutation, ep_group_expert, ep_send_rows,
+  ep_dispatch_bytes, forward(ep=n)                                - pinned
   capacity, assign_rows, permutation_by_prefix_sum                - pinned
   swiglu, expert_ffn, combine, forward, dense_all_experts,
   token_output                                                    - pinned

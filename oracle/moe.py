@@ -277,6 +277,56 @@ def permutation_by_prefix_sum(idx: np.ndarray, E: int):
 
 # ------------------------------------------------------------------ experts
 
+# ---------------------------------------------------------------- expert parallelism, simulated
+
+def ep_group_ids(idx: np.ndarray, E: int, n: int) -> np.ndarray:
+    """Expert parallelism over n ranks ([15-779] §5.1; [CME295] §5): rank r holds
+    experts [r·E/n, (r+1)·E/n) and tokens [r·T/n, (r+1)·T/n). An assignment (t, e)
+    travels from source rank s = t // (T/n) to destination rank r = e // (E/n).
+    Its group is (r, s, local expert) numbered destination-major, so the rows a
+    source sends to a destination, and everything a destination receives, are
+    contiguous: group = (r·n + s)·(E/n) + e mod (E/n)."""
+    idx = np.asarray(idx, np.int64)
+    T = idx.shape[0]
+    El, Tl = E // n, T // n
+    t = np.repeat(np.arange(T)[:, None], idx.shape[1], axis=1)
+    return ((idx // El) * n + t // Tl) * El + idx % El
+
+
+def ep_permutation(idx: np.ndarray, E: int, n: int):
+    """Rows grouped by (destination rank, source rank, local expert), token order
+    inside a group: the permutation by prefix sum ([15-779] §3.3) over the n·E
+    groups. Returns offsets[n·E + 1], dest[T, k], src[R]."""
+    a = assign_rows(ep_group_ids(idx, E, n), n * E)
+    return a["offsets"], a["dest"], a["src"]
+
+
+def ep_group_expert(g: np.ndarray, E: int, n: int) -> np.ndarray:
+    """Expert whose weights group g multiplies."""
+    El = E // n
+    g = np.asarray(g, np.int64)
+    return (g // (n * El)) * El + g % El
+
+
+def ep_send_rows(offsets: np.ndarray, E: int, n: int) -> np.ndarray:
+    """rows[s, r]: rows source rank s sends to destination rank r in the dispatch
+    all-to-all (s == r stays local); the combine all-to-all returns the same rows."""
+    El = E // n
+    o = np.asarray(offsets, np.int64)
+    rows = np.zeros((n, n), np.int64)
+    for r in range(n):
+        for s in range(n):
+            g0 = (r * n + s) * El
+            rows[s, r] = o[g0 + El] - o[g0]
+    return rows
+
+
+def ep_dispatch_bytes(tokens_per_rank: int, k: int, n: int, d: int, elt: int) -> float:
+    """Bytes one rank sends in one all-to-all under uniform routing:
+    N·k·(1 - 1/n)·d·bytes ([15-779] §5.1 and §10 exercise 6), independent of E."""
+    return tokens_per_rank * k * (1.0 - 1.0 / n) * d * elt
+
+
 def silu(u: np.ndarray) -> np.ndarray:
     with np.errstate(over="ignore"):
         return u / (1.0 + np.exp(-u))
@@ -331,12 +381,14 @@ def combine(yp: np.ndarray, dest: np.ndarray, gates: np.ndarray, d: int,
 
 def forward(x, w_router, experts: ExpertFn, k: int, gate: str = GATE_SELECTED,
             bias=None, cf: float = 0.0, shared=None, alpha: float = 0.0,
-            idx_override: Optional[np.ndarray] = None):
+            idx_override: Optional[np.ndarray] = None, ep: int = 1):
     """The whole layer: route -> permute -> grouped experts -> combine
     ([15-779] §3.2). ``shared`` is (W1, W3, W2) of an always-on expert whose
     output is added with weight 1 ([CME295] §4.1). ``idx_override`` replaces
     the selection (gates are recomputed from z for it), which lets a caller
-    evaluate the layer under another implementation's routing.
+    evaluate the layer under another implementation's routing. ``ep`` > 1 lays
+    the rows out as ``ep`` simulated expert-parallel ranks (``ep_permutation``;
+    no capacity).
 
     Returns a dict with every intermediate and the stats."""
     x = np.asarray(x, np.float64)
@@ -347,9 +399,19 @@ def forward(x, w_router, experts: ExpertFn, k: int, gate: str = GATE_SELECTED,
         r["gates"] = (gates_selected(r["z"], idx) if gate == GATE_SELECTED
                       else gates_all(r["z"], idx))
     E = np.asarray(w_router).shape[0]
-    p = assign_rows(idx, E, cf)
-    xp = x[p["src"]]
-    yp = expert_ffn(xp, p["offsets"], experts)
+    if ep > 1:
+        if cf > 0:
+            raise ValueError("capacity is not modelled with simulated expert parallelism")
+        offsets, dest, src = ep_permutation(idx, E, ep)
+        counts = np.bincount(idx.ravel(), minlength=E)
+        p = dict(counts=counts, kept=counts.copy(), offsets=offsets, dest=dest, src=src,
+                 n_dropped=0, C=None)
+        xp = x[src]
+        yp = expert_ffn(xp, offsets, lambda g: experts(int(ep_group_expert(g, E, ep))))
+    else:
+        p = assign_rows(idx, E, cf)
+        xp = x[p["src"]]
+        yp = expert_ffn(xp, p["offsets"], experts)
     sh = swiglu(x, *shared) if shared is not None else None
     y = combine(yp, p["dest"], r["gates"], d, sh)
     f = load_fractions(idx, E)

@@ -561,3 +561,85 @@ def test_bias_update_balances_a_skewed_router():
         b = om.bias_update(b, c, T, k, 0.01)
     assert ratios[0][0] > 1.3 and ratios[0][1] < 0.7
     assert ratios[-1][0] < 1.06 and ratios[-1][1] > 0.94
+
+
+# ---------------------------------------------------------------- simulated expert parallelism
+
+def test_ep_layout_brute_force():
+    """Rows sorted by (destination rank, source rank, local expert, token): the order a
+    destination receives the dispatch all-to-all in ([15-779] §5.1)."""
+    rng = np.random.default_rng(21)
+    for (T, E, n, k) in ((12, 6, 3, 2), (16, 8, 4, 1), (20, 8, 2, 3), (9, 3, 3, 3)):
+        z = rng.standard_normal((T, E))
+        idx, _ = om.select_topk(z, k)
+        offsets, dest, src = om.ep_permutation(idx, E, n)
+        El, Tl = E // n, T // n
+        pairs = sorted(((int(e) // El, t // Tl, int(e) % El, t, j) for t in range(T)
+                        for j, e in enumerate(idx[t])))
+        assert [p[3] for p in pairs] == src.tolist()
+        for row, (r, s, el, t, j) in enumerate(pairs):
+            assert dest[t, j] == row
+            g = (r * n + s) * El + el
+            assert offsets[g] <= row < offsets[g + 1]
+            assert om.ep_group_expert(g, E, n) == r * El + el
+
+
+def test_ep_forward_equals_single_device_layout():
+    """The layer computed in the expert-parallel layout equals the single-device layout
+    ([15-779] §5.1 reports a maximum difference of 0): every row's arithmetic is the same,
+    only float64 BLAS rounding may differ with the row grouping (<= 1e-12 relative)."""
+    rng = np.random.default_rng(22)
+    T, d, E, k, f = 24, 16, 8, 2, 12
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d))
+    W = [(rng.standard_normal((f, d)), rng.standard_normal((f, d)), rng.standard_normal((d, f)))
+         for _ in range(E)]
+    base = om.forward(x, wr, lambda e: W[e], k)
+    for n in (2, 4, 8):
+        ep = om.forward(x, wr, lambda e: W[e], k, ep=n)
+        scale = np.max(np.abs(base["y"]))
+        assert np.max(np.abs(ep["y"] - base["y"])) <= 1e-12 * scale
+        if n < E:   # with one expert per rank the two layouts coincide
+            assert not np.array_equal(ep["src"], base["src"])
+
+
+def test_ep_send_rows_identities():
+    """Each source sends all of its T/n tokens' k assignments (its own rank included);
+    each destination computes the rows of its experts; total = T·k."""
+    rng = np.random.default_rng(23)
+    T, E, n, k = 64, 16, 4, 2
+    idx, _ = om.select_topk(rng.standard_normal((T, E)), k)
+    offsets, _, _ = om.ep_permutation(idx, E, n)
+    rows = om.ep_send_rows(offsets, E, n)
+    assert (rows.sum(axis=1) == T // n * k).all()
+    counts = np.bincount(idx.ravel(), minlength=E)
+    assert rows.sum(axis=0).tolist() == counts.reshape(n, E // n).sum(axis=1).tolist()
+    assert rows.sum() == T * k
+
+
+def test_ep_printed_figures():
+    """[15-779] §10 exercise 6 (822 MB, 16.4 ms at 50 GB/s; k = 2: 205 MB, 4.1 ms) and the
+    §5.1 formula value 918 KB are the dispatch-bytes formula; under uniform random top-2
+    routing the §5.1 demo's busiest sender (926 KB printed) sits just above the formula and
+    the rows per device (998-1053 printed) spread a few percent around 1024."""
+    g = _gold("printed_numbers.json")["expert_parallel"]
+    x6 = g["ex6"]
+    b = om.ep_dispatch_bytes(x6["tokens_per_rank"], x6["k"], x6["n"], x6["d"], x6["elt"])
+    assert abs(b / 1e6 - x6["MB"]) < 0.5 and abs(b / 50e9 * 1e3 - x6["ms_at_50GBps"]) < 0.05
+    b2 = om.ep_dispatch_bytes(x6["tokens_per_rank"], 2, x6["n"], x6["d"], x6["elt"])
+    assert abs(b2 / 1e6 - x6["k2_MB"]) < 1.0 and abs(b2 / 50e9 * 1e3 - x6["k2_ms"]) < 0.05
+    dm = g["demo"]
+    n, E, Tl, k = dm["n"], dm["E"], dm["tokens_per_rank"], dm["k"]
+    d = 256   # the width the printed formula value implies: 512·2·(7/8)·d·4 B = 918 KB
+    formula = om.ep_dispatch_bytes(Tl, k, n, d, dm["elt"])
+    assert abs(formula / 1e3 - dm["formula_KB"]) < 0.5
+    for seed in range(5):
+        rng = np.random.default_rng(seed)
+        idx, _ = om.select_topk(rng.standard_normal((n * Tl, E)), k)
+        offsets, _, _ = om.ep_permutation(idx, E, n)
+        rows = om.ep_send_rows(offsets, E, n)
+        sent = (rows.sum(axis=1) - np.diag(rows)) * d * dm["elt"]
+        assert formula <= sent.max() <= 1.05 * formula            # printed 926 KB
+        per_dev = rows.sum(axis=0)
+        assert per_dev.mean() == dm["rows_mean"]
+        assert 0.93 * dm["rows_mean"] <= per_dev.min() and per_dev.max() <= 1.07 * dm["rows_mean"]
