@@ -11,7 +11,7 @@ roofline of the dominant kernel (the grouped gate/up GEMM), timed with HIP
 events recorded on the library's stream around that kernel in every timed
 step, and the float64 CPU oracle timed on a bounded sample of the workload.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--ep N]
   python bench.py --calibrate-copy     # plain 1 GiB copies, for counter scaling
 """
 from __future__ import annotations
@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens in the CPU-oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--ep", type=int, default=0,
+                    help="lay the rows out as N simulated expert-parallel ranks and report "
+                         "the dispatch volume per rank")
     return ap.parse_args()
 
 
@@ -129,13 +132,15 @@ def main():
 
     cfg = moe.make_config(T, wl.d, wl.E, wl.k, wl.d_ff, n_shared=wl.n_shared,
                           d_ff_shared=wl.d_ff_shared, gate=wl.gate, dtype=wl.dtype,
-                          capacity_factor=wl.capacity_factor, aux_alpha=wl.aux_alpha)
+                          capacity_factor=wl.capacity_factor, aux_alpha=wl.aux_alpha,
+                          ep_ranks=args.ep)
+    G = wl.E * (args.ep if args.ep > 1 else 1)
     R = T * wl.k
     rows = R + wl.n_shared * T
     i32 = torch.int32
     idx = torch.empty((T, wl.k), dtype=i32, device=dev)
     gates = torch.empty((T, wl.k), dtype=torch.float32, device=dev)
-    offsets = torch.empty(wl.E + 1, dtype=i32, device=dev)
+    offsets = torch.empty(G + 1, dtype=i32, device=dev)
     dest = torch.empty((T, wl.k), dtype=i32, device=dev)
     src = torch.empty(R, dtype=i32, device=dev)
     act = torch.empty((rows, moe.act_stride(cfg)), dtype=x.dtype, device=dev)
@@ -160,7 +165,7 @@ def main():
         moe.combine(cfg, y_perm, dest, gates, y, None, stream)
 
     # routing statistics of this batch (outside the timed region)
-    st = moe.Stats.alloc(wl.E)
+    st = moe.Stats.alloc(wl.E, groups=G)
     step(stats=st)
     torch.cuda.synchronize()
     kept = st.kept.cpu().numpy().astype(np.int64)
@@ -230,6 +235,22 @@ def main():
     step_gbps = B_step / (ms_step * 1e-3) / 1e9
     step_bound = "mfma" if F_step / (peak_f * 1e12) >= B_step / (PEAK_HBM_GBPS * 1e9) else "hbm"
 
+    ep_report = None
+    if args.ep > 1:
+        # dispatch volume of this batch in the simulated layout (the combine returns the same)
+        n = args.ep
+        rows = torch.empty(n * n, dtype=i32, device=dev)
+        moe.ep_traffic(cfg, offsets, rows, stream)
+        torch.cuda.synchronize()
+        rows = rows.cpu().numpy().astype(np.int64).reshape(n, n)
+        row_bytes = d * elt
+        sent = (rows.sum(axis=1) - np.diag(rows)) * row_bytes
+        ep_report = {"ranks": n, "max_send_bytes": int(sent.max()),
+                     "mean_send_bytes": float(sent.mean()),
+                     "formula_bytes": (T // n) * wl.k * (1.0 - 1.0 / n) * row_bytes,
+                     "rows_per_rank_min": int(rows.sum(axis=0).min()),
+                     "rows_per_rank_max": int(rows.sum(axis=0).max())}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, inp, host, args.cpu_sample)
@@ -259,6 +280,7 @@ def main():
                  "wall_s": round(wall, 4)},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "expert_parallel": ep_report,
     }
     print(json.dumps(out), flush=True)
 

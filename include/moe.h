@@ -107,7 +107,17 @@ typedef struct {
                                n_shared == 0)                                   */
   int32_t gate_mode;        /* moe_gate_mode                                    */
   int32_t dtype;            /* moe_dtype of x and all weights                   */
-  int32_t reserved;         /* must be 0                                        */
+  int32_t ep_ranks;         /* 0 or 1: one device. n > 1: lay the rows out as n
+                               simulated expert-parallel ranks ([15-779] §5.1):
+                               rank r holds experts [r*E/n, (r+1)*E/n) and
+                               tokens [r*T/n, (r+1)*T/n); rows are grouped by
+                               (destination rank, source rank, local expert),
+                               token order inside a group, so each rank's send
+                               and receive buffers are contiguous. n must
+                               divide E and T, n*E <= 1024, no capacity.
+                               offsets then has n*E + 1 entries (group
+                               g = (r*n + s)*(E/n) + local expert) and the
+                               stats counts/kept n*E (one per group).         */
   double capacity_factor;   /* cf <= 0: no capacity. Otherwise each expert keeps
                                at most C = ceil(cf*T*k/E) assignments, first
                                choices before second choices, tokens in order
@@ -224,12 +234,24 @@ moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t
                        const float* gates, float* y, void* ws, size_t ws_bytes,
                        void* stream);
 
+/* Dispatch volume of the simulated expert-parallel layout (cfg->ep_ranks = n
+ * > 1; [15-779] §5.1 and §10 exercise 6): rows[s*n + r] = rows source rank s
+ * sends to destination rank r in the dispatch all-to-all (s == r stays local;
+ * the combine all-to-all returns the same rows), read from the offsets that
+ * moe_permute / moe_forward produced. Bytes = rows * d * element size.
+ *   offsets[n*E + 1] int32, rows[n*n] int32 (both required).
+ * T == 0 leaves rows untouched. Errors: INVALID_ARG (bad config,
+ * ep_ranks <= 1, NULL or misaligned pointer).                                */
+moe_status moe_ep_traffic(const moe_config* cfg, const int32_t* offsets, int32_t* rows,
+                          void* stream);
+
 /* Auxiliary-loss-free balancing step ([CME295] §4.2; [15-779] §2.4): after a
  * step, bias[e] -= gamma if counts[e] > T*k/E, += gamma if counts[e] < T*k/E,
  * unchanged at the mean (compared exactly as counts[e]*E vs T*k). The bias is
  * the sel_bias of moe_route / moe_forward: it moves the top-k selection only,
  * never the gates.
- *   counts[E] int32 (e.g. moe_stats.counts of the step; required),
+ *   counts[E] int32 (e.g. moe_stats.counts of the step; with ep_ranks = n > 1
+ *   the per-group counts[n*E], summed per expert; required),
  *   bias[E] fp32, updated in place (required); gamma finite.
  * Errors: INVALID_ARG (bad config, NULL or misaligned pointer, non-finite
  * gamma) before anything is launched.                                        */

@@ -23,14 +23,14 @@ GATE_SELECTED, GATE_ALL = 0, 1
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_workspace_size", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_expert_gateup", "moe_expert_down",
-           "moe_act_stride", "moe_combine", "moe_forward", "moe_update_bias")
+           "moe_act_stride", "moe_combine", "moe_forward", "moe_update_bias", "moe_ep_traffic")
 
 
 class MoeConfig(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("d_ff_shared", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("ep_ranks", ctypes.c_int32),
                 ("capacity_factor", ctypes.c_double), ("aux_alpha", ctypes.c_float),
                 ("reserved2", ctypes.c_float)]
 
@@ -78,6 +78,7 @@ def load(path: str = LIB_PATH):
         "moe_forward": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        stp, vp, sz, vp]),
         "moe_update_bias": (ctypes.c_int, [cfgp, vp, ctypes.c_float, vp, vp]),
+        "moe_ep_traffic": (ctypes.c_int, [cfgp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -116,10 +117,11 @@ def _stream(stream) -> Optional[int]:
 
 def make_config(T: int, d: int, E: int, k: int, d_ff: int, *, n_shared: int = 0,
                 d_ff_shared: int = 0, gate: str = "selected", dtype: str = "bf16",
-                capacity_factor: float = 0.0, aux_alpha: float = 0.0) -> MoeConfig:
+                capacity_factor: float = 0.0, aux_alpha: float = 0.0,
+                ep_ranks: int = 0) -> MoeConfig:
     return MoeConfig(T=T, d=d, E=E, k=k, d_ff=d_ff, n_shared=n_shared, d_ff_shared=d_ff_shared,
                      gate_mode=GATE_ALL if gate == "all" else GATE_SELECTED,
-                     dtype=BF16 if dtype == "bf16" else F32, reserved=0,
+                     dtype=BF16 if dtype == "bf16" else F32, ep_ranks=int(ep_ranks),
                      capacity_factor=float(capacity_factor), aux_alpha=float(aux_alpha),
                      reserved2=0.0)
 
@@ -155,11 +157,14 @@ class Stats:
     top_gap: object = None
 
     @staticmethod
-    def alloc(E: int, device="cuda") -> "Stats":
+    def alloc(E: int, device="cuda", groups: Optional[int] = None) -> "Stats":
+        """counts/kept hold one entry per row group: E, or ep_ranks*E with the
+        expert-parallel layout (pass groups=ep_ranks*E then)."""
         import torch
         z = lambda n, dt: torch.zeros(n, dtype=dt, device=device)
         f1 = lambda: z(1, torch.float32)
-        return Stats(z(E, torch.int32), z(E, torch.int32), z(1, torch.int32),
+        G = groups or E
+        return Stats(z(G, torch.int32), z(G, torch.int32), z(1, torch.int32),
                      z(E, torch.float32), z(E, torch.float32), f1(), f1(), f1(), f1(), f1())
 
     def c(self) -> MoeStats:
@@ -221,6 +226,12 @@ def update_bias(cfg, counts, gamma: float, bias, stream=None):
     """bias[e] -= gamma above the mean load T*k/E, += gamma below (in place)."""
     _check(load().moe_update_bias(ctypes.byref(cfg), _p(counts), ctypes.c_float(gamma), _p(bias),
                                   _stream(stream)), "moe_update_bias")
+
+
+def ep_traffic(cfg, offsets, rows, stream=None):
+    """rows[s*n + r]: rows source rank s sends to rank r (cfg.ep_ranks = n > 1)."""
+    _check(load().moe_ep_traffic(ctypes.byref(cfg), _p(offsets), _p(rows), _stream(stream)),
+           "moe_ep_traffic")
 
 
 def forward(cfg, x, w_router, sel_bias, w1, w3, w2, ws1, ws3, ws2, y, idx=None, gates=None,

@@ -616,7 +616,7 @@ static hipError_t run_stream(const GemmTileMap& map, const uint16_t* xa, const i
 // ---------------------------------------------------------------- tile table
 
 __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restrict__ offsets,
-                                                        int E, int BM, int max_tiles,
+                                                        int E, int BM, int max_tiles, int ep,
                                                         int4* __restrict__ tiles) {
   __shared__ int part[1024];
   const int e = threadIdx.x;
@@ -636,7 +636,8 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
   }
   const int start = part[e] - nt;
   const int total = part[1023];
-  for (int i = 0; i < nt; ++i) tiles[start + i] = make_int4(e, lo + i * BM, min(BM, n - i * BM), 0);
+  const int w = tile_group_weights(e, E, ep);
+  for (int i = 0; i < nt; ++i) tiles[start + i] = make_int4(w, lo + i * BM, min(BM, n - i * BM), 0);
   for (int i = total + e; i < max_tiles; i += 1024) tiles[i] = make_int4(0, 0, 0, 0);
 }
 
@@ -658,9 +659,9 @@ int gemm_max_tiles(int BM, int R_max, int E) {
   return (R_max + BM - 1) / BM + (E < R_max ? E : R_max);
 }
 
-hipError_t launch_tile_map(const int32_t* offsets, int E, int BM, int max_tiles, int32_t* tiles,
-                           hipStream_t s) {
-  tile_map_kernel<<<dim3(1), dim3(1024), 0, s>>>(offsets, E, BM, max_tiles,
+hipError_t launch_tile_map(const int32_t* offsets, int E, int BM, int max_tiles, int ep,
+                           int32_t* tiles, hipStream_t s) {
+  tile_map_kernel<<<dim3(1), dim3(1024), 0, s>>>(offsets, E, BM, max_tiles, ep,
                                                  reinterpret_cast<int4*>(tiles));
   return hipGetLastError();
 }

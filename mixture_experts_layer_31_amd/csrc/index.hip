@@ -170,6 +170,51 @@ __global__ __launch_bounds__(kTB) void index_rank_kernel(
   }
 }
 
+// ---------------------------------------------------------------- expert parallelism
+//
+// Simulated expert parallelism over n ranks (CMU 15-779 notes §5.1): rank r
+// holds experts [r*E/n, (r+1)*E/n) and tokens [r*T/n, (r+1)*T/n). Assignment
+// (t, e) goes from source rank s = t / (T/n) to destination rank
+// r = e / (E/n); its row group is (r*n + s)*(E/n) + e % (E/n), so the index
+// over these n*E groups lays each rank's send and receive rows out
+// contiguously. An out-of-range expert id stays out of range.
+__global__ __launch_bounds__(256) void ep_group_ids_kernel(const int32_t* __restrict__ idx,
+                                                           int T, int k, int E, int n,
+                                                           int32_t* __restrict__ gid) {
+  const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<long long>(T) * k) return;
+  const int e = idx[i];
+  const int t = static_cast<int>(i / k);
+  const int El = E / n, Tl = T / n;
+  gid[i] = static_cast<unsigned>(e) < static_cast<unsigned>(E)
+               ? ((e / El) * n + t / Tl) * El + e % El
+               : -1;
+}
+
+hipError_t launch_ep_group_ids(const int32_t* idx, int T, int k, int E, int n, int32_t* gid,
+                               hipStream_t s) {
+  const long long R = static_cast<long long>(T) * k;
+  if (R == 0) return hipSuccess;
+  ep_group_ids_kernel<<<dim3((R + 255) / 256), dim3(256), 0, s>>>(idx, T, k, E, n, gid);
+  return hipGetLastError();
+}
+
+// rows[s*n + r] = rows of the groups (r, s, *): offsets over n*E groups
+__global__ __launch_bounds__(256) void ep_traffic_kernel(const int32_t* __restrict__ offsets,
+                                                         int n, int El,
+                                                         int32_t* __restrict__ rows) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n * n) return;
+  const int src = i / n, dst = i % n;
+  const int g0 = (dst * n + src) * El;
+  rows[i] = offsets[g0 + El] - offsets[g0];
+}
+
+hipError_t launch_ep_traffic(const int32_t* offsets, int n, int E, int32_t* rows, hipStream_t s) {
+  ep_traffic_kernel<<<dim3((n * n + 255) / 256), dim3(256), 0, s>>>(offsets, n, E / n, rows);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- one workgroup
 //
 // T <= 256 tokens and at most kIndexSingleMaxKeys keys (decode and small
@@ -183,7 +228,7 @@ __global__ __launch_bounds__(1024) void index_single_kernel(
     const int32_t* __restrict__ idx, int T, int k, int E, long long C,
     int32_t* __restrict__ offsets, int32_t* __restrict__ dest, int32_t* __restrict__ src,
     int32_t* __restrict__ counts_out, int32_t* __restrict__ kept_out,
-    int32_t* __restrict__ n_dropped, int BM, int max_tiles, int4* __restrict__ tiles) {
+    int32_t* __restrict__ n_dropped, int BM, int max_tiles, int ep, int4* __restrict__ tiles) {
   extern __shared__ uint32_t smem[];
   const int cap = C >= 0;
   const int nkeys = cap ? E * k : E;
@@ -298,7 +343,8 @@ __global__ __launch_bounds__(1024) void index_single_kernel(
   }
   const int start = part[tid] - nt;
   const int total = part[1023];
-  for (int i = 0; i < nt; ++i) tiles[start + i] = make_int4(e, lo + i * BM, min(BM, n - i * BM), 0);
+  const int w = tile_group_weights(e, E, ep);
+  for (int i = 0; i < nt; ++i) tiles[start + i] = make_int4(w, lo + i * BM, min(BM, n - i * BM), 0);
   for (int i = total + tid; i < max_tiles; i += 1024) tiles[i] = make_int4(0, 0, 0, 0);
 }
 
@@ -313,7 +359,7 @@ bool index_single_ok(int T, int E, int k, bool cap) {
 hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capacity,
                         int32_t* blk, int32_t* slot_base, int32_t* slot_keep, int32_t* offsets,
                         int32_t* dest, int32_t* src, int32_t* counts, int32_t* kept,
-                        int32_t* n_dropped, int BM, int max_tiles, int32_t* tiles,
+                        int32_t* n_dropped, int BM, int max_tiles, int ep, int32_t* tiles,
                         hipStream_t s) {
   const bool cap = capacity >= 0;
   if (index_single_ok(T, E, k, cap)) {
@@ -324,7 +370,7 @@ hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capac
     }
     index_single_kernel<<<dim3(1), dim3(1024), lds, s>>>(
         idx, T, k, E, cap ? capacity : -1, offsets, dest, src, counts, kept, n_dropped, BM,
-        max_tiles, reinterpret_cast<int4*>(tiles));
+        max_tiles, ep, reinterpret_cast<int4*>(tiles));
     return hipGetLastError();
   }
   const int nb = index_blocks(T);
@@ -348,7 +394,7 @@ hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capac
                                                      slot_base, slot_keep, offsets, dest, src);
   err = hipGetLastError();
   if (err != hipSuccess || tiles == nullptr) return err;
-  return launch_tile_map(offsets, E, BM, max_tiles, tiles, s);
+  return launch_tile_map(offsets, E, BM, max_tiles, ep, tiles, s);
 }
 
 }  // namespace moe

@@ -24,8 +24,8 @@ constexpr int kScaleStats = 4;
 hipError_t launch_router_select(const float* z, const float* bias, int T, int E, int k,
                                 int gate_all, int32_t* idx, float* gates, float* p_part,
                                 int32_t* c_part, float* q_part, hipStream_t s);
-hipError_t launch_bias_update(const int32_t* counts, int T, int k, int E, float gamma, float* bias,
-                              hipStream_t s);
+hipError_t launch_bias_update(const int32_t* counts, int T, int k, int E, int ep, float gamma,
+                              float* bias, hipStream_t s);
 hipError_t launch_router_stats(const float* p_part, const int32_t* c_part, const float* q_part,
                                int nblocks, int T, int E, float alpha, float* f, float* P,
                                float* aux, float* fp, float* z_loss, float* entropy,
@@ -45,8 +45,19 @@ bool index_single_ok(int T, int E, int k, bool cap);
 hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capacity,
                         int32_t* blk, int32_t* slot_base, int32_t* slot_keep, int32_t* offsets,
                         int32_t* dest, int32_t* src, int32_t* counts, int32_t* kept,
-                        int32_t* n_dropped, int BM, int max_tiles, int32_t* tiles,
+                        int32_t* n_dropped, int BM, int max_tiles, int ep, int32_t* tiles,
                         hipStream_t s);
+// Simulated expert parallelism (ep > 1 ranks): row-group ids and send-row matrix.
+hipError_t launch_ep_group_ids(const int32_t* idx, int T, int k, int E, int n, int32_t* gid,
+                               hipStream_t s);
+hipError_t launch_ep_traffic(const int32_t* offsets, int n, int E, int32_t* rows, hipStream_t s);
+// Weights index of row group g of G groups: g itself, or with ep > 1 ranks the
+// expert of group (r*ep + s)*El + l, namely r*El + l with El = G / ep^2.
+__host__ __device__ inline int tile_group_weights(int g, int G, int ep) {
+  if (ep <= 1) return g;
+  const int El = G / (ep * ep);
+  return (g / (ep * El)) * El + g % El;
+}
 
 // ---- row movement (rows.hip)
 hipError_t launch_gather_rows(int elt_bytes, const void* x, const int32_t* src,
@@ -70,7 +81,7 @@ struct GemmTileMap {
 // multiple of 256 and d_ff (and d_ff_shared) of 128, as the large tiles need
 int gemm_tile_rows(int dtype_bf16, int R_max, int groups, bool n256_ok);
 int gemm_max_tiles(int BM, int R_max, int E);
-hipError_t launch_tile_map(const int32_t* offsets, int E, int BM, int max_tiles,
+hipError_t launch_tile_map(const int32_t* offsets, int E, int BM, int max_tiles, int ep,
                            int32_t* tiles, hipStream_t s);
 
 struct GateUpArgs {

@@ -51,12 +51,14 @@ struct Shape {
   int BM, max_tiles;
   bool n256;            // d % 256 == 0 and d_ff, d_ff_shared % 128 == 0 (large tiles)
   int nb_sel, nb_idx, nkeys;
+  int ep;               // simulated expert-parallel ranks (1: off)
+  int G;                // row groups: E, or ep*E in the expert-parallel layout
 };
 
 moe_status validate(const moe_config* c, Shape* s) {
   if (c == nullptr) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
-  if (c->reserved != 0 || c->reserved2 != 0.0f)
-    return fail(MOE_ERR_INVALID_ARG, "reserved fields must be 0");
+  if (c->reserved2 != 0.0f) return fail(MOE_ERR_INVALID_ARG, "reserved fields must be 0");
+  if (c->ep_ranks < 0) return fail(MOE_ERR_INVALID_ARG, "ep_ranks=%d < 0", c->ep_ranks);
   if (c->T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d < 0", c->T);
   if (c->E < 1 || c->E > 1024) return fail(MOE_ERR_INVALID_ARG, "E=%d not in [1, 1024]", c->E);
   if (c->k < 1 || c->k > c->E || c->k > 16)
@@ -96,13 +98,25 @@ moe_status validate(const moe_config* c, Shape* s) {
     const double cd = std::ceil(static_cast<double>(R) / c->E * c->capacity_factor);
     if (cd < static_cast<double>(c->T)) s->C = static_cast<long long>(cd);
   }
-  s->nkeys = moe::index_keys(s->E, s->k, s->C >= 0);
+  s->ep = c->ep_ranks > 1 ? c->ep_ranks : 1;
+  s->G = s->E;
+  if (s->ep > 1) {
+    if (s->E % s->ep || s->T % s->ep)
+      return fail(MOE_ERR_INVALID_ARG, "ep_ranks=%d must divide E=%d and T=%d", s->ep, s->E, s->T);
+    if (c->capacity_factor > 0)
+      return fail(MOE_ERR_UNSUPPORTED, "capacity with ep_ranks > 1 is not supported");
+    if (static_cast<long long>(s->ep) * s->E > 1024)
+      return fail(MOE_ERR_UNSUPPORTED, "ep_ranks*E=%lld > 1024 row groups",
+                  static_cast<long long>(s->ep) * s->E);
+    s->G = s->ep * s->E;
+  }
+  s->nkeys = moe::index_keys(s->G, s->k, s->C >= 0);
   if (s->nkeys > moe::kIndexMaxKeys)
     return fail(MOE_ERR_UNSUPPORTED, "capacity with E*k=%d > %d is not supported", s->nkeys,
                 moe::kIndexMaxKeys);
   s->n256 = (s->d % 256 == 0) && (s->dff % 128 == 0) && (s->dffs % 128 == 0);
-  s->BM = moe::gemm_tile_rows(s->bf16, s->R, s->E, s->n256);
-  s->max_tiles = moe::gemm_max_tiles(s->BM, s->R, s->E);
+  s->BM = moe::gemm_tile_rows(s->bf16, s->R, s->G, s->n256);
+  s->max_tiles = moe::gemm_max_tiles(s->BM, s->R, s->G);
   s->nb_sel = moe::router_select_blocks(s->T);
   s->nb_idx = moe::index_blocks(s->T);
   return MOE_OK;
@@ -115,7 +129,8 @@ size_t route_bytes(const Shape& s) {
          al(static_cast<size_t>(s.nb_sel) * moe::kScaleStats * 4);
 }
 size_t permute_bytes(const Shape& s) {
-  return al(static_cast<size_t>(s.nb_idx + 1) * s.nkeys * 4) + 2 * al(static_cast<size_t>(s.k) * s.E * 4);
+  return al(static_cast<size_t>(s.nb_idx + 1) * s.nkeys * 4) + 2 * al(static_cast<size_t>(s.k) * s.G * 4) +
+         (s.ep > 1 ? al(static_cast<size_t>(s.R) * 4) : 0);
 }
 size_t tiles_bytes(const Shape& s) { return al(static_cast<size_t>(s.max_tiles) * 16); }
 size_t act_bytes(const Shape& s) {
@@ -124,7 +139,7 @@ size_t act_bytes(const Shape& s) {
 size_t yperm_bytes(const Shape& s) { return al(static_cast<size_t>(s.rows_total) * s.d * 4); }
 size_t forward_fixed_bytes(const Shape& s) {
   const size_t R4 = al(static_cast<size_t>(s.R) * 4);
-  return 4 * R4 + al(static_cast<size_t>(s.E + 1) * 4) + yperm_bytes(s) + act_bytes(s);
+  return 4 * R4 + al(static_cast<size_t>(s.G + 1) * 4) + yperm_bytes(s) + act_bytes(s);
 }
 
 size_t stage_bytes(const Shape& s, moe_stage st) {
@@ -214,14 +229,21 @@ moe_status do_permute(const Shape& s, const int32_t* idx, const void* x, int32_t
                       int32_t* tiles, hipStream_t stream) {
   Carver cv{static_cast<char*>(ws)};
   int32_t* blk = cv.take<int32_t>(static_cast<size_t>(s.nb_idx + 1) * s.nkeys * 4);
-  int32_t* slot_base = cv.take<int32_t>(static_cast<size_t>(s.k) * s.E * 4);
-  int32_t* slot_keep = cv.take<int32_t>(static_cast<size_t>(s.k) * s.E * 4);
-  MOE_HIP(moe::launch_index(idx, s.T, s.k, s.E, s.C, blk, slot_base, slot_keep, offsets, dest, src,
-                            st ? st->counts : nullptr, st ? st->kept : nullptr,
-                            st ? st->n_dropped : nullptr, s.BM, s.max_tiles, tiles, stream),
+  int32_t* slot_base = cv.take<int32_t>(static_cast<size_t>(s.k) * s.G * 4);
+  int32_t* slot_keep = cv.take<int32_t>(static_cast<size_t>(s.k) * s.G * 4);
+  const int32_t* keys = idx;
+  if (s.ep > 1) {
+    // expert-parallel layout: group (destination rank, source rank, local expert)
+    int32_t* gid = cv.take<int32_t>(static_cast<size_t>(s.R) * 4);
+    MOE_HIP(moe::launch_ep_group_ids(idx, s.T, s.k, s.E, s.ep, gid, stream), "ep_group_ids");
+    keys = gid;
+  }
+  MOE_HIP(moe::launch_index(keys, s.T, s.k, s.G, s.C, blk, slot_base, slot_keep, offsets, dest,
+                            src, st ? st->counts : nullptr, st ? st->kept : nullptr,
+                            st ? st->n_dropped : nullptr, s.BM, s.max_tiles, s.ep, tiles, stream),
           "index");
   if (x_perm != nullptr)
-    MOE_HIP(moe::launch_gather_rows(s.elt, x, src, offsets, s.E, s.R, s.d, x_perm, stream),
+    MOE_HIP(moe::launch_gather_rows(s.elt, x, src, offsets, s.G, s.R, s.d, x_perm, stream),
             "gather_rows");
   return MOE_OK;
 }
@@ -359,7 +381,7 @@ moe_status moe_expert_gateup(const moe_config* cfg, const void* x, const int32_t
   if (s.T == 0) return MOE_OK;
   hipStream_t strm = static_cast<hipStream_t>(stream);
   int32_t* tiles = static_cast<int32_t*>(ws);
-  MOE_HIP(moe::launch_tile_map(offsets, s.E, s.BM, s.max_tiles, tiles, strm), "tile_map");
+  MOE_HIP(moe::launch_tile_map(offsets, s.G, s.BM, s.max_tiles, s.ep, tiles, strm), "tile_map");
   return do_gateup(s, x, src, tiles, w1, w3, ws1, ws3, act, strm);
 }
 
@@ -376,7 +398,7 @@ moe_status moe_expert_down(const moe_config* cfg, const void* act, const int32_t
   if (s.T == 0) return MOE_OK;
   hipStream_t strm = static_cast<hipStream_t>(stream);
   int32_t* tiles = static_cast<int32_t*>(ws);
-  MOE_HIP(moe::launch_tile_map(offsets, s.E, s.BM, s.max_tiles, tiles, strm), "tile_map");
+  MOE_HIP(moe::launch_tile_map(offsets, s.G, s.BM, s.max_tiles, s.ep, tiles, strm), "tile_map");
   return do_down(s, act, tiles, w2, ws2, y_perm, strm);
 }
 
@@ -399,7 +421,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* s
   Carver cv{static_cast<char*>(ws)};
   void* act = cv.take<char>(static_cast<size_t>(s.rows_total) * s.act_stride * s.elt);
   int32_t* tiles = cv.take<int32_t>(static_cast<size_t>(s.max_tiles) * 16);
-  MOE_HIP(moe::launch_tile_map(offsets, s.E, s.BM, s.max_tiles, tiles, strm), "tile_map");
+  MOE_HIP(moe::launch_tile_map(offsets, s.G, s.BM, s.max_tiles, s.ep, tiles, strm), "tile_map");
   st = do_gateup(s, x, src, tiles, w1, w3, ws1, ws3, act, strm);
   if (st != MOE_OK) return st;
   return do_down(s, act, tiles, w2, ws2, y_perm, strm);
@@ -420,6 +442,19 @@ moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t
   return MOE_OK;
 }
 
+moe_status moe_ep_traffic(const moe_config* cfg, const int32_t* offsets, int32_t* rows,
+                          void* stream) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (s.ep <= 1) return fail(MOE_ERR_INVALID_ARG, "ep_ranks must be > 1");
+  REQUIRE(offsets); REQUIRE(rows);
+  if (s.T == 0) return MOE_OK;   // nothing routed: outputs untouched, as everywhere
+  MOE_HIP(moe::launch_ep_traffic(offsets, s.ep, s.E, rows, static_cast<hipStream_t>(stream)),
+          "ep_traffic");
+  return MOE_OK;
+}
+
 moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float gamma, float* bias,
                            void* stream) {
   Shape s;
@@ -428,7 +463,7 @@ moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float g
   REQUIRE(counts); REQUIRE(bias);
   if (!std::isfinite(gamma)) return fail(MOE_ERR_INVALID_ARG, "gamma must be finite");
   if (s.T == 0) return MOE_OK;   // no load to balance
-  MOE_HIP(moe::launch_bias_update(counts, s.T, s.k, s.E, gamma, bias,
+  MOE_HIP(moe::launch_bias_update(counts, s.T, s.k, s.E, s.ep, gamma, bias,
                                   static_cast<hipStream_t>(stream)),
           "bias_update");
   return MOE_OK;
@@ -456,7 +491,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   float* gates = cv.take<float>(R4);
   int32_t* dest = cv.take<int32_t>(R4);
   int32_t* src = cv.take<int32_t>(R4);
-  int32_t* offsets = cv.take<int32_t>(static_cast<size_t>(s.E + 1) * 4);
+  int32_t* offsets = cv.take<int32_t>(static_cast<size_t>(s.G + 1) * 4);
   float* y_perm = cv.take<float>(static_cast<size_t>(s.rows_total) * s.d * 4);
   void* act = cv.take<char>(static_cast<size_t>(s.rows_total) * s.act_stride * s.elt);
   void* scratch = cv.p;   // shared by the stages in turn (stream order)

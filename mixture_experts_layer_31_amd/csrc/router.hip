@@ -384,12 +384,21 @@ __global__ __launch_bounds__(256) void router_aux_kernel(
 
 // Auxiliary-loss-free balancing (CME295 notes §4.2; CMU 15-779 notes §2.4):
 // bias[e] moves by -gamma above the mean load T*k/E, +gamma below, 0 at it.
+// With ep > 1 simulated expert-parallel ranks the counts are per row group
+// (r*ep + s)*El + l; expert e = r*El + l sums its ep groups, in source order.
 __global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restrict__ counts,
-                                                          long long Tk, int E, float gamma,
+                                                          long long Tk, int E, int ep,
+                                                          float gamma,
                                                           float* __restrict__ bias) {
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= E) return;
-  const long long c = static_cast<long long>(counts[e]) * E;
+  long long ce = counts[e];
+  if (ep > 1) {
+    const int El = E / ep, r = e / El, l = e % El;
+    ce = 0;
+    for (int src = 0; src < ep; ++src) ce += counts[(r * ep + src) * El + l];
+  }
+  const long long c = ce * E;
   if (c > Tk) bias[e] -= gamma;
   else if (c < Tk) bias[e] += gamma;
 }
@@ -466,10 +475,10 @@ hipError_t launch_router_stats(const float* p_part, const int32_t* c_part, const
   return hipGetLastError();
 }
 
-hipError_t launch_bias_update(const int32_t* counts, int T, int k, int E, float gamma, float* bias,
-                              hipStream_t s) {
+hipError_t launch_bias_update(const int32_t* counts, int T, int k, int E, int ep, float gamma,
+                              float* bias, hipStream_t s) {
   bias_update_kernel<<<dim3((E + 255) / 256), dim3(256), 0, s>>>(
-      counts, static_cast<long long>(T) * k, E, gamma, bias);
+      counts, static_cast<long long>(T) * k, E, ep, gamma, bias);
   return hipGetLastError();
 }
 

@@ -79,14 +79,16 @@ def config_of(wl: wk.Workload, T: int) -> moe.MoeConfig:
                            capacity_factor=wl.capacity_factor, aux_alpha=wl.aux_alpha)
 
 
-def run_forward(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int, bias="default"):
+def run_forward(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int, bias="default",
+                ep: int = 0):
     """Fused moe_forward; returns numpy copies of y, idx, gates and the stats."""
     cfg = config_of(wl, T)
+    cfg.ep_ranks = ep
     x = to_dev(x_host, wl.dtype)
     y = torch.full((T, wl.d), float("nan"), dtype=torch.float32, device=dev())
     idx = torch.full((T, wl.k), -7, dtype=torch.int32, device=dev())
     gates = torch.full((T, wl.k), float("nan"), dtype=torch.float32, device=dev())
-    st = moe.Stats.alloc(wl.E)
+    st = moe.Stats.alloc(wl.E, groups=wl.E * (ep if ep > 1 else 1))
     ws = moe.alloc_workspace(cfg, moe.STAGE_FORWARD)
     b = W.bias if bias == "default" else bias
     moe.forward(cfg, x, W.wr, b, W.w1, W.w3, W.w2, W.s1, W.s3, W.s2, y, idx, gates, st, ws)
@@ -99,32 +101,41 @@ def run_forward(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int, bias="d
                 max_prob=float(st.max_prob.cpu()[0]), top_gap=float(st.top_gap.cpu()[0]))
 
 
-def run_staged(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int):
-    """route -> permute -> expert_ffn -> combine through the staged entry points."""
+def run_staged(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int, ep: int = 0):
+    """route -> permute -> expert_ffn -> combine through the staged entry points; ep > 1
+    lays the rows out as ep simulated expert-parallel ranks (and returns the send-row
+    matrix as "traffic")."""
     cfg = config_of(wl, T)
+    cfg.ep_ranks = ep
+    G = wl.E * (ep if ep > 1 else 1)
     x = to_dev(x_host, wl.dtype)
     R = T * wl.k
     idx = torch.empty((T, wl.k), dtype=torch.int32, device=dev())
     gates = torch.empty((T, wl.k), dtype=torch.float32, device=dev())
-    offsets = torch.empty(wl.E + 1, dtype=torch.int32, device=dev())
+    offsets = torch.empty(G + 1, dtype=torch.int32, device=dev())
     dest = torch.empty((T, wl.k), dtype=torch.int32, device=dev())
     src = torch.empty(R, dtype=torch.int32, device=dev())
     rows = R + wl.n_shared * T
     y_perm = torch.zeros((rows, wl.d), dtype=torch.float32, device=dev())
     y = torch.empty((T, wl.d), dtype=torch.float32, device=dev())
     x_perm = torch.zeros((R, wl.d), dtype=x.dtype, device=dev())
-    st = moe.Stats.alloc(wl.E)
+    st = moe.Stats.alloc(wl.E, groups=G)
     moe.route(cfg, x, W.wr, W.bias, idx, gates, st, moe.alloc_workspace(cfg, moe.STAGE_ROUTE))
     moe.permute(cfg, idx, x, offsets, dest, src, x_perm, st,
                 moe.alloc_workspace(cfg, moe.STAGE_PERMUTE))
     moe.expert_ffn(cfg, x, src, offsets, W.w1, W.w3, W.w2, W.s1, W.s3, W.s2, y_perm,
                    moe.alloc_workspace(cfg, moe.STAGE_EXPERT_FFN))
     moe.combine(cfg, y_perm, dest, gates, y, moe.alloc_workspace(cfg, moe.STAGE_COMBINE))
+    traffic = None
+    if ep > 1:
+        traffic = torch.full((ep * ep,), -1, dtype=torch.int32, device=dev())
+        moe.ep_traffic(cfg, offsets, traffic)
     torch.cuda.synchronize()
     out = dict(y=y.cpu().numpy(), idx=idx.cpu().numpy().astype(np.int64), gates=gates.cpu().numpy(),
                offsets=offsets.cpu().numpy(), dest=dest.cpu().numpy(), src=src.cpu().numpy(),
                counts=st.counts.cpu().numpy(), kept=st.kept.cpu().numpy(),
-               n_dropped=int(st.n_dropped.cpu()[0]), y_perm=y_perm.cpu().numpy())
+               n_dropped=int(st.n_dropped.cpu()[0]), y_perm=y_perm.cpu().numpy(),
+               traffic=None if traffic is None else traffic.cpu().numpy().reshape(ep, ep))
     if wl.dtype == wk.BF16:
         out["x_perm"] = x_perm.view(torch.int16).cpu().numpy().view(np.uint16)
     else:

@@ -95,7 +95,7 @@ def test_bad_enums_and_reserved(lib):
     assert lib.moe_workspace_size(ctypes.byref(c), 0, ctypes.byref(n)) == moe.ERR_INVALID_ARG
     c = _cfg(); c.dtype = 3
     assert lib.moe_workspace_size(ctypes.byref(c), 0, ctypes.byref(n)) == moe.ERR_INVALID_ARG
-    c = _cfg(); c.reserved = 1
+    c = _cfg(); c.reserved2 = 1.0
     assert lib.moe_workspace_size(ctypes.byref(c), 0, ctypes.byref(n)) == moe.ERR_INVALID_ARG
     assert lib.moe_workspace_size(None, 0, ctypes.byref(n)) == moe.ERR_INVALID_ARG
     assert lib.moe_workspace_size(ctypes.byref(_cfg()), 42, ctypes.byref(n)) == moe.ERR_INVALID_ARG
@@ -150,6 +150,28 @@ def test_update_bias_rejects_before_launch(lib):
     assert lib.moe_update_bias(ctypes.byref(_cfg(E=0)), P, g, P, None) == moe.ERR_INVALID_ARG
     assert lib.moe_update_bias(None, P, g, P, None) == moe.ERR_INVALID_ARG
     assert lib.moe_update_bias(ctypes.byref(_cfg(T=0)), P, g, P, None) == moe.OK
+
+
+def test_expert_parallel_config(lib):
+    """ep_ranks: must divide E and T, no capacity, ep*E <= 1024 groups; offsets grow to
+    ep*E + 1 entries (the forward workspace grows with them); moe_ep_traffic needs
+    ep_ranks > 1 and its pointers."""
+    n = ctypes.c_size_t(0)
+    ws = lambda c: lib.moe_workspace_size(ctypes.byref(c), moe.STAGE_FORWARD, ctypes.byref(n))
+    assert ws(_cfg(E=8, T=64, ep_ranks=4)) == moe.OK
+    assert ws(_cfg(E=8, T=64, ep_ranks=1)) == moe.OK
+    assert ws(_cfg(E=8, T=64, ep_ranks=-1)) == moe.ERR_INVALID_ARG
+    assert ws(_cfg(E=8, T=64, ep_ranks=3)) == moe.ERR_INVALID_ARG      # 3 does not divide 8
+    assert ws(_cfg(E=8, T=66, ep_ranks=4)) == moe.ERR_INVALID_ARG      # nor 66
+    assert ws(_cfg(E=8, T=64, ep_ranks=4, capacity_factor=1.0)) == moe.ERR_UNSUPPORTED
+    assert ws(_cfg(E=512, k=2, T=64, ep_ranks=4)) == moe.ERR_UNSUPPORTED   # 2048 groups
+    P = FAKE
+    c1 = _cfg(E=8, T=64)
+    c4 = _cfg(E=8, T=64, ep_ranks=4)
+    assert lib.moe_ep_traffic(ctypes.byref(c1), P, P, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_ep_traffic(ctypes.byref(c4), None, P, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_ep_traffic(ctypes.byref(c4), P, None, None) == moe.ERR_INVALID_ARG
+    assert lib.moe_ep_traffic(ctypes.byref(_cfg(E=8, T=0, ep_ranks=4)), P, P, None) == moe.OK
 
 
 def test_zero_tokens_is_a_noop(lib):
