@@ -421,6 +421,110 @@ def forward(x, w_router, experts: ExpertFn, k: int, gate: str = GATE_SELECTED,
                 yp=yp, shared_out=sh, **p)
 
 
+# ---------------------------------------------------------------- backward
+
+def silu_grad(u: np.ndarray) -> np.ndarray:
+    """d silu(u)/du = sigma(u) (1 + u (1 - sigma(u)))."""
+    u = np.asarray(u, np.float64)
+    s = 1.0 / (1.0 + np.exp(-u))
+    return s * (1.0 + u * (1.0 - s))
+
+
+def swiglu_backward(X, w1, w3, w2, dY):
+    """Gradients of sum <dY, W2 (silu(X W1^T) * (X W3^T))> for one expert's rows:
+    returns (dX, dW1, dW3, dW2) ([15-779] §7: dW2 = H^T dY and the other
+    transposed products of the two expert matmuls)."""
+    X = np.asarray(X, np.float64)
+    dY = np.asarray(dY, np.float64)
+    h1, h3 = X @ np.asarray(w1, np.float64).T, X @ np.asarray(w3, np.float64).T
+    a = silu(h1) * h3
+    dW2 = dY.T @ a
+    da = dY @ np.asarray(w2, np.float64)
+    dh3 = da * silu(h1)
+    dh1 = da * h3 * silu_grad(h1)
+    dW1, dW3 = dh1.T @ X, dh3.T @ X
+    dX = dh1 @ np.asarray(w1, np.float64) + dh3 @ np.asarray(w3, np.float64)
+    return dX, dW1, dW3, dW2
+
+
+def aux_loss_logit_grad(probs: np.ndarray, f: np.ndarray, alpha: float) -> np.ndarray:
+    """dL_aux/dz_{t,i} = (alpha E / T) p_{t,i} (f_i - sum_j p_{t,j} f_j), the
+    closed form of [CME295] §3.2 (f held constant: it is a count)."""
+    p = np.asarray(probs, np.float64)
+    T, E = p.shape
+    f = np.asarray(f, np.float64)
+    return alpha * E / T * p * (f[None, :] - (p @ f)[:, None])
+
+
+def backward(x, w_router, experts: ExpertFn, k: int, dy, gate: str = GATE_SELECTED,
+             bias=None, cf: float = 0.0, shared=None, alpha: float = 0.0):
+    """Gradients of L = sum_t <dy_t, y_t> + L_aux (L_aux only when alpha > 0) with
+    respect to x, W_r and every expert's (and the shared expert's) weights.
+
+    The top-k selection and the capacity drops are discrete and pass no gradient
+    ([CME295] §1.3: the router learns through the gates of the selected experts).
+    Gates: SELECTED mode g = softmax of the selected logits, so
+    dz_sel = g (dg - sum g dg) on the selected entries (dropped slots keep their
+    gate, with dg = 0); ALL mode g_j = p_{idx_j}, dz = p (dp - sum p dp) with dp
+    the dg summed per expert ([15-779] §2.5 contrasts the two for k = 1). The
+    selection bias enters neither gates nor gradients ([CME295] §4.2).
+
+    Returns dict(dx, dw_router, dw1[E], dw3[E], dw2[E], dws1, dws3, dws2, dz, dg, fwd)."""
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    wr = np.asarray(w_router, np.float64)
+    T, d = x.shape
+    E = wr.shape[0]
+    fwd = forward(x, wr, experts, k, gate, bias, cf, shared, alpha)
+    idx, gates, dest, src, offsets = fwd["idx"], fwd["gates"], fwd["dest"], fwd["src"], fwd["offsets"]
+    yp = fwd["yp"]
+    # combine backward
+    dg = np.zeros((T, k))
+    dyp = np.zeros_like(yp)
+    for t in range(T):
+        for j in range(k):
+            r = dest[t, j]
+            if r >= 0:
+                dg[t, j] = float(dy[t] @ yp[r])
+                dyp[r] = gates[t, j] * dy[t]
+    # experts
+    dx = np.zeros_like(x)
+    dw1, dw3, dw2 = [None] * E, [None] * E, [None] * E
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        w1, w3, w2 = (np.asarray(w, np.float64) for w in experts(e))
+        if hi > lo:
+            rows_t = src[lo:hi]
+            dX, dw1[e], dw3[e], dw2[e] = swiglu_backward(x[rows_t], w1, w3, w2, dyp[lo:hi])
+            np.add.at(dx, rows_t, dX)
+        else:
+            dw1[e], dw3[e], dw2[e] = np.zeros_like(w1), np.zeros_like(w3), np.zeros_like(w2)
+    dws1 = dws3 = dws2 = None
+    if shared is not None:
+        dXs, dws1, dws3, dws2 = swiglu_backward(x, *shared, dy)
+        dx += dXs
+    # gates -> logits
+    z = fwd["z"]
+    dz = np.zeros((T, E))
+    if gate == GATE_SELECTED:
+        s = (gates * dg).sum(axis=1, keepdims=True)
+        dsel = gates * (dg - s)
+        for j in range(k):
+            np.add.at(dz, (np.arange(T), idx[:, j]), dsel[:, j])
+    else:
+        p = fwd["probs"]
+        dp = np.zeros((T, E))
+        for j in range(k):
+            np.add.at(dp, (np.arange(T), idx[:, j]), dg[:, j])
+        dz = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    if alpha > 0:
+        dz = dz + aux_loss_logit_grad(fwd["probs"], fwd["f"], alpha)
+    dw_router = dz.T @ x
+    dx += dz @ wr
+    return dict(dx=dx, dw_router=dw_router, dw1=dw1, dw3=dw3, dw2=dw2, dws1=dws1,
+                dws3=dws3, dws2=dws2, dz=dz, dg=dg, fwd=fwd)
+
+
 def dense_all_experts(x, experts: ExpertFn, G: np.ndarray) -> np.ndarray:
     """Every expert on every token, weighted by a dense [T, E] gate matrix:
     y = sum_e G[:, e] f_e(x) ([15-779] §3.4 formulation 0; with G zero outside

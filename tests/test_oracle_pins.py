@@ -643,3 +643,106 @@ def test_ep_printed_figures():
         per_dev = rows.sum(axis=0)
         assert per_dev.mean() == dm["rows_mean"]
         assert 0.93 * dm["rows_mean"] <= per_dev.min() and per_dev.max() <= 1.07 * dm["rows_mean"]
+
+
+# ---------------------------------------------------------------- backward
+
+def _tiny_layer(seed, T, d, E, k, f, shared=False, bias=False):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d))
+    W = [[rng.standard_normal((f, d)) * 0.7, rng.standard_normal((f, d)) * 0.7,
+          rng.standard_normal((d, f)) * 0.7] for _ in range(E)]
+    sh = [rng.standard_normal((f, d)) * 0.7, rng.standard_normal((f, d)) * 0.7,
+          rng.standard_normal((d, f)) * 0.7] if shared else None
+    b = rng.uniform(-0.3, 0.3, E) if bias else None
+    dy = rng.standard_normal((T, d))
+    return x, wr, W, sh, b, dy
+
+
+def _objective(x, wr, W, sh, b, dy, k, gate, cf, alpha):
+    out = om.forward(x, wr, lambda e: W[e], k, gate, b, cf, sh, alpha)
+    return float((dy * out["y"]).sum() + (out["aux"] if alpha > 0 else 0.0)), out
+
+
+@pytest.mark.parametrize("case", ["selected_shared_bias_aux", "all_capacity_aux", "top1_selected",
+                                  "dense_e1"])
+def test_backward_finite_differences(case):
+    """Every gradient of L = <dy, y> + L_aux against central differences of the forward
+    pass (h = 1e-6, float64) on tiny layers whose top-k margins are far from any tie."""
+    cfgs = {"selected_shared_bias_aux": dict(seed=31, T=6, d=5, E=4, k=2, f=3, shared=True,
+                                             bias=True, gate=om.GATE_SELECTED, cf=0.0, alpha=0.3),
+            "all_capacity_aux": dict(seed=32, T=8, d=4, E=4, k=2, f=3, shared=False, bias=False,
+                                     gate=om.GATE_ALL, cf=0.75, alpha=0.2),
+            "top1_selected": dict(seed=33, T=5, d=4, E=3, k=1, f=2, shared=False, bias=False,
+                                  gate=om.GATE_SELECTED, cf=0.0, alpha=0.0),
+            "dense_e1": dict(seed=34, T=4, d=3, E=1, k=1, f=4, shared=False, bias=False,
+                             gate=om.GATE_SELECTED, cf=0.0, alpha=0.0)}
+    c = cfgs[case]
+    x, wr, W, sh, b, dy = _tiny_layer(c["seed"], c["T"], c["d"], c["E"], c["k"], c["f"],
+                                      c["shared"], c["bias"])
+    k, gate, cf, alpha = c["k"], c["gate"], c["cf"], c["alpha"]
+    L0, out = _objective(x, wr, W, sh, b, dy, k, gate, cf, alpha)
+    assert np.all(out["margin"] > 1e-3)
+    if case == "all_capacity_aux":
+        assert out["n_dropped"] > 0
+    g = om.backward(x, wr, lambda e: W[e], k, dy, gate, b, cf, sh, alpha)
+    h = 1e-6
+
+    def fd(arr, grad):
+        num = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            keep = arr[i]
+            arr[i] = keep + h
+            lp, _ = _objective(x, wr, W, sh, b, dy, k, gate, cf, alpha)
+            arr[i] = keep - h
+            lm, _ = _objective(x, wr, W, sh, b, dy, k, gate, cf, alpha)
+            arr[i] = keep
+            num[i] = (lp - lm) / (2 * h)
+        assert np.max(np.abs(num - grad)) <= 1e-6 * max(1.0, np.max(np.abs(num))), \
+            f"{case}: max |fd - analytic| {np.max(np.abs(num - grad)):.3g}"
+
+    fd(x, g["dx"])
+    fd(wr, g["dw_router"])
+    for e in range(c["E"]):
+        fd(W[e][0], g["dw1"][e])
+        fd(W[e][1], g["dw3"][e])
+        fd(W[e][2], g["dw2"][e])
+    if sh is not None:
+        fd(sh[0], g["dws1"])
+        fd(sh[1], g["dws3"])
+        fd(sh[2], g["dws2"])
+
+
+def test_top1_selected_gate_passes_no_router_gradient():
+    """[15-779] §2.5: with k = 1, gates renormalised over the selection are identically 1,
+    so the router's gradient from the task is exactly 0; the Switch form g = p_i is not."""
+    x, wr, W, _, _, dy = _tiny_layer(35, 8, 4, 4, 1, 3)
+    sel = om.backward(x, wr, lambda e: W[e], 1, dy, om.GATE_SELECTED)
+    assert np.all(sel["dz"] == 0.0) and np.all(sel["dw_router"] == 0.0)
+    allg = om.backward(x, wr, lambda e: W[e], 1, dy, om.GATE_ALL)
+    assert np.max(np.abs(allg["dz"])) > 1e-3
+
+
+def test_aux_logit_gradient_closed_form_by_differences():
+    """[CME295] §3.2's closed form dL_aux/dz against central differences of
+    alpha E sum_i f_i mean_t softmax(z_t)_i with f held fixed, and its sign reading:
+    near-uniform probabilities push experts loaded above the mean down, below it up."""
+    rng = np.random.default_rng(36)
+    T, E, alpha = 7, 5, 0.01
+    z = rng.standard_normal((T, E)) * 0.05
+    f = np.array([0.5, 0.3, 0.1, 0.05, 0.05]) * 2     # k = 2 fractions, sum 2
+
+    def Laux(zz):
+        return alpha * E * float(f @ om.softmax(zz).mean(axis=0))
+    num = np.zeros_like(z)
+    for i in np.ndindex(z.shape):
+        keep = z[i]
+        z[i] = keep + 1e-7; lp = Laux(z)
+        z[i] = keep - 1e-7; lm = Laux(z)
+        z[i] = keep
+        num[i] = (lp - lm) / 2e-7
+    g = om.aux_loss_logit_grad(om.softmax(z), f, alpha)
+    assert np.max(np.abs(num - g)) <= 1e-9
+    mean_load = f.mean()
+    assert (np.sign(g.sum(axis=0)) == np.sign(f - mean_load)).all()
