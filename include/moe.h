@@ -88,7 +88,8 @@ typedef enum {
   MOE_STAGE_COMBINE = 3,
   MOE_STAGE_FORWARD = 4,
   MOE_STAGE_EXPERT_GATEUP = 5,
-  MOE_STAGE_EXPERT_DOWN = 6
+  MOE_STAGE_EXPERT_DOWN = 6,
+  MOE_STAGE_BACKWARD = 7
 } moe_stage;
 
 /* Layer shape and options. Names follow the pages: E experts
@@ -233,6 +234,34 @@ int32_t moe_act_stride(const moe_config* cfg);
 moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* dest,
                        const float* gates, float* y, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* Backward of the layer: gradients of L = sum_t <dy_t, y_t> + L_aux (L_aux only
+ * when cfg->aux_alpha > 0; [CME295] §3.2) with respect to x, W_r and every
+ * expert's (and the shared expert's) weights. The forward is recomputed from
+ * the same inputs (router, index, the expert pre-activations), so nothing has
+ * to be kept from moe_forward. The top-k selection and capacity drops pass no
+ * gradient ([CME295] §1.3); SELECTED gates: dz = g (dg - sum g dg) on the
+ * selected logits, ALL gates: dz = p (dp - sum p dp) ([15-779] §2.5); the
+ * expert products are the transposed GEMMs ([15-779] §7: dW2 = H^T dY, ...),
+ * bf16 operands with fp32 accumulation (the SwiGLU pre-activations are kept
+ * in fp32, the activation and the propagated gradients rounded to bf16 before
+ * each product).
+ *   inputs as moe_forward (bf16 only), dy[T,d] fp32 (required);
+ *   outputs fp32, every one required except the shared expert's (required
+ *   when n_shared = 1): dx[T,d], dw_router[E,d], dw1/dw3[E,d_ff,d],
+ *   dw2[E,d,d_ff], dws1/dws3[d_ff_shared,d], dws2[d,d_ff_shared]; experts
+ *   that receive no row get zero gradients.
+ *   ws: moe_workspace_size(cfg, MOE_STAGE_BACKWARD). T == 0 leaves the
+ *   outputs untouched.
+ * Errors: INVALID_ARG (bad config, NULL or misaligned pointer), WORKSPACE,
+ * UNSUPPORTED (fp32, ep_ranks > 1, or d, d_ff, d_ff_shared not multiples of
+ * 256).                                                                       */
+moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_router,
+                        const float* sel_bias, const void* w1, const void* w3, const void* w2,
+                        const void* ws1, const void* ws3, const void* ws2, const float* dy,
+                        float* dx, float* dw_router, float* dw1, float* dw3, float* dw2,
+                        float* dws1, float* dws3, float* dws2, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /* Dispatch volume of the simulated expert-parallel layout (cfg->ep_ranks = n
  * > 1; [15-779] §5.1 and §10 exercise 6): rows[s*n + r] = rows source rank s

@@ -19,11 +19,12 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, BF16 = 0, 1
 GATE_SELECTED, GATE_ALL = 0, 1
 (STAGE_ROUTE, STAGE_PERMUTE, STAGE_EXPERT_FFN, STAGE_COMBINE, STAGE_FORWARD,
- STAGE_EXPERT_GATEUP, STAGE_EXPERT_DOWN) = range(7)
+ STAGE_EXPERT_GATEUP, STAGE_EXPERT_DOWN, STAGE_BACKWARD) = range(8)
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_workspace_size", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_expert_gateup", "moe_expert_down",
-           "moe_act_stride", "moe_combine", "moe_forward", "moe_update_bias", "moe_ep_traffic")
+           "moe_act_stride", "moe_combine", "moe_forward", "moe_update_bias", "moe_ep_traffic",
+           "moe_backward")
 
 
 class MoeConfig(ctypes.Structure):
@@ -79,6 +80,7 @@ def load(path: str = LIB_PATH):
                                        stp, vp, sz, vp]),
         "moe_update_bias": (ctypes.c_int, [cfgp, vp, ctypes.c_float, vp, vp]),
         "moe_ep_traffic": (ctypes.c_int, [cfgp, vp, vp, vp]),
+        "moe_backward": (ctypes.c_int, [cfgp] + [vp] * 19 + [sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -226,6 +228,16 @@ def update_bias(cfg, counts, gamma: float, bias, stream=None):
     """bias[e] -= gamma above the mean load T*k/E, += gamma below (in place)."""
     _check(load().moe_update_bias(ctypes.byref(cfg), _p(counts), ctypes.c_float(gamma), _p(bias),
                                   _stream(stream)), "moe_update_bias")
+
+
+def backward(cfg, x, w_router, sel_bias, w1, w3, w2, ws1, ws3, ws2, dy, dx, dw_router, dw1, dw3,
+             dw2, dws1=None, dws3=None, dws2=None, ws=None, stream=None):
+    """Gradients of <dy, y> + L_aux (recomputes the forward); fp32 outputs."""
+    wp, wb = _ws(ws)
+    _check(load().moe_backward(ctypes.byref(cfg), _p(x), _p(w_router), _p(sel_bias), _p(w1),
+                               _p(w3), _p(w2), _p(ws1), _p(ws3), _p(ws2), _p(dy), _p(dx),
+                               _p(dw_router), _p(dw1), _p(dw3), _p(dw2), _p(dws1), _p(dws3),
+                               _p(dws2), wp, wb, _stream(stream)), "moe_backward")
 
 
 def ep_traffic(cfg, offsets, rows, stream=None):

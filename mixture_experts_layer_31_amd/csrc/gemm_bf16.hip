@@ -275,7 +275,13 @@ __device__ __forceinline__ void with_count(int n, F&& f) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool GATEUP, int ST>
+// GK (grouped K, the weight gradients): tile m_tile is (group g, BM-row block
+// m_tile % n_single of A), the reduction runs over the group's K range
+// [tiles[g], tiles[g+1]) of two K-contiguous operands (rows padded to multiples
+// of 64 per group), B is shared by all groups, and group g's fp32 output starts
+// w_stride elements after group g-1's. Every output tile is written, so a group
+// with no rows gets zeros.
+template <int BM, int BN, int WM, int WN, bool GATEUP, int ST, bool GK = false>
 __global__ __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_lds_kernel(
     const int32_t* __restrict__ tiles, int max_tiles, int n_single, int n_logical,
@@ -300,11 +306,25 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
 
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[];
 
+  static_assert(!GK || !GATEUP, "grouped K is a plain GEMM");
   int m_tile, n_tile;
   xcd_tile(n_logical, max_tiles, m_tile, n_tile);
   if (m_tile < 0) return;
-  const TileCoord tc = lookup_tile(tiles, n_single, BM, m_tile);
-  if (tc.rows <= 0) return;
+  TileCoord tc;
+  int k0 = 0, nk = K / kBK;
+  size_t obase = 0;
+  if constexpr (GK) {
+    const int g = m_tile / n_single;
+    tc.group = g;
+    tc.row0 = (m_tile % n_single) * BM;
+    tc.rows = BM;
+    k0 = tiles[g];
+    nk = (tiles[g + 1] - k0) / kBK;
+    obase = static_cast<size_t>(g) * static_cast<size_t>(w_stride);
+  } else {
+    tc = lookup_tile(tiles, n_single, BM, m_tile);
+    if (tc.rows <= 0) return;
+  }
   const int n0 = n_tile * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -320,16 +340,16 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
     const int r = 8 * (i * NW + wave) + lrow8;
     int grow = tc.row0 + min(r, tc.rows - 1);
     if (src != nullptr) grow = src[grow];
-    xg[i] = xa + (static_cast<size_t>(a_row0) + grow) * a_stride + lchunk * 8;
+    xg[i] = xa + (static_cast<size_t>(a_row0) + grow) * a_stride + lchunk * 8 + k0;
   }
   const uint16_t* wg[WD];
-  const size_t wbase = static_cast<size_t>(tc.group) * w_stride;
+  const size_t wbase = GK ? 0 : static_cast<size_t>(tc.group) * w_stride;
 #pragma unroll
   for (int i = 0; i < WD; ++i) {
     const int r = 8 * (i * NW + wave) + lrow8;
     const uint16_t* wsrc = (!GATEUP || r < BN) ? w_a : w_b;
     const int n = n0 + ((GATEUP && r >= BN) ? r - BN : r);
-    wg[i] = wsrc + wbase + static_cast<size_t>(n) * K + lchunk * 8;
+    wg[i] = wsrc + wbase + static_cast<size_t>(n) * K + lchunk * 8 + k0;
   }
   // the stage's XD + WD LDS-DMA instructions, issued in slices: instruction j
   // goes out in slice j * kDmaSlices / (XD + WD)
@@ -401,12 +421,11 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
   // The loop is specialised on the number of this wave's token blocks that
   // hold rows (NA): a full tile runs NA = MT, a ragged tail only the MFMAs of
   // its rows, so it costs about its share of a full tile.
-  const int nk = K / kBK;
   int nd_stage = WD;                 // LDS-DMA instructions this wave issues per stage
 #pragma unroll
   for (int j = 0; j < XD; ++j) nd_stage += 8 * (j * NW + wave) < tc.rows ? 1 : 0;
   auto kloop = [&](auto na_c) {
-    dma(0, 0);
+    if (nk > 0) dma(0, 0);
     if (ST == 3 && nk > 1) dma(1, 1);
     int cur = 0;
     for (int kt = 0; kt < nk; ++kt) {
@@ -463,7 +482,7 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
           f32x4 v;
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = acc[a][b][4 * rq + q];
-          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow * out_stride + n) = v;
+          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + obase + orow * out_stride + n) = v;
         }
       }
     }
@@ -743,6 +762,17 @@ static int gemm_down_cols(int BM, int m_tiles, int N) {
   return static_cast<long long>(m_tiles) * (N / 256) < 2 * kNumCUs ? 128 : 256;
 }
 
+hipError_t launch_gemm_groupk_bf16(const int32_t* koffs, int G, const uint16_t* At, int N1,
+                                   const uint16_t* Bt, int N2, int Kstride, float* out,
+                                   hipStream_t s) {
+  if (N1 % 256 || N2 % 256 || Kstride % kBK) return hipErrorInvalidValue;
+  constexpr size_t lds = 2 * static_cast<size_t>(256 + 256) * kRowBytes;
+  const GemmTileMap map{koffs, G * (N1 / 256), N1 / 256};
+  return launch_tiled(gemm_bf16_lds_kernel<256, 256, 2, 4, false, 2, true>, 256, 256, 512, lds,
+                      map, At, nullptr, Kstride, 0, Bt, nullptr,
+                      static_cast<long long>(N1) * N2, out, N2, 0, Kstride, N2, s);
+}
+
 hipError_t launch_gemm_down_bf16(const GemmTileMap& map, const DownArgs& a, int BM,
                                  hipStream_t s) {
   const auto* act = static_cast<const uint16_t*>(a.act);
@@ -750,17 +780,17 @@ hipError_t launch_gemm_down_bf16(const GemmTileMap& map, const DownArgs& a, int 
   if (BM == 256) {
     const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + BM - 1) / BM;
     if (gemm_down_cols(BM, m_tiles, a.N) == 128)
-      return run_lds<256, 128, 2, 4, false>(map, act, nullptr, a.act_stride, a.in_row0, w2,
+      return run_lds<256, 128, 2, 4, false>(map, act, a.src, a.act_stride, a.in_row0, w2,
                                             nullptr, a.w_stride, a.y, a.N, a.out_row0, a.K,
                                             a.N, s);
-    return run_lds<256, 256, 2, 4, false>(map, act, nullptr, a.act_stride, a.in_row0, w2,
+    return run_lds<256, 256, 2, 4, false>(map, act, a.src, a.act_stride, a.in_row0, w2,
                                           nullptr, a.w_stride, a.y, a.N, a.out_row0, a.K, a.N,
                                           s);
   }
   if (BM == 16)
-    return run_stream<false>(map, act, nullptr, a.act_stride, a.in_row0, w2, nullptr, a.w_stride,
+    return run_stream<false>(map, act, a.src, a.act_stride, a.in_row0, w2, nullptr, a.w_stride,
                              a.y, a.N, a.out_row0, a.K, a.N, s);
-  return run_small<32, 64, 1, 2, false>(map, act, nullptr, a.act_stride, a.in_row0, w2, nullptr,
+  return run_small<32, 64, 1, 2, false>(map, act, a.src, a.act_stride, a.in_row0, w2, nullptr,
                                         a.w_stride, a.y, a.N, a.out_row0, a.K, a.N, s);
 }
 

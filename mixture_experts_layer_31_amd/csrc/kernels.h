@@ -12,6 +12,31 @@ namespace moe {
 // setting the attribute before every launch measurably slows the launches.
 hipError_t allow_large_lds(const void* kernel, size_t bytes);
 
+// ---- backward (backward.hip)
+hipError_t launch_pad_offsets(const int32_t* offsets, int G, int32_t* poff, hipStream_t s);
+hipError_t launch_single_group_offsets(int rows, int32_t* off, hipStream_t s);
+hipError_t launch_transpose_rows(const uint16_t* in, int in_stride, const int32_t* src,
+                                 int in_row0, const int32_t* offsets, const int32_t* poff, int G,
+                                 int max_rows, int C, uint16_t* out, int out_stride,
+                                 hipStream_t s);
+hipError_t launch_transpose_mat(const uint16_t* in, int B, int M, int N, uint16_t* out,
+                                int out_stride, int col0, long long out_batch, hipStream_t s);
+hipError_t launch_swiglu_fwd(const float* h1, const float* h3, int stride, int row0, int rows,
+                             int n, uint16_t* act, hipStream_t s);
+hipError_t launch_swiglu_bwd(const float* da, const float* h1, const float* h3, int stride,
+                             int row0, int rows, int n, uint16_t* dH, hipStream_t s);
+hipError_t launch_combine_bwd(const float* dy, const float* yp, const int32_t* dest,
+                              const float* gates, int T, int k, int d, int shared_row0, float* dg,
+                              uint16_t* dyp, hipStream_t s);
+hipError_t launch_gate_bwd(const float* z, const int32_t* idx, const float* gates, const float* dg,
+                           const int32_t* counts, int T, int E, int k, int gate_all, float alpha,
+                           float* dz, hipStream_t s);
+hipError_t launch_unpermute_dx(int dtype_bf16, const float* dxp, const int32_t* dest,
+                               const float* dz, const void* wr, int T, int k, int E, int d,
+                               int shared_row0, float* dx, hipStream_t s);
+hipError_t launch_router_wgrad(int dtype_bf16, const float* dz, const void* x, int T, int E, int d,
+                               float* dwr, hipStream_t s);
+
 // ---- router (router.hip)
 constexpr int kSelectMaxBlocks = 1024;
 int router_select_tokens(int T);   // tokens per router_select workgroup
@@ -98,13 +123,21 @@ struct GateUpArgs {
 struct DownArgs {
   const void* act;        // [rows][act_stride]
   int act_stride;
-  int in_row0;            // input row = in_row0 + grouped row
+  int in_row0;            // input row = in_row0 + grouped row (after src, if set)
   const void* w2;         // [G][N][K]
   long long w_stride;
   float* y;               // [rows][N]
   int out_row0;
   int K, N;               // K = d_ff, N = d
+  const int32_t* src = nullptr;   // grouped row -> input row (nullable: identity)
 };
+// Grouped-K GEMM for weight gradients: out[g][n1][n2] = sum over k in
+// [koffs[g], koffs[g+1]) of At[n1][k] * Bt[n2][k] (fp32), every group's tile
+// written (zeros for an empty range). At [N1][Kstride], Bt [N2][Kstride] bf16;
+// N1, N2 multiples of 256, koffs and Kstride multiples of 64.
+hipError_t launch_gemm_groupk_bf16(const int32_t* koffs, int G, const uint16_t* At, int N1,
+                                   const uint16_t* Bt, int N2, int Kstride, float* out,
+                                   hipStream_t s);
 hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, int BM,
                                    hipStream_t s);
 hipError_t launch_gemm_down_bf16(const GemmTileMap& map, const DownArgs& a, int BM,

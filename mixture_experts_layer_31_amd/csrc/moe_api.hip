@@ -142,6 +142,75 @@ size_t forward_fixed_bytes(const Shape& s) {
   return 4 * R4 + al(static_cast<size_t>(s.G + 1) * 4) + yperm_bytes(s) + act_bytes(s);
 }
 
+struct Carver {
+  char* p;
+  template <typename T>
+  T* take(size_t bytes) {
+    T* r = reinterpret_cast<T*>(p);
+    p += al(bytes);
+    return r;
+  }
+};
+
+// Workspace of moe_backward: every buffer of the recomputed forward and of the
+// backward, carved in this order (a null base only measures the size).
+struct BwdBufs {
+  float *z, *gates, *h1, *h3, *yp, *dg, *dz, *dact, *dxp;
+  int32_t *idx, *dest, *src, *offsets, *counts, *kept, *ndrop, *poff, *soff, *spoff, *tiles;
+  int32_t *blk, *slot_base, *slot_keep;
+  uint16_t *act, *dyp, *dH, *w2t, *w13t, *w2st, *w13st;
+  uint16_t *dypT, *actT, *dHT, *xT, *dysT, *actsT, *dHsT, *xsT;
+  int Rp, Tp;
+};
+
+size_t backward_layout(const Shape& s, char* base, BwdBufs* b) {
+  Carver cv{base};
+  const size_t T = s.T, E = s.E, k = s.k, R = s.R, d = s.d, As = s.act_stride;
+  const size_t rows = s.rows_total, dff = s.dff, dffs = s.dffs;
+  b->Rp = (s.R + 63) / 64 * 64 + 64 * s.E;
+  b->Tp = (s.T + 63) / 64 * 64;
+  const size_t Rp = b->Rp, Tp = b->Tp;
+  b->z = cv.take<float>(T * E * 4);
+  b->idx = cv.take<int32_t>(T * k * 4);
+  b->gates = cv.take<float>(T * k * 4);
+  b->dest = cv.take<int32_t>(T * k * 4);
+  b->src = cv.take<int32_t>(R * 4);
+  b->offsets = cv.take<int32_t>((E + 1) * 4);
+  b->counts = cv.take<int32_t>(E * 4);
+  b->kept = cv.take<int32_t>(E * 4);
+  b->ndrop = cv.take<int32_t>(4);
+  b->poff = cv.take<int32_t>((E + 1) * 4);
+  b->soff = cv.take<int32_t>(2 * 4);
+  b->spoff = cv.take<int32_t>(2 * 4);
+  b->tiles = cv.take<int32_t>(static_cast<size_t>(s.max_tiles) * 16);
+  b->blk = cv.take<int32_t>(static_cast<size_t>(s.nb_idx + 1) * s.nkeys * 4);
+  b->slot_base = cv.take<int32_t>(k * E * 4);
+  b->slot_keep = cv.take<int32_t>(k * E * 4);
+  b->h1 = cv.take<float>(rows * As * 4);
+  b->h3 = cv.take<float>(rows * As * 4);
+  b->act = cv.take<uint16_t>(rows * As * 2);
+  b->yp = cv.take<float>(R * d * 4);
+  b->dyp = cv.take<uint16_t>(rows * d * 2);
+  b->dg = cv.take<float>(T * k * 4);
+  b->dz = cv.take<float>(T * E * 4);
+  b->dact = cv.take<float>(rows * As * 4);
+  b->dH = cv.take<uint16_t>(rows * 2 * As * 2);
+  b->dxp = cv.take<float>(rows * d * 4);
+  b->w2t = cv.take<uint16_t>(E * dff * d * 2);
+  b->w13t = cv.take<uint16_t>(E * d * 2 * dff * 2);
+  b->w2st = cv.take<uint16_t>(dffs * d * 2);
+  b->w13st = cv.take<uint16_t>(d * 2 * dffs * 2);
+  b->dypT = cv.take<uint16_t>(d * Rp * 2);
+  b->actT = cv.take<uint16_t>(dff * Rp * 2);
+  b->dHT = cv.take<uint16_t>(2 * dff * Rp * 2);
+  b->xT = cv.take<uint16_t>(d * Rp * 2);
+  b->dysT = cv.take<uint16_t>(s.nsh ? d * Tp * 2 : 0);
+  b->actsT = cv.take<uint16_t>(s.nsh ? dffs * Tp * 2 : 0);
+  b->dHsT = cv.take<uint16_t>(s.nsh ? 2 * dffs * Tp * 2 : 0);
+  b->xsT = cv.take<uint16_t>(s.nsh ? d * Tp * 2 : 0);
+  return static_cast<size_t>(cv.p - base);
+}
+
 size_t stage_bytes(const Shape& s, moe_stage st) {
   size_t b = 0;
   switch (st) {
@@ -158,19 +227,16 @@ size_t stage_bytes(const Shape& s, moe_stage st) {
       b = forward_fixed_bytes(s) + scratch;
       break;
     }
+    case MOE_STAGE_BACKWARD: {
+      BwdBufs bb;
+      b = backward_layout(s, nullptr, &bb);
+      break;
+    }
   }
   return b < kAlign ? kAlign : b;
 }
 
-struct Carver {
-  char* p;
-  template <typename T>
-  T* take(size_t bytes) {
-    T* r = reinterpret_cast<T*>(p);
-    p += al(bytes);
-    return r;
-  }
-};
+
 
 moe_status check_ws(const Shape& s, moe_stage st, const void* ws, size_t ws_bytes) {
   if (st == MOE_STAGE_COMBINE) return MOE_OK;   // uses no scratch: ws may be NULL
@@ -320,7 +386,7 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 moe_status moe_workspace_size(const moe_config* cfg, moe_stage stage, size_t* bytes) {
   if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
-  if (stage < MOE_STAGE_ROUTE || stage > MOE_STAGE_EXPERT_DOWN)
+  if (stage < MOE_STAGE_ROUTE || stage > MOE_STAGE_BACKWARD)
     return fail(MOE_ERR_INVALID_ARG, "unknown stage %d", static_cast<int>(stage));
   Shape s;
   moe_status st = validate(cfg, &s);
@@ -439,6 +505,159 @@ moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t
   MOE_HIP(moe::launch_combine(y_perm, dest, gates, s.T, s.k, s.d, s.nsh ? s.R : -1, y,
                               static_cast<hipStream_t>(stream)),
           "combine");
+  return MOE_OK;
+}
+
+moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_router,
+                        const float* sel_bias, const void* w1, const void* w3, const void* w2,
+                        const void* ws1, const void* ws3, const void* ws2, const float* dy,
+                        float* dx, float* dw_router, float* dw1, float* dw3, float* dw2,
+                        float* dws1, float* dws3, float* dws2, void* ws, size_t ws_bytes,
+                        void* stream) {
+  Shape s;
+  moe_status st = validate(cfg, &s);
+  if (st != MOE_OK) return st;
+  if (!s.bf16) return fail(MOE_ERR_UNSUPPORTED, "the backward runs on bf16 inputs");
+  if (s.ep > 1) return fail(MOE_ERR_UNSUPPORTED, "the backward does not take ep_ranks > 1");
+  if (s.d % 256 || s.dff % 256 || s.dffs % 256)
+    return fail(MOE_ERR_UNSUPPORTED, "the backward needs d, d_ff, d_ff_shared multiples of 256");
+  REQUIRE(x); REQUIRE(w_router); REQUIRE(w1); REQUIRE(w3); REQUIRE(w2); REQUIRE(dy);
+  REQUIRE(dx); REQUIRE(dw_router); REQUIRE(dw1); REQUIRE(dw3); REQUIRE(dw2);
+  if (s.nsh) { REQUIRE(ws1); REQUIRE(ws3); REQUIRE(ws2); REQUIRE(dws1); REQUIRE(dws3); REQUIRE(dws2); }
+  if (sel_bias != nullptr && (reinterpret_cast<uintptr_t>(sel_bias) & 3))
+    return fail(MOE_ERR_INVALID_ARG, "sel_bias not 4-byte aligned");
+  st = check_ws(s, MOE_STAGE_BACKWARD, ws, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (s.T == 0) return MOE_OK;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  BwdBufs b;
+  backward_layout(s, static_cast<char*>(ws), &b);
+  const int T = s.T, E = s.E, k = s.k, R = s.R, d = s.d, dff = s.dff, dffs = s.dffs;
+  const int As = s.act_stride;
+  const int sh_row0 = s.nsh ? R : -1;
+  auto u16 = [](const void* p) { return static_cast<const uint16_t*>(p); };
+
+  // ---- forward, recomputed: routing, index, pre-activations, activation, y_perm
+  MOE_HIP(moe::launch_router_scores(1, x, w_router, T, d, E, b.z, strm), "router_scores");
+  MOE_HIP(moe::launch_router_select(b.z, sel_bias, T, E, k, s.gate_all, b.idx, b.gates, nullptr,
+                                    nullptr, nullptr, strm),
+          "router_select");
+  MOE_HIP(moe::launch_index(b.idx, T, k, E, s.C, b.blk, b.slot_base, b.slot_keep, b.offsets, b.dest,
+                            b.src, b.counts, b.kept, b.ndrop, s.BM, s.max_tiles, 1, b.tiles, strm),
+          "index");
+  MOE_HIP(moe::launch_pad_offsets(b.offsets, E, b.poff, strm), "pad_offsets");
+  const moe::GemmTileMap map{b.tiles, s.max_tiles, 0};
+  const moe::GemmTileMap map1{nullptr, 0, T};
+  const int bm1 = moe::gemm_tile_rows(1, T, 1, s.n256);
+  // h1 = X W1^T, h3 = X W3^T on the gathered token rows (fp32 out)
+  {
+    moe::DownArgs a{x, d, 0, w1, static_cast<long long>(dff) * d, b.h1, 0, d, dff, b.src};
+    MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "h1");
+    a.w2 = w3;
+    a.y = b.h3;
+    MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "h3");
+    MOE_HIP(moe::launch_swiglu_fwd(b.h1, b.h3, As, 0, R, dff, b.act, strm), "swiglu_fwd");
+    if (s.nsh) {
+      moe::DownArgs c{x, d, 0, ws1, 0, b.h1, R, d, dffs};
+      MOE_HIP(moe::launch_gemm_down_bf16(map1, c, bm1, strm), "h1 shared");
+      c.w2 = ws3;
+      c.y = b.h3;
+      MOE_HIP(moe::launch_gemm_down_bf16(map1, c, bm1, strm), "h3 shared");
+      MOE_HIP(moe::launch_swiglu_fwd(b.h1, b.h3, As, R, T, dffs, b.act, strm), "swiglu_fwd shared");
+    }
+    moe::DownArgs y{b.act, As, 0, w2, static_cast<long long>(d) * dff, b.yp, 0, dff, d};
+    MOE_HIP(moe::launch_gemm_down_bf16(map, y, s.BM, strm), "y_perm");
+  }
+
+  // ---- combine and gates
+  MOE_HIP(moe::launch_combine_bwd(dy, b.yp, b.dest, b.gates, T, k, d, sh_row0, b.dg, b.dyp, strm),
+          "combine_bwd");
+  MOE_HIP(moe::launch_gate_bwd(b.z, b.idx, b.gates, b.dg, b.counts, T, E, k, s.gate_all,
+                               cfg->aux_alpha, b.dz, strm),
+          "gate_bwd");
+
+  // ---- down: dact = dY_perm W2 (W2 transposed once per call), then SwiGLU
+  MOE_HIP(moe::launch_transpose_mat(u16(w2), E, d, dff, b.w2t, d, 0,
+                                    static_cast<long long>(dff) * d, strm),
+          "transpose w2");
+  {
+    moe::DownArgs a{b.dyp, d, 0, b.w2t, static_cast<long long>(dff) * d, b.dact, 0, d, dff};
+    MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "dact");
+  }
+  MOE_HIP(moe::launch_swiglu_bwd(b.dact, b.h1, b.h3, As, 0, R, dff, b.dH, strm), "swiglu_bwd");
+  if (s.nsh) {
+    MOE_HIP(moe::launch_transpose_mat(u16(ws2), 1, d, dffs, b.w2st, d, 0, 0, strm), "transpose ws2");
+    moe::DownArgs a{b.dyp, d, R, b.w2st, 0, b.dact, R, d, dffs};
+    MOE_HIP(moe::launch_gemm_down_bf16(map1, a, bm1, strm), "dact shared");
+    MOE_HIP(moe::launch_swiglu_bwd(b.dact, b.h1, b.h3, As, R, T, dffs, b.dH, strm),
+            "swiglu_bwd shared");
+  }
+
+  // ---- gate/up: dX_perm = [dh1 dh3] [W1; W3] with K = 2 d_ff
+  MOE_HIP(moe::launch_transpose_mat(u16(w1), E, dff, d, b.w13t, 2 * dff, 0,
+                                    static_cast<long long>(d) * 2 * dff, strm),
+          "transpose w1");
+  MOE_HIP(moe::launch_transpose_mat(u16(w3), E, dff, d, b.w13t, 2 * dff, dff,
+                                    static_cast<long long>(d) * 2 * dff, strm),
+          "transpose w3");
+  {
+    moe::DownArgs a{b.dH, 2 * As, 0, b.w13t, static_cast<long long>(d) * 2 * dff, b.dxp, 0,
+                    2 * dff, d};
+    MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "dx_perm");
+  }
+  if (s.nsh) {
+    MOE_HIP(moe::launch_transpose_mat(u16(ws1), 1, dffs, d, b.w13st, 2 * dffs, 0, 0, strm),
+            "transpose ws1");
+    MOE_HIP(moe::launch_transpose_mat(u16(ws3), 1, dffs, d, b.w13st, 2 * dffs, dffs, 0, strm),
+            "transpose ws3");
+    moe::DownArgs a{b.dH, 2 * As, R, b.w13st, 0, b.dxp, R, 2 * dffs, d};
+    MOE_HIP(moe::launch_gemm_down_bf16(map1, a, bm1, strm), "dx_perm shared");
+  }
+  MOE_HIP(moe::launch_unpermute_dx(1, b.dxp, b.dest, b.dz, w_router, T, k, E, d, sh_row0, dx, strm),
+          "unpermute_dx");
+  MOE_HIP(moe::launch_router_wgrad(1, b.dz, x, T, E, d, dw_router, strm), "router_wgrad");
+
+  // ---- weight gradients over each expert's rows (K = the group's rows, padded)
+  MOE_HIP(moe::launch_transpose_rows(b.dyp, d, nullptr, 0, b.offsets, b.poff, E, R, d, b.dypT, b.Rp,
+                                     strm),
+          "transpose dY_perm");
+  MOE_HIP(moe::launch_transpose_rows(b.act, As, nullptr, 0, b.offsets, b.poff, E, R, dff, b.actT,
+                                     b.Rp, strm),
+          "transpose act");
+  MOE_HIP(moe::launch_transpose_rows(b.dH, 2 * As, nullptr, 0, b.offsets, b.poff, E, R, 2 * dff,
+                                     b.dHT, b.Rp, strm),
+          "transpose dH");
+  MOE_HIP(moe::launch_transpose_rows(u16(x), d, b.src, 0, b.offsets, b.poff, E, R, d, b.xT, b.Rp,
+                                     strm),
+          "transpose x");
+  MOE_HIP(moe::launch_gemm_groupk_bf16(b.poff, E, b.dypT, d, b.actT, dff, b.Rp, dw2, strm), "dW2");
+  MOE_HIP(moe::launch_gemm_groupk_bf16(b.poff, E, b.dHT, dff, b.xT, d, b.Rp, dw1, strm), "dW1");
+  MOE_HIP(moe::launch_gemm_groupk_bf16(b.poff, E, b.dHT + static_cast<size_t>(dff) * b.Rp, dff,
+                                       b.xT, d, b.Rp, dw3, strm),
+          "dW3");
+  if (s.nsh) {
+    MOE_HIP(moe::launch_single_group_offsets(T, b.soff, strm), "shared offsets");
+    MOE_HIP(moe::launch_pad_offsets(b.soff, 1, b.spoff, strm), "shared padded offsets");
+    MOE_HIP(moe::launch_transpose_rows(b.dyp, d, nullptr, R, b.soff, b.spoff, 1, T, d, b.dysT, b.Tp,
+                                       strm),
+            "transpose dY shared");
+    MOE_HIP(moe::launch_transpose_rows(b.act, As, nullptr, R, b.soff, b.spoff, 1, T, dffs, b.actsT,
+                                       b.Tp, strm),
+            "transpose act shared");
+    MOE_HIP(moe::launch_transpose_rows(b.dH, 2 * As, nullptr, R, b.soff, b.spoff, 1, T, 2 * dffs,
+                                       b.dHsT, b.Tp, strm),
+            "transpose dH shared");
+    MOE_HIP(moe::launch_transpose_rows(u16(x), d, nullptr, 0, b.soff, b.spoff, 1, T, d, b.xsT, b.Tp,
+                                       strm),
+            "transpose x shared");
+    MOE_HIP(moe::launch_gemm_groupk_bf16(b.spoff, 1, b.dysT, d, b.actsT, dffs, b.Tp, dws2, strm),
+            "dWs2");
+    MOE_HIP(moe::launch_gemm_groupk_bf16(b.spoff, 1, b.dHsT, dffs, b.xsT, d, b.Tp, dws1, strm),
+            "dWs1");
+    MOE_HIP(moe::launch_gemm_groupk_bf16(b.spoff, 1, b.dHsT + static_cast<size_t>(dffs) * b.Tp,
+                                         dffs, b.xsT, d, b.Tp, dws3, strm),
+            "dWs3");
+  }
   return MOE_OK;
 }
 

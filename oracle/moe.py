@@ -457,7 +457,8 @@ def aux_loss_logit_grad(probs: np.ndarray, f: np.ndarray, alpha: float) -> np.nd
 
 
 def backward(x, w_router, experts: ExpertFn, k: int, dy, gate: str = GATE_SELECTED,
-             bias=None, cf: float = 0.0, shared=None, alpha: float = 0.0):
+             bias=None, cf: float = 0.0, shared=None, alpha: float = 0.0,
+             idx_override: Optional[np.ndarray] = None):
     """Gradients of L = sum_t <dy_t, y_t> + L_aux (L_aux only when alpha > 0) with
     respect to x, W_r and every expert's (and the shared expert's) weights.
 
@@ -469,13 +470,16 @@ def backward(x, w_router, experts: ExpertFn, k: int, dy, gate: str = GATE_SELECT
     the dg summed per expert ([15-779] §2.5 contrasts the two for k = 1). The
     selection bias enters neither gates nor gradients ([CME295] §4.2).
 
+    ``idx_override`` evaluates everything under another implementation's
+    selection (as in ``forward``).
+
     Returns dict(dx, dw_router, dw1[E], dw3[E], dw2[E], dws1, dws3, dws2, dz, dg, fwd)."""
     x = np.asarray(x, np.float64)
     dy = np.asarray(dy, np.float64)
     wr = np.asarray(w_router, np.float64)
     T, d = x.shape
     E = wr.shape[0]
-    fwd = forward(x, wr, experts, k, gate, bias, cf, shared, alpha)
+    fwd = forward(x, wr, experts, k, gate, bias, cf, shared, alpha, idx_override=idx_override)
     idx, gates, dest, src, offsets = fwd["idx"], fwd["gates"], fwd["dest"], fwd["src"], fwd["offsets"]
     yp = fwd["yp"]
     # combine backward

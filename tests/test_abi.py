@@ -174,6 +174,30 @@ def test_expert_parallel_config(lib):
     assert lib.moe_ep_traffic(ctypes.byref(_cfg(E=8, T=0, ep_ranks=4)), P, P, None) == moe.OK
 
 
+def test_backward_rejects_before_launch(lib):
+    """moe_backward: fp32, ep_ranks > 1 and widths that are not multiples of 256 are
+    UNSUPPORTED; NULL outputs, a missing shared gradient and a short workspace are rejected;
+    T == 0 is a no-op."""
+    P = FAKE
+    c = _cfg(d=256, d_ff=256, dtype="bf16", E=4, k=2, T=64)
+    ws = moe.workspace_size(c, moe.STAGE_BACKWARD)
+    assert ws > moe.workspace_size(c, moe.STAGE_FORWARD)
+    args = lambda cc, dx=P, dws=(None, None, None), w=ws: (
+        ctypes.byref(cc), P, P, None, P, P, P, None, None, None, P, dx, P, P, P, P, *dws, P, w, None)
+    assert lib.moe_backward(*args(_cfg(d=256, d_ff=256, dtype="f32"))) == moe.ERR_UNSUPPORTED
+    assert lib.moe_backward(*args(_cfg(d=256, d_ff=256, dtype="bf16", E=4, T=64,
+                                       ep_ranks=2))) == moe.ERR_UNSUPPORTED
+    assert lib.moe_backward(*args(_cfg(d=192, d_ff=256, dtype="bf16"))) == moe.ERR_UNSUPPORTED
+    assert lib.moe_backward(*args(c, dx=None)) == moe.ERR_INVALID_ARG
+    assert lib.moe_backward(*args(c, w=256)) == moe.ERR_WORKSPACE
+    cs = _cfg(d=256, d_ff=256, dtype="bf16", n_shared=1, d_ff_shared=256)
+    wss = moe.workspace_size(cs, moe.STAGE_BACKWARD)
+    assert lib.moe_backward(ctypes.byref(cs), P, P, None, P, P, P, P, P, P, P, P, P, P, P, P,
+                            None, P, P, P, wss, None) == moe.ERR_INVALID_ARG
+    c0 = _cfg(d=256, d_ff=256, dtype="bf16", T=0)
+    assert lib.moe_backward(*args(c0, w=moe.workspace_size(c0, moe.STAGE_BACKWARD))) == moe.OK
+
+
 def test_zero_tokens_is_a_noop(lib):
     """T == 0 validates and returns MOE_OK without touching any pointer."""
     c = _cfg(T=0)

@@ -321,6 +321,87 @@ def test_expert_parallel_mixtral_4096_bitwise():
     assert np.array_equal(a["y"].view(np.uint32), b["y"].view(np.uint32))
 
 
+# ------------------------------------------------------------------ backward
+
+_U_BF16 = 2.0 ** -9  # bf16 unit roundoff (8 significand bits, round to nearest even)
+
+_BWD_CASES = {
+    # name: (workload kwargs, T)
+    "selected_aux": (dict(d=256, E=8, k=2, d_ff=256, aux_alpha=0.01), 256),
+    "all_gate_capacity": (dict(d=256, E=8, k=1, d_ff=512, gate="all", capacity_factor=1.0,
+                               aux_alpha=0.01, offset_var=1.5), 512),
+    "shared_bias": (dict(d=512, E=16, k=4, d_ff=256, n_shared=1, d_ff_shared=256,
+                         bias_range=0.1), 128),
+    "large_tiles": (dict(d=512, E=8, k=2, d_ff=1024, router="orthonormal"), 2048),
+    "decode": (dict(d=256, E=8, k=2, d_ff=256), 8),
+}
+
+
+@pytest.mark.parametrize("case", list(_BWD_CASES))
+def test_backward_matches_oracle(case):
+    """moe_backward against the float64 oracle's gradients of <dy, y> + L_aux, evaluated
+    under the GPU's own routing: dx, dW_r, dW1/dW3/dW2 (and the shared expert's).
+
+    The GEMM operands dyp = g dy, act = silu(h1) h3 and dH are bf16 (unit roundoff
+    u = 2^-9) and every product accumulates in fp32, so each gradient carries a chain of
+    at most three bf16 roundings of independent sign: rms(got - want) is about u rms(want)
+    (measured 0.9-1.2 u) and the bar is 4 u. A weight-gradient element sums products over
+    the expert's rows, and its error scales with that row's and column's magnitude, so the
+    largest error sits 10-14 error-rms out; a 64 u rms(want) bound on the largest element
+    catches a single wrong row or element without tripping on that tail."""
+    kw, T = _BWD_CASES[case]
+    wl = _adhoc(f"bwd_{case}", 110 + list(_BWD_CASES).index(case), T=T, dtype=wk.BF16, **kw)
+    W = Weights(wl)
+    inp = wk.make_inputs(wl, T=T)
+    cfg = config_of(wl, T)
+    rng = np.random.default_rng(7)
+    dy_h = rng.standard_normal((T, wl.d)).astype(np.float32)
+    x = to_dev(inp.x, wl.dtype)
+    f32 = lambda *shape: torch.full(shape, float("nan"), dtype=torch.float32, device=dev())
+    E, d, dff = wl.E, wl.d, wl.d_ff
+    out = dict(dx=f32(T, d), dwr=f32(E, d), dw1=f32(E, dff, d), dw3=f32(E, dff, d),
+               dw2=f32(E, d, dff))
+    if wl.n_shared:
+        dffs = wl.d_ff_shared
+        out.update(dws1=f32(dffs, d), dws3=f32(dffs, d), dws2=f32(d, dffs))
+    log(f"[case] backward {case} T={T}")
+    moe.backward(cfg, x, W.wr, W.bias, W.w1, W.w3, W.w2, W.s1, W.s3, W.s2,
+                 torch.from_numpy(dy_h).to(dev()), out["dx"], out["dwr"], out["dw1"],
+                 out["dw3"], out["dw2"], out.get("dws1"), out.get("dws3"), out.get("dws2"),
+                 moe.alloc_workspace(cfg, moe.STAGE_BACKWARD))
+    # the forward's routing, for the oracle
+    fw = run_forward(wl, W, inp.x, T)
+    torch.cuda.synchronize()
+    g = {n: t.cpu().numpy().astype(np.float64) for n, t in out.items()}
+    x64 = wk.to_f64(inp.x, wl.dtype)
+    ref = om.backward(x64, wk.to_f64(W.wr_host, wl.dtype), W.expert64, wl.k,
+                      dy_h.astype(np.float64), wl.gate, W.bias_host, wl.capacity_factor,
+                      W.shared64(), wl.aux_alpha, idx_override=fw["idx"])
+    pairs = [("dx", ref["dx"]), ("dwr", ref["dw_router"]),
+             ("dw1", np.stack(ref["dw1"])), ("dw3", np.stack(ref["dw3"])),
+             ("dw2", np.stack(ref["dw2"]))]
+    if wl.n_shared:
+        pairs += [("dws1", ref["dws1"]), ("dws3", ref["dws3"]), ("dws2", ref["dws2"])]
+    worst = []
+    for name, want in pairs:
+        got = g[name]
+        assert np.all(np.isfinite(got)), f"{case}: {name} not finite"
+        rms = float(np.sqrt(np.mean(want ** 2)))
+        diff = got - want
+        err_rms = float(np.sqrt(np.mean(diff ** 2)))
+        err = float(np.max(np.abs(diff)))
+        worst.append(f"{name} rms {err_rms / max(rms, 1e-30) / _U_BF16:.2f}u "
+                     f"max {err / max(rms, 1e-30) / _U_BF16:.1f}u")
+        assert err_rms <= 4 * _U_BF16 * rms + 1e-12, \
+            f"{case}: {name} rms|d| {err_rms:.3g} vs rms {rms:.3g}"
+        assert err <= 64 * _U_BF16 * rms + 1e-12, \
+            f"{case}: {name} max|d| {err:.3g} vs rms {rms:.3g}"
+    untouched = np.setdiff1d(np.arange(E), fw["idx"].ravel())
+    for e in untouched:
+        assert not g["dw1"][e].any() and not g["dw2"][e].any()
+    log(f"[ok] backward {case}: " + ", ".join(worst))
+
+
 def test_bias_changes_selection_not_gates():
     """DeepSeek-style selection bias on the GPU: tokens whose selection the bias does not move
     get bitwise-identical gates (CME295 notes §4.2)."""
