@@ -12,6 +12,7 @@ events recorded on the library's stream around that kernel in every timed
 step, and the float64 CPU oracle timed on a bounded sample of the workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--ep N]
+                  [--backward]
   python bench.py --calibrate-copy     # plain 1 GiB copies, for counter scaling
 """
 from __future__ import annotations
@@ -51,6 +52,8 @@ def parse():
     ap.add_argument("--ep", type=int, default=0,
                     help="lay the rows out as N simulated expert-parallel ranks and report "
                          "the dispatch volume per rank")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time moe_backward (gradients of the layer) on the same batch")
     return ap.parse_args()
 
 
@@ -251,6 +254,11 @@ def main():
                      "rows_per_rank_min": int(rows.sum(axis=0).min()),
                      "rows_per_rank_max": int(rows.sum(axis=0).max())}
 
+    bwd_report = None
+    if args.backward:
+        bwd_report = time_backward(args, cfg, wl, x, wr, bias, (w1, w3, w2), (s1, s3, s2),
+                                   R_kept, stream, peak_f)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, inp, host, args.cpu_sample)
@@ -281,8 +289,62 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "expert_parallel": ep_report,
+        "backward": bwd_report,
     }
     print(json.dumps(out), flush=True)
+
+
+def time_backward(args, cfg, wl, x, wr, bias, experts, shared, R_kept, stream, peak_f):
+    """moe_backward over the same batch (dy ~ N(0, 1)), K timed calls between HIP events
+    on the library's stream. Algorithmic work per kept row: 12 d d_ff flop (the
+    activation gradient, dx through W1/W3 and the three weight gradients; twice the
+    forward's 6 d d_ff), plus 4 d d_ff to recompute h1 and h3, which the library does
+    instead of keeping them from the forward."""
+    import numpy as np
+    import torch
+    import mixture_experts_layer_31_amd as moe
+
+    dev = x.device
+    T, d, E, dff = wl.T, wl.d, wl.E, wl.d_ff
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    dy = torch.randn((T, d), generator=gen, dtype=torch.float32, device=dev)
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    dx, dwr = f32(T, d), f32(E, d)
+    dw1, dw3, dw2 = f32(E, dff, d), f32(E, dff, d), f32(E, d, dff)
+    dws = (None, None, None)
+    if wl.n_shared:
+        dffs = wl.d_ff_shared
+        dws = (f32(dffs, d), f32(dffs, d), f32(d, dffs))
+    ws = moe.alloc_workspace(cfg, moe.STAGE_BACKWARD)
+
+    def call():
+        moe.backward(cfg, x, wr, bias, *experts, *shared, dy, dx, dwr, dw1, dw3, dw2, *dws,
+                     ws, stream)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    b0 = torch.cuda.Event(enable_timing=True)
+    b1 = torch.cuda.Event(enable_timing=True)
+    K = args.steps
+    b0.record(stream)
+    for _ in range(K):
+        call()
+    b1.record(stream)
+    torch.cuda.synchronize()
+    ms = b0.elapsed_time(b1) / K
+    rows_sh = wl.n_shared * T
+    F = (12.0 * d * dff * R_kept + 12.0 * d * wl.d_ff_shared * rows_sh
+         + 4.0 * T * d * E)
+    F_re = 4.0 * d * dff * R_kept + 4.0 * d * wl.d_ff_shared * rows_sh
+    tf = F / (ms * 1e-3) / 1e12
+    tf_all = (F + F_re) / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "algorithmic_flops": F, "recompute_flops": F_re,
+            "tflops": round(tf, 2), "frac_mfma": round(tf / peak_f, 4),
+            "tflops_with_recompute": round(tf_all, 2),
+            "workspace_bytes": int(ws.numel())}
 
 
 def cpu_baseline(wl, inp, host, sample):

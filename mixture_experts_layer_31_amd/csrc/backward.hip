@@ -39,16 +39,69 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __rest
   if (g == 0) poff[0] = 0;
 }
 
+// A 64-row x 128-column tile of 16-bit values, transposed through LDS: in_row(rr)
+// gives row rr's first column (nullptr: a zero row), out_row(n) the 64-value
+// output row that receives column n. LDS holds 32-bit words pairing rows 2i and
+// 2i+1 of one column (low half = row 2i), so every output row is 32 contiguous
+// words; 16-byte global loads, 8-byte LDS reads, 16-byte global stores. The row
+// pitch of 34 words puts the two column halves of a wave's stores 32 banks apart.
+constexpr int kTrPitch = 34;
+constexpr int kTrLdsWords = 128 * kTrPitch;
+
+template <class InRow, class OutRow>
+__device__ __forceinline__ void transpose_tile(InRow in_row, OutRow out_row, uint32_t* lds) {
+  const int tid = threadIdx.x;
+  {
+    const int i = tid & 31, cg = tid >> 5;     // rows 2i, 2i+1; columns 16 cg .. 16 cg + 15
+    const uint16_t* pa = in_row(2 * i);
+    const uint16_t* pb = in_row(2 * i + 1);
+    u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = a0, b0 = a0, b1 = a0;
+    if (pa != nullptr) {
+      const u32x4* q = reinterpret_cast<const u32x4*>(pa + cg * 16);
+      a0 = q[0];
+      a1 = q[1];
+    }
+    if (pb != nullptr) {
+      const u32x4* q = reinterpret_cast<const u32x4*>(pb + cg * 16);
+      b0 = q[0];
+      b1 = q[1];
+    }
+    uint32_t* w = lds + cg * 16 * kTrPitch + i;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w[(2 * q) * kTrPitch] = (a0[q] & 0xFFFFu) | (b0[q] << 16);
+      w[(2 * q + 1) * kTrPitch] = (a0[q] >> 16) | (b0[q] & 0xFFFF0000u);
+      w[(8 + 2 * q) * kTrPitch] = (a1[q] & 0xFFFFu) | (b1[q] << 16);
+      w[(8 + 2 * q + 1) * kTrPitch] = (a1[q] >> 16) | (b1[q] & 0xFFFF0000u);
+    }
+  }
+  __syncthreads();
+  {
+    const int n = tid >> 1, h = tid & 1;       // output row n, values 32 h .. 32 h + 31
+    const uint32_t* w = lds + n * kTrPitch + h * 16;
+    u32x4 o[4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(w + 2 * j);
+      o[j >> 1][(j & 1) * 2] = v[0];
+      o[j >> 1][(j & 1) * 2 + 1] = v[1];
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(out_row(n) + h * 32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[j] = o[j];
+  }
+}
+
 // out[c][poff[g] + (r - offsets[g])] = in[row(r)][c] for every row r of group g,
 // row(r) = src[r] (gather) or in_row0 + r; the padding columns of each group
 // are zeros. grid.x: 64-column chunks of the padded row space (groups start at
 // multiples of 64, so a chunk lies in one group; chunks past poff[G] exit),
-// grid.y: 64-wide chunks of C.
+// grid.y: 128-wide chunks of C.
 __global__ __launch_bounds__(256) void transpose_rows_kernel(
     const uint16_t* __restrict__ in, int in_stride, const int32_t* __restrict__ src, int in_row0,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ poff, int G, int C,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ poff, int G,
     uint16_t* __restrict__ out, int out_stride) {
-  __shared__ uint16_t tile[64][64 + 2];
+  __shared__ uint32_t lds[kTrLdsWords];
   const int p0 = blockIdx.x * 64;
   if (p0 >= poff[G]) return;
   int lo = 0, hi = G;                       // largest g with poff[g] <= p0
@@ -59,81 +112,31 @@ __global__ __launch_bounds__(256) void transpose_rows_kernel(
   const int g = lo;
   const int r0 = offsets[g] + (p0 - poff[g]);
   const int nrows = min(64, max(0, offsets[g + 1] - r0));
-  const int c0 = blockIdx.y * 64;
-  const int tid = threadIdx.x;
-  {
-    const int rr = tid >> 2, cc = (tid & 3) * 16;   // row rr, 16 columns from cc
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (rr < nrows) {
-      const int r = r0 + rr;
-      const size_t row = src != nullptr ? static_cast<size_t>(src[r]) : static_cast<size_t>(in_row0) + r;
-      const u32x4* p = reinterpret_cast<const u32x4*>(in + row * in_stride + c0 + cc);
-      a = p[0];
-      b = p[1];
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      tile[rr][cc + 2 * q] = static_cast<uint16_t>(a[q] & 0xFFFFu);
-      tile[rr][cc + 2 * q + 1] = static_cast<uint16_t>(a[q] >> 16);
-      tile[rr][cc + 8 + 2 * q] = static_cast<uint16_t>(b[q] & 0xFFFFu);
-      tile[rr][cc + 8 + 2 * q + 1] = static_cast<uint16_t>(b[q] >> 16);
-    }
-  }
-  __syncthreads();
-  {
-    const int cc = tid >> 2, pp = (tid & 3) * 16;   // output row c0 + cc, 16 columns
-    u32x4 a, b;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      a[q] = static_cast<uint32_t>(tile[pp + 2 * q][cc]) |
-             (static_cast<uint32_t>(tile[pp + 2 * q + 1][cc]) << 16);
-      b[q] = static_cast<uint32_t>(tile[pp + 8 + 2 * q][cc]) |
-             (static_cast<uint32_t>(tile[pp + 8 + 2 * q + 1][cc]) << 16);
-    }
-    u32x4* o = reinterpret_cast<u32x4*>(out + static_cast<size_t>(c0 + cc) * out_stride + p0 + pp);
-    o[0] = a;
-    o[1] = b;
-  }
+  const int c0 = blockIdx.y * 128;
+  transpose_tile(
+      [&](int rr) -> const uint16_t* {
+        if (rr >= nrows) return nullptr;
+        const int r = r0 + rr;
+        const size_t row = src != nullptr ? static_cast<size_t>(src[r])
+                                          : static_cast<size_t>(in_row0) + r;
+        return in + row * in_stride + c0;
+      },
+      [&](int n) { return out + static_cast<size_t>(c0 + n) * out_stride + p0; }, lds);
 }
 
-// out[b][n][col0 + m] = in[b][m][n] for in [B][M][N]; M, N multiples of 64.
-// grid (N/64, M/64, B).
+// out[b][n][col0 + m] = in[b][m][n] for in [B][M][N]; M a multiple of 64, N of 128.
+// grid (N/128, M/64, B).
 __global__ __launch_bounds__(256) void transpose_mat_kernel(const uint16_t* __restrict__ in, int M,
                                                             int N, uint16_t* __restrict__ out,
                                                             int out_stride, int col0,
                                                             long long out_batch) {
-  __shared__ uint16_t tile[64][64 + 2];
-  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
+  __shared__ uint32_t lds[kTrLdsWords];
+  const int n0 = blockIdx.x * 128, m0 = blockIdx.y * 64;
   const uint16_t* ib = in + static_cast<size_t>(blockIdx.z) * M * N;
   uint16_t* ob = out + static_cast<size_t>(blockIdx.z) * out_batch;
-  const int tid = threadIdx.x;
-  {
-    const int rr = tid >> 2, cc = (tid & 3) * 16;
-    const u32x4* p = reinterpret_cast<const u32x4*>(ib + static_cast<size_t>(m0 + rr) * N + n0 + cc);
-    const u32x4 a = p[0], b = p[1];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      tile[rr][cc + 2 * q] = static_cast<uint16_t>(a[q] & 0xFFFFu);
-      tile[rr][cc + 2 * q + 1] = static_cast<uint16_t>(a[q] >> 16);
-      tile[rr][cc + 8 + 2 * q] = static_cast<uint16_t>(b[q] & 0xFFFFu);
-      tile[rr][cc + 8 + 2 * q + 1] = static_cast<uint16_t>(b[q] >> 16);
-    }
-  }
-  __syncthreads();
-  {
-    const int cc = tid >> 2, pp = (tid & 3) * 16;
-    u32x4 a, b;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      a[q] = static_cast<uint32_t>(tile[pp + 2 * q][cc]) |
-             (static_cast<uint32_t>(tile[pp + 2 * q + 1][cc]) << 16);
-      b[q] = static_cast<uint32_t>(tile[pp + 8 + 2 * q][cc]) |
-             (static_cast<uint32_t>(tile[pp + 8 + 2 * q + 1][cc]) << 16);
-    }
-    u32x4* o = reinterpret_cast<u32x4*>(ob + static_cast<size_t>(n0 + cc) * out_stride + col0 + m0 + pp);
-    o[0] = a;
-    o[1] = b;
-  }
+  transpose_tile(
+      [&](int rr) -> const uint16_t* { return ib + static_cast<size_t>(m0 + rr) * N + n0; },
+      [&](int n) { return ob + static_cast<size_t>(n0 + n) * out_stride + col0 + m0; }, lds);
 }
 
 // act = silu(h1) * h3 rounded to bf16, rows [row0, row0 + rows), n columns.
@@ -147,84 +150,101 @@ __global__ __launch_bounds__(256) void swiglu_fwd_kernel(const float* __restrict
   act[o] = f32_to_bf16(silu(h1[o]) * h3[o]);
 }
 
-// dh1 = da * h3 * silu'(h1), dh3 = da * silu(h1), silu'(u) = s (1 + u (1 - s)),
-// s = 1 / (1 + e^-u); written as bf16 into dH[row][0..n) and dH[row][n..2n)
-// (dH row stride 2 * stride).
-__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict__ da,
+// Row-wise SwiGLU backward, one workgroup per row r in [row0, row0 + rows):
+// da = g_r u_r (g_r = row_gate[r]; 1 when row_gate is null), dh1 = da h3 silu'(h1),
+// dh3 = da silu(h1), silu'(v) = s (1 + v (1 - s)), s = 1 / (1 + e^-v); written as
+// bf16 into dH[r][0..n) and dH[r][n..2n) (row stride 2 stride). u_r = dy_t W2 is the
+// ungated gradient of the row's expert output, so with dg_row the gate's gradient
+// <dy_t, y_perm[r]> = <act_r, u_r> comes out here too (act as stored, bf16): per
+// thread in column order, then a fixed tree.
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict__ u,
                                                          const float* __restrict__ h1,
                                                          const float* __restrict__ h3,
-                                                         int stride, int row0, int rows, int n,
-                                                         uint16_t* __restrict__ dH) {
-  const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= static_cast<long long>(rows) * n) return;
-  const size_t r = static_cast<size_t>(row0 + i / n);
-  const int f = static_cast<int>(i % n);
-  const size_t o = r * stride + f;
-  const float u = h1[o];
-  const float s = 1.0f / (1.0f + __expf(-u));
-  const float g = da[o];
-  dH[r * 2 * stride + f] = f32_to_bf16(g * h3[o] * s * (1.0f + u * (1.0f - s)));
-  dH[r * 2 * stride + n + f] = f32_to_bf16(g * u * s);
-}
-
-// One workgroup per token: dg[t,j] = <dy_t, yp[dest[t,j]]> (0 for a dropped
-// slot), dyp[dest[t,j]] = g[t,j] dy_t in bf16; with a shared expert its rows
-// dyp[shared_row0 + t] = dy_t. The dot products sum per thread in index order,
-// then over threads in a fixed tree.
-__global__ __launch_bounds__(256) void combine_bwd_kernel(const float* __restrict__ dy,
-                                                          const float* __restrict__ yp,
-                                                          const int32_t* __restrict__ dest,
-                                                          const float* __restrict__ gates,
-                                                          int k, int d, int shared_row0,
-                                                          float* __restrict__ dg,
-                                                          uint16_t* __restrict__ dyp) {
+                                                         const uint16_t* __restrict__ act,
+                                                         const float* __restrict__ row_gate,
+                                                         int stride, int row0, int n,
+                                                         uint16_t* __restrict__ dH,
+                                                         float* __restrict__ dg_row) {
   __shared__ float red[256];
-  const int t = blockIdx.x, tid = threadIdx.x;
-  const float* dyt = dy + static_cast<size_t>(t) * d;
-  for (int j = 0; j < k; ++j) {
-    const int r = dest[static_cast<size_t>(t) * k + j];
-    if (r < 0) {
-      if (tid == 0) dg[static_cast<size_t>(t) * k + j] = 0.f;
-      continue;
+  const int tid = threadIdx.x;
+  const size_t r = static_cast<size_t>(row0) + blockIdx.x;
+  const float g = row_gate != nullptr ? row_gate[r] : 1.0f;
+  float acc = 0.f;
+  for (int f = tid * 4; f < n; f += 1024) {
+    const size_t o = r * stride + f;
+    const f32x4 uu = *reinterpret_cast<const f32x4*>(u + o);
+    const f32x4 v1 = *reinterpret_cast<const f32x4*>(h1 + o);
+    const f32x4 v3 = *reinterpret_cast<const f32x4*>(h3 + o);
+    float d1[4], d3[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float da = g * uu[q];
+      const float sg = 1.0f / (1.0f + __expf(-v1[q]));
+      d1[q] = da * v3[q] * sg * (1.0f + v1[q] * (1.0f - sg));
+      d3[q] = da * v1[q] * sg;
     }
-    const float g = gates[static_cast<size_t>(t) * k + j];
-    const float* ypr = yp + static_cast<size_t>(r) * d;
-    uint16_t* dr = dyp + static_cast<size_t>(r) * d;
-    float acc = 0.f;
-    for (int i = tid * 4; i < d; i += 1024) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(dyt + i);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(ypr + i);
-      acc = fmaf(a[0], b[0], acc);
-      acc = fmaf(a[1], b[1], acc);
-      acc = fmaf(a[2], b[2], acc);
-      acc = fmaf(a[3], b[3], acc);
-      u32x2 pk;
-      pk[0] = pack_bf16x2(g * a[0], g * a[1]);
-      pk[1] = pack_bf16x2(g * a[2], g * a[3]);
-      *reinterpret_cast<u32x2*>(dr + i) = pk;
+    if (dg_row != nullptr) {
+      float av[4];
+      Elt<uint16_t>::load4(act + o, av);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc = fmaf(av[q], uu[q], acc);
     }
+    uint16_t* dr = dH + r * 2 * stride + f;
+    u32x2 p1, p3;
+    p1[0] = pack_bf16x2(d1[0], d1[1]);
+    p1[1] = pack_bf16x2(d1[2], d1[3]);
+    p3[0] = pack_bf16x2(d3[0], d3[1]);
+    p3[1] = pack_bf16x2(d3[2], d3[3]);
+    *reinterpret_cast<u32x2*>(dr) = p1;
+    *reinterpret_cast<u32x2*>(dr + n) = p3;
+  }
+  if (dg_row != nullptr) {
     red[tid] = acc;
     __syncthreads();
     for (int h = 128; h >= 1; h >>= 1) {
       if (tid < h) red[tid] += red[tid + h];
       __syncthreads();
     }
-    if (tid == 0) dg[static_cast<size_t>(t) * k + j] = red[0];
-    __syncthreads();
-  }
-  if (shared_row0 >= 0) {
-    uint16_t* dr = dyp + static_cast<size_t>(shared_row0 + t) * d;
-    for (int i = tid * 4; i < d; i += 1024) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(dyt + i);
-      u32x2 pk;
-      pk[0] = pack_bf16x2(a[0], a[1]);
-      pk[1] = pack_bf16x2(a[2], a[3]);
-      *reinterpret_cast<u32x2*>(dr + i) = pk;
-    }
+    if (tid == 0) dg_row[r] = red[0];
   }
 }
 
-// One wave per token: the logits' gradient dz[t, :] from the gates' gradient.
+// One workgroup per token: dyb[t] = bf16(dy_t), the operand of the activation
+// gradient's GEMM; for every kept slot j, dyp[dest[t,j]] = bf16(g[t,j] dy_t), the
+// operand of dW2, and row_gate[dest[t,j]] = g[t,j].
+__global__ __launch_bounds__(256) void dy_rows_kernel(const float* __restrict__ dy,
+                                                      const int32_t* __restrict__ dest,
+                                                      const float* __restrict__ gates, int k,
+                                                      int d, uint16_t* __restrict__ dyb,
+                                                      uint16_t* __restrict__ dyp,
+                                                      float* __restrict__ row_gate) {
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const float* dyt = dy + static_cast<size_t>(t) * d;
+  const int32_t* dt = dest + static_cast<size_t>(t) * k;
+  const float* gt = gates + static_cast<size_t>(t) * k;
+  for (int i = tid * 4; i < d; i += 1024) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(dyt + i);
+    u32x2 pk;
+    pk[0] = pack_bf16x2(a[0], a[1]);
+    pk[1] = pack_bf16x2(a[2], a[3]);
+    *reinterpret_cast<u32x2*>(dyb + static_cast<size_t>(t) * d + i) = pk;
+    for (int j = 0; j < k; ++j) {
+      const int r = dt[j];
+      if (r < 0) continue;
+      const float g = gt[j];
+      pk[0] = pack_bf16x2(g * a[0], g * a[1]);
+      pk[1] = pack_bf16x2(g * a[2], g * a[3]);
+      *reinterpret_cast<u32x2*>(dyp + static_cast<size_t>(r) * d + i) = pk;
+    }
+  }
+  if (tid < k) {
+    const int r = dt[tid];
+    if (r >= 0) row_gate[r] = gt[tid];
+  }
+}
+
+// One wave per token: the logits' gradient dz[t, :] from the gates' gradient
+// dg[t,j] = dg_row[dest[t,j]] (0 for a dropped slot).
 // SELECTED: g = softmax of the selected logits, dz_e = g_j (dg_j - sum_l g_l dg_l)
 // for e = idx_j, 0 elsewhere. ALL: g_j = p_{idx_j}, dz = p (dp - sum p dp) with
 // dp_e the dg of the slots that chose e. alpha > 0 adds the balance-loss term
@@ -232,7 +252,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const float* __restric
 __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__ z,
                                                        const int32_t* __restrict__ idx,
                                                        const float* __restrict__ gates,
-                                                       const float* __restrict__ dg,
+                                                       const int32_t* __restrict__ dest,
+                                                       const float* __restrict__ dg_row,
                                                        const int32_t* __restrict__ counts, int T,
                                                        int E, int k, int gate_all, float alpha,
                                                        float* __restrict__ dz) {
@@ -244,7 +265,8 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
   // slot j < k lives in lane j
   const int my_e = lane < k ? idx[static_cast<size_t>(t) * k + lane] : -1;
   const float my_g = lane < k ? gates[static_cast<size_t>(t) * k + lane] : 0.f;
-  const float my_dg = lane < k ? dg[static_cast<size_t>(t) * k + lane] : 0.f;
+  const int my_r = lane < k ? dest[static_cast<size_t>(t) * k + lane] : -1;
+  const float my_dg = my_r >= 0 ? dg_row[my_r] : 0.f;   // a dropped slot passes nothing
   const bool need_p = gate_all || alpha > 0.f;
   float m = -INFINITY, se = 0.f;
   if (need_p) {
@@ -294,44 +316,121 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
   }
 }
 
-// One workgroup per token: dx_t = sum_j dXp[dest[t,j]] (slot order)
-// + dXp[shared_row0 + t] + sum_e dz[t,e] W_r[e] (expert order), fp32.
-template <typename Tw>
+// dx_t = sum_j dXp[dest[t,j]] (slot order) + dXp[shared_row0 + t]
+// + sum_e dz[t,e] W_r[e] (expert order), fp32. A workgroup takes TT tokens and
+// 1024 columns (4 per thread), so each W_r row segment is loaded once for TT
+// tokens; the TT tokens' dz rows sit in LDS. grid (d / 1024, ceil(T / TT)).
+template <typename Tw, int TT>
 __global__ __launch_bounds__(256) void unpermute_dx_kernel(const float* __restrict__ dxp,
                                                            const int32_t* __restrict__ dest,
                                                            const float* __restrict__ dz,
-                                                           const Tw* __restrict__ wr, int k,
-                                                           int E, int d, int shared_row0,
+                                                           const Tw* __restrict__ wr, int T,
+                                                           int k, int E, int d, int shared_row0,
                                                            float* __restrict__ dx) {
-  const int t = blockIdx.x;
-  const int32_t* dt = dest + static_cast<size_t>(t) * k;
-  const float* dzt = dz + static_cast<size_t>(t) * E;
-  for (int i = threadIdx.x; i < d; i += 256) {
-    float acc = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int r = dt[j];
-      if (r >= 0) acc += dxp[static_cast<size_t>(r) * d + i];
+  extern __shared__ float sdz[];   // [TT][E]
+  const int t0 = blockIdx.y * TT;
+  const int nt = min(TT, T - t0);
+  for (int q = threadIdx.x; q < nt * E; q += 256) sdz[q] = dz[static_cast<size_t>(t0) * E + q];
+  __syncthreads();
+  const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= d) return;
+  float acc[TT][4], ra[TT][4];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[tt][q] = ra[tt][q] = 0.f;
+    if (tt < nt) {
+      const int t = t0 + tt;
+      for (int j = 0; j < k; ++j) {
+        const int r = dest[static_cast<size_t>(t) * k + j];
+        if (r < 0) continue;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(dxp + static_cast<size_t>(r) * d + i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[tt][q] += v[q];
+      }
+      if (shared_row0 >= 0) {
+        const f32x4 v =
+            *reinterpret_cast<const f32x4*>(dxp + static_cast<size_t>(shared_row0 + t) * d + i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[tt][q] += v[q];
+      }
     }
-    if (shared_row0 >= 0) acc += dxp[static_cast<size_t>(shared_row0 + t) * d + i];
-    float ra = 0.f;
-    for (int e = 0; e < E; ++e) ra = fmaf(dzt[e], Elt<Tw>::load1(wr + static_cast<size_t>(e) * d + i), ra);
-    dx[static_cast<size_t>(t) * d + i] = acc + ra;
+  }
+  for (int e = 0; e < E; ++e) {
+    float w[4];
+    Elt<Tw>::load4(wr + static_cast<size_t>(e) * d + i, w);
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const float z = sdz[(tt < nt ? tt : 0) * E + e];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ra[tt][q] = fmaf(z, w[q], ra[tt][q]);
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    if (tt < nt) {
+      f32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = acc[tt][q] + ra[tt][q];
+      *reinterpret_cast<f32x4*>(dx + static_cast<size_t>(t0 + tt) * d + i) = o;
+    }
   }
 }
 
-// dW_r[e][i] = sum_t dz[t][e] x[t][i], tokens in order.
-template <typename Tx>
-__global__ __launch_bounds__(256) void router_wgrad_kernel(const float* __restrict__ dz,
-                                                           const Tx* __restrict__ x, int T,
-                                                           int E, int d,
-                                                           float* __restrict__ dwr) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  const int e = blockIdx.y;
+// dW_r[e][i] = sum_t dz[t][e] x[t][i] in two fixed-order passes. Pass 1: token
+// chunks of tc tokens, part[c][e][i] = sum over the chunk's tokens in order; a
+// workgroup takes 512 columns (2 per thread) and EB experts, the chunk's dz
+// columns in LDS, so each x row segment is read once per EB experts.
+// grid (ceil(d / 512), ceil(E / EB), chunks). Pass 2 sums the chunks in order.
+template <typename Tx, int EB>
+__global__ __launch_bounds__(256) void router_wgrad_part_kernel(const float* __restrict__ dz,
+                                                                const Tx* __restrict__ x, int T,
+                                                                int E, int d, int tc,
+                                                                float* __restrict__ part) {
+  extern __shared__ float sdz[];   // [tc][EB]
+  const int c = blockIdx.z, e0 = blockIdx.y * EB;
+  const int t0 = c * tc;
+  const int nt = min(tc, T - t0);
+  for (int q = threadIdx.x; q < nt * EB; q += 256) {
+    const int tt = q / EB, ee = q - tt * EB;
+    sdz[q] = e0 + ee < E ? dz[static_cast<size_t>(t0 + tt) * E + e0 + ee] : 0.f;
+  }
+  __syncthreads();
+  const int i = (blockIdx.x * 256 + threadIdx.x) * 2;
   if (i >= d) return;
+  float a0[EB], a1[EB];
+#pragma unroll
+  for (int ee = 0; ee < EB; ++ee) a0[ee] = a1[ee] = 0.f;
+  for (int tt = 0; tt < nt; ++tt) {
+    float xv[2];
+    Elt<Tx>::load2(x + static_cast<size_t>(t0 + tt) * d + i, xv);
+    const float* zr = sdz + tt * EB;
+#pragma unroll
+    for (int ee = 0; ee < EB; ++ee) {
+      a0[ee] = fmaf(zr[ee], xv[0], a0[ee]);
+      a1[ee] = fmaf(zr[ee], xv[1], a1[ee]);
+    }
+  }
+#pragma unroll
+  for (int ee = 0; ee < EB; ++ee) {
+    if (e0 + ee < E) {
+      float* pp = part + (static_cast<size_t>(c) * E + e0 + ee) * d + i;
+      u32x2 v;
+      v[0] = __float_as_uint(a0[ee]);
+      v[1] = __float_as_uint(a1[ee]);
+      *reinterpret_cast<u32x2*>(pp) = v;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void router_wgrad_sum_kernel(const float* __restrict__ part,
+                                                               int chunks, long long n,
+                                                               float* __restrict__ dwr) {
+  const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
   float acc = 0.f;
-  for (int t = 0; t < T; ++t)
-    acc = fmaf(dz[static_cast<size_t>(t) * E + e], Elt<Tx>::load1(x + static_cast<size_t>(t) * d + i), acc);
-  dwr[static_cast<size_t>(e) * d + i] = acc;
+  for (int c = 0; c < chunks; ++c) acc += part[static_cast<size_t>(c) * n + i];
+  dwr[i] = acc;
 }
 
 __global__ void single_group_offsets_kernel(int rows, int32_t* __restrict__ off) {
@@ -356,16 +455,18 @@ hipError_t launch_transpose_rows(const uint16_t* in, int in_stride, const int32_
                                  int in_row0, const int32_t* offsets, const int32_t* poff, int G,
                                  int max_rows, int C, uint16_t* out, int out_stride,
                                  hipStream_t s) {
+  if (C % 128 || in_stride % 8 || out_stride % 8) return hipErrorInvalidValue;
   const int chunks = (max_rows + kPadRows * G + 63) / 64;
-  transpose_rows_kernel<<<dim3(chunks, C / 64), dim3(256), 0, s>>>(
-      in, in_stride, src, in_row0, offsets, poff, G, C, out, out_stride);
+  transpose_rows_kernel<<<dim3(chunks, C / 128), dim3(256), 0, s>>>(
+      in, in_stride, src, in_row0, offsets, poff, G, out, out_stride);
   return hipGetLastError();
 }
 
 hipError_t launch_transpose_mat(const uint16_t* in, int B, int M, int N, uint16_t* out,
                                 int out_stride, int col0, long long out_batch, hipStream_t s) {
-  transpose_mat_kernel<<<dim3(N / 64, M / 64, B), dim3(256), 0, s>>>(in, M, N, out, out_stride,
-                                                                     col0, out_batch);
+  if (M % 64 || N % 128 || out_stride % 8 || col0 % 8) return hipErrorInvalidValue;
+  transpose_mat_kernel<<<dim3(N / 128, M / 64, B), dim3(256), 0, s>>>(in, M, N, out, out_stride,
+                                                                      col0, out_batch);
   return hipGetLastError();
 }
 
@@ -377,52 +478,90 @@ hipError_t launch_swiglu_fwd(const float* h1, const float* h3, int stride, int r
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu_bwd(const float* da, const float* h1, const float* h3, int stride,
-                             int row0, int rows, int n, uint16_t* dH, hipStream_t s) {
-  const long long cnt = static_cast<long long>(rows) * n;
-  if (cnt == 0) return hipSuccess;
-  swiglu_bwd_kernel<<<dim3(blocks_for(cnt)), dim3(256), 0, s>>>(da, h1, h3, stride, row0, rows,
-                                                                n, dH);
+hipError_t launch_swiglu_bwd(const float* u, const float* h1, const float* h3,
+                             const uint16_t* act, const float* row_gate, int stride, int row0,
+                             int rows, int n, uint16_t* dH, float* dg_row, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (n % 4 || stride % 4) return hipErrorInvalidValue;
+  swiglu_bwd_kernel<<<dim3(rows), dim3(256), 0, s>>>(u, h1, h3, act, row_gate, stride, row0, n,
+                                                     dH, dg_row);
   return hipGetLastError();
 }
 
-hipError_t launch_combine_bwd(const float* dy, const float* yp, const int32_t* dest,
-                              const float* gates, int T, int k, int d, int shared_row0, float* dg,
-                              uint16_t* dyp, hipStream_t s) {
-  combine_bwd_kernel<<<dim3(T), dim3(256), 0, s>>>(dy, yp, dest, gates, k, d, shared_row0, dg,
-                                                   dyp);
+hipError_t launch_dy_rows(const float* dy, const int32_t* dest, const float* gates, int T, int k,
+                          int d, uint16_t* dyb, uint16_t* dyp, float* row_gate, hipStream_t s) {
+  if (d % 4) return hipErrorInvalidValue;
+  dy_rows_kernel<<<dim3(T), dim3(256), 0, s>>>(dy, dest, gates, k, d, dyb, dyp, row_gate);
   return hipGetLastError();
 }
 
-hipError_t launch_gate_bwd(const float* z, const int32_t* idx, const float* gates, const float* dg,
-                           const int32_t* counts, int T, int E, int k, int gate_all, float alpha,
-                           float* dz, hipStream_t s) {
-  gate_bwd_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(z, idx, gates, dg, counts, T, E, k,
-                                                          gate_all, alpha, dz);
+hipError_t launch_gate_bwd(const float* z, const int32_t* idx, const float* gates,
+                           const int32_t* dest, const float* dg_row, const int32_t* counts, int T,
+                           int E, int k, int gate_all, float alpha, float* dz, hipStream_t s) {
+  gate_bwd_kernel<<<dim3((T + 3) / 4), dim3(256), 0, s>>>(z, idx, gates, dest, dg_row, counts, T,
+                                                          E, k, gate_all, alpha, dz);
   return hipGetLastError();
+}
+
+template <typename Tw, int TT>
+static void unpermute_dx_as(const float* dxp, const int32_t* dest, const float* dz, const void* wr,
+                            int T, int k, int E, int d, int shared_row0, float* dx, hipStream_t s) {
+  const dim3 grid(d / 1024 + (d % 1024 ? 1 : 0), (T + TT - 1) / TT);
+  unpermute_dx_kernel<Tw, TT><<<grid, dim3(256), TT * E * sizeof(float), s>>>(
+      dxp, dest, dz, static_cast<const Tw*>(wr), T, k, E, d, shared_row0, dx);
 }
 
 hipError_t launch_unpermute_dx(int dtype_bf16, const float* dxp, const int32_t* dest,
                                const float* dz, const void* wr, int T, int k, int E, int d,
                                int shared_row0, float* dx, hipStream_t s) {
-  if (dtype_bf16)
-    unpermute_dx_kernel<uint16_t><<<dim3(T), dim3(256), 0, s>>>(
-        dxp, dest, dz, static_cast<const uint16_t*>(wr), k, E, d, shared_row0, dx);
-  else
-    unpermute_dx_kernel<float><<<dim3(T), dim3(256), 0, s>>>(
-        dxp, dest, dz, static_cast<const float*>(wr), k, E, d, shared_row0, dx);
+  if (d % 4) return hipErrorInvalidValue;
+  const bool wide = E > 32;   // more W_r rows per token: share each load among more tokens
+  if (dtype_bf16) {
+    if (wide) unpermute_dx_as<uint16_t, 16>(dxp, dest, dz, wr, T, k, E, d, shared_row0, dx, s);
+    else unpermute_dx_as<uint16_t, 8>(dxp, dest, dz, wr, T, k, E, d, shared_row0, dx, s);
+  } else {
+    if (wide) unpermute_dx_as<float, 16>(dxp, dest, dz, wr, T, k, E, d, shared_row0, dx, s);
+    else unpermute_dx_as<float, 8>(dxp, dest, dz, wr, T, k, E, d, shared_row0, dx, s);
+  }
   return hipGetLastError();
 }
 
+RouterWgradPlan router_wgrad_plan(int T, int E, int d) {
+  RouterWgradPlan p;
+  p.eb = E <= 8 ? 8 : (E <= 16 ? 16 : 32);
+  const int xy = ((d + 511) / 512) * ((E + p.eb - 1) / p.eb);
+  const int want = (2048 + xy - 1) / xy;                        // about 2048 workgroups
+  int tc = (T + want - 1) / want;
+  tc = (tc + 15) / 16 * 16;
+  p.tc = tc < 16 ? 16 : (tc > 256 ? 256 : tc);
+  p.chunks = T > 0 ? (T + p.tc - 1) / p.tc : 0;
+  return p;
+}
+
+template <typename Tx, int EB>
+static void router_wgrad_as(const float* dz, const void* x, int T, int E, int d,
+                            const RouterWgradPlan& p, float* part, hipStream_t s) {
+  const dim3 grid((d + 511) / 512, (E + EB - 1) / EB, p.chunks);
+  router_wgrad_part_kernel<Tx, EB><<<grid, dim3(256), p.tc * EB * sizeof(float), s>>>(
+      dz, static_cast<const Tx*>(x), T, E, d, p.tc, part);
+}
+
 hipError_t launch_router_wgrad(int dtype_bf16, const float* dz, const void* x, int T, int E, int d,
-                               float* dwr, hipStream_t s) {
-  const dim3 grid((d + 255) / 256, E);
-  if (dtype_bf16)
-    router_wgrad_kernel<uint16_t><<<grid, dim3(256), 0, s>>>(dz, static_cast<const uint16_t*>(x),
-                                                              T, E, d, dwr);
-  else
-    router_wgrad_kernel<float><<<grid, dim3(256), 0, s>>>(dz, static_cast<const float*>(x), T, E,
-                                                           d, dwr);
+                               float* part, float* dwr, hipStream_t s) {
+  if (d % 2) return hipErrorInvalidValue;
+  const RouterWgradPlan p = router_wgrad_plan(T, E, d);
+  if (p.chunks == 0) return hipSuccess;
+  if (dtype_bf16) {
+    if (p.eb == 8) router_wgrad_as<uint16_t, 8>(dz, x, T, E, d, p, part, s);
+    else if (p.eb == 16) router_wgrad_as<uint16_t, 16>(dz, x, T, E, d, p, part, s);
+    else router_wgrad_as<uint16_t, 32>(dz, x, T, E, d, p, part, s);
+  } else {
+    if (p.eb == 8) router_wgrad_as<float, 8>(dz, x, T, E, d, p, part, s);
+    else if (p.eb == 16) router_wgrad_as<float, 16>(dz, x, T, E, d, p, part, s);
+    else router_wgrad_as<float, 32>(dz, x, T, E, d, p, part, s);
+  }
+  const long long n = static_cast<long long>(E) * d;
+  router_wgrad_sum_kernel<<<dim3(blocks_for(n)), dim3(256), 0, s>>>(part, p.chunks, n, dwr);
   return hipGetLastError();
 }
 

@@ -41,6 +41,14 @@ template <> struct Elt<float> {
     out[4] = b[0]; out[5] = b[1]; out[6] = b[2]; out[7] = b[3];
   }
   __device__ __forceinline__ static float load1(const float* p) { return *p; }
+  __device__ __forceinline__ static void load2(const float* p, float* out) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    out[0] = __uint_as_float(v[0]); out[1] = __uint_as_float(v[1]);
+  }
+  __device__ __forceinline__ static void load4(const float* p, float* out) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    out[0] = a[0]; out[1] = a[1]; out[2] = a[2]; out[3] = a[3];
+  }
 };
 template <> struct Elt<uint16_t> {
   static constexpr int kBytes = 2;
@@ -53,6 +61,15 @@ template <> struct Elt<uint16_t> {
     }
   }
   __device__ __forceinline__ static float load1(const uint16_t* p) { return bf16_to_f32(*p); }
+  __device__ __forceinline__ static void load2(const uint16_t* p, float* out) {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
+    out[0] = __uint_as_float(v << 16); out[1] = __uint_as_float(v & 0xFFFF0000u);
+  }
+  __device__ __forceinline__ static void load4(const uint16_t* p, float* out) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    out[0] = __uint_as_float(v[0] << 16); out[1] = __uint_as_float(v[0] & 0xFFFF0000u);
+    out[2] = __uint_as_float(v[1] << 16); out[3] = __uint_as_float(v[1] & 0xFFFF0000u);
+  }
 };
 
 // Wave-wide butterfly sum: every lane ends with the total; the pairing order is

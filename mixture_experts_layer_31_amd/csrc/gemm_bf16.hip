@@ -775,23 +775,24 @@ hipError_t launch_gemm_groupk_bf16(const int32_t* koffs, int G, const uint16_t* 
 
 hipError_t launch_gemm_down_bf16(const GemmTileMap& map, const DownArgs& a, int BM,
                                  hipStream_t s) {
+  const int ys = a.out_stride > 0 ? a.out_stride : a.N;
   const auto* act = static_cast<const uint16_t*>(a.act);
   const auto* w2 = static_cast<const uint16_t*>(a.w2);
   if (BM == 256) {
     const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + BM - 1) / BM;
     if (gemm_down_cols(BM, m_tiles, a.N) == 128)
       return run_lds<256, 128, 2, 4, false>(map, act, a.src, a.act_stride, a.in_row0, w2,
-                                            nullptr, a.w_stride, a.y, a.N, a.out_row0, a.K,
+                                            nullptr, a.w_stride, a.y, ys, a.out_row0, a.K,
                                             a.N, s);
     return run_lds<256, 256, 2, 4, false>(map, act, a.src, a.act_stride, a.in_row0, w2,
-                                          nullptr, a.w_stride, a.y, a.N, a.out_row0, a.K, a.N,
+                                          nullptr, a.w_stride, a.y, ys, a.out_row0, a.K, a.N,
                                           s);
   }
   if (BM == 16)
     return run_stream<false>(map, act, a.src, a.act_stride, a.in_row0, w2, nullptr, a.w_stride,
-                             a.y, a.N, a.out_row0, a.K, a.N, s);
+                             a.y, ys, a.out_row0, a.K, a.N, s);
   return run_small<32, 64, 1, 2, false>(map, act, a.src, a.act_stride, a.in_row0, w2, nullptr,
-                                        a.w_stride, a.y, a.N, a.out_row0, a.K, a.N, s);
+                                        a.w_stride, a.y, ys, a.out_row0, a.K, a.N, s);
 }
 
 }  // namespace moe

@@ -23,19 +23,25 @@ hipError_t launch_transpose_mat(const uint16_t* in, int B, int M, int N, uint16_
                                 int out_stride, int col0, long long out_batch, hipStream_t s);
 hipError_t launch_swiglu_fwd(const float* h1, const float* h3, int stride, int row0, int rows,
                              int n, uint16_t* act, hipStream_t s);
-hipError_t launch_swiglu_bwd(const float* da, const float* h1, const float* h3, int stride,
-                             int row0, int rows, int n, uint16_t* dH, hipStream_t s);
-hipError_t launch_combine_bwd(const float* dy, const float* yp, const int32_t* dest,
-                              const float* gates, int T, int k, int d, int shared_row0, float* dg,
-                              uint16_t* dyp, hipStream_t s);
-hipError_t launch_gate_bwd(const float* z, const int32_t* idx, const float* gates, const float* dg,
-                           const int32_t* counts, int T, int E, int k, int gate_all, float alpha,
-                           float* dz, hipStream_t s);
+hipError_t launch_swiglu_bwd(const float* u, const float* h1, const float* h3,
+                             const uint16_t* act, const float* row_gate, int stride, int row0,
+                             int rows, int n, uint16_t* dH, float* dg_row, hipStream_t s);
+hipError_t launch_dy_rows(const float* dy, const int32_t* dest, const float* gates, int T, int k,
+                          int d, uint16_t* dyb, uint16_t* dyp, float* row_gate, hipStream_t s);
+hipError_t launch_gate_bwd(const float* z, const int32_t* idx, const float* gates,
+                           const int32_t* dest, const float* dg_row, const int32_t* counts, int T,
+                           int E, int k, int gate_all, float alpha, float* dz, hipStream_t s);
 hipError_t launch_unpermute_dx(int dtype_bf16, const float* dxp, const int32_t* dest,
                                const float* dz, const void* wr, int T, int k, int E, int d,
                                int shared_row0, float* dx, hipStream_t s);
+// dW_r = dz^T x in token chunks (part: chunks * E * d floats of scratch), then the
+// chunks summed in order.
+struct RouterWgradPlan {
+  int eb = 8, tc = 16, chunks = 0;
+};
+RouterWgradPlan router_wgrad_plan(int T, int E, int d);
 hipError_t launch_router_wgrad(int dtype_bf16, const float* dz, const void* x, int T, int E, int d,
-                               float* dwr, hipStream_t s);
+                               float* part, float* dwr, hipStream_t s);
 
 // ---- router (router.hip)
 constexpr int kSelectMaxBlocks = 1024;
@@ -130,6 +136,7 @@ struct DownArgs {
   int out_row0;
   int K, N;               // K = d_ff, N = d
   const int32_t* src = nullptr;   // grouped row -> input row (nullable: identity)
+  int out_stride = 0;             // y row stride in floats (0: N)
 };
 // Grouped-K GEMM for weight gradients: out[g][n1][n2] = sum over k in
 // [koffs[g], koffs[g+1]) of At[n1][k] * Bt[n2][k] (fp32), every group's tile

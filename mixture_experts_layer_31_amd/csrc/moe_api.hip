@@ -155,10 +155,10 @@ struct Carver {
 // Workspace of moe_backward: every buffer of the recomputed forward and of the
 // backward, carved in this order (a null base only measures the size).
 struct BwdBufs {
-  float *z, *gates, *h1, *h3, *yp, *dg, *dz, *dact, *dxp;
+  float *z, *gates, *h1, *h3, *row_gate, *dg_row, *dz, *u, *dxp, *wpart;
   int32_t *idx, *dest, *src, *offsets, *counts, *kept, *ndrop, *poff, *soff, *spoff, *tiles;
   int32_t *blk, *slot_base, *slot_keep;
-  uint16_t *act, *dyp, *dH, *w2t, *w13t, *w2st, *w13st;
+  uint16_t *act, *dyb, *dyp, *dH, *w2t, *w13t, *w2st, *w13st;
   uint16_t *dypT, *actT, *dHT, *xT, *dysT, *actsT, *dHsT, *xsT;
   int Rp, Tp;
 };
@@ -189,11 +189,14 @@ size_t backward_layout(const Shape& s, char* base, BwdBufs* b) {
   b->h1 = cv.take<float>(rows * As * 4);
   b->h3 = cv.take<float>(rows * As * 4);
   b->act = cv.take<uint16_t>(rows * As * 2);
-  b->yp = cv.take<float>(R * d * 4);
-  b->dyp = cv.take<uint16_t>(rows * d * 2);
-  b->dg = cv.take<float>(T * k * 4);
+  b->dyb = cv.take<uint16_t>(T * d * 2);
+  b->dyp = cv.take<uint16_t>(R * d * 2);
+  b->row_gate = cv.take<float>(R * 4);
+  b->dg_row = cv.take<float>(R * 4);
   b->dz = cv.take<float>(T * E * 4);
-  b->dact = cv.take<float>(rows * As * 4);
+  b->u = cv.take<float>(rows * As * 4);
+  b->wpart = cv.take<float>(static_cast<size_t>(moe::router_wgrad_plan(s.T, s.E, s.d).chunks) *
+                            E * d * 4);
   b->dH = cv.take<uint16_t>(rows * 2 * As * 2);
   b->dxp = cv.take<float>(rows * d * 4);
   b->w2t = cv.take<uint16_t>(E * dff * d * 2);
@@ -537,7 +540,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   const int sh_row0 = s.nsh ? R : -1;
   auto u16 = [](const void* p) { return static_cast<const uint16_t*>(p); };
 
-  // ---- forward, recomputed: routing, index, pre-activations, activation, y_perm
+  // ---- forward, recomputed: routing, index, pre-activations, activation
   MOE_HIP(moe::launch_router_scores(1, x, w_router, T, d, E, b.z, strm), "router_scores");
   MOE_HIP(moe::launch_router_select(b.z, sel_bias, T, E, k, s.gate_all, b.idx, b.gates, nullptr,
                                     nullptr, nullptr, strm),
@@ -551,47 +554,49 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   const int bm1 = moe::gemm_tile_rows(1, T, 1, s.n256);
   // h1 = X W1^T, h3 = X W3^T on the gathered token rows (fp32 out)
   {
-    moe::DownArgs a{x, d, 0, w1, static_cast<long long>(dff) * d, b.h1, 0, d, dff, b.src};
+    moe::DownArgs a{x, d, 0, w1, static_cast<long long>(dff) * d, b.h1, 0, d, dff, b.src, As};
     MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "h1");
     a.w2 = w3;
     a.y = b.h3;
     MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "h3");
     MOE_HIP(moe::launch_swiglu_fwd(b.h1, b.h3, As, 0, R, dff, b.act, strm), "swiglu_fwd");
     if (s.nsh) {
-      moe::DownArgs c{x, d, 0, ws1, 0, b.h1, R, d, dffs};
+      moe::DownArgs c{x, d, 0, ws1, 0, b.h1, R, d, dffs, nullptr, As};
       MOE_HIP(moe::launch_gemm_down_bf16(map1, c, bm1, strm), "h1 shared");
       c.w2 = ws3;
       c.y = b.h3;
       MOE_HIP(moe::launch_gemm_down_bf16(map1, c, bm1, strm), "h3 shared");
       MOE_HIP(moe::launch_swiglu_fwd(b.h1, b.h3, As, R, T, dffs, b.act, strm), "swiglu_fwd shared");
     }
-    moe::DownArgs y{b.act, As, 0, w2, static_cast<long long>(d) * dff, b.yp, 0, dff, d};
-    MOE_HIP(moe::launch_gemm_down_bf16(map, y, s.BM, strm), "y_perm");
   }
 
-  // ---- combine and gates
-  MOE_HIP(moe::launch_combine_bwd(dy, b.yp, b.dest, b.gates, T, k, d, sh_row0, b.dg, b.dyp, strm),
-          "combine_bwd");
-  MOE_HIP(moe::launch_gate_bwd(b.z, b.idx, b.gates, b.dg, b.counts, T, E, k, s.gate_all,
-                               cfg->aux_alpha, b.dz, strm),
-          "gate_bwd");
-
-  // ---- down: dact = dY_perm W2 (W2 transposed once per call), then SwiGLU
+  // ---- down: u = dy W2 per row (W2 transposed once per call), then the SwiGLU
+  // backward with the row's gate, which also yields the gates' gradient
+  // <dy_t, y_perm[r]> = <act_r, u_r>; then the logits' gradient.
+  MOE_HIP(moe::launch_dy_rows(dy, b.dest, b.gates, T, k, d, b.dyb, b.dyp, b.row_gate, strm),
+          "dy_rows");
   MOE_HIP(moe::launch_transpose_mat(u16(w2), E, d, dff, b.w2t, d, 0,
                                     static_cast<long long>(dff) * d, strm),
           "transpose w2");
   {
-    moe::DownArgs a{b.dyp, d, 0, b.w2t, static_cast<long long>(dff) * d, b.dact, 0, d, dff};
-    MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "dact");
+    moe::DownArgs a{b.dyb, d, 0, b.w2t, static_cast<long long>(dff) * d, b.u, 0, d, dff, b.src,
+                    As};
+    MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "u");
   }
-  MOE_HIP(moe::launch_swiglu_bwd(b.dact, b.h1, b.h3, As, 0, R, dff, b.dH, strm), "swiglu_bwd");
+  MOE_HIP(moe::launch_swiglu_bwd(b.u, b.h1, b.h3, b.act, b.row_gate, As, 0, R, dff, b.dH,
+                                 b.dg_row, strm),
+          "swiglu_bwd");
   if (s.nsh) {
     MOE_HIP(moe::launch_transpose_mat(u16(ws2), 1, d, dffs, b.w2st, d, 0, 0, strm), "transpose ws2");
-    moe::DownArgs a{b.dyp, d, R, b.w2st, 0, b.dact, R, d, dffs};
-    MOE_HIP(moe::launch_gemm_down_bf16(map1, a, bm1, strm), "dact shared");
-    MOE_HIP(moe::launch_swiglu_bwd(b.dact, b.h1, b.h3, As, R, T, dffs, b.dH, strm),
+    moe::DownArgs a{b.dyb, d, 0, b.w2st, 0, b.u, R, d, dffs, nullptr, As};
+    MOE_HIP(moe::launch_gemm_down_bf16(map1, a, bm1, strm), "u shared");
+    MOE_HIP(moe::launch_swiglu_bwd(b.u, b.h1, b.h3, b.act, nullptr, As, R, T, dffs, b.dH, nullptr,
+                                   strm),
             "swiglu_bwd shared");
   }
+  MOE_HIP(moe::launch_gate_bwd(b.z, b.idx, b.gates, b.dest, b.dg_row, b.counts, T, E, k,
+                               s.gate_all, cfg->aux_alpha, b.dz, strm),
+          "gate_bwd");
 
   // ---- gate/up: dX_perm = [dh1 dh3] [W1; W3] with K = 2 d_ff
   MOE_HIP(moe::launch_transpose_mat(u16(w1), E, dff, d, b.w13t, 2 * dff, 0,
@@ -615,7 +620,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   }
   MOE_HIP(moe::launch_unpermute_dx(1, b.dxp, b.dest, b.dz, w_router, T, k, E, d, sh_row0, dx, strm),
           "unpermute_dx");
-  MOE_HIP(moe::launch_router_wgrad(1, b.dz, x, T, E, d, dw_router, strm), "router_wgrad");
+  MOE_HIP(moe::launch_router_wgrad(1, b.dz, x, T, E, d, b.wpart, dw_router, strm), "router_wgrad");
 
   // ---- weight gradients over each expert's rows (K = the group's rows, padded)
   MOE_HIP(moe::launch_transpose_rows(b.dyp, d, nullptr, 0, b.offsets, b.poff, E, R, d, b.dypT, b.Rp,
@@ -638,7 +643,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   if (s.nsh) {
     MOE_HIP(moe::launch_single_group_offsets(T, b.soff, strm), "shared offsets");
     MOE_HIP(moe::launch_pad_offsets(b.soff, 1, b.spoff, strm), "shared padded offsets");
-    MOE_HIP(moe::launch_transpose_rows(b.dyp, d, nullptr, R, b.soff, b.spoff, 1, T, d, b.dysT, b.Tp,
+    MOE_HIP(moe::launch_transpose_rows(b.dyb, d, nullptr, 0, b.soff, b.spoff, 1, T, d, b.dysT, b.Tp,
                                        strm),
             "transpose dY shared");
     MOE_HIP(moe::launch_transpose_rows(b.act, As, nullptr, R, b.soff, b.spoff, 1, T, dffs, b.actsT,

@@ -149,6 +149,15 @@ def test_k_equals_E_is_full_softmax():
     assert np.allclose(np.take_along_axis(p, g["idx"], 1), g["gates"], atol=1e-6)
 
 
+def test_shared_expert_wider_than_routed():
+    """d_ff_shared != d_ff: the shared rows of the activation buffer are wider than the
+    routed ones, so every row sits at the common act stride."""
+    wl = _adhoc("shared_wide", 116, T=150, d=256, E=8, k=2, d_ff=128, n_shared=1,
+                d_ff_shared=384, dtype=wk.BF16)
+    W = Weights(wl)
+    full_check(wl, W, 150)
+
+
 def test_single_expert_is_dense_swiglu():
     """E = 1, k = 1: the layer is the dense SwiGLU FFN (CME295 notes §B)."""
     wl = _adhoc("dense_e1", 102, T=70, d=128, E=1, k=1, d_ff=192, dtype=wk.BF16)
@@ -334,6 +343,8 @@ _BWD_CASES = {
                          bias_range=0.1), 128),
     "large_tiles": (dict(d=512, E=8, k=2, d_ff=1024, router="orthonormal"), 2048),
     "decode": (dict(d=256, E=8, k=2, d_ff=256), 8),
+    # a shared expert wider than the routed ones: rows of act, h and u at act_stride
+    "shared_wide": (dict(d=256, E=8, k=2, d_ff=256, n_shared=1, d_ff_shared=512), 160),
 }
 
 
