@@ -19,7 +19,7 @@ LIB_NAME = "libmoe_mi355x.so"
 LIB = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["moe_api.hip", "router.hip", "index.hip", "rows.hip", "gemm_bf16.hip", "gemm_f32.hip",
-           "backward.hip"]
+           "backward.hip", "gemm_kmajor.hip"]
 
 # packed fp32 VALU ops are disabled: the compiler would otherwise form them from
 # plain float code, and this build keeps every fp32 operation scalar

@@ -30,38 +30,10 @@
 #include <type_traits>
 
 #include "common.h"
+#include "gemm_common.h"
 #include "kernels.h"
 
 namespace moe {
-
-constexpr int kBK = 64;
-constexpr int kPitch = kBK + 8;   // LDS row pitch in bf16 elements (144 bytes)
-
-struct TileCoord {
-  int group, row0, rows;
-};
-
-__device__ __forceinline__ TileCoord lookup_tile(const int32_t* tiles, int n_single, int BM,
-                                                 int m_tile) {
-  TileCoord c;
-  if (tiles != nullptr) {
-    const int4 t = reinterpret_cast<const int4*>(tiles)[m_tile];
-    c.group = t.x; c.row0 = t.y; c.rows = t.z;
-  } else {
-    c.group = 0; c.row0 = m_tile * BM; c.rows = min(BM, n_single - c.row0);
-  }
-  return c;
-}
-
-// Launch index -> (m_tile, n_tile), XCD-contiguous (see the file comment).
-__device__ __forceinline__ void xcd_tile(int n_logical, int max_tiles, int& m_tile, int& n_tile) {
-  const int L = blockIdx.x;
-  const int per = (n_logical + 7) >> 3;
-  const int logical = (L & 7) * per + (L >> 3);
-  if (logical >= n_logical) { m_tile = -1; n_tile = 0; return; }
-  m_tile = logical % max_tiles;
-  n_tile = logical / max_tiles;
-}
 
 template <int BM, int BN, int WM, int WN, bool GATEUP>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(
@@ -217,71 +189,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(
 
 // ---------------------------------------------------------------- large tiles
 
-#if defined(__HIP_DEVICE_COMPILE__)
-// s_waitcnt with vmcnt = n and the other counters not waited on (gfx9 encoding)
-#define MOE_WAIT_VMCNT(n) \
-  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
-// 16 bytes per lane from global memory to LDS at lds_base + 16 * lane
-#define MOE_LDS_DMA16(g, l) __builtin_amdgcn_global_load_lds((g), (l), 16, 0, 0)
-// s_waitcnt vmcnt(n) for a wave-uniform n <= N (the count is an immediate)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_at_most(int n) {
-  if constexpr (N == 0) {
-    MOE_WAIT_VMCNT(0);
-  } else {
-    if (n >= N) MOE_WAIT_VMCNT(N);
-    else wait_vmcnt_at_most<N - 1>(n);
-  }
-}
-// keeps vector-memory instructions on their side of this point; every other
-// instruction kind may still be scheduled across it
-#define MOE_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0x78F)
-#else
-#define MOE_SCHED_FENCE() ((void)0)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_at_most(int) {}
-#define MOE_WAIT_VMCNT(n) ((void)0)
-#define MOE_LDS_DMA16(g, l) ((void)(g), (void)(l))
-#endif
-
-constexpr int kRowBytes = 128;   // one LDS row holds 64 bf16 of K
-constexpr size_t kMaxLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
-constexpr int kNumCUs = 256;                    // MI355X
-
-// The next stage's LDS-DMA loads are spread over this many points of the
-// K-step instead of issued in one burst after the barrier: a burst of 1 KB
-// loads from every wave fills the CU's vector-memory queue, and the waves
-// then stall at their later loads instead of issuing MFMAs.
-#ifndef MOE_DMA_SLICES
-#define MOE_DMA_SLICES 2
-#endif
-constexpr int kDmaSlices = MOE_DMA_SLICES;
-static_assert(kDmaSlices == 1 || kDmaSlices == 2 || kDmaSlices == 4, "1, 2 or 4 slices");
-#ifndef MOE_DMA_SLICES3
-#define MOE_DMA_SLICES3 4
-#endif
-constexpr int kDmaSlices3 = MOE_DMA_SLICES3;   // with three LDS stages
-static_assert(kDmaSlices3 == 1 || kDmaSlices3 == 2 || kDmaSlices3 == 4, "1, 2 or 4 slices");
-
-// f(integral_constant<int, min(n, N)>) for 0 <= n: a runtime count turned into
-// a compile-time one, so each count gets its own fully unrolled code.
-template <int N, class F>
-__device__ __forceinline__ void with_count(int n, F&& f) {
-  if constexpr (N == 0) {
-    f(std::integral_constant<int, 0>{});
-  } else {
-    if (n >= N) f(std::integral_constant<int, N>{});
-    else with_count<N - 1>(n, f);
-  }
-}
-
-// GK (grouped K, the weight gradients): tile m_tile is (group g, BM-row block
-// m_tile % n_single of A), the reduction runs over the group's K range
-// [tiles[g], tiles[g+1]) of two K-contiguous operands (rows padded to multiples
-// of 64 per group), B is shared by all groups, and group g's fp32 output starts
-// w_stride elements after group g-1's. Every output tile is written, so a group
-// with no rows gets zeros.
-template <int BM, int BN, int WM, int WN, bool GATEUP, int ST, bool GK = false>
+template <int BM, int BN, int WM, int WN, bool GATEUP, int ST>
 __global__ __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_lds_kernel(
     const int32_t* __restrict__ tiles, int max_tiles, int n_single, int n_logical,
@@ -306,25 +214,12 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
 
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[];
 
-  static_assert(!GK || !GATEUP, "grouped K is a plain GEMM");
   int m_tile, n_tile;
   xcd_tile(n_logical, max_tiles, m_tile, n_tile);
   if (m_tile < 0) return;
-  TileCoord tc;
-  int k0 = 0, nk = K / kBK;
-  size_t obase = 0;
-  if constexpr (GK) {
-    const int g = m_tile / n_single;
-    tc.group = g;
-    tc.row0 = (m_tile % n_single) * BM;
-    tc.rows = BM;
-    k0 = tiles[g];
-    nk = (tiles[g + 1] - k0) / kBK;
-    obase = static_cast<size_t>(g) * static_cast<size_t>(w_stride);
-  } else {
-    tc = lookup_tile(tiles, n_single, BM, m_tile);
-    if (tc.rows <= 0) return;
-  }
+  const TileCoord tc = lookup_tile(tiles, n_single, BM, m_tile);
+  if (tc.rows <= 0) return;
+  const int nk = K / kBK;
   const int n0 = n_tile * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -340,16 +235,16 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
     const int r = 8 * (i * NW + wave) + lrow8;
     int grow = tc.row0 + min(r, tc.rows - 1);
     if (src != nullptr) grow = src[grow];
-    xg[i] = xa + (static_cast<size_t>(a_row0) + grow) * a_stride + lchunk * 8 + k0;
+    xg[i] = xa + (static_cast<size_t>(a_row0) + grow) * a_stride + lchunk * 8;
   }
   const uint16_t* wg[WD];
-  const size_t wbase = GK ? 0 : static_cast<size_t>(tc.group) * w_stride;
+  const size_t wbase = static_cast<size_t>(tc.group) * w_stride;
 #pragma unroll
   for (int i = 0; i < WD; ++i) {
     const int r = 8 * (i * NW + wave) + lrow8;
     const uint16_t* wsrc = (!GATEUP || r < BN) ? w_a : w_b;
     const int n = n0 + ((GATEUP && r >= BN) ? r - BN : r);
-    wg[i] = wsrc + wbase + static_cast<size_t>(n) * K + lchunk * 8 + k0;
+    wg[i] = wsrc + wbase + static_cast<size_t>(n) * K + lchunk * 8;
   }
   // the stage's XD + WD LDS-DMA instructions, issued in slices: instruction j
   // goes out in slice j * kDmaSlices / (XD + WD)
@@ -482,7 +377,7 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
           f32x4 v;
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = acc[a][b][4 * rq + q];
-          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + obase + orow * out_stride + n) = v;
+          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow * out_stride + n) = v;
         }
       }
     }
@@ -760,17 +655,6 @@ hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, 
 static int gemm_down_cols(int BM, int m_tiles, int N) {
   if (BM != 256 || N % 256 != 0) return 256;
   return static_cast<long long>(m_tiles) * (N / 256) < 2 * kNumCUs ? 128 : 256;
-}
-
-hipError_t launch_gemm_groupk_bf16(const int32_t* koffs, int G, const uint16_t* At, int N1,
-                                   const uint16_t* Bt, int N2, int Kstride, float* out,
-                                   hipStream_t s) {
-  if (N1 % 256 || N2 % 256 || Kstride % kBK) return hipErrorInvalidValue;
-  constexpr size_t lds = 2 * static_cast<size_t>(256 + 256) * kRowBytes;
-  const GemmTileMap map{koffs, G * (N1 / 256), N1 / 256};
-  return launch_tiled(gemm_bf16_lds_kernel<256, 256, 2, 4, false, 2, true>, 256, 256, 512, lds,
-                      map, At, nullptr, Kstride, 0, Bt, nullptr,
-                      static_cast<long long>(N1) * N2, out, N2, 0, Kstride, N2, s);
 }
 
 hipError_t launch_gemm_down_bf16(const GemmTileMap& map, const DownArgs& a, int BM,

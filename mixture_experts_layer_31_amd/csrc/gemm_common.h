@@ -1,0 +1,96 @@
+// Device helpers shared by the grouped GEMM kernels (gemm_bf16.hip, gemm_kmajor.hip).
+#pragma once
+#include <type_traits>
+
+#include "common.h"
+
+namespace moe {
+
+constexpr int kBK = 64;
+constexpr int kPitch = kBK + 8;   // LDS row pitch in bf16 elements (144 bytes)
+
+struct TileCoord {
+  int group, row0, rows;
+};
+
+__device__ __forceinline__ TileCoord lookup_tile(const int32_t* tiles, int n_single, int BM,
+                                                 int m_tile) {
+  TileCoord c;
+  if (tiles != nullptr) {
+    const int4 t = reinterpret_cast<const int4*>(tiles)[m_tile];
+    c.group = t.x; c.row0 = t.y; c.rows = t.z;
+  } else {
+    c.group = 0; c.row0 = m_tile * BM; c.rows = min(BM, n_single - c.row0);
+  }
+  return c;
+}
+
+// Launch index -> (m_tile, n_tile), XCD-contiguous (see the file comment).
+__device__ __forceinline__ void xcd_tile(int n_logical, int max_tiles, int& m_tile, int& n_tile) {
+  const int L = blockIdx.x;
+  const int per = (n_logical + 7) >> 3;
+  const int logical = (L & 7) * per + (L >> 3);
+  if (logical >= n_logical) { m_tile = -1; n_tile = 0; return; }
+  m_tile = logical % max_tiles;
+  n_tile = logical / max_tiles;
+}
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// s_waitcnt with vmcnt = n and the other counters not waited on (gfx9 encoding)
+#define MOE_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+// 16 bytes per lane from global memory to LDS at lds_base + 16 * lane
+#define MOE_LDS_DMA16(g, l) __builtin_amdgcn_global_load_lds((g), (l), 16, 0, 0)
+// s_waitcnt vmcnt(n) for a wave-uniform n <= N (the count is an immediate)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_at_most(int n) {
+  if constexpr (N == 0) {
+    MOE_WAIT_VMCNT(0);
+  } else {
+    if (n >= N) MOE_WAIT_VMCNT(N);
+    else wait_vmcnt_at_most<N - 1>(n);
+  }
+}
+// keeps vector-memory instructions on their side of this point; every other
+// instruction kind may still be scheduled across it
+#define MOE_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0x78F)
+#else
+#define MOE_SCHED_FENCE() ((void)0)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_at_most(int) {}
+#define MOE_WAIT_VMCNT(n) ((void)0)
+#define MOE_LDS_DMA16(g, l) ((void)(g), (void)(l))
+#endif
+
+constexpr int kRowBytes = 128;   // one LDS row holds 64 bf16 of K
+constexpr size_t kMaxLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
+constexpr int kNumCUs = 256;                    // MI355X
+
+// The next stage's LDS-DMA loads are spread over this many points of the
+// K-step instead of issued in one burst after the barrier: a burst of 1 KB
+// loads from every wave fills the CU's vector-memory queue, and the waves
+// then stall at their later loads instead of issuing MFMAs.
+#ifndef MOE_DMA_SLICES
+#define MOE_DMA_SLICES 2
+#endif
+constexpr int kDmaSlices = MOE_DMA_SLICES;
+static_assert(kDmaSlices == 1 || kDmaSlices == 2 || kDmaSlices == 4, "1, 2 or 4 slices");
+#ifndef MOE_DMA_SLICES3
+#define MOE_DMA_SLICES3 4
+#endif
+constexpr int kDmaSlices3 = MOE_DMA_SLICES3;   // with three LDS stages
+static_assert(kDmaSlices3 == 1 || kDmaSlices3 == 2 || kDmaSlices3 == 4, "1, 2 or 4 slices");
+
+// f(integral_constant<int, min(n, N)>) for 0 <= n: a runtime count turned into
+// a compile-time one, so each count gets its own fully unrolled code.
+template <int N, class F>
+__device__ __forceinline__ void with_count(int n, F&& f) {
+  if constexpr (N == 0) {
+    f(std::integral_constant<int, 0>{});
+  } else {
+    if (n >= N) f(std::integral_constant<int, N>{});
+    else with_count<N - 1>(n, f);
+  }
+}
+
+}  // namespace moe

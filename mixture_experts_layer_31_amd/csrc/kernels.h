@@ -13,12 +13,7 @@ namespace moe {
 hipError_t allow_large_lds(const void* kernel, size_t bytes);
 
 // ---- backward (backward.hip)
-hipError_t launch_pad_offsets(const int32_t* offsets, int G, int32_t* poff, hipStream_t s);
 hipError_t launch_single_group_offsets(int rows, int32_t* off, hipStream_t s);
-hipError_t launch_transpose_rows(const uint16_t* in, int in_stride, const int32_t* src,
-                                 int in_row0, const int32_t* offsets, const int32_t* poff, int G,
-                                 int max_rows, int C, uint16_t* out, int out_stride,
-                                 hipStream_t s);
 hipError_t launch_transpose_mat(const uint16_t* in, int B, int M, int N, uint16_t* out,
                                 int out_stride, int col0, long long out_batch, hipStream_t s);
 hipError_t launch_swiglu_fwd(const float* h1, const float* h3, int stride, int row0, int rows,
@@ -138,13 +133,31 @@ struct DownArgs {
   const int32_t* src = nullptr;   // grouped row -> input row (nullable: identity)
   int out_stride = 0;             // y row stride in floats (0: N)
 };
-// Grouped-K GEMM for weight gradients: out[g][n1][n2] = sum over k in
-// [koffs[g], koffs[g+1]) of At[n1][k] * Bt[n2][k] (fp32), every group's tile
-// written (zeros for an empty range). At [N1][Kstride], Bt [N2][Kstride] bf16;
-// N1, N2 multiples of 256, koffs and Kstride multiples of 64.
-hipError_t launch_gemm_groupk_bf16(const int32_t* koffs, int G, const uint16_t* At, int N1,
-                                   const uint16_t* Bt, int N2, int Kstride, float* out,
-                                   hipStream_t s);
+// K-major grouped GEMMs (gemm_kmajor.hip), 256 x 256 tiles.
+// Data mode: y[y_row0 + row][n] = sum_k x[x_row0 + row(r)][k] * W_g[k][n] for the
+// rows of a 256-row tile table (row(r) = src[r] when src is set), with
+// W_g[k] = wa + g w_stride + k ldw for k < ksplit, wb + g w_stride + (k - ksplit) ldw
+// after; K and ksplit multiples of 64, N of 256.
+struct KmDataArgs {
+  const uint16_t* x;
+  int lda;
+  const int32_t* src;   // nullable
+  int x_row0;
+  const uint16_t* wa;
+  const uint16_t* wb;   // used for k >= ksplit
+  int ksplit, ldw;
+  long long w_stride;
+  float* y;
+  int y_stride, y_row0;
+  int K, N;
+};
+hipError_t launch_gemm_kmajor_data(const GemmTileMap& map, const KmDataArgs& a, hipStream_t s);
+// Grouped K: out[g][m][n] = sum over rows r in [offsets[g], offsets[g+1]) of
+// A[r][m] * B[r][n] (fp32 out, [G][N1][N2]); A [rows][lda], B [rows][ldb] bf16,
+// N1 and N2 multiples of 256.
+hipError_t launch_gemm_kmajor_groupk(const int32_t* offsets, int G, const uint16_t* A, int lda,
+                                     int N1, const uint16_t* B, int ldb, int N2, float* out,
+                                     hipStream_t s);
 hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, int BM,
                                    hipStream_t s);
 hipError_t launch_gemm_down_bf16(const GemmTileMap& map, const DownArgs& a, int BM,

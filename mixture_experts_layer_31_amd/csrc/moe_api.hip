@@ -156,20 +156,29 @@ struct Carver {
 // backward, carved in this order (a null base only measures the size).
 struct BwdBufs {
   float *z, *gates, *h1, *h3, *row_gate, *dg_row, *dz, *u, *dxp, *wpart;
-  int32_t *idx, *dest, *src, *offsets, *counts, *kept, *ndrop, *poff, *soff, *spoff, *tiles;
+  int32_t *idx, *dest, *src, *offsets, *counts, *kept, *ndrop, *soff, *tiles, *tiles256;
   int32_t *blk, *slot_base, *slot_keep;
-  uint16_t *act, *dyb, *dyp, *dH, *w2t, *w13t, *w2st, *w13st;
-  uint16_t *dypT, *actT, *dHT, *xT, *dysT, *actsT, *dHsT, *xsT;
-  int Rp, Tp;
+  uint16_t *act, *dyb, *dyp, *dH, *xp, *w2t, *w13t, *w2st, *w13st;
+  int max_tiles256;
+  bool tr_routed, tr_shared;   // weights transposed once per call (else read K-major)
 };
+
+// The activation products (u = dy W2, dX = dH [W1; W3]) either transpose the
+// weights once per call (5.5 TB/s read + write) and run the forward's
+// K-contiguous kernel, or read the weights K-major: the transposes cost 2 bytes
+// moved per weight byte, the K-major kernel runs these shapes at about 0.6 of
+// the K-contiguous one's rate, so the transposes pay off from about 650 rows per
+// expert (measured on the Mixtral and DeepSeek layer shapes).
+constexpr int kTransposeMinRows = 512;
 
 size_t backward_layout(const Shape& s, char* base, BwdBufs* b) {
   Carver cv{base};
   const size_t T = s.T, E = s.E, k = s.k, R = s.R, d = s.d, As = s.act_stride;
-  const size_t rows = s.rows_total, dff = s.dff, dffs = s.dffs;
-  b->Rp = (s.R + 63) / 64 * 64 + 64 * s.E;
-  b->Tp = (s.T + 63) / 64 * 64;
-  const size_t Rp = b->Rp, Tp = b->Tp;
+  const size_t rows = s.rows_total;
+  b->max_tiles256 = moe::gemm_max_tiles(256, s.R, s.E);
+  b->tr_routed = s.R >= static_cast<long long>(kTransposeMinRows) * s.E;
+  b->tr_shared = s.nsh && s.T >= kTransposeMinRows;
+  const size_t dff = s.dff, dffs = s.dffs;
   b->z = cv.take<float>(T * E * 4);
   b->idx = cv.take<int32_t>(T * k * 4);
   b->gates = cv.take<float>(T * k * 4);
@@ -179,10 +188,9 @@ size_t backward_layout(const Shape& s, char* base, BwdBufs* b) {
   b->counts = cv.take<int32_t>(E * 4);
   b->kept = cv.take<int32_t>(E * 4);
   b->ndrop = cv.take<int32_t>(4);
-  b->poff = cv.take<int32_t>((E + 1) * 4);
   b->soff = cv.take<int32_t>(2 * 4);
-  b->spoff = cv.take<int32_t>(2 * 4);
   b->tiles = cv.take<int32_t>(static_cast<size_t>(s.max_tiles) * 16);
+  b->tiles256 = cv.take<int32_t>(static_cast<size_t>(b->max_tiles256) * 16);
   b->blk = cv.take<int32_t>(static_cast<size_t>(s.nb_idx + 1) * s.nkeys * 4);
   b->slot_base = cv.take<int32_t>(k * E * 4);
   b->slot_keep = cv.take<int32_t>(k * E * 4);
@@ -191,26 +199,19 @@ size_t backward_layout(const Shape& s, char* base, BwdBufs* b) {
   b->act = cv.take<uint16_t>(rows * As * 2);
   b->dyb = cv.take<uint16_t>(T * d * 2);
   b->dyp = cv.take<uint16_t>(R * d * 2);
+  b->xp = cv.take<uint16_t>(R * d * 2);
   b->row_gate = cv.take<float>(R * 4);
   b->dg_row = cv.take<float>(R * 4);
   b->dz = cv.take<float>(T * E * 4);
   b->u = cv.take<float>(rows * As * 4);
-  b->wpart = cv.take<float>(static_cast<size_t>(moe::router_wgrad_plan(s.T, s.E, s.d).chunks) *
-                            E * d * 4);
   b->dH = cv.take<uint16_t>(rows * 2 * As * 2);
   b->dxp = cv.take<float>(rows * d * 4);
-  b->w2t = cv.take<uint16_t>(E * dff * d * 2);
-  b->w13t = cv.take<uint16_t>(E * d * 2 * dff * 2);
-  b->w2st = cv.take<uint16_t>(dffs * d * 2);
-  b->w13st = cv.take<uint16_t>(d * 2 * dffs * 2);
-  b->dypT = cv.take<uint16_t>(d * Rp * 2);
-  b->actT = cv.take<uint16_t>(dff * Rp * 2);
-  b->dHT = cv.take<uint16_t>(2 * dff * Rp * 2);
-  b->xT = cv.take<uint16_t>(d * Rp * 2);
-  b->dysT = cv.take<uint16_t>(s.nsh ? d * Tp * 2 : 0);
-  b->actsT = cv.take<uint16_t>(s.nsh ? dffs * Tp * 2 : 0);
-  b->dHsT = cv.take<uint16_t>(s.nsh ? 2 * dffs * Tp * 2 : 0);
-  b->xsT = cv.take<uint16_t>(s.nsh ? d * Tp * 2 : 0);
+  b->wpart = cv.take<float>(static_cast<size_t>(moe::router_wgrad_plan(s.T, s.E, s.d).chunks) *
+                            E * d * 4);
+  b->w2t = cv.take<uint16_t>(b->tr_routed ? E * dff * d * 2 : 0);
+  b->w13t = cv.take<uint16_t>(b->tr_routed ? E * d * 2 * dff * 2 : 0);
+  b->w2st = cv.take<uint16_t>(b->tr_shared ? dffs * d * 2 : 0);
+  b->w13st = cv.take<uint16_t>(b->tr_shared ? d * 2 * dffs * 2 : 0);
   return static_cast<size_t>(cv.p - base);
 }
 
@@ -548,10 +549,16 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   MOE_HIP(moe::launch_index(b.idx, T, k, E, s.C, b.blk, b.slot_base, b.slot_keep, b.offsets, b.dest,
                             b.src, b.counts, b.kept, b.ndrop, s.BM, s.max_tiles, 1, b.tiles, strm),
           "index");
-  MOE_HIP(moe::launch_pad_offsets(b.offsets, E, b.poff, strm), "pad_offsets");
   const moe::GemmTileMap map{b.tiles, s.max_tiles, 0};
   const moe::GemmTileMap map1{nullptr, 0, T};
   const int bm1 = moe::gemm_tile_rows(1, T, 1, s.n256);
+  // the K-major products run 256-row tiles
+  moe::GemmTileMap map256 = map;
+  if (s.BM != 256 && !b.tr_routed) {
+    MOE_HIP(moe::launch_tile_map(b.offsets, E, 256, b.max_tiles256, 1, b.tiles256, strm),
+            "tile_map 256");
+    map256 = moe::GemmTileMap{b.tiles256, b.max_tiles256, 0};
+  }
   // h1 = X W1^T, h3 = X W3^T on the gathered token rows (fp32 out)
   {
     moe::DownArgs a{x, d, 0, w1, static_cast<long long>(dff) * d, b.h1, 0, d, dff, b.src, As};
@@ -570,26 +577,35 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     }
   }
 
-  // ---- down: u = dy W2 per row (W2 transposed once per call), then the SwiGLU
-  // backward with the row's gate, which also yields the gates' gradient
-  // <dy_t, y_perm[r]> = <act_r, u_r>; then the logits' gradient.
+  // ---- down: u = dy W2 per row (W2 read K-major), then the SwiGLU backward with
+  // the row's gate, which also yields the gates' gradient <dy_t, y_perm[r]> =
+  // <act_r, u_r>; then the logits' gradient.
   MOE_HIP(moe::launch_dy_rows(dy, b.dest, b.gates, T, k, d, b.dyb, b.dyp, b.row_gate, strm),
           "dy_rows");
-  MOE_HIP(moe::launch_transpose_mat(u16(w2), E, d, dff, b.w2t, d, 0,
-                                    static_cast<long long>(dff) * d, strm),
-          "transpose w2");
-  {
-    moe::DownArgs a{b.dyb, d, 0, b.w2t, static_cast<long long>(dff) * d, b.u, 0, d, dff, b.src,
-                    As};
+  if (b.tr_routed) {
+    MOE_HIP(moe::launch_transpose_mat(u16(w2), E, d, dff, b.w2t, d, 0,
+                                      static_cast<long long>(dff) * d, strm),
+            "transpose w2");
+    moe::DownArgs a{b.dyb, d, 0, b.w2t, static_cast<long long>(dff) * d, b.u, 0, d, dff, b.src, As};
     MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "u");
+  } else {
+    moe::KmDataArgs a{b.dyb, d, b.src, 0, u16(w2), nullptr, d, dff,
+                      static_cast<long long>(d) * dff, b.u, As, 0, d, dff};
+    MOE_HIP(moe::launch_gemm_kmajor_data(map256, a, strm), "u");
   }
   MOE_HIP(moe::launch_swiglu_bwd(b.u, b.h1, b.h3, b.act, b.row_gate, As, 0, R, dff, b.dH,
                                  b.dg_row, strm),
           "swiglu_bwd");
   if (s.nsh) {
-    MOE_HIP(moe::launch_transpose_mat(u16(ws2), 1, d, dffs, b.w2st, d, 0, 0, strm), "transpose ws2");
-    moe::DownArgs a{b.dyb, d, 0, b.w2st, 0, b.u, R, d, dffs, nullptr, As};
-    MOE_HIP(moe::launch_gemm_down_bf16(map1, a, bm1, strm), "u shared");
+    if (b.tr_shared) {
+      MOE_HIP(moe::launch_transpose_mat(u16(ws2), 1, d, dffs, b.w2st, d, 0, 0, strm),
+              "transpose ws2");
+      moe::DownArgs a{b.dyb, d, 0, b.w2st, 0, b.u, R, d, dffs, nullptr, As};
+      MOE_HIP(moe::launch_gemm_down_bf16(map1, a, bm1, strm), "u shared");
+    } else {
+      moe::KmDataArgs a{b.dyb, d, nullptr, 0, u16(ws2), nullptr, d, dffs, 0, b.u, As, R, d, dffs};
+      MOE_HIP(moe::launch_gemm_kmajor_data(map1, a, strm), "u shared");
+    }
     MOE_HIP(moe::launch_swiglu_bwd(b.u, b.h1, b.h3, b.act, nullptr, As, R, T, dffs, b.dH, nullptr,
                                    strm),
             "swiglu_bwd shared");
@@ -598,69 +614,61 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
                                s.gate_all, cfg->aux_alpha, b.dz, strm),
           "gate_bwd");
 
-  // ---- gate/up: dX_perm = [dh1 dh3] [W1; W3] with K = 2 d_ff
-  MOE_HIP(moe::launch_transpose_mat(u16(w1), E, dff, d, b.w13t, 2 * dff, 0,
-                                    static_cast<long long>(d) * 2 * dff, strm),
-          "transpose w1");
-  MOE_HIP(moe::launch_transpose_mat(u16(w3), E, dff, d, b.w13t, 2 * dff, dff,
-                                    static_cast<long long>(d) * 2 * dff, strm),
-          "transpose w3");
-  {
+  // ---- gate/up: dX_perm = [dh1 dh3] [W1; W3], K = 2 d_ff over W1 then W3 (K-major)
+  if (b.tr_routed) {
+    MOE_HIP(moe::launch_transpose_mat(u16(w1), E, dff, d, b.w13t, 2 * dff, 0,
+                                      static_cast<long long>(d) * 2 * dff, strm),
+            "transpose w1");
+    MOE_HIP(moe::launch_transpose_mat(u16(w3), E, dff, d, b.w13t, 2 * dff, dff,
+                                      static_cast<long long>(d) * 2 * dff, strm),
+            "transpose w3");
     moe::DownArgs a{b.dH, 2 * As, 0, b.w13t, static_cast<long long>(d) * 2 * dff, b.dxp, 0,
                     2 * dff, d};
     MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "dx_perm");
+  } else {
+    moe::KmDataArgs a{b.dH, 2 * As, nullptr, 0, u16(w1), u16(w3), dff, d,
+                      static_cast<long long>(dff) * d, b.dxp, d, 0, 2 * dff, d};
+    MOE_HIP(moe::launch_gemm_kmajor_data(map256, a, strm), "dx_perm");
   }
   if (s.nsh) {
-    MOE_HIP(moe::launch_transpose_mat(u16(ws1), 1, dffs, d, b.w13st, 2 * dffs, 0, 0, strm),
-            "transpose ws1");
-    MOE_HIP(moe::launch_transpose_mat(u16(ws3), 1, dffs, d, b.w13st, 2 * dffs, dffs, 0, strm),
-            "transpose ws3");
-    moe::DownArgs a{b.dH, 2 * As, R, b.w13st, 0, b.dxp, R, 2 * dffs, d};
-    MOE_HIP(moe::launch_gemm_down_bf16(map1, a, bm1, strm), "dx_perm shared");
+    if (b.tr_shared) {
+      MOE_HIP(moe::launch_transpose_mat(u16(ws1), 1, dffs, d, b.w13st, 2 * dffs, 0, 0, strm),
+              "transpose ws1");
+      MOE_HIP(moe::launch_transpose_mat(u16(ws3), 1, dffs, d, b.w13st, 2 * dffs, dffs, 0, strm),
+              "transpose ws3");
+      moe::DownArgs a{b.dH, 2 * As, R, b.w13st, 0, b.dxp, R, 2 * dffs, d};
+      MOE_HIP(moe::launch_gemm_down_bf16(map1, a, bm1, strm), "dx_perm shared");
+    } else {
+      moe::KmDataArgs a{b.dH, 2 * As, nullptr, R, u16(ws1), u16(ws3), dffs, d, 0, b.dxp, d, R,
+                        2 * dffs, d};
+      MOE_HIP(moe::launch_gemm_kmajor_data(map1, a, strm), "dx_perm shared");
+    }
   }
   MOE_HIP(moe::launch_unpermute_dx(1, b.dxp, b.dest, b.dz, w_router, T, k, E, d, sh_row0, dx, strm),
           "unpermute_dx");
   MOE_HIP(moe::launch_router_wgrad(1, b.dz, x, T, E, d, b.wpart, dw_router, strm), "router_wgrad");
 
-  // ---- weight gradients over each expert's rows (K = the group's rows, padded)
-  MOE_HIP(moe::launch_transpose_rows(b.dyp, d, nullptr, 0, b.offsets, b.poff, E, R, d, b.dypT, b.Rp,
-                                     strm),
-          "transpose dY_perm");
-  MOE_HIP(moe::launch_transpose_rows(b.act, As, nullptr, 0, b.offsets, b.poff, E, R, dff, b.actT,
-                                     b.Rp, strm),
-          "transpose act");
-  MOE_HIP(moe::launch_transpose_rows(b.dH, 2 * As, nullptr, 0, b.offsets, b.poff, E, R, 2 * dff,
-                                     b.dHT, b.Rp, strm),
-          "transpose dH");
-  MOE_HIP(moe::launch_transpose_rows(u16(x), d, b.src, 0, b.offsets, b.poff, E, R, d, b.xT, b.Rp,
-                                     strm),
-          "transpose x");
-  MOE_HIP(moe::launch_gemm_groupk_bf16(b.poff, E, b.dypT, d, b.actT, dff, b.Rp, dw2, strm), "dW2");
-  MOE_HIP(moe::launch_gemm_groupk_bf16(b.poff, E, b.dHT, dff, b.xT, d, b.Rp, dw1, strm), "dW1");
-  MOE_HIP(moe::launch_gemm_groupk_bf16(b.poff, E, b.dHT + static_cast<size_t>(dff) * b.Rp, dff,
-                                       b.xT, d, b.Rp, dw3, strm),
+  // ---- weight gradients over each expert's rows: dW2 = dY_perm^T act,
+  // dW1 = dH1^T X_perm, dW3 = dH3^T X_perm (both operands K-major)
+  MOE_HIP(moe::launch_gather_rows(2, x, b.src, b.offsets, E, R, d, b.xp, strm), "x_perm");
+  MOE_HIP(moe::launch_gemm_kmajor_groupk(b.offsets, E, b.dyp, d, d, b.act, As, dff, dw2, strm),
+          "dW2");
+  MOE_HIP(moe::launch_gemm_kmajor_groupk(b.offsets, E, b.dH, 2 * As, dff, b.xp, d, d, dw1, strm),
+          "dW1");
+  MOE_HIP(moe::launch_gemm_kmajor_groupk(b.offsets, E, b.dH + dff, 2 * As, dff, b.xp, d, d, dw3,
+                                         strm),
           "dW3");
   if (s.nsh) {
+    const size_t r0 = static_cast<size_t>(R);
     MOE_HIP(moe::launch_single_group_offsets(T, b.soff, strm), "shared offsets");
-    MOE_HIP(moe::launch_pad_offsets(b.soff, 1, b.spoff, strm), "shared padded offsets");
-    MOE_HIP(moe::launch_transpose_rows(b.dyb, d, nullptr, 0, b.soff, b.spoff, 1, T, d, b.dysT, b.Tp,
-                                       strm),
-            "transpose dY shared");
-    MOE_HIP(moe::launch_transpose_rows(b.act, As, nullptr, R, b.soff, b.spoff, 1, T, dffs, b.actsT,
-                                       b.Tp, strm),
-            "transpose act shared");
-    MOE_HIP(moe::launch_transpose_rows(b.dH, 2 * As, nullptr, R, b.soff, b.spoff, 1, T, 2 * dffs,
-                                       b.dHsT, b.Tp, strm),
-            "transpose dH shared");
-    MOE_HIP(moe::launch_transpose_rows(u16(x), d, nullptr, 0, b.soff, b.spoff, 1, T, d, b.xsT, b.Tp,
-                                       strm),
-            "transpose x shared");
-    MOE_HIP(moe::launch_gemm_groupk_bf16(b.spoff, 1, b.dysT, d, b.actsT, dffs, b.Tp, dws2, strm),
+    MOE_HIP(moe::launch_gemm_kmajor_groupk(b.soff, 1, b.dyb, d, d, b.act + r0 * As, As, dffs, dws2,
+                                           strm),
             "dWs2");
-    MOE_HIP(moe::launch_gemm_groupk_bf16(b.spoff, 1, b.dHsT, dffs, b.xsT, d, b.Tp, dws1, strm),
+    MOE_HIP(moe::launch_gemm_kmajor_groupk(b.soff, 1, b.dH + r0 * 2 * As, 2 * As, dffs, u16(x), d,
+                                           d, dws1, strm),
             "dWs1");
-    MOE_HIP(moe::launch_gemm_groupk_bf16(b.spoff, 1, b.dHsT + static_cast<size_t>(dffs) * b.Tp,
-                                         dffs, b.xsT, d, b.Tp, dws3, strm),
+    MOE_HIP(moe::launch_gemm_kmajor_groupk(b.soff, 1, b.dH + r0 * 2 * As + dffs, 2 * As, dffs,
+                                           u16(x), d, d, dws3, strm),
             "dWs3");
   }
   return MOE_OK;

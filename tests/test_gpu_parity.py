@@ -345,6 +345,9 @@ _BWD_CASES = {
     "decode": (dict(d=256, E=8, k=2, d_ff=256), 8),
     # a shared expert wider than the routed ones: rows of act, h and u at act_stride
     "shared_wide": (dict(d=256, E=8, k=2, d_ff=256, n_shared=1, d_ff_shared=512), 160),
+    # 512 tokens: the shared expert's weights are transposed once, the routed ones
+    # (128 rows per expert) read K-major
+    "shared_transposed": (dict(d=256, E=8, k=2, d_ff=256, n_shared=1, d_ff_shared=512), 512),
 }
 
 
