@@ -12,6 +12,7 @@ Parity status of each function (the pins are the ``-m "not gpu"`` tests in
   ep_group_ids, ep_permutation, ep_group_expert, ep_send_rows,
   ep_dispatch_bytes, forward(ep=n)                                - pinned
   silu_grad, swiglu_backward, aux_loss_logit_grad, backward       - pinned
+  token_input_grad, expert_unit_grads                             - pinned
   capacity, assign_rows, permutation_by_prefix_sum                - pinned
   swiglu, expert_ffn, combine, forward, dense_all_experts,
   token_output                                                    - pinned

@@ -529,6 +529,83 @@ def backward(x, w_router, experts: ExpertFn, k: int, dy, gate: str = GATE_SELECT
                 dws3=dws3, dws2=dws2, dz=dz, dg=dg, fwd=fwd)
 
 
+def token_input_grad(x_t, dy_t, z_t, idx_t, gates_t, experts: ExpertFn, w_router,
+                     gate: str = GATE_SELECTED, keep_t=None, shared=None, alpha: float = 0.0,
+                     f=None, T: int = 1) -> np.ndarray:
+    """dx for one token, from its own slots only (the same quantity as ``backward``'s
+    dx row, without the other tokens' products).
+
+    Per kept slot j (expert e, gate g): h1 = W1 x, h3 = W3 x, da = g W2^T dy,
+    dx += W1^T (da h3 silu'(h1)) + W3^T (da silu(h1)) ([15-779] §7), and the gate's
+    gradient dg_j = <dy, f_e(x)> (0 for a dropped slot). The logits' gradient dz
+    follows from dg as in ``backward`` (selected or full softmax), plus, when
+    alpha > 0, the balance-loss term (alpha E / T) p (f - p.f) with the layer's load
+    fractions f over all T tokens ([CME295] §3.2); dx += dz W_r. A shared expert adds
+    its own input gradient with gate 1."""
+    x = np.asarray(x_t, np.float64)
+    dy = np.asarray(dy_t, np.float64)
+    wr = np.asarray(w_router, np.float64)
+    E = wr.shape[0]
+    k = len(idx_t)
+
+    def expert_dx(w1, w3, w2, g):
+        w1, w3, w2 = (np.asarray(w, np.float64) for w in (w1, w3, w2))
+        h1, h3 = w1 @ x, w3 @ x
+        u = w2.T @ dy
+        da = g * u
+        dx_e = w1.T @ (da * h3 * silu_grad(h1)) + w3.T @ (da * silu(h1))
+        return dx_e, float(u @ (silu(h1) * h3))      # <dy, W2 act> = <W2^T dy, act>
+
+    dx = np.zeros_like(x)
+    dg = np.zeros(k)
+    for j in range(k):
+        if keep_t is not None and not keep_t[j]:
+            continue
+        dx_e, dg[j] = expert_dx(*experts(int(idx_t[j])), float(gates_t[j]))
+        dx += dx_e
+    if shared is not None:
+        dx += expert_dx(*shared, 1.0)[0]
+    g = np.asarray(gates_t, np.float64)
+    dz = np.zeros(E)
+    p = softmax(np.asarray(z_t, np.float64)[None, :])[0]
+    if gate == GATE_SELECTED:
+        sgd = float(g @ dg)
+        for j in range(k):
+            dz[int(idx_t[j])] += g[j] * (dg[j] - sgd)
+    else:
+        dp = np.zeros(E)
+        for j in range(k):
+            dp[int(idx_t[j])] += dg[j]
+        dz = p * (dp - p @ dp)
+    if alpha > 0:
+        fv = np.asarray(f, np.float64)
+        dz = dz + alpha * E / T * p * (fv - p @ fv)
+    return dx + dz @ wr
+
+
+def expert_unit_grads(X_rows, dY_rows, g_rows, w1, w3, w2, units):
+    """Weight gradients of one expert for the hidden units ``units`` only: rows
+    dW1[units, :], dW3[units, :] and columns dW2[:, units], summed over the expert's
+    rows (token x_r, upstream gradient g_r dy_r), from the per-unit chain rule
+    h1 = x W1[f], h3 = x W3[f], a = silu(h1) h3, da = g_r dy_r W2[:, f]:
+    dW2[:, f] = sum_r g_r dy_r a_r, dW1[f] = sum_r da_r h3_r silu'(h1_r) x_r,
+    dW3[f] = sum_r da_r silu(h1_r) x_r ([15-779] §7). Equal to those entries of
+    ``swiglu_backward`` on the same rows. Returns (dW1u [n, d], dW3u [n, d], dW2u [d, n])."""
+    X = np.asarray(X_rows, np.float64)
+    dY = np.asarray(dY_rows, np.float64) * np.asarray(g_rows, np.float64)[:, None]
+    units = np.asarray(units)
+    w1u = np.asarray(w1, np.float64)[units]
+    w3u = np.asarray(w3, np.float64)[units]
+    w2u = np.asarray(w2, np.float64)[:, units]
+    h1, h3 = X @ w1u.T, X @ w3u.T
+    a = silu(h1) * h3
+    da = dY @ w2u
+    dW2u = dY.T @ a
+    dW1u = (da * h3 * silu_grad(h1)).T @ X
+    dW3u = (da * silu(h1)).T @ X
+    return dW1u, dW3u, dW2u
+
+
 def dense_all_experts(x, experts: ExpertFn, G: np.ndarray) -> np.ndarray:
     """Every expert on every token, weighted by a dense [T, E] gate matrix:
     y = sum_e G[:, e] f_e(x) ([15-779] §3.4 formulation 0; with G zero outside

@@ -416,6 +416,90 @@ def test_backward_matches_oracle(case):
     log(f"[ok] backward {case}: " + ", ".join(worst))
 
 
+def _backward_full_sampled(name, T, n_tokens, n_experts, n_units, seed):
+    """moe_backward at a full layer size against the oracle, sampled: dx of sampled
+    tokens (token_input_grad, each token's own slots) and, for sampled experts and
+    hidden units, the rows dW1[e][f], dW3[e][f] and columns dW2[e][:, f] over all of
+    the expert's rows (expert_unit_grads); the shared expert likewise. Evaluated
+    under the GPU's own routing; the bar of test_backward_matches_oracle over the
+    sampled entries of each gradient."""
+    W = weights(name)
+    wl = W.wl
+    assert wl.capacity_factor == 0
+    inp = wk.make_inputs(wl, T=T)
+    cfg = config_of(wl, T)
+    rng = np.random.default_rng(seed)
+    dy_h = rng.standard_normal((T, wl.d)).astype(np.float32)
+    E, d, dff = wl.E, wl.d, wl.d_ff
+    f32 = lambda *shape: torch.full(shape, float("nan"), dtype=torch.float32, device=dev())
+    out = dict(dx=f32(T, d), dwr=f32(E, d), dw1=f32(E, dff, d), dw3=f32(E, dff, d),
+               dw2=f32(E, d, dff))
+    if wl.n_shared:
+        dffs = wl.d_ff_shared
+        out.update(dws1=f32(dffs, d), dws3=f32(dffs, d), dws2=f32(d, dffs))
+    log(f"[case] backward full size {name} T={T}")
+    ws = moe.alloc_workspace(cfg, moe.STAGE_BACKWARD)
+    moe.backward(cfg, to_dev(inp.x, wl.dtype), W.wr, W.bias, W.w1, W.w3, W.w2, W.s1, W.s3, W.s2,
+                 torch.from_numpy(dy_h).to(dev()), out["dx"], out["dwr"], out["dw1"],
+                 out["dw3"], out["dw2"], out.get("dws1"), out.get("dws3"), out.get("dws2"), ws)
+    torch.cuda.synchronize()
+    del ws
+    idx = run_forward(wl, W, inp.x, T)["idx"]
+    x64 = wk.to_f64(inp.x, wl.dtype)
+    wr64 = wk.to_f64(W.wr_host, wl.dtype)
+    dy64 = dy_h.astype(np.float64)
+    z = om.router_logits(x64, wr64)
+    gates = (om.gates_selected(z, idx) if wl.gate == wk.GATE_SELECTED else om.gates_all(z, idx))
+    fr = om.load_fractions(idx, E)
+    shared = W.shared64()
+    pairs = {}
+
+    def add(kind, got, want):
+        g0, w0 = pairs.get(kind, ([], []))
+        pairs[kind] = (g0 + [np.ravel(got)], w0 + [np.ravel(want)])
+
+    tokens = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n_tokens, replace=False)]))
+    got_dx = out["dx"][torch.from_numpy(tokens).to(dev())].cpu().numpy()
+    for i, t in enumerate(tokens):
+        add("dx", got_dx[i], om.token_input_grad(x64[t], dy64[t], z[t], idx[t], gates[t],
+                                                 W.expert64, wr64, wl.gate, None, shared,
+                                                 wl.aux_alpha, fr, T))
+    counts = np.bincount(idx.ravel(), minlength=E)
+    experts = np.unique(np.concatenate([[int(counts.argmax()), int(counts.argmin())],
+                                        rng.choice(E, n_experts, replace=False)]))
+    for e in experts:
+        tt, jj = np.nonzero(idx == e)
+        units = np.sort(rng.choice(dff, n_units, replace=False))
+        d1, d3, d2 = om.expert_unit_grads(x64[tt], dy64[tt], gates[tt, jj], *W.expert64(int(e)),
+                                          units)
+        ut = torch.from_numpy(units).to(dev())
+        add("dw1", out["dw1"][int(e)][ut].cpu().numpy(), d1)
+        add("dw3", out["dw3"][int(e)][ut].cpu().numpy(), d3)
+        add("dw2", out["dw2"][int(e)][:, ut].cpu().numpy(), d2)
+    if shared is not None:
+        units = np.sort(rng.choice(wl.d_ff_shared, n_units, replace=False))
+        d1, d3, d2 = om.expert_unit_grads(x64, dy64, np.ones(T), *shared, units)
+        ut = torch.from_numpy(units).to(dev())
+        add("dws1", out["dws1"][ut].cpu().numpy(), d1)
+        add("dws3", out["dws3"][ut].cpu().numpy(), d3)
+        add("dws2", out["dws2"][:, ut].cpu().numpy(), d2)
+    report = []
+    for kind, (g0, w0) in pairs.items():
+        got, want = np.concatenate(g0).astype(np.float64), np.concatenate(w0)
+        assert np.all(np.isfinite(got)), f"{name}: {kind} not finite"
+        rms = float(np.sqrt(np.mean(want ** 2)))
+        diff = got - want
+        err_rms = float(np.sqrt(np.mean(diff ** 2)))
+        err = float(np.max(np.abs(diff)))
+        report.append(f"{kind} rms {err_rms / rms / _U_BF16:.2f}u max {err / rms / _U_BF16:.1f}u")
+        assert err_rms <= 4 * _U_BF16 * rms, f"{name}: {kind} rms|d| {err_rms:.3g} vs rms {rms:.3g}"
+        assert err <= 64 * _U_BF16 * rms, f"{name}: {kind} max|d| {err:.3g} vs rms {rms:.3g}"
+    log(f"[ok] backward full size {name} T={T}: " + ", ".join(report))
+    for t in list(out):
+        del out[t]
+    torch.cuda.empty_cache()
+
+
 def test_bias_changes_selection_not_gates():
     """DeepSeek-style selection bias on the GPU: tokens whose selection the bias does not move
     get bitwise-identical gates (CME295 notes §4.2)."""
@@ -449,6 +533,11 @@ def test_mixtral_prefill_512():
 def test_mixtral_prefill_4096():
     W = weights("mixtral_t32")
     full_check(W.wl, W, 4096, sample=32)
+
+
+@pytest.mark.timeout(300)
+def test_mixtral_backward_4096_sampled():
+    _backward_full_sampled("mixtral_t32", 4096, n_tokens=8, n_experts=2, n_units=6, seed=11)
 
 
 @pytest.mark.timeout(300)
@@ -490,3 +579,8 @@ def test_deepseek_t64():
 def test_deepseek_t4096():
     W = weights("deepseek_t64")
     full_check(W.wl, W, 4096, sample=3)
+
+
+@pytest.mark.timeout(300)
+def test_deepseek_backward_4096_sampled():
+    _backward_full_sampled("deepseek_t64", 4096, n_tokens=4, n_experts=6, n_units=8, seed=12)

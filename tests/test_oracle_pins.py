@@ -746,3 +746,49 @@ def test_aux_logit_gradient_closed_form_by_differences():
     assert np.max(np.abs(num - g)) <= 1e-9
     mean_load = f.mean()
     assert (np.sign(g.sum(axis=0)) == np.sign(f - mean_load)).all()
+
+
+@pytest.mark.parametrize("case", ["selected_shared_bias_aux", "all_capacity_aux", "top1_selected"])
+def test_sampled_backward_equals_full_backward(case):
+    """token_input_grad and expert_unit_grads, which evaluate one token's dx and a few
+    hidden units' weight gradients from the chain rule alone (what full-size sampled
+    checks use), equal the corresponding entries of the finite-difference-pinned
+    backward on tiny layers, drops and balance loss included."""
+    cfgs = {"selected_shared_bias_aux": dict(seed=41, T=9, d=6, E=4, k=2, f=5, shared=True,
+                                             bias=True, gate=om.GATE_SELECTED, cf=0.0, alpha=0.3),
+            "all_capacity_aux": dict(seed=42, T=10, d=5, E=4, k=2, f=4, shared=False, bias=False,
+                                     gate=om.GATE_ALL, cf=0.75, alpha=0.2),
+            "top1_selected": dict(seed=43, T=7, d=4, E=3, k=1, f=3, shared=False, bias=False,
+                                  gate=om.GATE_SELECTED, cf=0.0, alpha=0.0)}
+    c = cfgs[case]
+    x, wr, W, sh, b, dy = _tiny_layer(c["seed"], c["T"], c["d"], c["E"], c["k"], c["f"],
+                                      c["shared"], c["bias"])
+    k, gate, cf, alpha = c["k"], c["gate"], c["cf"], c["alpha"]
+    full = om.backward(x, wr, lambda e: W[e], k, dy, gate, b, cf, sh, alpha)
+    fwd = full["fwd"]
+    if case == "all_capacity_aux":
+        assert fwd["n_dropped"] > 0
+    keep = fwd["dest"] >= 0
+    for t in range(c["T"]):
+        dx_t = om.token_input_grad(x[t], dy[t], fwd["z"][t], fwd["idx"][t], fwd["gates"][t],
+                                   lambda e: W[e], wr, gate, keep[t], sh, alpha, fwd["f"], c["T"])
+        assert np.allclose(dx_t, full["dx"][t], rtol=1e-12, atol=1e-12), t
+    offsets, src = fwd["offsets"], fwd["src"]
+    for e in range(c["E"]):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        rows = src[lo:hi]
+        slot = [int(np.nonzero(fwd["dest"][t] == r)[0][0]) for t, r in zip(rows, range(lo, hi))]
+        g = fwd["gates"][rows, slot]
+        units = np.array([0, c["f"] - 1])
+        d1, d3, d2 = om.expert_unit_grads(x[rows], dy[rows], g, *W[e], units)
+        assert np.allclose(d1, full["dw1"][e][units], rtol=1e-12, atol=1e-12)
+        assert np.allclose(d3, full["dw3"][e][units], rtol=1e-12, atol=1e-12)
+        assert np.allclose(d2, full["dw2"][e][:, units], rtol=1e-12, atol=1e-12)
+    if sh is not None:
+        units = np.arange(c["f"])
+        d1, d3, d2 = om.expert_unit_grads(x, dy, np.ones(c["T"]), *sh, units)
+        assert np.allclose(d1, full["dws1"], rtol=1e-12, atol=1e-12)
+        assert np.allclose(d3, full["dws3"], rtol=1e-12, atol=1e-12)
+        assert np.allclose(d2, full["dws2"], rtol=1e-12, atol=1e-12)
