@@ -189,13 +189,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(
 
 // ---------------------------------------------------------------- large tiles
 
-template <int BM, int BN, int WM, int WN, bool GATEUP, int ST>
+// HOUT (gate/up only): the epilogue also stores the pre-activations h1 = X W1^T
+// and h3 = X W3^T in fp32 to h1o / h3o, at the activation's row index and stride
+// (the backward's recompute).
+template <int BM, int BN, int WM, int WN, bool GATEUP, int ST, bool HOUT = false>
 __global__ __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_lds_kernel(
     const int32_t* __restrict__ tiles, int max_tiles, int n_single, int n_logical,
     const uint16_t* __restrict__ xa, const int32_t* __restrict__ src, int a_stride, int a_row0,
     const uint16_t* __restrict__ w_a, const uint16_t* __restrict__ w_b, long long w_stride,
-    void* __restrict__ out, int out_stride, int out_row0, int K, int N) {
+    void* __restrict__ out, int out_stride, int out_row0, int K, int N,
+    float* __restrict__ h1o, float* __restrict__ h3o) {
+  static_assert(!HOUT || GATEUP, "pre-activations come from the gate/up product");
   constexpr int NW = WM * WN;
   constexpr int WR = GATEUP ? 2 * BN : BN;     // weight rows per tile
   constexpr int XD = BM / 8 / NW;              // LDS-DMA instructions per wave per stage
@@ -373,6 +378,16 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
           pk[0] = pack_bf16x2(h[0], h[1]);
           pk[1] = pack_bf16x2(h[2], h[3]);
           *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow * out_stride + n) = pk;
+          if constexpr (HOUT) {
+            f32x4 v1, v3;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              v1[q] = acc[a][b][4 * rq + q];
+              v3[q] = acc[a][NT + b][4 * rq + q];
+            }
+            *reinterpret_cast<f32x4*>(h1o + orow * out_stride + n) = v1;
+            *reinterpret_cast<f32x4*>(h3o + orow * out_stride + n) = v3;
+          }
         } else {
           f32x4 v;
 #pragma unroll
@@ -582,12 +597,12 @@ hipError_t launch_tile_map(const int32_t* offsets, int E, int BM, int max_tiles,
 
 // ---------------------------------------------------------------- launchers
 
-template <typename Kern>
+template <typename Kern, typename... Extra>
 static hipError_t launch_tiled(Kern kern, int BM, int BN, int threads, size_t lds,
                                const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
                                int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
                                long long w_stride, void* out, int out_stride, int out_row0, int K,
-                               int N, hipStream_t s) {
+                               int N, hipStream_t s, Extra... extra) {
   if (lds > 65536) {
     hipError_t e = allow_large_lds(reinterpret_cast<const void*>(kern), lds);
     if (e != hipSuccess) return e;
@@ -597,7 +612,7 @@ static hipError_t launch_tiled(Kern kern, int BM, int BN, int threads, size_t ld
   const long long grid = ((n_logical + 7) / 8) * 8;
   kern<<<dim3(static_cast<unsigned>(grid)), dim3(threads), lds, s>>>(
       map.tiles, m_tiles, map.n_single, static_cast<int>(n_logical), xa, src, a_stride, a_row0,
-      wa, wb, w_stride, out, out_stride, out_row0, K, N);
+      wa, wb, w_stride, out, out_stride, out_row0, K, N, extra...);
   return hipGetLastError();
 }
 
@@ -618,18 +633,18 @@ static hipError_t run_small(const GemmTileMap& map, const uint16_t* xa, const in
 // Three LDS stages where they fit (256 x 128 down tiles: 3 x 48 KB), which
 // keeps two stages of loads in flight per CU; those tiles serve short groups,
 // where the weights stream from HBM and load latency matters most.
-template <int BM, int BN, int WM, int WN, bool GATEUP>
+template <int BM, int BN, int WM, int WN, bool GATEUP, bool HOUT = false>
 static hipError_t run_lds(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
                           int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
                           long long w_stride, void* out, int out_stride, int out_row0, int K,
-                          int N, hipStream_t s) {
+                          int N, hipStream_t s, float* h1o = nullptr, float* h3o = nullptr) {
   constexpr int WR = GATEUP ? 2 * BN : BN;
   constexpr size_t kStage = static_cast<size_t>(BM + WR) * kRowBytes;
   constexpr int ST = 3 * kStage <= kMaxLdsBytes ? 3 : 2;
   const size_t lds = ST * kStage;
-  return launch_tiled(gemm_bf16_lds_kernel<BM, BN, WM, WN, GATEUP, ST>, BM, BN, 64 * WM * WN,
-                      lds, map, xa, src, a_stride, a_row0, wa, wb, w_stride, out, out_stride,
-                      out_row0, K, N, s);
+  return launch_tiled(gemm_bf16_lds_kernel<BM, BN, WM, WN, GATEUP, ST, HOUT>, BM, BN,
+                      64 * WM * WN, lds, map, xa, src, a_stride, a_row0, wa, wb, w_stride, out,
+                      out_stride, out_row0, K, N, s, h1o, h3o);
 }
 
 // BM = 256 needs N % 256 == 0 (down) / N % 128 == 0 (gate/up); the
@@ -639,6 +654,12 @@ hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, 
   const auto* x = static_cast<const uint16_t*>(a.x);
   const auto* w1 = static_cast<const uint16_t*>(a.w1);
   const auto* w3 = static_cast<const uint16_t*>(a.w3);
+  if (a.h1 != nullptr) {   // pre-activations too: 256-row tiles only
+    if (BM != 256 || a.h3 == nullptr) return hipErrorInvalidValue;
+    return run_lds<256, 128, 2, 4, true, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
+                                               a.act_stride, a.out_row0, a.K, a.N, s, a.h1,
+                                               a.h3);
+  }
   if (BM == 256)
     return run_lds<256, 128, 2, 4, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
                                          a.act_stride, a.out_row0, a.K, a.N, s);

@@ -120,6 +120,8 @@ struct GateUpArgs {
   int act_stride;
   int out_row0;           // output row = out_row0 + grouped row
   int K, N;               // K = d, N = d_ff
+  float* h1 = nullptr;    // optional fp32 pre-activations X W1^T, X W3^T at the
+  float* h3 = nullptr;    // activation's rows and stride (256-row tiles only)
 };
 struct DownArgs {
   const void* act;        // [rows][act_stride]

@@ -559,22 +559,31 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
             "tile_map 256");
     map256 = moe::GemmTileMap{b.tiles256, b.max_tiles256, 0};
   }
-  // h1 = X W1^T, h3 = X W3^T on the gathered token rows (fp32 out)
-  {
-    moe::DownArgs a{x, d, 0, w1, static_cast<long long>(dff) * d, b.h1, 0, d, dff, b.src, As};
-    MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "h1");
-    a.w2 = w3;
-    a.y = b.h3;
-    MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "h3");
-    MOE_HIP(moe::launch_swiglu_fwd(b.h1, b.h3, As, 0, R, dff, b.act, strm), "swiglu_fwd");
-    if (s.nsh) {
-      moe::DownArgs c{x, d, 0, ws1, 0, b.h1, R, d, dffs, nullptr, As};
-      MOE_HIP(moe::launch_gemm_down_bf16(map1, c, bm1, strm), "h1 shared");
-      c.w2 = ws3;
-      c.y = b.h3;
-      MOE_HIP(moe::launch_gemm_down_bf16(map1, c, bm1, strm), "h3 shared");
-      MOE_HIP(moe::launch_swiglu_fwd(b.h1, b.h3, As, R, T, dffs, b.act, strm), "swiglu_fwd shared");
+  // h1 = X W1^T, h3 = X W3^T (fp32) and act on the gathered token rows: with 256-row
+  // tiles the forward's gate/up kernel stores all three; else two plain products
+  // and the activation pass
+  auto preact = [&](const moe::GemmTileMap& m, int bm, const void* wa, const void* wb,
+                    long long wst, const int32_t* rows, int row0, int nrows, int n) -> moe_status {
+    if (bm == 256) {
+      moe::GateUpArgs g{x, rows, wa, wb, wst, b.act, As, row0, d, n};
+      g.h1 = b.h1;
+      g.h3 = b.h3;
+      MOE_HIP(moe::launch_gemm_gateup_bf16(m, g, bm, strm), "h1/h3/act");
+      return MOE_OK;
     }
+    moe::DownArgs a{x, d, 0, wa, wst, b.h1, row0, d, n, rows, As};
+    MOE_HIP(moe::launch_gemm_down_bf16(m, a, bm, strm), "h1");
+    a.w2 = wb;
+    a.y = b.h3;
+    MOE_HIP(moe::launch_gemm_down_bf16(m, a, bm, strm), "h3");
+    MOE_HIP(moe::launch_swiglu_fwd(b.h1, b.h3, As, row0, nrows, n, b.act, strm), "swiglu_fwd");
+    return MOE_OK;
+  };
+  st = preact(map, s.BM, w1, w3, static_cast<long long>(dff) * d, b.src, 0, R, dff);
+  if (st != MOE_OK) return st;
+  if (s.nsh) {
+    st = preact(map1, bm1, ws1, ws3, 0, nullptr, R, T, dffs);
+    if (st != MOE_OK) return st;
   }
 
   // ---- down: u = dy W2 per row (W2 read K-major), then the SwiGLU backward with
