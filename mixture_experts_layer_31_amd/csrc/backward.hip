@@ -393,11 +393,13 @@ hipError_t launch_single_group_offsets(int rows, int32_t* off, hipStream_t s) {
 }
 
 hipError_t launch_transpose_mat(const uint16_t* in, int B, int M, int N, uint16_t* out,
-                                int out_stride, int col0, long long out_batch, hipStream_t s) {
+                                int out_stride, int col0, long long out_batch, hipStream_t s,
+                                bool narrow) {
   if (M % 128 || N % 128 || out_stride % 8 || col0 % 8) return hipErrorInvalidValue;
   // measured: 128-row tiles are 2-3 % faster for wide inputs (N > M), 64-row tiles
-  // 7-9 % faster for tall ones
-  if (M > N)
+  // 7-9 % faster for tall ones; `narrow` asks for 64-row tiles (17 KB of LDS), which
+  // fit on a CU beside a 128 KB GEMM workgroup
+  if (narrow || M > N)
     transpose_mat_kernel<64><<<dim3(M / 64, N / 128, B), dim3(256), 0, s>>>(
         in, M, N, out, out_stride, col0, out_batch);
   else

@@ -15,7 +15,8 @@ hipError_t allow_large_lds(const void* kernel, size_t bytes);
 // ---- backward (backward.hip)
 hipError_t launch_single_group_offsets(int rows, int32_t* off, hipStream_t s);
 hipError_t launch_transpose_mat(const uint16_t* in, int B, int M, int N, uint16_t* out,
-                                int out_stride, int col0, long long out_batch, hipStream_t s);
+                                int out_stride, int col0, long long out_batch, hipStream_t s,
+                                bool narrow = false);
 hipError_t launch_swiglu_fwd(const float* h1, const float* h3, int stride, int row0, int rows,
                              int n, uint16_t* act, hipStream_t s);
 hipError_t launch_swiglu_bwd(const float* u, const float* h1, const float* h3,

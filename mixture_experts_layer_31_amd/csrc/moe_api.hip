@@ -512,6 +512,44 @@ moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t
   return MOE_OK;
 }
 
+// A second stream per device for the part of a call that reads only the call's
+// inputs (the backward's weight transposes): it forks from the caller's stream
+// and joins back into it through events, so that part runs beside the caller
+// stream's kernels (they leave LDS and vector registers for a transpose
+// workgroup on every CU). Default priority, non-blocking, created on first use.
+namespace {
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;   // held by a call from its fork to its join
+constexpr int kMaxDevices = 64;
+
+// The device's side stream, or nullptr if it cannot be created (the caller then
+// keeps that work on its own stream). Call with g_side_mu held.
+SideStream* side_stream() {
+  static SideStream side[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& ss = side[dev];
+  if (ss.s == nullptr) {
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+      if (f != nullptr) (void)hipEventDestroy(f);
+      (void)hipStreamDestroy(st);
+      return nullptr;
+    }
+    ss.s = st;
+    ss.fork = f;
+    ss.join = j;
+  }
+  return &ss;
+}
+}  // namespace
+
 moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_router,
                         const float* sel_bias, const void* w1, const void* w3, const void* w2,
                         const void* ws1, const void* ws3, const void* ws2, const float* dy,
@@ -540,6 +578,43 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   const int As = s.act_stride;
   const int sh_row0 = s.nsh ? R : -1;
   auto u16 = [](const void* p) { return static_cast<const uint16_t*>(p); };
+
+  // ---- weight transposes (experts of >= kTransposeMinRows rows): on the side
+  // stream, beside the recomputed forward; joined before the first product
+  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+  SideStream* side = nullptr;
+  if (b.tr_routed || b.tr_shared) {
+    side_lock.lock();
+    side = side_stream();
+    hipStream_t ts = strm;
+    if (side != nullptr) {
+      MOE_HIP(hipEventRecord(side->fork, strm), "fork");
+      MOE_HIP(hipStreamWaitEvent(side->s, side->fork, 0), "fork");
+      ts = side->s;
+    }
+    const bool narrow = side != nullptr;
+    if (b.tr_routed) {
+      MOE_HIP(moe::launch_transpose_mat(u16(w2), E, d, dff, b.w2t, d, 0,
+                                        static_cast<long long>(dff) * d, ts, narrow),
+              "transpose w2");
+      MOE_HIP(moe::launch_transpose_mat(u16(w1), E, dff, d, b.w13t, 2 * dff, 0,
+                                        static_cast<long long>(d) * 2 * dff, ts, narrow),
+              "transpose w1");
+      MOE_HIP(moe::launch_transpose_mat(u16(w3), E, dff, d, b.w13t, 2 * dff, dff,
+                                        static_cast<long long>(d) * 2 * dff, ts, narrow),
+              "transpose w3");
+    }
+    if (b.tr_shared) {
+      MOE_HIP(moe::launch_transpose_mat(u16(ws2), 1, d, dffs, b.w2st, d, 0, 0, ts, narrow),
+              "transpose ws2");
+      MOE_HIP(moe::launch_transpose_mat(u16(ws1), 1, dffs, d, b.w13st, 2 * dffs, 0, 0, ts, narrow),
+              "transpose ws1");
+      MOE_HIP(moe::launch_transpose_mat(u16(ws3), 1, dffs, d, b.w13st, 2 * dffs, dffs, 0, ts,
+                                        narrow),
+              "transpose ws3");
+    }
+    if (side != nullptr) MOE_HIP(hipEventRecord(side->join, side->s), "join");
+  }
 
   // ---- forward, recomputed: routing, index, pre-activations, activation
   MOE_HIP(moe::launch_router_scores(1, x, w_router, T, d, E, b.z, strm), "router_scores");
@@ -591,10 +666,11 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   // <act_r, u_r>; then the logits' gradient.
   MOE_HIP(moe::launch_dy_rows(dy, b.dest, b.gates, T, k, d, b.dyb, b.dyp, b.row_gate, strm),
           "dy_rows");
+  if (side != nullptr) {
+    MOE_HIP(hipStreamWaitEvent(strm, side->join, 0), "join");
+    side_lock.unlock();
+  }
   if (b.tr_routed) {
-    MOE_HIP(moe::launch_transpose_mat(u16(w2), E, d, dff, b.w2t, d, 0,
-                                      static_cast<long long>(dff) * d, strm),
-            "transpose w2");
     moe::DownArgs a{b.dyb, d, 0, b.w2t, static_cast<long long>(dff) * d, b.u, 0, d, dff, b.src, As};
     MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "u");
   } else {
@@ -607,8 +683,6 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
           "swiglu_bwd");
   if (s.nsh) {
     if (b.tr_shared) {
-      MOE_HIP(moe::launch_transpose_mat(u16(ws2), 1, d, dffs, b.w2st, d, 0, 0, strm),
-              "transpose ws2");
       moe::DownArgs a{b.dyb, d, 0, b.w2st, 0, b.u, R, d, dffs, nullptr, As};
       MOE_HIP(moe::launch_gemm_down_bf16(map1, a, bm1, strm), "u shared");
     } else {
@@ -625,12 +699,6 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
 
   // ---- gate/up: dX_perm = [dh1 dh3] [W1; W3], K = 2 d_ff over W1 then W3 (K-major)
   if (b.tr_routed) {
-    MOE_HIP(moe::launch_transpose_mat(u16(w1), E, dff, d, b.w13t, 2 * dff, 0,
-                                      static_cast<long long>(d) * 2 * dff, strm),
-            "transpose w1");
-    MOE_HIP(moe::launch_transpose_mat(u16(w3), E, dff, d, b.w13t, 2 * dff, dff,
-                                      static_cast<long long>(d) * 2 * dff, strm),
-            "transpose w3");
     moe::DownArgs a{b.dH, 2 * As, 0, b.w13t, static_cast<long long>(d) * 2 * dff, b.dxp, 0,
                     2 * dff, d};
     MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "dx_perm");
@@ -641,10 +709,6 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   }
   if (s.nsh) {
     if (b.tr_shared) {
-      MOE_HIP(moe::launch_transpose_mat(u16(ws1), 1, dffs, d, b.w13st, 2 * dffs, 0, 0, strm),
-              "transpose ws1");
-      MOE_HIP(moe::launch_transpose_mat(u16(ws3), 1, dffs, d, b.w13st, 2 * dffs, dffs, 0, strm),
-              "transpose ws3");
       moe::DownArgs a{b.dH, 2 * As, R, b.w13st, 0, b.dxp, R, 2 * dffs, d};
       MOE_HIP(moe::launch_gemm_down_bf16(map1, a, bm1, strm), "dx_perm shared");
     } else {
