@@ -189,18 +189,40 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(
 
 // ---------------------------------------------------------------- large tiles
 
+// Real tiles of a launch: the tile table's prefix of entries with rows (one
+// group: its tiles). Every thread of the workgroup gets the count.
+template <int BM>
+__device__ __forceinline__ int real_tiles(const int32_t* tiles, int max_tiles, int n_single,
+                                          int* s_real) {
+  if (tiles == nullptr) return (n_single + BM - 1) / BM;
+  if (threadIdx.x == 0) *s_real = max_tiles;
+  __syncthreads();
+  for (int i = threadIdx.x; i < max_tiles; i += blockDim.x)
+    if (tiles[4 * i + 2] <= 0) atomicMin(s_real, i);
+  __syncthreads();
+  return *s_real;
+}
+
 // HOUT (gate/up only): the epilogue also stores the pre-activations h1 = X W1^T
 // and h3 = X W3^T in fp32 to h1o / h3o, at the activation's row index and stride
 // (the backward's recompute).
-template <int BM, int BN, int WM, int WN, bool GATEUP, int ST, bool HOUT = false>
+// SK (stream-K, plain products): a persistent grid of P workgroups, one per CU,
+// in which workgroup p takes an equal share [U p / P, U (p+1) / P) of the
+// U = tiles x K-steps of the launch, tiles in the one-tile-per-workgroup order
+// (m fastest); the launch index is remapped so each XCD holds a contiguous
+// eighth. With shares of at least one tile's K-steps a tile is split at most
+// once: its last part writes out, its first part writes the fp32 tile to
+// sk_part slot p (the share's end), and streamk_fixup_kernel adds it after.
+template <int BM, int BN, int WM, int WN, bool GATEUP, int ST, bool HOUT = false, bool SK = false>
 __global__ __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_lds_kernel(
     const int32_t* __restrict__ tiles, int max_tiles, int n_single, int n_logical,
     const uint16_t* __restrict__ xa, const int32_t* __restrict__ src, int a_stride, int a_row0,
     const uint16_t* __restrict__ w_a, const uint16_t* __restrict__ w_b, long long w_stride,
     void* __restrict__ out, int out_stride, int out_row0, int K, int N,
-    float* __restrict__ h1o, float* __restrict__ h3o) {
+    float* __restrict__ h1o, float* __restrict__ h3o, float* __restrict__ sk_part) {
   static_assert(!HOUT || GATEUP, "pre-activations come from the gate/up product");
+  static_assert(!SK || !GATEUP, "stream-K splits plain fp32 products");
   constexpr int NW = WM * WN;
   constexpr int WR = GATEUP ? 2 * BN : BN;     // weight rows per tile
   constexpr int XD = BM / 8 / NW;              // LDS-DMA instructions per wave per stage
@@ -219,186 +241,274 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
 
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[];
 
-  int m_tile, n_tile;
-  xcd_tile(n_logical, max_tiles, m_tile, n_tile);
-  if (m_tile < 0) return;
-  const TileCoord tc = lookup_tile(tiles, n_single, BM, m_tile);
-  if (tc.rows <= 0) return;
-  const int nk = K / kBK;
-  const int n0 = n_tile * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
+  const int nk_all = K / kBK;
 
-  // DMA instruction i of this wave fills LDS rows 8*(i*NW + wave) .. +7 (1 KB);
-  // lane l writes row +l/8, physical chunk l%8, which holds logical K-chunk
-  // (l%8) ^ (l/8): the row's chunks are XOR-swizzled by the row index.
-  const int lrow8 = lane >> 3;
-  const int lchunk = (lane & 7) ^ lrow8;
-  const uint16_t* xg[XD];
+  // One output tile over K-steps [kt0, kt1). part != nullptr (stream-K): the
+  // fp32 tile goes there (rows * BN, tile-local) instead of to out.
+  auto run_tile = [&](int m_tile, int n_tile, int kt0, int kt1, float* part) {
+    if constexpr (SK) __syncthreads();   // the previous tile's reads of the LDS stages are done
+    const TileCoord tc = lookup_tile(tiles, n_single, BM, m_tile);
+    if (tc.rows <= 0) return;
+    const int nk = kt1 - kt0;
+    const int n0 = n_tile * BN;
+
+    // DMA instruction i of this wave fills LDS rows 8*(i*NW + wave) .. +7 (1 KB);
+    // lane l writes row +l/8, physical chunk l%8, which holds logical K-chunk
+    // (l%8) ^ (l/8): the row's chunks are XOR-swizzled by the row index.
+    const int lrow8 = lane >> 3;
+    const int lchunk = (lane & 7) ^ lrow8;
+    const uint16_t* xg[XD];
 #pragma unroll
-  for (int i = 0; i < XD; ++i) {
-    const int r = 8 * (i * NW + wave) + lrow8;
-    int grow = tc.row0 + min(r, tc.rows - 1);
-    if (src != nullptr) grow = src[grow];
-    xg[i] = xa + (static_cast<size_t>(a_row0) + grow) * a_stride + lchunk * 8;
-  }
-  const uint16_t* wg[WD];
-  const size_t wbase = static_cast<size_t>(tc.group) * w_stride;
-#pragma unroll
-  for (int i = 0; i < WD; ++i) {
-    const int r = 8 * (i * NW + wave) + lrow8;
-    const uint16_t* wsrc = (!GATEUP || r < BN) ? w_a : w_b;
-    const int n = n0 + ((GATEUP && r >= BN) ? r - BN : r);
-    wg[i] = wsrc + wbase + static_cast<size_t>(n) * K + lchunk * 8;
-  }
-  // the stage's XD + WD LDS-DMA instructions, issued in slices: instruction j
-  // goes out in slice j * kDmaSlices / (XD + WD)
-  constexpr int ND = XD + WD;
-  auto dma_slice = [&](int kt, int buf, auto slice_c) {
-    constexpr int S = decltype(slice_c)::value;
-    const int ko = kt * kBK;
-    unsigned char* xs = lds_raw + buf * STAGE;
-    unsigned char* ws = xs + XBYTES;
-#pragma unroll
-    for (int j = 0; j < ND; ++j) {
-      if (j * SL / ND != S) continue;
-      if (j < XD) {
-        // token rows past the tile's last row are never stored: skip their loads
-        if (8 * (j * NW + wave) < tc.rows) MOE_LDS_DMA16(xg[j] + ko, xs + (j * NW + wave) * 1024);
-      } else {
-        MOE_LDS_DMA16(wg[j - XD] + ko, ws + ((j - XD) * NW + wave) * 1024);
-      }
+    for (int i = 0; i < XD; ++i) {
+      const int r = 8 * (i * NW + wave) + lrow8;
+      int grow = tc.row0 + min(r, tc.rows - 1);
+      if (src != nullptr) grow = src[grow];
+      xg[i] = xa + (static_cast<size_t>(a_row0) + grow) * a_stride + lchunk * 8;
     }
-  };
-  auto dma = [&](int kt, int buf) {
-    dma_slice(kt, buf, std::integral_constant<int, 0>{});
-    dma_slice(kt, buf, std::integral_constant<int, 1>{});
-    dma_slice(kt, buf, std::integral_constant<int, 2>{});
-    dma_slice(kt, buf, std::integral_constant<int, 3>{});
-  };
-
-  f32x16 acc[MT][NTW];
+    const uint16_t* wg[WD];
+    const size_t wbase = static_cast<size_t>(tc.group) * w_stride;
 #pragma unroll
-  for (int a = 0; a < MT; ++a)
-#pragma unroll
-    for (int b = 0; b < NTW; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-
-  // fragment reads: row lane%32 of a 32-row block, logical K-chunk 2*kk + lane/32
-  const int frow = lane & 31, fhi = lane >> 5;
-  int koff[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) koff[kk] = frow * kRowBytes + (((2 * kk + fhi) ^ (frow & 7)) << 4);
-  // token block a of wave row wm is the tile's 32-row block a*WM + wm: the
-  // blocks of a short (ragged-tail) tile are shared by all wave rows
-  bf16x8 fa[4][NTW], fb[4][MT];
-  auto rfrag = [&](int buf, int kk, auto na_c) {
-    constexpr int NA = decltype(na_c)::value;
-    const unsigned char* xs = lds_raw + buf * STAGE;
-    const unsigned char* ws = xs + XBYTES;
-#pragma unroll
-    for (int b = 0; b < NTW; ++b) {
-      const int wrow = (b < NT) ? wn * (BN / WN) + b * 32 : BN + wn * (BN / WN) + (b - NT) * 32;
-      fa[kk][b] = *reinterpret_cast<const bf16x8*>(ws + wrow * kRowBytes + koff[kk]);
+    for (int i = 0; i < WD; ++i) {
+      const int r = 8 * (i * NW + wave) + lrow8;
+      const uint16_t* wsrc = (!GATEUP || r < BN) ? w_a : w_b;
+      const int n = n0 + ((GATEUP && r >= BN) ? r - BN : r);
+      wg[i] = wsrc + wbase + static_cast<size_t>(n) * K + lchunk * 8;
     }
+    // the stage's XD + WD LDS-DMA instructions, issued in slices: instruction j
+    // goes out in slice j * kDmaSlices / (XD + WD)
+    constexpr int ND = XD + WD;
+    auto dma_slice = [&](int kt, int buf, auto slice_c) {
+      constexpr int S = decltype(slice_c)::value;
+      const int ko = (kt0 + kt) * kBK;
+      unsigned char* xs = lds_raw + buf * STAGE;
+      unsigned char* ws = xs + XBYTES;
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
-      fb[kk][a] = *reinterpret_cast<const bf16x8*>(xs + (a * WM + wm) * 32 * kRowBytes + koff[kk]);
-  };
-  auto mfmas = [&](int kk, auto na_c) {
-    constexpr int NA = decltype(na_c)::value;
-#pragma unroll
-    for (int a = 0; a < NA; ++a)
-#pragma unroll
-      for (int b = 0; b < NTW; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][b], fb[kk][a], acc[a][b], 0, 0, 0);
-  };
-
-  // one barrier per K-step: it publishes stage kt (every thread waited for its
-  // own LDS-DMA loads of that stage) and retires all reads of the buffer that
-  // this step's loads fill, stage kt + ST - 1 (ST buffers in rotation).
-  // The loop is specialised on the number of this wave's token blocks that
-  // hold rows (NA): a full tile runs NA = MT, a ragged tail only the MFMAs of
-  // its rows, so it costs about its share of a full tile.
-  int nd_stage = WD;                 // LDS-DMA instructions this wave issues per stage
-#pragma unroll
-  for (int j = 0; j < XD; ++j) nd_stage += 8 * (j * NW + wave) < tc.rows ? 1 : 0;
-  auto kloop = [&](auto na_c) {
-    if (nk > 0) dma(0, 0);
-    if (ST == 3 && nk > 1) dma(1, 1);
-    int cur = 0;
-    for (int kt = 0; kt < nk; ++kt) {
-      // loads complete in issue order: stage kt has landed once no more than
-      // the next stage's nd_stage loads are outstanding
-      if (ST == 3 && kt + 1 < nk) wait_vmcnt_at_most<ND>(nd_stage);
-      else MOE_WAIT_VMCNT(0);
-      __syncthreads();
-      const int ahead = kt + ST - 1;
-      const bool more = ahead < nk;
-      const int nbuf = cur == 0 ? ST - 1 : cur - 1;   // (cur + ST - 1) % ST
-      if (more) dma_slice(ahead, nbuf, std::integral_constant<int, 0>{});
-      MOE_SCHED_FENCE();
-      rfrag(cur, 0, na_c);
-      rfrag(cur, 1, na_c);
-      mfmas(0, na_c);
-      if (more && SL > 1) dma_slice(ahead, nbuf, std::integral_constant<int, 1>{});
-      MOE_SCHED_FENCE();
-      rfrag(cur, 2, na_c);
-      mfmas(1, na_c);
-      if (more && SL > 2) dma_slice(ahead, nbuf, std::integral_constant<int, 2>{});
-      MOE_SCHED_FENCE();
-      rfrag(cur, 3, na_c);
-      mfmas(2, na_c);
-      if (more && SL > 3) dma_slice(ahead, nbuf, std::integral_constant<int, 3>{});
-      MOE_SCHED_FENCE();
-      mfmas(3, na_c);
-      cur = cur + 1 == ST ? 0 : cur + 1;
-    }
-  };
-  const int nb = (min(tc.rows, BM) + 31) / 32;
-  with_count<MT>((nb - wm + WM - 1) / WM, kloop);
-
-#pragma unroll
-  for (int a = 0; a < MT; ++a) {
-    const int m = (a * WM + wm) * 32 + frow;
-    if (m >= tc.rows) continue;
-    const size_t orow = static_cast<size_t>(out_row0) + tc.row0 + m;
-#pragma unroll
-    for (int b = 0; b < NT; ++b) {
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int n = n0 + wn * (BN / WN) + b * 32 + 8 * rq + 4 * fhi;
-        if (GATEUP) {
-          float h[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            h[q] = silu(acc[a][b][4 * rq + q]) * acc[a][NT + b][4 * rq + q];
-          u32x2 pk;
-          pk[0] = pack_bf16x2(h[0], h[1]);
-          pk[1] = pack_bf16x2(h[2], h[3]);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow * out_stride + n) = pk;
-          if constexpr (HOUT) {
-            f32x4 v1, v3;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              v1[q] = acc[a][b][4 * rq + q];
-              v3[q] = acc[a][NT + b][4 * rq + q];
-            }
-            *reinterpret_cast<f32x4*>(h1o + orow * out_stride + n) = v1;
-            *reinterpret_cast<f32x4*>(h3o + orow * out_stride + n) = v3;
-          }
+      for (int j = 0; j < ND; ++j) {
+        if (j * SL / ND != S) continue;
+        if (j < XD) {
+          // token rows past the tile's last row are never stored: skip their loads
+          if (8 * (j * NW + wave) < tc.rows) MOE_LDS_DMA16(xg[j] + ko, xs + (j * NW + wave) * 1024);
         } else {
-          f32x4 v;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = acc[a][b][4 * rq + q];
-          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow * out_stride + n) = v;
+          MOE_LDS_DMA16(wg[j - XD] + ko, ws + ((j - XD) * NW + wave) * 1024);
         }
       }
+    };
+    auto dma = [&](int kt, int buf) {
+      dma_slice(kt, buf, std::integral_constant<int, 0>{});
+      dma_slice(kt, buf, std::integral_constant<int, 1>{});
+      dma_slice(kt, buf, std::integral_constant<int, 2>{});
+      dma_slice(kt, buf, std::integral_constant<int, 3>{});
+    };
+
+    f32x16 acc[MT][NTW];
+#pragma unroll
+    for (int a = 0; a < MT; ++a)
+#pragma unroll
+      for (int b = 0; b < NTW; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+    // fragment reads: row lane%32 of a 32-row block, logical K-chunk 2*kk + lane/32
+    const int frow = lane & 31, fhi = lane >> 5;
+    int koff[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) koff[kk] = frow * kRowBytes + (((2 * kk + fhi) ^ (frow & 7)) << 4);
+    // token block a of wave row wm is the tile's 32-row block a*WM + wm: the
+    // blocks of a short (ragged-tail) tile are shared by all wave rows
+    bf16x8 fa[4][NTW], fb[4][MT];
+    auto rfrag = [&](int buf, int kk, auto na_c) {
+      constexpr int NA = decltype(na_c)::value;
+      const unsigned char* xs = lds_raw + buf * STAGE;
+      const unsigned char* ws = xs + XBYTES;
+#pragma unroll
+      for (int b = 0; b < NTW; ++b) {
+        const int wrow = (b < NT) ? wn * (BN / WN) + b * 32 : BN + wn * (BN / WN) + (b - NT) * 32;
+        fa[kk][b] = *reinterpret_cast<const bf16x8*>(ws + wrow * kRowBytes + koff[kk]);
+      }
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+        fb[kk][a] = *reinterpret_cast<const bf16x8*>(xs + (a * WM + wm) * 32 * kRowBytes + koff[kk]);
+    };
+    auto mfmas = [&](int kk, auto na_c) {
+      constexpr int NA = decltype(na_c)::value;
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int b = 0; b < NTW; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][b], fb[kk][a], acc[a][b], 0, 0, 0);
+    };
+
+    // one barrier per K-step: it publishes stage kt (every thread waited for its
+    // own LDS-DMA loads of that stage) and retires all reads of the buffer that
+    // this step's loads fill, stage kt + ST - 1 (ST buffers in rotation).
+    // The loop is specialised on the number of this wave's token blocks that
+    // hold rows (NA): a full tile runs NA = MT, a ragged tail only the MFMAs of
+    // its rows, so it costs about its share of a full tile.
+    int nd_stage = WD;                 // LDS-DMA instructions this wave issues per stage
+#pragma unroll
+    for (int j = 0; j < XD; ++j) nd_stage += 8 * (j * NW + wave) < tc.rows ? 1 : 0;
+    auto kloop = [&](auto na_c) {
+      if (nk > 0) dma(0, 0);
+      if (ST == 3 && nk > 1) dma(1, 1);
+      int cur = 0;
+      for (int kt = 0; kt < nk; ++kt) {
+        // loads complete in issue order: stage kt has landed once no more than
+        // the next stage's nd_stage loads are outstanding
+        if (ST == 3 && kt + 1 < nk) wait_vmcnt_at_most<ND>(nd_stage);
+        else MOE_WAIT_VMCNT(0);
+        __syncthreads();
+        const int ahead = kt + ST - 1;
+        const bool more = ahead < nk;
+        const int nbuf = cur == 0 ? ST - 1 : cur - 1;   // (cur + ST - 1) % ST
+        if (more) dma_slice(ahead, nbuf, std::integral_constant<int, 0>{});
+        MOE_SCHED_FENCE();
+        rfrag(cur, 0, na_c);
+        rfrag(cur, 1, na_c);
+        mfmas(0, na_c);
+        if (more && SL > 1) dma_slice(ahead, nbuf, std::integral_constant<int, 1>{});
+        MOE_SCHED_FENCE();
+        rfrag(cur, 2, na_c);
+        mfmas(1, na_c);
+        if (more && SL > 2) dma_slice(ahead, nbuf, std::integral_constant<int, 2>{});
+        MOE_SCHED_FENCE();
+        rfrag(cur, 3, na_c);
+        mfmas(2, na_c);
+        if (more && SL > 3) dma_slice(ahead, nbuf, std::integral_constant<int, 3>{});
+        MOE_SCHED_FENCE();
+        mfmas(3, na_c);
+        cur = cur + 1 == ST ? 0 : cur + 1;
+      }
+    };
+    const int nb = (min(tc.rows, BM) + 31) / 32;
+    with_count<MT>((nb - wm + WM - 1) / WM, kloop);
+
+    if constexpr (SK) {
+      if (part != nullptr) {
+#pragma unroll
+        for (int a = 0; a < MT; ++a) {
+          const int m = (a * WM + wm) * 32 + frow;
+          if (m >= tc.rows) continue;
+#pragma unroll
+          for (int b = 0; b < NT; ++b)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+              f32x4 v;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[q] = acc[a][b][4 * rq + q];
+              *reinterpret_cast<f32x4*>(part + static_cast<size_t>(m) * BN + wn * (BN / WN) +
+                                        b * 32 + 8 * rq + 4 * fhi) = v;
+            }
+        }
+        return;
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < MT; ++a) {
+      const int m = (a * WM + wm) * 32 + frow;
+      if (m >= tc.rows) continue;
+      const size_t orow = static_cast<size_t>(out_row0) + tc.row0 + m;
+#pragma unroll
+      for (int b = 0; b < NT; ++b) {
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int n = n0 + wn * (BN / WN) + b * 32 + 8 * rq + 4 * fhi;
+          if (GATEUP) {
+            float h[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              h[q] = silu(acc[a][b][4 * rq + q]) * acc[a][NT + b][4 * rq + q];
+            u32x2 pk;
+            pk[0] = pack_bf16x2(h[0], h[1]);
+            pk[1] = pack_bf16x2(h[2], h[3]);
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow * out_stride + n) = pk;
+            if constexpr (HOUT) {
+              f32x4 v1, v3;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                v1[q] = acc[a][b][4 * rq + q];
+                v3[q] = acc[a][NT + b][4 * rq + q];
+              }
+              *reinterpret_cast<f32x4*>(h1o + orow * out_stride + n) = v1;
+              *reinterpret_cast<f32x4*>(h3o + orow * out_stride + n) = v3;
+            }
+          } else {
+            f32x4 v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = acc[a][b][4 * rq + q];
+            *reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow * out_stride + n) = v;
+          }
+        }
+      }
+    }
+  };
+
+  if constexpr (!SK) {
+    int m_tile, n_tile;
+    xcd_tile(n_logical, max_tiles, m_tile, n_tile);
+    if (m_tile < 0) return;
+    run_tile(m_tile, n_tile, 0, nk_all, nullptr);
+  } else {
+    __shared__ int s_real;
+    const int n_real = real_tiles<BM>(tiles, max_tiles, n_single, &s_real);
+    const long long n_tiles = static_cast<long long>(n_real) * (N / BN);
+    const long long U = n_tiles * nk_all;
+    const int P = gridDim.x;   // a multiple of 8
+    const int L = blockIdx.x;
+    const int p = (L & 7) * (P >> 3) + (L >> 3);
+    if (U < static_cast<long long>(P) * nk_all) {
+      // under one tile per workgroup: whole tiles, no split
+      for (long long t = p; t < n_tiles; t += P)
+        run_tile(static_cast<int>(t % n_real), static_cast<int>(t / n_real), 0, nk_all, nullptr);
+      return;
+    }
+    const long long u1 = U * (p + 1) / P;
+    for (long long u = U * p / P; u < u1;) {
+      const long long t = u / nk_all;
+      const int kt0 = static_cast<int>(u - t * nk_all);
+      const int kt1 = static_cast<int>(min(static_cast<long long>(nk_all), kt0 + (u1 - u)));
+      // a segment that stops before its tile's end is that tile's first part
+      float* part = kt1 < nk_all ? sk_part + static_cast<size_t>(p) * BM * BN : nullptr;
+      run_tile(static_cast<int>(t % n_real), static_cast<int>(t / n_real), kt0, kt1, part);
+      u += kt1 - kt0;
     }
   }
 }
 
+
+// out tile += the fp32 first part of each tile that a stream-K share boundary
+// splits (its last part already wrote out): workgroups (p, q) take the boundary
+// between shares p and p + 1, recomputed as in the GEMM, q the q-th quarter of
+// the tile's rows. One fp32 addition per element, so the result does not depend
+// on which part finished first.
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void streamk_fixup_kernel(
+    const int32_t* __restrict__ tiles, int max_tiles, int n_single, int K, int N, int P,
+    const float* __restrict__ sk_part, float* __restrict__ out, int out_stride, int out_row0) {
+  __shared__ int s_real;
+  const int n_real = real_tiles<BM>(tiles, max_tiles, n_single, &s_real);
+  const int nk_all = K / kBK;
+  const long long U = static_cast<long long>(n_real) * (N / BN) * nk_all;
+  if (U < static_cast<long long>(P) * nk_all) return;   // nothing was split
+  const int p = blockIdx.x;
+  const long long ub = U * (p + 1) / P;
+  const long long t = ub / nk_all;
+  if (ub == t * nk_all) return;                          // the boundary falls between tiles
+  const TileCoord tc = lookup_tile(tiles, n_single, BM, static_cast<int>(t % n_real));
+  const int n0 = static_cast<int>(t / n_real) * BN;
+  const float* part = sk_part + static_cast<size_t>(p) * BM * BN;
+  constexpr int QR = BM / 4;   // rows per quarter
+  const int m_lo = blockIdx.y * QR;
+  const int m_hi = min(tc.rows, m_lo + QR);
+  for (int i = m_lo * (BN / 4) + threadIdx.x; i < m_hi * (BN / 4); i += 256) {
+    const int m = i / (BN / 4), c = (i % (BN / 4)) * 4;
+    f32x4* y = reinterpret_cast<f32x4*>(out + (static_cast<size_t>(out_row0) + tc.row0 + m) *
+                                                  out_stride + n0 + c);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(part + static_cast<size_t>(m) * BN + c);
+    *y = *y + v;
+  }
+}
 // ---------------------------------------------------------------- decode tiles
 //
 // Groups of at most a few rows (decode): the time is reading the experts'
@@ -644,7 +754,43 @@ static hipError_t run_lds(const GemmTileMap& map, const uint16_t* xa, const int3
   const size_t lds = ST * kStage;
   return launch_tiled(gemm_bf16_lds_kernel<BM, BN, WM, WN, GATEUP, ST, HOUT>, BM, BN,
                       64 * WM * WN, lds, map, xa, src, a_stride, a_row0, wa, wb, w_stride, out,
-                      out_stride, out_row0, K, N, s, h1o, h3o);
+                      out_stride, out_row0, K, N, s, h1o, h3o, static_cast<float*>(nullptr));
+}
+
+// Workgroups of a stream-K launch: one per CU of the current device (a multiple
+// of 8, at most kStreamKMaxWorkgroups), or 0 if the count is unavailable.
+static int streamk_workgroups() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  cus = cus < kStreamKMaxWorkgroups ? cus : kStreamKMaxWorkgroups;
+  return cus / 8 * 8;
+}
+
+// Plain 256 x 256 products as stream-K (see gemm_bf16_lds_kernel) when the
+// launch has at least one tile per workgroup: the fix-up kernel follows.
+// Returns hipErrorNotSupported when stream-K does not apply.
+static hipError_t run_lds_streamk(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
+                                  int a_stride, int a_row0, const uint16_t* wa, long long w_stride,
+                                  float* out, int out_stride, int out_row0, int K, int N,
+                                  float* sk_part, hipStream_t s) {
+  constexpr int BM = 256, BN = 256;
+  constexpr size_t lds = 2 * static_cast<size_t>(BM + BN) * kRowBytes;
+  const int P = streamk_workgroups();
+  const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + BM - 1) / BM;
+  if (P < 8 || static_cast<long long>(m_tiles) * (N / BN) < P) return hipErrorNotSupported;
+  auto kern = gemm_bf16_lds_kernel<BM, BN, 2, 4, false, 2, false, true>;
+  hipError_t e = allow_large_lds(reinterpret_cast<const void*>(kern), lds);
+  if (e != hipSuccess) return e;
+  kern<<<dim3(P), dim3(512), lds, s>>>(map.tiles, m_tiles, map.n_single, 0, xa, src, a_stride,
+                                       a_row0, wa, nullptr, w_stride, out, out_stride, out_row0,
+                                       K, N, nullptr, nullptr, sk_part);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  streamk_fixup_kernel<BM, BN><<<dim3(P - 1, 4), dim3(256), 0, s>>>(
+      map.tiles, m_tiles, map.n_single, K, N, P, sk_part, out, out_stride, out_row0);
+  return hipGetLastError();
 }
 
 // BM = 256 needs N % 256 == 0 (down) / N % 128 == 0 (gate/up); the
@@ -689,6 +835,11 @@ hipError_t launch_gemm_down_bf16(const GemmTileMap& map, const DownArgs& a, int 
       return run_lds<256, 128, 2, 4, false>(map, act, a.src, a.act_stride, a.in_row0, w2,
                                             nullptr, a.w_stride, a.y, ys, a.out_row0, a.K,
                                             a.N, s);
+    if (a.sk_part != nullptr) {
+      const hipError_t e = run_lds_streamk(map, act, a.src, a.act_stride, a.in_row0, w2,
+                                           a.w_stride, a.y, ys, a.out_row0, a.K, a.N, a.sk_part, s);
+      if (e != hipErrorNotSupported) return e;
+    }
     return run_lds<256, 256, 2, 4, false>(map, act, a.src, a.act_stride, a.in_row0, w2,
                                           nullptr, a.w_stride, a.y, ys, a.out_row0, a.K, a.N,
                                           s);

@@ -135,7 +135,12 @@ struct DownArgs {
   int K, N;               // K = d_ff, N = d
   const int32_t* src = nullptr;   // grouped row -> input row (nullable: identity)
   int out_stride = 0;             // y row stride in floats (0: N)
+  float* sk_part = nullptr;       // stream-K partial tiles (streamk_part_bytes), nullable
 };
+// Stream-K down products: at most this many workgroups, each with one partial
+// 256 x 256 fp32 tile of scratch.
+constexpr int kStreamKMaxWorkgroups = 256;
+constexpr size_t kStreamKPartBytes = static_cast<size_t>(kStreamKMaxWorkgroups) * 256 * 256 * 4;
 // K-major grouped GEMMs (gemm_kmajor.hip), 256 x 256 tiles.
 // Data mode: y[y_row0 + row][n] = sum_k x[x_row0 + row(r)][k] * W_g[k][n] for the
 // rows of a 256-row tile table (row(r) = src[r] when src is set), with

@@ -133,6 +133,8 @@ size_t permute_bytes(const Shape& s) {
          (s.ep > 1 ? al(static_cast<size_t>(s.R) * 4) : 0);
 }
 size_t tiles_bytes(const Shape& s) { return al(static_cast<size_t>(s.max_tiles) * 16); }
+// stream-K partial tiles of the down product (256-row tiles only)
+size_t sk_bytes(const Shape& s) { return s.bf16 && s.BM == 256 ? moe::kStreamKPartBytes : 0; }
 size_t act_bytes(const Shape& s) {
   return al(static_cast<size_t>(s.rows_total) * s.act_stride * s.elt);
 }
@@ -155,7 +157,7 @@ struct Carver {
 // Workspace of moe_backward: every buffer of the recomputed forward and of the
 // backward, carved in this order (a null base only measures the size).
 struct BwdBufs {
-  float *z, *gates, *h1, *h3, *row_gate, *dg_row, *dz, *u, *dxp, *wpart;
+  float *z, *gates, *h1, *h3, *row_gate, *dg_row, *dz, *u, *dxp, *wpart, *sk;
   int32_t *idx, *dest, *src, *offsets, *counts, *kept, *ndrop, *soff, *tiles, *tiles256;
   int32_t *blk, *slot_base, *slot_keep;
   uint16_t *act, *dyb, *dyp, *dH, *xp, *w2t, *w13t, *w2st, *w13st;
@@ -212,6 +214,7 @@ size_t backward_layout(const Shape& s, char* base, BwdBufs* b) {
   b->w13t = cv.take<uint16_t>(b->tr_routed ? E * d * 2 * dff * 2 : 0);
   b->w2st = cv.take<uint16_t>(b->tr_shared ? dffs * d * 2 : 0);
   b->w13st = cv.take<uint16_t>(b->tr_shared ? d * 2 * dffs * 2 : 0);
+  b->sk = cv.take<float>(b->tr_routed || b->tr_shared ? moe::kStreamKPartBytes : 0);
   return static_cast<size_t>(cv.p - base);
 }
 
@@ -220,14 +223,14 @@ size_t stage_bytes(const Shape& s, moe_stage st) {
   switch (st) {
     case MOE_STAGE_ROUTE: b = route_bytes(s); break;
     case MOE_STAGE_PERMUTE: b = permute_bytes(s); break;
-    case MOE_STAGE_EXPERT_GATEUP:
-    case MOE_STAGE_EXPERT_DOWN: b = tiles_bytes(s); break;
-    case MOE_STAGE_EXPERT_FFN: b = act_bytes(s) + tiles_bytes(s); break;
+    case MOE_STAGE_EXPERT_GATEUP: b = tiles_bytes(s); break;
+    case MOE_STAGE_EXPERT_DOWN: b = tiles_bytes(s) + sk_bytes(s); break;
+    case MOE_STAGE_EXPERT_FFN: b = act_bytes(s) + tiles_bytes(s) + sk_bytes(s); break;
     case MOE_STAGE_COMBINE: b = 0; break;
     case MOE_STAGE_FORWARD: {
       size_t scratch = route_bytes(s);
       if (permute_bytes(s) > scratch) scratch = permute_bytes(s);
-      if (tiles_bytes(s) > scratch) scratch = tiles_bytes(s);
+      if (tiles_bytes(s) + sk_bytes(s) > scratch) scratch = tiles_bytes(s) + sk_bytes(s);
       b = forward_fixed_bytes(s) + scratch;
       break;
     }
@@ -337,14 +340,16 @@ moe_status do_gateup(const Shape& s, const void* x, const int32_t* src, const in
 }
 
 moe_status do_down(const Shape& s, const void* act, const int32_t* tiles, const void* w2,
-                   const void* ws2, float* y_perm, hipStream_t stream) {
+                   const void* ws2, float* y_perm, float* sk_part, hipStream_t stream) {
   moe::GemmTileMap map{tiles, s.max_tiles, 0};
   moe::DownArgs a{act, s.act_stride, 0, w2, static_cast<long long>(s.d) * s.dff, y_perm, 0, s.dff, s.d};
+  a.sk_part = sk_part;
   if (s.bf16) MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, stream), "gemm_down");
   else MOE_HIP(moe::launch_gemm_down_f32(map, a, stream), "gemm_down");
   if (s.nsh) {
     moe::GemmTileMap m1{nullptr, 0, s.T};
     moe::DownArgs b{act, s.act_stride, s.R, ws2, 0, y_perm, s.R, s.dffs, s.d};
+    b.sk_part = sk_part;
     const int bm = moe::gemm_tile_rows(1, s.T, 1, s.n256);
     if (s.bf16) MOE_HIP(moe::launch_gemm_down_bf16(m1, b, bm, stream), "gemm_down_shared");
     else MOE_HIP(moe::launch_gemm_down_f32(m1, b, stream), "gemm_down_shared");
@@ -468,8 +473,9 @@ moe_status moe_expert_down(const moe_config* cfg, const void* act, const int32_t
   if (s.T == 0) return MOE_OK;
   hipStream_t strm = static_cast<hipStream_t>(stream);
   int32_t* tiles = static_cast<int32_t*>(ws);
+  float* sk = sk_bytes(s) ? reinterpret_cast<float*>(static_cast<char*>(ws) + tiles_bytes(s)) : nullptr;
   MOE_HIP(moe::launch_tile_map(offsets, s.G, s.BM, s.max_tiles, s.ep, tiles, strm), "tile_map");
-  return do_down(s, act, tiles, w2, ws2, y_perm, strm);
+  return do_down(s, act, tiles, w2, ws2, y_perm, sk, strm);
 }
 
 moe_status moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* src,
@@ -491,10 +497,11 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* s
   Carver cv{static_cast<char*>(ws)};
   void* act = cv.take<char>(static_cast<size_t>(s.rows_total) * s.act_stride * s.elt);
   int32_t* tiles = cv.take<int32_t>(static_cast<size_t>(s.max_tiles) * 16);
+  float* sk = sk_bytes(s) ? cv.take<float>(sk_bytes(s)) : nullptr;
   MOE_HIP(moe::launch_tile_map(offsets, s.G, s.BM, s.max_tiles, s.ep, tiles, strm), "tile_map");
   st = do_gateup(s, x, src, tiles, w1, w3, ws1, ws3, act, strm);
   if (st != MOE_OK) return st;
-  return do_down(s, act, tiles, w2, ws2, y_perm, strm);
+  return do_down(s, act, tiles, w2, ws2, y_perm, sk, strm);
 }
 
 moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* dest,
@@ -672,6 +679,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   }
   if (b.tr_routed) {
     moe::DownArgs a{b.dyb, d, 0, b.w2t, static_cast<long long>(dff) * d, b.u, 0, d, dff, b.src, As};
+    a.sk_part = b.sk;
     MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "u");
   } else {
     moe::KmDataArgs a{b.dyb, d, b.src, 0, u16(w2), nullptr, d, dff,
@@ -684,6 +692,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   if (s.nsh) {
     if (b.tr_shared) {
       moe::DownArgs a{b.dyb, d, 0, b.w2st, 0, b.u, R, d, dffs, nullptr, As};
+      a.sk_part = b.sk;
       MOE_HIP(moe::launch_gemm_down_bf16(map1, a, bm1, strm), "u shared");
     } else {
       moe::KmDataArgs a{b.dyb, d, nullptr, 0, u16(ws2), nullptr, d, dffs, 0, b.u, As, R, d, dffs};
@@ -701,6 +710,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   if (b.tr_routed) {
     moe::DownArgs a{b.dH, 2 * As, 0, b.w13t, static_cast<long long>(d) * 2 * dff, b.dxp, 0,
                     2 * dff, d};
+    a.sk_part = b.sk;
     MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "dx_perm");
   } else {
     moe::KmDataArgs a{b.dH, 2 * As, nullptr, 0, u16(w1), u16(w3), dff, d,
@@ -710,6 +720,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   if (s.nsh) {
     if (b.tr_shared) {
       moe::DownArgs a{b.dH, 2 * As, R, b.w13st, 0, b.dxp, R, 2 * dffs, d};
+      a.sk_part = b.sk;
       MOE_HIP(moe::launch_gemm_down_bf16(map1, a, bm1, strm), "dx_perm shared");
     } else {
       moe::KmDataArgs a{b.dH, 2 * As, nullptr, R, u16(ws1), u16(ws3), dffs, d, 0, b.dxp, d, R,
@@ -810,7 +821,9 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   if (st != MOE_OK) return st;
   st = do_gateup(s, x, src, tiles, w1, w3, ws1, ws3, act, strm);
   if (st != MOE_OK) return st;
-  st = do_down(s, act, tiles, w2, ws2, y_perm, strm);
+  float* sk = sk_bytes(s) ? reinterpret_cast<float*>(static_cast<char*>(scratch) + tiles_bytes(s))
+                         : nullptr;
+  st = do_down(s, act, tiles, w2, ws2, y_perm, sk, strm);
   if (st != MOE_OK) return st;
   MOE_HIP(moe::launch_combine(y_perm, dest, gates, s.T, s.k, s.d, s.nsh ? s.R : -1, y, strm),
           "combine");

