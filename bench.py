@@ -9,10 +9,13 @@ The default workload is the Mixtral-shaped layer at T = 4096 tokens.
 Prints ONE JSON line (rank 0). Besides the step throughput it reports the
 roofline of the dominant kernel (the grouped gate/up GEMM), timed with HIP
 events recorded on the library's stream around that kernel in every timed
-step, and the float64 CPU oracle timed on a bounded sample of the workload.
+step, the float64 CPU oracle timed on a bounded sample of the workload, and
+the ceilings this device reaches on both rooflines (an MFMA loop and a
+streaming read). Steps of HBM-bound workloads start from cold caches (a 1 GiB
+read between steps, outside the timed step).
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--ep N]
-                  [--backward]
+                  [--backward] [--no-flush] [--no-calibration]
   python bench.py --calibrate-copy     # plain 1 GiB copies, for counter scaling
 """
 from __future__ import annotations
@@ -34,6 +37,7 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 METRIC = "MoE-layer tokens/s at 1 GPU + % MFMA peak (prefill) / % HBM BW (decode)"
 GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_31_amd", "csrc", "gemm_bf16.hip")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_gateup_mixtral_t4096_counters.md")
+CALIB_LIB = os.path.join(ROOT, "mixture_experts_layer_31_amd", "libmoe_calibrate.so")
 
 
 def log(msg):
@@ -52,6 +56,9 @@ def parse():
     ap.add_argument("--ep", type=int, default=0,
                     help="lay the rows out as N simulated expert-parallel ranks and report "
                          "the dispatch volume per rank")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="HBM-bound workloads: time steps back to back (warm MALL/L2)")
+    ap.add_argument("--no-calibration", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="also time moe_backward (gradients of the layer) on the same batch")
     return ap.parse_args()
@@ -69,6 +76,54 @@ def calibrate_copy():
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "elementwise add", "bytes_read": 4 * n,
                       "bytes_written": 4 * n, "launches": 5}))
+
+
+def device_ceilings():
+    """What this device reaches on the two rooflines, beside the nominal peaks: a
+    dense MFMA loop (v_mfma_f32_32x32x16_bf16 on pseudo-random register operands, 2048
+    workgroups of 4 waves) and a streaming read of 2 GiB (8x the MALL), with the
+    kernels of libmoe_calibrate.so; the best of 3 timed launches each."""
+    import ctypes
+    import torch
+    if not os.path.exists(CALIB_LIB):
+        raise RuntimeError(f"{CALIB_LIB} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(CALIB_LIB)
+    lib.moe_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_calib_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.moe_calib_mfma_flops.restype = ctypes.c_double
+    lib.moe_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def best_ms(launch):
+        if launch() != 0:
+            raise RuntimeError("calibration kernel launch failed")
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    blocks, iters = 2048, 2048
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    ms = best_ms(lambda: lib.moe_calib_mfma(blocks, iters, ctypes.c_void_p(out.data_ptr()), sp))
+    tflops = lib.moe_calib_mfma_flops(blocks, iters) / (ms * 1e-3) / 1e12
+    buf = torch.ones(1 << 29, dtype=torch.float32, device="cuda")     # 2 GiB
+    rblocks = 4096
+    outr = torch.empty(rblocks * 256, dtype=torch.int32, device="cuda")
+    ms = best_ms(lambda: lib.moe_calib_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * 4,
+                                            rblocks, ctypes.c_void_p(outr.data_ptr()), sp))
+    gbps = buf.numel() * 4 / (ms * 1e-3) / 1e9
+    del buf, out, outr
+    torch.cuda.empty_cache()
+    return {"mfma_loop_tflops": round(tflops, 1), "mfma_loop_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "hbm_read_gbps": round(gbps, 1), "hbm_read_frac": round(gbps / PEAK_HBM_GBPS, 4)}
 
 
 def kernel_source_hash():
@@ -108,6 +163,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     moe.load()
+    calib = None if args.no_calibration else device_ceilings()
     wl = wk.get(args.workload)
     T = wl.T
     t0 = time.time()
@@ -175,6 +231,21 @@ def main():
     R_kept = int(kept.sum())
     touched = int((kept > 0).sum())
 
+    # algorithmic work, from this batch's routing
+    elt = 2 if wl.dtype == wk.BF16 else 4
+    d, dff, dffs, nsh = wl.d, wl.d_ff, wl.d_ff_shared, wl.n_shared
+    F_step = 2.0 * T * d * wl.E + 6.0 * d * dff * R_kept + 6.0 * d * dffs * T * nsh
+    B_step = (touched * 3.0 * d * dff * elt + nsh * 3.0 * d * dffs * elt + wl.E * d * elt
+              + T * d * elt + T * d * 4.0)
+    peak_f = PEAK_BF16_TFLOPS if wl.dtype == wk.BF16 else PEAK_F32_TFLOPS
+    step_bound = "mfma" if F_step / (peak_f * 1e12) >= B_step / (PEAK_HBM_GBPS * 1e9) else "hbm"
+    # HBM-bound steps start from cold caches: reading 1 GiB between steps evicts the
+    # 256 MB MALL and the L2 (with clean lines: a write would leave dirty ones for
+    # the step to write back), outside the timed step
+    flush = step_bound == "hbm" and not args.no_flush
+    scratch = torch.zeros(1 << 28, dtype=torch.float32, device=dev) if flush else None
+    sink = torch.zeros((), dtype=torch.float32, device=dev) if flush else None
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -182,18 +253,27 @@ def main():
     K = args.steps
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(K)]
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     start.record(stream)
     for i in range(K):
+        if flush:
+            torch.sum(scratch, dim=0, out=sink)
+        sev[i][0].record(stream)
         step(*evs[i])
+        sev[i][1].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms_step = start.elapsed_time(stop) / K
+    step_ms = np.array([a.elapsed_time(b) for a, b in sev])
+    # back to back, the span over the K steps; with flushes, the steps' own times
+    ms_step = float(step_ms.mean()) if flush else start.elapsed_time(stop) / K
     gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    del scratch, sink
 
     # the fused single-call entry point on the same batch, same K
     for _ in range(2):
@@ -208,16 +288,9 @@ def main():
     torch.cuda.synchronize()
     fwd_ms = f0.elapsed_time(f1) / K
 
-    # algorithmic work, from this batch's routing
-    elt = 2 if wl.dtype == wk.BF16 else 4
-    d, dff, dffs, nsh = wl.d, wl.d_ff, wl.d_ff_shared, wl.n_shared
-    F_step = 2.0 * T * d * wl.E + 6.0 * d * dff * R_kept + 6.0 * d * dffs * T * nsh
-    B_step = (touched * 3.0 * d * dff * elt + nsh * 3.0 * d * dffs * elt + wl.E * d * elt
-              + T * d * elt + T * d * 4.0)
     F_g = 4.0 * d * dff * R_kept + 4.0 * d * dffs * T * nsh
     B_g = (touched * 2.0 * d * dff * elt + nsh * 2.0 * d * dffs * elt + T * d * elt
            + (R_kept * dff + nsh * T * dffs) * elt)
-    peak_f = PEAK_BF16_TFLOPS if wl.dtype == wk.BF16 else PEAK_F32_TFLOPS
     g_bound = "mfma" if F_g / (peak_f * 1e12) >= B_g / (PEAK_HBM_GBPS * 1e9) else "hbm"
     if g_bound == "mfma":
         achieved = F_g / (gemm_ms * 1e-3) / 1e12
@@ -236,7 +309,6 @@ def main():
 
     step_tflops = F_step / (ms_step * 1e-3) / 1e12
     step_gbps = B_step / (ms_step * 1e-3) / 1e9
-    step_bound = "mfma" if F_step / (peak_f * 1e12) >= B_step / (PEAK_HBM_GBPS * 1e9) else "hbm"
 
     ep_report = None
     if args.ep > 1:
@@ -285,7 +357,12 @@ def main():
                  "frac_mfma": round(step_tflops / peak_f, 4),
                  "frac_hbm": round(step_gbps / PEAK_HBM_GBPS, 4),
                  "fused_forward_ms": round(fwd_ms, 4),
+                 "step_ms_median": round(float(np.median(step_ms)), 4),
+                 "step_ms_min": round(float(step_ms.min()), 4),
+                 "step_ms_max": round(float(step_ms.max()), 4),
+                 "cold_caches": flush,
                  "wall_s": round(wall, 4)},
+        "calibration": calib,
         "roofline": roof,
         "cpu_baseline": cpu,
         "expert_parallel": ep_report,

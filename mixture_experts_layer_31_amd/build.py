@@ -1,4 +1,6 @@
-"""Build the gfx950 MoE library (libmoe_mi355x.so) in-tree with hipcc.
+"""Build the gfx950 MoE library (libmoe_mi355x.so) in-tree with hipcc, and the
+small calibration library (libmoe_calibrate.so: MFMA-loop and streaming-read
+kernels the benchmark reports beside the nominal peaks).
 
 Usage: python -m mixture_experts_layer_31_amd.build   (or build() from Python)
 """
@@ -20,6 +22,8 @@ LIB = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["moe_api.hip", "router.hip", "index.hip", "rows.hip", "gemm_bf16.hip", "gemm_f32.hip",
            "backward.hip", "gemm_kmajor.hip"]
+CALIB_SOURCE = "calibrate.hip"
+CALIB_LIB = os.path.join(PKG, "libmoe_calibrate.so")
 
 # packed fp32 VALU ops are disabled: the compiler would otherwise form them from
 # plain float code, and this build keeps every fp32 operation scalar
@@ -58,11 +62,15 @@ def build(verbose: bool = False) -> str:
             print(out)
         return obj
 
-    with ThreadPoolExecutor(max(1, min(len(SOURCES), os.cpu_count() or 1))) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+    with ThreadPoolExecutor(max(1, min(len(SOURCES) + 1, os.cpu_count() or 1))) as ex:
+        objs = list(ex.map(compile_one, SOURCES + [CALIB_SOURCE]))
+    calib_obj = objs.pop()
     tmp = LIB + ".tmp"
     _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    tmp = CALIB_LIB + ".tmp"
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, calib_obj])
+    os.replace(tmp, CALIB_LIB)
     return LIB
 
 
