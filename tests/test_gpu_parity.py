@@ -356,6 +356,12 @@ _BWD_CASES = {
     # 512 tokens: the shared expert's weights are transposed once, the routed ones
     # (128 rows per expert) read K-major
     "shared_transposed": (dict(d=256, E=8, k=2, d_ff=256, n_shared=1, d_ff_shared=512), 512),
+    # E = 1, k = 1: a dense SwiGLU layer; the selected gate is identically 1
+    "dense_e1": (dict(d=256, E=1, k=1, d_ff=256), 96),
+    # fine-grained: > 32 experts (wide router-gradient and dx kernels), 32-row tiles
+    # beside the 256-row K-major tile table, K-major shared products
+    "fine_grained": (dict(d=256, E=64, k=8, d_ff=256, n_shared=1, d_ff_shared=256,
+                          bias_range=0.1), 256),
 }
 
 
@@ -421,6 +427,10 @@ def test_backward_matches_oracle(case):
     untouched = np.setdiff1d(np.arange(E), fw["idx"].ravel())
     for e in untouched:
         assert not g["dw1"][e].any() and not g["dw2"][e].any()
+    if wl.k == 1 and wl.gate == wk.GATE_SELECTED and wl.aux_alpha == 0:
+        # g = softmax over one selected logit = 1: no gradient reaches the router
+        # (CMU 15-779 notes, §2.5)
+        assert not g["dwr"].any()
     log(f"[ok] backward {case}: " + ", ".join(worst))
 
 
@@ -506,6 +516,24 @@ def _backward_full_sampled(name, T, n_tokens, n_experts, n_units, seed):
     for t in list(out):
         del out[t]
     torch.cuda.empty_cache()
+
+
+def test_backward_zero_tokens_leaves_outputs():
+    """T = 0: moe_backward launches nothing and leaves every output untouched."""
+    wl = _adhoc("bwd_empty", 130, T=0, d=256, E=8, k=2, d_ff=256, dtype=wk.BF16)
+    W = Weights(wl)
+    cfg = config_of(wl, 0)
+    E, d, dff = wl.E, wl.d, wl.d_ff
+    fill = lambda *shape: torch.full(shape, 3.0, dtype=torch.float32, device=dev())
+    out = dict(dx=fill(1, d), dwr=fill(E, d), dw1=fill(E, dff, d), dw3=fill(E, dff, d),
+               dw2=fill(E, d, dff))
+    x = torch.zeros((1, d), dtype=torch.bfloat16, device=dev())
+    moe.backward(cfg, x, W.wr, None, W.w1, W.w3, W.w2, None, None, None, fill(1, d), out["dx"],
+                 out["dwr"], out["dw1"], out["dw3"], out["dw2"],
+                 ws=moe.alloc_workspace(cfg, moe.STAGE_BACKWARD))
+    torch.cuda.synchronize()
+    for name, t in out.items():
+        assert (t == 3.0).all(), name
 
 
 def test_bias_changes_selection_not_gates():
