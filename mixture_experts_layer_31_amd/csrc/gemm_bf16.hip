@@ -757,16 +757,18 @@ static hipError_t run_lds(const GemmTileMap& map, const uint16_t* xa, const int3
                       out_stride, out_row0, K, N, s, h1o, h3o, static_cast<float*>(nullptr));
 }
 
-// Workgroups of a stream-K launch: one per CU of the current device (a multiple
-// of 8, at most kStreamKMaxWorkgroups), or 0 if the count is unavailable.
-static int streamk_workgroups() {
+// Workgroups of a persistent launch: one per CU of the current device, a multiple
+// of 8 (one share per XCD), at most `cap`; 0 if the count is unavailable.
+int persistent_workgroups(int cap) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  cus = cus < kStreamKMaxWorkgroups ? cus : kStreamKMaxWorkgroups;
+  cus = cus < cap ? cus : cap;
   return cus / 8 * 8;
 }
+
+static int streamk_workgroups() { return persistent_workgroups(kStreamKMaxWorkgroups); }
 
 // Plain 256 x 256 products as stream-K (see gemm_bf16_lds_kernel) when the
 // launch has at least one tile per workgroup: the fix-up kernel follows.

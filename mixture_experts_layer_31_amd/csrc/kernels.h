@@ -137,6 +137,9 @@ struct DownArgs {
   int out_stride = 0;             // y row stride in floats (0: N)
   float* sk_part = nullptr;       // stream-K partial tiles (streamk_part_bytes), nullable
 };
+// Workgroups of a persistent launch: one per CU (a multiple of 8), at most cap; 0 if
+// the CU count is unavailable.
+int persistent_workgroups(int cap);
 // Stream-K down products: at most this many workgroups, each with one partial
 // 256 x 256 fp32 tile of scratch.
 constexpr int kStreamKMaxWorkgroups = 256;
