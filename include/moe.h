@@ -253,6 +253,12 @@ moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t
  *   that receive no row get zero gradients.
  *   ws: moe_workspace_size(cfg, MOE_STAGE_BACKWARD). T == 0 leaves the
  *   outputs untouched.
+ * Streams: all work is ordered after what precedes the call on `stream`, and
+ * everything after it on `stream` sees the results. When experts average at
+ * least 512 rows, the weights are transposed once per call on a second stream
+ * that the library keeps per device (default priority), forked from and joined
+ * back into `stream` through events; calls from several host threads take turns
+ * on it. Two calls that share a workspace must be ordered on one stream.
  * Errors: INVALID_ARG (bad config, NULL or misaligned pointer), WORKSPACE,
  * UNSUPPORTED (fp32, ep_ranks > 1, or d, d_ff, d_ff_shared not multiples of
  * 256).                                                                       */
