@@ -358,7 +358,9 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
         // the next stage's nd_stage loads are outstanding
         if (ST == 3 && kt + 1 < nk) wait_vmcnt_at_most<ND>(nd_stage);
         else MOE_WAIT_VMCNT(0);
-        __syncthreads();
+        // with three stages the next stage's loads stay in flight across it
+        if constexpr (ST == 3) dma_barrier();
+        else __syncthreads();
         const int ahead = kt + ST - 1;
         const bool more = ahead < nk;
         const int nbuf = cur == 0 ? ST - 1 : cur - 1;   // (cur + ST - 1) % ST

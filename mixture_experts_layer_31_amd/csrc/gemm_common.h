@@ -54,8 +54,23 @@ __device__ __forceinline__ void wait_vmcnt_at_most(int n) {
 // keeps vector-memory instructions on their side of this point; every other
 // instruction kind may still be scheduled across it
 #define MOE_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0x78F)
+// Workgroup barrier for pipelines with LDS-DMA loads of later stages still in
+// flight. __syncthreads() carries a workgroup fence, for which the compiler
+// waits for every outstanding vector-memory load (an LDS-DMA load counts as a
+// pending LDS write), so it would drain those stages too. Here each wave has
+// already waited (s_waitcnt vmcnt) for the loads of the stage it is about to
+// publish; the barrier then waits only for the wave's own LDS accesses
+// (lgkmcnt(0)), and the empty asm statements keep the compiler from moving any
+// memory access across it.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited on
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 #else
 #define MOE_SCHED_FENCE() ((void)0)
+__device__ __forceinline__ void dma_barrier() {}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_at_most(int) {}
 #define MOE_WAIT_VMCNT(n) ((void)0)

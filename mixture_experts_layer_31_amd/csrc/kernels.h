@@ -43,8 +43,21 @@ hipError_t launch_router_wgrad(int dtype_bf16, const float* dz, const void* x, i
 constexpr int kSelectMaxBlocks = 1024;
 int router_select_tokens(int T);   // tokens per router_select workgroup
 int router_select_blocks(int T);
+// bf16 scores: the vector-unit kernel for a few tokens (gemv), the one-block
+// MFMA kernel for up to 16 experts (narrow), else the tiled MFMA kernel's tile
+// shape (32 wt tokens x 32 we experts), expert tiles and K-splits; groups =
+// workgroups launched
+struct RouterScorePlan {
+  bool gemv = false, narrow = false;
+  int wt = 2, we = 2, n_et = 0, S = 1;
+  long long groups = 0;
+};
+RouterScorePlan router_score_plan(int T, int d, int E);
+// floats of scratch the scores need for split-K partial sums (0: none)
+size_t router_scores_part_floats(int dtype_bf16, int T, int d, int E);
+// part: router_scores_part_floats(...) floats (may be null when that is 0)
 hipError_t launch_router_scores(int dtype_bf16, const void* x, const void* w, int T, int d, int E,
-                                float* z, hipStream_t s);
+                                float* z, float* part, hipStream_t s);
 // q_part (nullable): per-block sums of the four scale statistics (z-loss,
 // entropy, top probability, top-2 gap), [blocks][kScaleStats]
 constexpr int kScaleStats = 4;

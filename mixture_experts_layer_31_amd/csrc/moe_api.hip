@@ -123,10 +123,13 @@ moe_status validate(const moe_config* c, Shape* s) {
 }
 
 // workspace sizes per stage
+size_t zpart_bytes(const Shape& s) {
+  return al(moe::router_scores_part_floats(s.bf16, s.T, s.d, s.E) * 4);
+}
 size_t route_bytes(const Shape& s) {
   return al(static_cast<size_t>(s.T) * s.E * 4) + 2 * al(static_cast<size_t>(s.nb_sel) * s.E * 4) +
          al(static_cast<size_t>(s.E) * 4) +
-         al(static_cast<size_t>(s.nb_sel) * moe::kScaleStats * 4);
+         al(static_cast<size_t>(s.nb_sel) * moe::kScaleStats * 4) + zpart_bytes(s);
 }
 size_t permute_bytes(const Shape& s) {
   return al(static_cast<size_t>(s.nb_idx + 1) * s.nkeys * 4) + 2 * al(static_cast<size_t>(s.k) * s.G * 4) +
@@ -157,7 +160,7 @@ struct Carver {
 // Workspace of moe_backward: every buffer of the recomputed forward and of the
 // backward, carved in this order (a null base only measures the size).
 struct BwdBufs {
-  float *z, *gates, *h1, *h3, *row_gate, *dg_row, *dz, *u, *dxp, *wpart, *sk;
+  float *z, *zpart, *gates, *h1, *h3, *row_gate, *dg_row, *dz, *u, *dxp, *wpart, *sk;
   int32_t *idx, *dest, *src, *offsets, *counts, *kept, *ndrop, *soff, *tiles, *tiles256;
   int32_t *blk, *slot_base, *slot_keep;
   uint16_t *act, *dyb, *dyp, *dH, *xp, *w2t, *w13t, *w2st, *w13st;
@@ -182,6 +185,7 @@ size_t backward_layout(const Shape& s, char* base, BwdBufs* b) {
   b->tr_shared = s.nsh && s.T >= kTransposeMinRows;
   const size_t dff = s.dff, dffs = s.dffs;
   b->z = cv.take<float>(T * E * 4);
+  b->zpart = cv.take<float>(zpart_bytes(s));
   b->idx = cv.take<int32_t>(T * k * 4);
   b->gates = cv.take<float>(T * k * 4);
   b->dest = cv.take<int32_t>(T * k * 4);
@@ -280,9 +284,11 @@ moe_status do_route(const Shape& s, float alpha, const void* x, const void* wr, 
   int32_t* c_part = cv.take<int32_t>(static_cast<size_t>(s.nb_sel) * s.E * 4);
   float* fp = cv.take<float>(static_cast<size_t>(s.E) * 4);
   float* q_part = cv.take<float>(static_cast<size_t>(s.nb_sel) * moe::kScaleStats * 4);
+  float* zpart = cv.take<float>(zpart_bytes(s));
   const bool stats = want_route_stats(st);
   const bool scale = stats && (st->z_loss || st->entropy || st->max_prob || st->top_gap);
-  MOE_HIP(moe::launch_router_scores(s.bf16, x, wr, s.T, s.d, s.E, z, stream), "router_scores");
+  MOE_HIP(moe::launch_router_scores(s.bf16, x, wr, s.T, s.d, s.E, z, zpart, stream),
+          "router_scores");
   MOE_HIP(moe::launch_router_select(z, bias, s.T, s.E, s.k, s.gate_all, idx, gates,
                                     stats ? p_part : nullptr, stats ? c_part : nullptr,
                                     scale ? q_part : nullptr, stream),
@@ -624,7 +630,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   }
 
   // ---- forward, recomputed: routing, index, pre-activations, activation
-  MOE_HIP(moe::launch_router_scores(1, x, w_router, T, d, E, b.z, strm), "router_scores");
+  MOE_HIP(moe::launch_router_scores(1, x, w_router, T, d, E, b.z, b.zpart, strm), "router_scores");
   MOE_HIP(moe::launch_router_select(b.z, sel_bias, T, E, k, s.gate_all, b.idx, b.gates, nullptr,
                                     nullptr, nullptr, strm),
           "router_select");

@@ -199,6 +199,59 @@ def test_router_many_experts_max_k():
     check_gates(wl, gi, gates.cpu().numpy(), r["z"])
 
 
+# (T, d, E, k): the vector-unit kernel (T <= 8, including a d that leaves masked
+# chunks), the one-block kernel (E <= 16), and the MFMA tiles of each shape,
+# unsplit and split over d (uneven split ranges, every reduction width), with T
+# and E ragged against the tiles
+_ROUTER_PATHS = {
+    "gemv": (5, 512, 40, 4),
+    "gemv_masked_chunks": (3, 6144, 16, 2),
+    "narrow_e8": (100, 512, 8, 2),
+    "narrow_e16_d_tail": (1000, 1088, 16, 2),
+    "narrow_e1": (37, 256, 1, 1),
+    "tiles_32x128_split": (20, 1024, 40, 2),
+    "tiles_128x32_split": (300, 1024, 24, 2),
+    "tiles_64x64_unsplit": (333, 256, 100, 4),
+    "tiles_64x64_split_uneven": (130, 2048, 72, 6),
+    "tiles_split_64": (40, 8192, 24, 2),
+    "tiles_split_2": (1000, 512, 64, 2),
+}
+
+
+@pytest.mark.parametrize("case", list(_ROUTER_PATHS))
+def test_router_scores_every_path(case):
+    """Every router score against the oracle's float64 z on the same bf16 operands, to
+    the worst-case bound of an fp32 sum of d exact products in any order and with
+    any rounding the adder uses, (d - 1) 2^-23 sum_i |x_i w_i|; then the routing,
+    ALL gates and statistics.
+    moe_route keeps z at the head of its workspace (T x E fp32), where it is read."""
+    T, d, E, k = _ROUTER_PATHS[case]
+    wl = _adhoc(f"router_{case}", 117, T=T, d=d, E=E, k=k, d_ff=64, dtype=wk.BF16,
+                gate=wk.GATE_ALL)
+    inp = wk.make_inputs(wl, T=T)
+    cfg = config_of(wl, T)
+    ws = moe.alloc_workspace(cfg, moe.STAGE_ROUTE)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev())
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev())
+    st = moe.Stats.alloc(E)
+    log(f"[case] router path {case} T={T} d={d} E={E}")
+    moe.route(cfg, to_dev(inp.x, wl.dtype), to_dev(inp.w_router, wl.dtype), None, idx, gates, st,
+              ws)
+    torch.cuda.synchronize()
+    z = ws[: T * E * 4].view(torch.float32).view(T, E).cpu().numpy().astype(np.float64)
+    x64 = wk.to_f64(inp.x, wl.dtype)
+    w64 = wk.to_f64(inp.w_router, wl.dtype)
+    r = om.route(x64, w64, k, gate=wl.gate)
+    bound = (d - 1) * 2.0 ** -23 * (np.abs(x64) @ np.abs(w64).T)
+    err = np.abs(z - r["z"])
+    assert (err <= bound).all(), f"{case}: max err {err.max():.3e}, worst ratio {(err / bound).max():.3f}"
+    gi = idx.cpu().numpy().astype(np.int64)
+    check_routing(wl, gi, r)
+    check_gates(wl, gi, gates.cpu().numpy(), r["z"])
+    g = {n: float(getattr(st, n).cpu()[0]) for n in ("z_loss", "entropy", "max_prob", "top_gap")}
+    check_scale_stats(g, r["z"], case)
+
+
 @pytest.mark.parametrize("std", [1, 5, 20])
 def test_router_scale_statistics(std):
     """z-loss, entropy, top probability and top-2 gap at router logits of standard
