@@ -72,18 +72,108 @@ template <> struct Elt<uint16_t> {
   }
 };
 
-// Wave-wide butterfly sum: every lane ends with the total; the pairing order is
-// fixed, so the result is deterministic.
-__device__ __forceinline__ float wave_allsum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+
+// DPP lane moves within rows of 16 lanes (gfx9 encodings): the value of the
+// lane the control names, with no trip through the LDS unit.
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowRor4 = 0x124;   // rotate the 16-lane row by 4
+constexpr int kDppRowRor8 = 0x128;   // rotate the 16-lane row by 8
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// Wave-wide max (all 64 lanes active): within each 16-lane row by DPP (after xor 1, xor 2 and the
+// row rotations by 4 and 8 every lane holds its row's max), then the four row
+// maxima through scalar registers. Max is exact, so every lane ends with the
+// same value whatever the pairing order.
 __device__ __forceinline__ float wave_allmax(float v) {
+  v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f<kDppRowRor4>(v));
+  v = fmaxf(v, dpp_f<kDppRowRor8>(v));
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)),
+               fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+
+// Wave-wide sum in a fixed order: each 16-lane row is summed by DPP steps
+// (lane 0 of row r ends with that row's sum in one fixed association), and the
+// four row sums are added in row order in scalar registers, so every lane gets
+// the same, deterministic total. Call with all 64 lanes active.
+__device__ __forceinline__ float wave_allsum(float v) {
+  v += dpp_f<kDppQuadXor1>(v);
+  v += dpp_f<kDppQuadXor2>(v);
+  v += dpp_f<kDppRowRor4>(v);
+  v += dpp_f<kDppRowRor8>(v);
+  return ((readlane_f(v, 0) + readlane_f(v, 16)) + readlane_f(v, 32)) + readlane_f(v, 48);
+}
+
+// Wave-wide argmax of (v, e): the largest v, ties to the smallest e, by the
+// same DPP steps and the four rows' winners in scalar registers; both results
+// are wave-uniform.
+__device__ __forceinline__ void wave_argmax(float& v, int& e) {
+  auto take = [&](float ov, int oe) {
+    if (ov > v || (ov == v && oe < e)) { v = ov; e = oe; }
+  };
+  { const float ov = dpp_f<kDppQuadXor1>(v); const int oe = dpp_i<kDppQuadXor1>(e); take(ov, oe); }
+  { const float ov = dpp_f<kDppQuadXor2>(v); const int oe = dpp_i<kDppQuadXor2>(e); take(ov, oe); }
+  { const float ov = dpp_f<kDppRowRor4>(v); const int oe = dpp_i<kDppRowRor4>(e); take(ov, oe); }
+  { const float ov = dpp_f<kDppRowRor8>(v); const int oe = dpp_i<kDppRowRor8>(e); take(ov, oe); }
+  float bv = readlane_f(v, 0);
+  int be = __builtin_amdgcn_readlane(e, 0);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
+  for (int r = 1; r < 4; ++r) {
+    const float ov = readlane_f(v, 16 * r);
+    const int oe = __builtin_amdgcn_readlane(e, 16 * r);
+    if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+  }
+  v = bv;
+  e = be;
+}
+
+// Inclusive prefix sum of an int over the wave's 64 lanes (all active): DPP
+// row shifts by 1, 2, 4 and 8 scan each 16-lane row (a lane with no source in
+// its row adds 0), then each row adds the totals of the rows before it, read
+// from lanes 15, 31 and 47.
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
+// Inclusive prefix sum over a workgroup of 1024 threads, in thread order: a
+// wave scan, then each wave adds the totals of the waves before it (wtot: 16
+// ints of LDS). *total receives the sum over all threads. Every thread of the
+// workgroup must call it; it holds two barriers.
+__device__ __forceinline__ int block_scan_1024(int v, int* wtot, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  v = wave_inclusive_scan(v, lane);
+  if (lane == 63) wtot[wv] = v;
+  __syncthreads();
+  int add = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int t = wtot[w];
+    add += w < wv ? t : 0;
+    all += t;
+  }
+  __syncthreads();   // wtot is free for the next call
+  *total = all;
+  return v + add;
 }
 
 __device__ __forceinline__ int wave_allsum_int(int v) {

@@ -213,7 +213,8 @@ __device__ __forceinline__ int real_tiles(const int32_t* tiles, int max_tiles, i
 // eighth. With shares of at least one tile's K-steps a tile is split at most
 // once: its last part writes out, its first part writes the fp32 tile to
 // sk_part slot p (the share's end), and streamk_fixup_kernel adds it after.
-template <int BM, int BN, int WM, int WN, bool GATEUP, int ST, bool HOUT = false, bool SK = false>
+template <int BM, int BN, int WM, int WN, bool GATEUP, int ST, bool HOUT = false, bool SK = false,
+          bool NF = false>
 __global__ __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_lds_kernel(
     const int32_t* __restrict__ tiles, int max_tiles, int n_single, int n_logical,
@@ -448,7 +449,8 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
 
   if constexpr (!SK) {
     int m_tile, n_tile;
-    xcd_tile(n_logical, max_tiles, m_tile, n_tile);
+    if constexpr (NF) xcd_tile_nfast(max_tiles, N / BN, m_tile, n_tile);
+    else xcd_tile(n_logical, max_tiles, m_tile, n_tile);
     if (m_tile < 0) return;
     run_tile(m_tile, n_tile, 0, nk_all, nullptr);
   } else {
@@ -629,6 +631,24 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
   }
 }
 
+// Decode launch shape, measured on MI355X from cold caches over the Mixtral,
+// DeepSeek and Switch shapes at 1-32 tokens: K split over KS = 4 waves while
+// the items are few and the groups hold at most 2 rows (more waves in flight
+// per weight byte), fewer splits as either grows; batches of U = 8 steps,
+// or 4 when a wave's K range is short (one batch) or, in the down product,
+// very long (more waves per SIMD in place of deeper batches).
+template <bool GATEUP, int U, int KS>
+static void launch_stream(long long items, const GemmTileMap& map, int m_tiles,
+                          const uint16_t* xa, const int32_t* src, int a_stride, int a_row0,
+                          const uint16_t* wa, const uint16_t* wb, long long w_stride, void* out,
+                          int out_stride, int out_row0, int K, int N, hipStream_t s) {
+  constexpr int IPB = 4 / KS;
+  gemm_bf16_stream_kernel<GATEUP, U, KS>
+      <<<dim3(static_cast<unsigned>((items + IPB - 1) / IPB)), dim3(256), 0, s>>>(
+          map.tiles, m_tiles, map.n_single, xa, src, a_stride, a_row0, wa, wb, w_stride, out,
+          out_stride, out_row0, K, N);
+}
+
 template <bool GATEUP>
 static hipError_t run_stream(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
                              int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
@@ -636,21 +656,23 @@ static hipError_t run_stream(const GemmTileMap& map, const uint16_t* xa, const i
                              int N, hipStream_t s) {
   const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + 15) / 16;
   const long long items = static_cast<long long>(m_tiles) * (N / 16);
-  // real items (upper bound): split K when there are too few waves to keep
-  // enough weight bytes in flight across the 1024 SIMDs
-  if (items < 2048) {
-    gemm_bf16_stream_kernel<GATEUP, 8, 4><<<dim3(static_cast<unsigned>(items)), dim3(256), 0, s>>>(
-        map.tiles, m_tiles, map.n_single, xa, src, a_stride, a_row0, wa, wb, w_stride, out,
-        out_stride, out_row0, K, N);
-  } else if (items < 8192) {
-    gemm_bf16_stream_kernel<GATEUP, 8, 2><<<dim3(static_cast<unsigned>((items + 1) / 2)), dim3(256), 0, s>>>(
-        map.tiles, m_tiles, map.n_single, xa, src, a_stride, a_row0, wa, wb, w_stride, out,
-        out_stride, out_row0, K, N);
+  const int avg = map.tiles ? map.avg_rows : map.n_single;
+  int KS = 1;
+  if (items < 8192 && avg <= 2) KS = 4;
+  else if (items < 16384 && avg <= 4) KS = 2;
+  const int steps = K / 32 / KS;
+  const bool u4 = steps < 16 || (!GATEUP && steps >= 100);
+#define MOE_STREAM(U_, KS_)                                                                  \
+  launch_stream<GATEUP, U_, KS_>(items, map, m_tiles, xa, src, a_stride, a_row0, wa, wb,     \
+                                 w_stride, out, out_stride, out_row0, K, N, s)
+  if (KS == 4) {
+    if (u4) MOE_STREAM(4, 4); else MOE_STREAM(8, 4);
+  } else if (KS == 2) {
+    if (u4) MOE_STREAM(4, 2); else MOE_STREAM(8, 2);
   } else {
-    gemm_bf16_stream_kernel<GATEUP, 8, 1><<<dim3(static_cast<unsigned>((items + 3) / 4)), dim3(256), 0, s>>>(
-        map.tiles, m_tiles, map.n_single, xa, src, a_stride, a_row0, wa, wb, w_stride, out,
-        out_stride, out_row0, K, N);
+    if (u4) MOE_STREAM(4, 1); else MOE_STREAM(8, 1);
   }
+#undef MOE_STREAM
   return hipGetLastError();
 }
 
@@ -659,7 +681,7 @@ static hipError_t run_stream(const GemmTileMap& map, const uint16_t* xa, const i
 __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restrict__ offsets,
                                                         int E, int BM, int max_tiles, int ep,
                                                         int4* __restrict__ tiles) {
-  __shared__ int part[1024];
+  __shared__ int part[16];
   const int e = threadIdx.x;
   int lo = 0, n = 0, nt = 0;
   if (e < E) {
@@ -667,18 +689,11 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
     n = offsets[e + 1] - lo;
     nt = (n + BM - 1) / BM;
   }
-  part[e] = nt;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = e >= off ? part[e - off] : 0;
-    __syncthreads();
-    part[e] += v;
-    __syncthreads();
-  }
-  const int start = part[e] - nt;
-  const int total = part[1023];
+  int total = 0;
+  const int start = block_scan_1024(nt, part, &total) - nt;
   const int w = tile_group_weights(e, E, ep);
-  for (int i = 0; i < nt; ++i) tiles[start + i] = make_int4(w, lo + i * BM, min(BM, n - i * BM), 0);
+  for (int i = 0; i < nt && start + i < max_tiles; ++i)
+    tiles[start + i] = make_int4(w, lo + i * BM, min(BM, n - i * BM), 0);
   for (int i = total + e; i < max_tiles; i += 1024) tiles[i] = make_int4(0, 0, 0, 0);
 }
 
@@ -693,6 +708,15 @@ int gemm_tile_rows(int dtype_bf16, int R_max, int groups, bool n256_ok) {
   // one 256-row tile covers a group of up to 256 rows, so each expert's weight
   // panel is read once; the MFMAs and loads of a tail's empty rows are skipped
   return 256;
+}
+
+// Measured on MI355X from cold caches (DeepSeek shape, 256 groups of ~128 rows:
+// gate/up -9 %, down -10 % against the m-fastest order with stream-K; 64 groups:
+// -2 % and -11 %); with 8 groups the m-fastest order stays ahead.
+constexpr int kNFastMinGroups = 32;
+
+bool gemm_n_fast(int BM, long long R_max, int groups) {
+  return BM == 256 && groups >= kNFastMinGroups && R_max <= 256LL * groups;
 }
 
 int gemm_max_tiles(int BM, int R_max, int E) {
@@ -710,7 +734,7 @@ hipError_t launch_tile_map(const int32_t* offsets, int E, int BM, int max_tiles,
 // ---------------------------------------------------------------- launchers
 
 template <typename Kern, typename... Extra>
-static hipError_t launch_tiled(Kern kern, int BM, int BN, int threads, size_t lds,
+static hipError_t launch_tiled(Kern kern, bool n_fast, int BM, int BN, int threads, size_t lds,
                                const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
                                int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
                                long long w_stride, void* out, int out_stride, int out_row0, int K,
@@ -721,7 +745,7 @@ static hipError_t launch_tiled(Kern kern, int BM, int BN, int threads, size_t ld
   }
   const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + BM - 1) / BM;
   const long long n_logical = static_cast<long long>(m_tiles) * (N / BN);
-  const long long grid = ((n_logical + 7) / 8) * 8;
+  const long long grid = n_fast ? 8LL * ((m_tiles + 7) / 8) * (N / BN) : ((n_logical + 7) / 8) * 8;
   kern<<<dim3(static_cast<unsigned>(grid)), dim3(threads), lds, s>>>(
       map.tiles, m_tiles, map.n_single, static_cast<int>(n_logical), xa, src, a_stride, a_row0,
       wa, wb, w_stride, out, out_stride, out_row0, K, N, extra...);
@@ -736,7 +760,7 @@ static hipError_t run_small(const GemmTileMap& map, const uint16_t* xa, const in
                             int N, hipStream_t s) {
   constexpr int WR = GATEUP ? 2 * BN : BN;
   const size_t lds = static_cast<size_t>(2) * (BM + WR) * kPitch * sizeof(uint16_t);
-  return launch_tiled(gemm_bf16_kernel<BM, BN, WM, WN, GATEUP>, BM, BN, 64 * WM * WN, lds, map,
+  return launch_tiled(gemm_bf16_kernel<BM, BN, WM, WN, GATEUP>, false, BM, BN, 64 * WM * WN, lds, map,
                       xa, src, a_stride, a_row0, wa, wb, w_stride, out, out_stride, out_row0, K,
                       N, s);
 }
@@ -745,7 +769,7 @@ static hipError_t run_small(const GemmTileMap& map, const uint16_t* xa, const in
 // Three LDS stages where they fit (256 x 128 down tiles: 3 x 48 KB), which
 // keeps two stages of loads in flight per CU; those tiles serve short groups,
 // where the weights stream from HBM and load latency matters most.
-template <int BM, int BN, int WM, int WN, bool GATEUP, bool HOUT = false>
+template <int BM, int BN, int WM, int WN, bool GATEUP, bool HOUT = false, bool NF = false>
 static hipError_t run_lds(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
                           int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
                           long long w_stride, void* out, int out_stride, int out_row0, int K,
@@ -754,7 +778,7 @@ static hipError_t run_lds(const GemmTileMap& map, const uint16_t* xa, const int3
   constexpr size_t kStage = static_cast<size_t>(BM + WR) * kRowBytes;
   constexpr int ST = 3 * kStage <= kMaxLdsBytes ? 3 : 2;
   const size_t lds = ST * kStage;
-  return launch_tiled(gemm_bf16_lds_kernel<BM, BN, WM, WN, GATEUP, ST, HOUT>, BM, BN,
+  return launch_tiled(gemm_bf16_lds_kernel<BM, BN, WM, WN, GATEUP, ST, HOUT, false, NF>, NF, BM, BN,
                       64 * WM * WN, lds, map, xa, src, a_stride, a_row0, wa, wb, w_stride, out,
                       out_stride, out_row0, K, N, s, h1o, h3o, static_cast<float*>(nullptr));
 }
@@ -806,10 +830,17 @@ hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, 
   const auto* w3 = static_cast<const uint16_t*>(a.w3);
   if (a.h1 != nullptr) {   // pre-activations too: 256-row tiles only
     if (BM != 256 || a.h3 == nullptr) return hipErrorInvalidValue;
+    if (map.n_fast)
+      return run_lds<256, 128, 2, 4, true, true, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride,
+                                                       a.act, a.act_stride, a.out_row0, a.K, a.N,
+                                                       s, a.h1, a.h3);
     return run_lds<256, 128, 2, 4, true, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
                                                a.act_stride, a.out_row0, a.K, a.N, s, a.h1,
                                                a.h3);
   }
+  if (BM == 256 && map.n_fast)
+    return run_lds<256, 128, 2, 4, true, false, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride,
+                                                      a.act, a.act_stride, a.out_row0, a.K, a.N, s);
   if (BM == 256)
     return run_lds<256, 128, 2, 4, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
                                          a.act_stride, a.out_row0, a.K, a.N, s);
@@ -833,6 +864,11 @@ hipError_t launch_gemm_down_bf16(const GemmTileMap& map, const DownArgs& a, int 
   const int ys = a.out_stride > 0 ? a.out_stride : a.N;
   const auto* act = static_cast<const uint16_t*>(a.act);
   const auto* w2 = static_cast<const uint16_t*>(a.w2);
+  // weight-streaming shapes: 256 x 128 tiles (three LDS stages) in n-fastest order
+  if (BM == 256 && map.n_fast && a.N % 128 == 0)
+    return run_lds<256, 128, 2, 4, false, false, true>(map, act, a.src, a.act_stride, a.in_row0,
+                                                       w2, nullptr, a.w_stride, a.y, ys,
+                                                       a.out_row0, a.K, a.N, s);
   if (BM == 256) {
     const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + BM - 1) / BM;
     if (gemm_down_cols(BM, m_tiles, a.N) == 128)

@@ -25,7 +25,8 @@ __device__ __forceinline__ TileCoord lookup_tile(const int32_t* tiles, int n_sin
   return c;
 }
 
-// Launch index -> (m_tile, n_tile), XCD-contiguous (see the file comment).
+// Launch index -> (m_tile, n_tile), XCD-contiguous (see the file comment):
+// m fastest over a contiguous range of (n, m) pairs per XCD.
 __device__ __forceinline__ void xcd_tile(int n_logical, int max_tiles, int& m_tile, int& n_tile) {
   const int L = blockIdx.x;
   const int per = (n_logical + 7) >> 3;
@@ -33,6 +34,20 @@ __device__ __forceinline__ void xcd_tile(int n_logical, int max_tiles, int& m_ti
   if (logical >= n_logical) { m_tile = -1; n_tile = 0; return; }
   m_tile = logical % max_tiles;
   n_tile = logical / max_tiles;
+}
+
+// Launch index -> (m_tile, n_tile) with the n tiles of one m tile in a row on
+// one XCD: m tile m runs on XCD m % 8, its n_tiles tiles consecutively, so the
+// workgroups that share its token rows share an L2 and stream neighbouring
+// panels of one weight matrix at the same time; the empty m tiles at the end of
+// the table fall evenly on all XCDs. Grid: 8 * ceil(max_tiles / 8) * n_tiles.
+__device__ __forceinline__ void xcd_tile_nfast(int max_tiles, int n_tiles, int& m_tile,
+                                               int& n_tile) {
+  const int L = blockIdx.x;
+  const int j = L >> 3;
+  m_tile = (j / n_tiles) * 8 + (L & 7);
+  n_tile = j % n_tiles;
+  if (m_tile >= max_tiles) m_tile = -1;
 }
 
 #if defined(__HIP_DEVICE_COMPILE__)

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(1024) void index_scan_kernel(
     int32_t* __restrict__ slot_base, int32_t* __restrict__ slot_keep,
     int32_t* __restrict__ offsets, int32_t* __restrict__ counts_out,
     int32_t* __restrict__ kept_out, int32_t* __restrict__ n_dropped) {
-  __shared__ int32_t part[1024];
+  __shared__ int32_t part[16];
   const int cap = C >= 0;
   const int nkeys = cap ? E * k : E;
   int32_t* tot = blk + static_cast<size_t>(nb) * nkeys;   // row nb holds the key totals
@@ -111,19 +111,13 @@ __global__ __launch_bounds__(1024) void index_scan_kernel(
     if (counts_out) counts_out[e] = cnt;
     if (kept_out) kept_out[e] = keep_e;
   }
-  // exclusive scan of kept over experts (E <= 1024 = blockDim.x)
-  part[threadIdx.x] = (e < E) ? keep_e : 0;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
-  }
-  if (e < E) offsets[e + 1] = part[e];
+  // scan of kept over experts (E <= 1024 = blockDim.x)
+  int kept_total = 0;
+  const int incl = block_scan_1024((e < E) ? keep_e : 0, part, &kept_total);
+  if (e < E) offsets[e + 1] = incl;
   if (threadIdx.x == 0) {
     offsets[0] = 0;
-    if (n_dropped) n_dropped[0] = T * k - part[E - 1];
+    if (n_dropped) n_dropped[0] = T * k - kept_total;
   }
 }
 
@@ -237,7 +231,7 @@ __global__ __launch_bounds__(1024) void index_single_kernel(
   int32_t* sbase = tot + nkeys;                                     // [nkeys]
   int32_t* skeep = sbase + nkeys;                                   // [nkeys]
   int32_t* off = skeep + nkeys;                                     // [E + 1]
-  int32_t* part = off + (E + 1);                                    // [1024]
+  int32_t* part = off + (E + 1);                                    // [16]
   const int tid = threadIdx.x;
 
   for (int i = tid; i < nkeys * kWords; i += 1024) bm[i] = 0u;
@@ -279,19 +273,13 @@ __global__ __launch_bounds__(1024) void index_single_kernel(
     if (counts_out) counts_out[e] = cnt;
     if (kept_out) kept_out[e] = keep_e;
   }
-  part[tid] = (e < E) ? keep_e : 0;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  if (e < E) { off[e + 1] = part[e]; offsets[e + 1] = part[e]; }
+  int kept_total = 0;
+  const int incl = block_scan_1024((e < E) ? keep_e : 0, part, &kept_total);
+  if (e < E) { off[e + 1] = incl; offsets[e + 1] = incl; }
   if (tid == 0) {
     off[0] = 0;
     offsets[0] = 0;
-    if (n_dropped) n_dropped[0] = T * k - part[E - 1];
+    if (n_dropped) n_dropped[0] = T * k - kept_total;
   }
   __syncthreads();
 
@@ -332,24 +320,16 @@ __global__ __launch_bounds__(1024) void index_single_kernel(
     n = off[e + 1] - lo;
     nt = (n + BM - 1) / BM;
   }
-  __syncthreads();            // every thread has read part[] above
-  part[tid] = nt;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  const int start = part[tid] - nt;
-  const int total = part[1023];
+  int total = 0;
+  const int start = block_scan_1024(nt, part, &total) - nt;
   const int w = tile_group_weights(e, E, ep);
-  for (int i = 0; i < nt; ++i) tiles[start + i] = make_int4(w, lo + i * BM, min(BM, n - i * BM), 0);
+  for (int i = 0; i < nt && start + i < max_tiles; ++i)
+    tiles[start + i] = make_int4(w, lo + i * BM, min(BM, n - i * BM), 0);
   for (int i = total + tid; i < max_tiles; i += 1024) tiles[i] = make_int4(0, 0, 0, 0);
 }
 
 static size_t index_single_lds(int E, int nkeys) {
-  return (static_cast<size_t>(nkeys) * (kWords + 3) + (E + 1) + 1024) * sizeof(uint32_t);
+  return (static_cast<size_t>(nkeys) * (kWords + 3) + (E + 1) + 16) * sizeof(uint32_t);
 }
 
 bool index_single_ok(int T, int E, int k, bool cap) {

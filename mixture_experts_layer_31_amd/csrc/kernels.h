@@ -115,7 +115,14 @@ struct GemmTileMap {
   const int32_t* tiles;   // [max_tiles][4], or nullptr for one group of n_single rows
   int max_tiles;
   int n_single;
+  bool n_fast = false;    // 256-row tiles: run the n tiles of each m tile together
+  int avg_rows = 0;       // rows per non-empty group on average (decode kernels; 0: unknown)
 };
+
+// Tile order of the 256-row kernels for R_max rows in G groups: n tiles fastest
+// (gemm_bf16.hip, xcd_tile_nfast) when there are many groups of at most one
+// tile each on average, which makes those products weight-streaming.
+bool gemm_n_fast(int BM, long long R_max, int groups);
 
 // BM of the grouped GEMMs for R_max rows in `groups` groups; n256_ok: d is a
 // multiple of 256 and d_ff (and d_ff_shared) of 128, as the large tiles need

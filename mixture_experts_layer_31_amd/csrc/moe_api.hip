@@ -327,10 +327,16 @@ moe_status do_permute(const Shape& s, const int32_t* idx, const void* x, int32_t
   return MOE_OK;
 }
 
+// rows per non-empty group on average (at most R groups hold rows)
+int avg_group_rows(const Shape& s) {
+  const int g = s.G < s.R ? s.G : s.R;
+  return g > 0 ? s.R / g : 0;
+}
+
 moe_status do_gateup(const Shape& s, const void* x, const int32_t* src, const int32_t* tiles,
                      const void* w1, const void* w3, const void* ws1, const void* ws3, void* act,
                      hipStream_t stream) {
-  moe::GemmTileMap map{tiles, s.max_tiles, 0};
+  moe::GemmTileMap map{tiles, s.max_tiles, 0, moe::gemm_n_fast(s.BM, s.R, s.G), avg_group_rows(s)};
   moe::GateUpArgs a{x, src, w1, w3, static_cast<long long>(s.dff) * s.d, act, s.act_stride, 0,
                     s.d, s.dff};
   if (s.bf16) MOE_HIP(moe::launch_gemm_gateup_bf16(map, a, s.BM, stream), "gemm_gateup");
@@ -347,7 +353,7 @@ moe_status do_gateup(const Shape& s, const void* x, const int32_t* src, const in
 
 moe_status do_down(const Shape& s, const void* act, const int32_t* tiles, const void* w2,
                    const void* ws2, float* y_perm, float* sk_part, hipStream_t stream) {
-  moe::GemmTileMap map{tiles, s.max_tiles, 0};
+  moe::GemmTileMap map{tiles, s.max_tiles, 0, moe::gemm_n_fast(s.BM, s.R, s.G), avg_group_rows(s)};
   moe::DownArgs a{act, s.act_stride, 0, w2, static_cast<long long>(s.d) * s.dff, y_perm, 0, s.dff, s.d};
   a.sk_part = sk_part;
   if (s.bf16) MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, stream), "gemm_down");
@@ -637,7 +643,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   MOE_HIP(moe::launch_index(b.idx, T, k, E, s.C, b.blk, b.slot_base, b.slot_keep, b.offsets, b.dest,
                             b.src, b.counts, b.kept, b.ndrop, s.BM, s.max_tiles, 1, b.tiles, strm),
           "index");
-  const moe::GemmTileMap map{b.tiles, s.max_tiles, 0};
+  const moe::GemmTileMap map{b.tiles, s.max_tiles, 0, moe::gemm_n_fast(s.BM, s.R, E),
+                            avg_group_rows(s)};
   const moe::GemmTileMap map1{nullptr, 0, T};
   const int bm1 = moe::gemm_tile_rows(1, T, 1, s.n256);
   // the K-major products run 256-row tiles

@@ -466,18 +466,13 @@ __global__ __launch_bounds__(256) void router_select_kernel(
         const int e = lane + 64 * i;
         if (e < E && (sl[i] > bv || (sl[i] == bv && e < be))) { bv = sl[i]; be = e; }
       }
-#pragma unroll
-      for (int msk = 32; msk >= 1; msk >>= 1) {
-        const float ov = __shfl_xor(bv, msk, 64);
-        const int oe = __shfl_xor(be, msk, 64);
-        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-      }
+      wave_argmax(bv, be);
       const int owner = be & 63, slot = be >> 6;
       float zsel = 0.f;
 #pragma unroll
       for (int i = 0; i < NE; ++i)
         if (i == slot) zsel = zl[i];
-      zsel = __shfl(zsel, owner, 64);
+      zsel = readlane_f(zsel, owner);
       // the winner cannot win again: its score becomes -inf while at least
       // E - r - 1 >= 1 unselected experts keep finite scores
       if (lane == owner) {
