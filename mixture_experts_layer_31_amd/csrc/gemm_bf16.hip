@@ -213,8 +213,15 @@ __device__ __forceinline__ int real_tiles(const int32_t* tiles, int max_tiles, i
 // eighth. With shares of at least one tile's K-steps a tile is split at most
 // once: its last part writes out, its first part writes the fp32 tile to
 // sk_part slot p (the share's end), and streamk_fixup_kernel adds it after.
+// LDS ring of a K loop: st stages of `stage` bytes, the token rows in the first
+// xb bytes of each, loads issued in sl slices per K-step.
+template <int ST_, int XB_, int STAGE_, int SL_>
+struct LdsRing {
+  static constexpr int st = ST_, xb = XB_, stage = STAGE_, sl = SL_;
+};
+
 template <int BM, int BN, int WM, int WN, bool GATEUP, int ST, bool HOUT = false, bool SK = false,
-          bool NF = false>
+          bool NF = false, int XS = 0>
 __global__ __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_lds_kernel(
     const int32_t* __restrict__ tiles, int max_tiles, int n_single, int n_logical,
@@ -239,6 +246,13 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
   // by ST - 1 steps (with three stages every slice still has a full step of
   // latency to hide)
   constexpr int SL = ST == 3 ? kDmaSlices3 : kDmaSlices;
+  // XS > 0: tiles of at most XS rows run a three-stage ring whose stages hold
+  // only XS token rows (the LDS holds three of those but two full stages)
+  static_assert(XS == 0 || (XS % 32 == 0 && XS < BM && 3 * (XS + WR) * kRowBytes <= kMaxLdsBytes),
+                "three short stages must fit");
+  using FullRing = LdsRing<ST, XBYTES, STAGE, SL>;
+  using ShortRing = LdsRing<3, (XS > 0 ? XS : BM) * kRowBytes, ((XS > 0 ? XS : BM) + WR) * kRowBytes,
+                            kDmaSlices3>;
 
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[];
 
@@ -280,14 +294,15 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
     // the stage's XD + WD LDS-DMA instructions, issued in slices: instruction j
     // goes out in slice j * kDmaSlices / (XD + WD)
     constexpr int ND = XD + WD;
-    auto dma_slice = [&](int kt, int buf, auto slice_c) {
+    auto dma_slice = [&](int kt, int buf, auto slice_c, auto ring) {
+      using R = decltype(ring);
       constexpr int S = decltype(slice_c)::value;
       const int ko = (kt0 + kt) * kBK;
-      unsigned char* xs = lds_raw + buf * STAGE;
-      unsigned char* ws = xs + XBYTES;
+      unsigned char* xs = lds_raw + buf * R::stage;
+      unsigned char* ws = xs + R::xb;
 #pragma unroll
       for (int j = 0; j < ND; ++j) {
-        if (j * SL / ND != S) continue;
+        if (j * R::sl / ND != S) continue;
         if (j < XD) {
           // token rows past the tile's last row are never stored: skip their loads
           if (8 * (j * NW + wave) < tc.rows) MOE_LDS_DMA16(xg[j] + ko, xs + (j * NW + wave) * 1024);
@@ -296,11 +311,11 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
         }
       }
     };
-    auto dma = [&](int kt, int buf) {
-      dma_slice(kt, buf, std::integral_constant<int, 0>{});
-      dma_slice(kt, buf, std::integral_constant<int, 1>{});
-      dma_slice(kt, buf, std::integral_constant<int, 2>{});
-      dma_slice(kt, buf, std::integral_constant<int, 3>{});
+    auto dma = [&](int kt, int buf, auto ring) {
+      dma_slice(kt, buf, std::integral_constant<int, 0>{}, ring);
+      dma_slice(kt, buf, std::integral_constant<int, 1>{}, ring);
+      dma_slice(kt, buf, std::integral_constant<int, 2>{}, ring);
+      dma_slice(kt, buf, std::integral_constant<int, 3>{}, ring);
     };
 
     f32x16 acc[MT][NTW];
@@ -319,10 +334,11 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
     // token block a of wave row wm is the tile's 32-row block a*WM + wm: the
     // blocks of a short (ragged-tail) tile are shared by all wave rows
     bf16x8 fa[4][NTW], fb[4][MT];
-    auto rfrag = [&](int buf, int kk, auto na_c) {
+    auto rfrag = [&](int buf, int kk, auto na_c, auto ring) {
+      using R = decltype(ring);
       constexpr int NA = decltype(na_c)::value;
-      const unsigned char* xs = lds_raw + buf * STAGE;
-      const unsigned char* ws = xs + XBYTES;
+      const unsigned char* xs = lds_raw + buf * R::stage;
+      const unsigned char* ws = xs + R::xb;
 #pragma unroll
       for (int b = 0; b < NTW; ++b) {
         const int wrow = (b < NT) ? wn * (BN / WN) + b * 32 : BN + wn * (BN / WN) + (b - NT) * 32;
@@ -350,42 +366,48 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
     int nd_stage = WD;                 // LDS-DMA instructions this wave issues per stage
 #pragma unroll
     for (int j = 0; j < XD; ++j) nd_stage += 8 * (j * NW + wave) < tc.rows ? 1 : 0;
-    auto kloop = [&](auto na_c) {
-      if (nk > 0) dma(0, 0);
-      if (ST == 3 && nk > 1) dma(1, 1);
+    auto kloop = [&](auto na_c, auto ring) {
+      using R = decltype(ring);
+      constexpr int RS = R::st;
+      if (nk > 0) dma(0, 0, ring);
+      if (RS == 3 && nk > 1) dma(1, 1, ring);
       int cur = 0;
       for (int kt = 0; kt < nk; ++kt) {
         // loads complete in issue order: stage kt has landed once no more than
         // the next stage's nd_stage loads are outstanding
-        if (ST == 3 && kt + 1 < nk) wait_vmcnt_at_most<ND>(nd_stage);
+        if (RS == 3 && kt + 1 < nk) wait_vmcnt_at_most<ND>(nd_stage);
         else MOE_WAIT_VMCNT(0);
         // with three stages the next stage's loads stay in flight across it
-        if constexpr (ST == 3) dma_barrier();
+        if constexpr (RS == 3) dma_barrier();
         else __syncthreads();
-        const int ahead = kt + ST - 1;
+        const int ahead = kt + RS - 1;
         const bool more = ahead < nk;
-        const int nbuf = cur == 0 ? ST - 1 : cur - 1;   // (cur + ST - 1) % ST
-        if (more) dma_slice(ahead, nbuf, std::integral_constant<int, 0>{});
+        const int nbuf = cur == 0 ? RS - 1 : cur - 1;   // (cur + RS - 1) % RS
+        if (more) dma_slice(ahead, nbuf, std::integral_constant<int, 0>{}, ring);
         MOE_SCHED_FENCE();
-        rfrag(cur, 0, na_c);
-        rfrag(cur, 1, na_c);
+        rfrag(cur, 0, na_c, ring);
+        rfrag(cur, 1, na_c, ring);
         mfmas(0, na_c);
-        if (more && SL > 1) dma_slice(ahead, nbuf, std::integral_constant<int, 1>{});
+        if (more && R::sl > 1) dma_slice(ahead, nbuf, std::integral_constant<int, 1>{}, ring);
         MOE_SCHED_FENCE();
-        rfrag(cur, 2, na_c);
+        rfrag(cur, 2, na_c, ring);
         mfmas(1, na_c);
-        if (more && SL > 2) dma_slice(ahead, nbuf, std::integral_constant<int, 2>{});
+        if (more && R::sl > 2) dma_slice(ahead, nbuf, std::integral_constant<int, 2>{}, ring);
         MOE_SCHED_FENCE();
-        rfrag(cur, 3, na_c);
+        rfrag(cur, 3, na_c, ring);
         mfmas(2, na_c);
-        if (more && SL > 3) dma_slice(ahead, nbuf, std::integral_constant<int, 3>{});
+        if (more && R::sl > 3) dma_slice(ahead, nbuf, std::integral_constant<int, 3>{}, ring);
         MOE_SCHED_FENCE();
         mfmas(3, na_c);
-        cur = cur + 1 == ST ? 0 : cur + 1;
+        cur = cur + 1 == RS ? 0 : cur + 1;
       }
     };
     const int nb = (min(tc.rows, BM) + 31) / 32;
-    with_count<MT>((nb - wm + WM - 1) / WM, kloop);
+    const int na_count = (nb - wm + WM - 1) / WM;
+    if (XS > 0 && tc.rows <= XS)
+      with_count<MT>(na_count, [&](auto na_c) { kloop(na_c, ShortRing{}); });
+    else
+      with_count<MT>(na_count, [&](auto na_c) { kloop(na_c, FullRing{}); });
 
     if constexpr (SK) {
       if (part != nullptr) {
@@ -769,7 +791,8 @@ static hipError_t run_small(const GemmTileMap& map, const uint16_t* xa, const in
 // Three LDS stages where they fit (256 x 128 down tiles: 3 x 48 KB), which
 // keeps two stages of loads in flight per CU; those tiles serve short groups,
 // where the weights stream from HBM and load latency matters most.
-template <int BM, int BN, int WM, int WN, bool GATEUP, bool HOUT = false, bool NF = false>
+template <int BM, int BN, int WM, int WN, bool GATEUP, bool HOUT = false, bool NF = false,
+          int XS = 0>
 static hipError_t run_lds(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
                           int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
                           long long w_stride, void* out, int out_stride, int out_row0, int K,
@@ -777,8 +800,9 @@ static hipError_t run_lds(const GemmTileMap& map, const uint16_t* xa, const int3
   constexpr int WR = GATEUP ? 2 * BN : BN;
   constexpr size_t kStage = static_cast<size_t>(BM + WR) * kRowBytes;
   constexpr int ST = 3 * kStage <= kMaxLdsBytes ? 3 : 2;
-  const size_t lds = ST * kStage;
-  return launch_tiled(gemm_bf16_lds_kernel<BM, BN, WM, WN, GATEUP, ST, HOUT, false, NF>, NF, BM, BN,
+  constexpr size_t kShort = XS > 0 ? 3 * static_cast<size_t>(XS + WR) * kRowBytes : 0;
+  const size_t lds = ST * kStage > kShort ? ST * kStage : kShort;
+  return launch_tiled(gemm_bf16_lds_kernel<BM, BN, WM, WN, GATEUP, ST, HOUT, false, NF, XS>, NF, BM, BN,
                       64 * WM * WN, lds, map, xa, src, a_stride, a_row0, wa, wb, w_stride, out,
                       out_stride, out_row0, K, N, s, h1o, h3o, static_cast<float*>(nullptr));
 }
@@ -821,6 +845,13 @@ static hipError_t run_lds_streamk(const GemmTileMap& map, const uint16_t* xa, co
   return hipGetLastError();
 }
 
+// Token rows of the short three-stage ring of the 256 x 128 gate/up tiles:
+// 3 x (160 + 256) x 128 B = 156 KB of LDS. Measured from cold caches: gate/up
+// at the DeepSeek shape (4096 tokens) 3.22 -> 3.06 ms with the shared expert,
+// Mixtral shape at 512 tokens 0.43 -> 0.39 ms; with full tiles (4096 tokens) the
+// larger LDS allotment cost 1-3 %, hence the average-rows condition.
+constexpr int kShortRingRows = 160;
+
 // BM = 256 needs N % 256 == 0 (down) / N % 128 == 0 (gate/up); the
 // caller picks BM with gemm_tile_rows(), which checks that.
 hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, int BM,
@@ -828,19 +859,29 @@ hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, 
   const auto* x = static_cast<const uint16_t*>(a.x);
   const auto* w1 = static_cast<const uint16_t*>(a.w1);
   const auto* w3 = static_cast<const uint16_t*>(a.w3);
+  // groups of at most kShortRingRows rows on average: tiles that short take
+  // three LDS stages of kShortRingRows token rows (gemm_bf16_lds_kernel, XS)
+  const bool short_ring = map.tiles != nullptr && map.avg_rows > 0 && map.avg_rows <= kShortRingRows;
   if (a.h1 != nullptr) {   // pre-activations too: 256-row tiles only
     if (BM != 256 || a.h3 == nullptr) return hipErrorInvalidValue;
     if (map.n_fast)
-      return run_lds<256, 128, 2, 4, true, true, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride,
-                                                       a.act, a.act_stride, a.out_row0, a.K, a.N,
-                                                       s, a.h1, a.h3);
+      return run_lds<256, 128, 2, 4, true, true, true, kShortRingRows>(
+          map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act, a.act_stride, a.out_row0, a.K, a.N, s,
+          a.h1, a.h3);
+    if (short_ring)
+      return run_lds<256, 128, 2, 4, true, true, false, kShortRingRows>(
+          map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act, a.act_stride, a.out_row0, a.K, a.N, s,
+          a.h1, a.h3);
     return run_lds<256, 128, 2, 4, true, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
                                                a.act_stride, a.out_row0, a.K, a.N, s, a.h1,
                                                a.h3);
   }
   if (BM == 256 && map.n_fast)
-    return run_lds<256, 128, 2, 4, true, false, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride,
-                                                      a.act, a.act_stride, a.out_row0, a.K, a.N, s);
+    return run_lds<256, 128, 2, 4, true, false, true, kShortRingRows>(
+        map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act, a.act_stride, a.out_row0, a.K, a.N, s);
+  if (BM == 256 && short_ring)
+    return run_lds<256, 128, 2, 4, true, false, false, kShortRingRows>(
+        map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act, a.act_stride, a.out_row0, a.K, a.N, s);
   if (BM == 256)
     return run_lds<256, 128, 2, 4, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
                                          a.act_stride, a.out_row0, a.K, a.N, s);

@@ -169,6 +169,16 @@ def test_single_expert_is_dense_swiglu():
     check_y(wl, g["y"], om.swiglu(x64, *W.expert64(0)), "dense")
 
 
+def test_weight_streaming_tile_order():
+    """32 groups of about 128 rows (256-row tiles, >= 32 groups of at most one tile on
+    average): the grouped GEMMs run n tiles fastest and the down product takes 256 x 128
+    tiles with three LDS stages; every token against the oracle."""
+    wl = _adhoc("nfast", 118, T=2048, d=256, E=32, k=2, d_ff=256, dtype=wk.BF16)
+    W = Weights(wl)
+    g, _, _ = full_check(wl, W, 2048)
+    assert g["counts"].max() <= 256 and g["counts"].sum() == 4096
+
+
 @pytest.mark.parametrize("T", [200, 256, 300])
 def test_capacity_with_two_choices(T):
     """k = 2 with a binding capacity: first choices before second choices (GShard rule).
@@ -415,6 +425,8 @@ _BWD_CASES = {
     # beside the 256-row K-major tile table, K-major shared products
     "fine_grained": (dict(d=256, E=64, k=8, d_ff=256, n_shared=1, d_ff_shared=256,
                           bias_range=0.1), 256),
+    # 32 groups of ~128 rows: the 256-row gate/up recompute in n-fastest tile order
+    "weight_streaming": (dict(d=256, E=32, k=2, d_ff=256), 2048),
 }
 
 
