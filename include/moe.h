@@ -41,15 +41,20 @@
  *     scratch and accepts ws == NULL.
  *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *     asynchronously; the call never synchronises the host and never reads
- *     device data back.
+ *     device data back. moe_backward, and the expert entry points (moe_expert_*,
+ *     moe_forward) for decode-sized batches with a shared expert, run part of
+ *     their work on a side stream the library keeps per device, forked from
+ *     `stream` by an event and joined back into it, so every effect of the call
+ *     is still ordered on `stream`.
  *   - Arguments are validated before anything is enqueued. On any error the
  *     call returns a non-zero moe_status, enqueues nothing and leaves all
  *     outputs untouched. A failed kernel launch returns MOE_ERR_HIP (work
  *     enqueued before the failure may have run). moe_last_error() gives a
  *     message for the calling thread's most recent error.
  *   - T == 0 is valid and enqueues nothing.
- *   - The library keeps no state between calls; calls from several host threads
- *     are safe when they use distinct workspaces and outputs.
+ *   - The library keeps no data between calls (only the side streams and their
+ *     events); calls from several host threads are safe when they use distinct
+ *     workspaces and outputs.
  *   - Results are deterministic: the same inputs give bitwise-equal outputs.
  */
 #ifndef MOE_MI355X_H

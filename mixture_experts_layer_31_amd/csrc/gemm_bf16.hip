@@ -654,9 +654,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
 }
 
 // Decode launch shape, measured on MI355X from cold caches over the Mixtral,
-// DeepSeek and Switch shapes at 1-32 tokens: K split over KS = 4 waves while
-// the items are few and the groups hold at most 2 rows (more waves in flight
-// per weight byte), fewer splits as either grows; batches of U = 8 steps,
+// DeepSeek and Switch shapes at 1-32 tokens and a single group of 16-128 rows:
+// K split over KS = 4 waves while the items are very few, or few and the groups
+// hold at most 2 rows (more waves in flight per weight byte), fewer splits as
+// either grows; batches of U = 8 steps,
 // or 4 when a wave's K range is short (one batch) or, in the down product,
 // very long (more waves per SIMD in place of deeper batches).
 template <bool GATEUP, int U, int KS>
@@ -680,7 +681,7 @@ static hipError_t run_stream(const GemmTileMap& map, const uint16_t* xa, const i
   const long long items = static_cast<long long>(m_tiles) * (N / 16);
   const int avg = map.tiles ? map.avg_rows : map.n_single;
   int KS = 1;
-  if (items < 8192 && avg <= 2) KS = 4;
+  if (items < 1024 || (items < 8192 && avg <= 2)) KS = 4;
   else if (items < 16384 && avg <= 4) KS = 2;
   const int steps = K / 32 / KS;
   const bool u4 = steps < 16 || (!GATEUP && steps >= 100);
