@@ -68,7 +68,7 @@ __device__ __forceinline__ int km_frag_off(int lane, int col) {
 
 }  // namespace
 
-template <bool GK>
+template <bool GK, bool NF = false>
 __global__ __launch_bounds__(64 * kKmNW)
 __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kmajor_kernel(
     const int32_t* __restrict__ tiles, int max_tiles, int n_single, int n_logical,
@@ -83,7 +83,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kmajor_kernel(
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[];
 
   int m_tile, n_tile;
-  xcd_tile(n_logical, max_tiles, m_tile, n_tile);
+  if constexpr (NF) xcd_tile_nfast(max_tiles, n_logical / max_tiles, m_tile, n_tile);
+  else xcd_tile(n_logical, max_tiles, m_tile, n_tile);
   if (m_tile < 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -300,13 +301,15 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kmajor_kernel(
 hipError_t launch_gemm_kmajor_data(const GemmTileMap& map, const KmDataArgs& a, hipStream_t s) {
   if (a.K % kBK || a.ksplit % kBK || a.N % kKmBN || a.lda % 8 || a.ldw % 8)
     return hipErrorInvalidValue;
-  auto kern = gemm_kmajor_kernel<false>;
+  // weight-streaming shapes (gemm_n_fast): the n tiles of each m tile together
+  auto kern = map.n_fast ? gemm_kmajor_kernel<false, true> : gemm_kmajor_kernel<false>;
   hipError_t e = allow_large_lds(reinterpret_cast<const void*>(kern), kKmLds);
   if (e != hipSuccess) return e;
   const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + kKmBM - 1) / kKmBM;
   const long long n_logical = static_cast<long long>(m_tiles) * (a.N / kKmBN);
   if (n_logical == 0) return hipSuccess;
-  const long long grid = ((n_logical + 7) / 8) * 8;
+  const long long grid = map.n_fast ? 8LL * ((m_tiles + 7) / 8) * (a.N / kKmBN)
+                                    : ((n_logical + 7) / 8) * 8;
   kern<<<dim3(static_cast<unsigned>(grid)), dim3(64 * kKmNW), kKmLds, s>>>(
       map.tiles, m_tiles, map.n_single, static_cast<int>(n_logical), a.x, a.lda, a.src, a.x_row0,
       a.wa, a.wb, a.ksplit, a.ldw, a.w_stride, a.y, a.y_stride, a.y_row0, a.K);
