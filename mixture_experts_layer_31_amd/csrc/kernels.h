@@ -186,9 +186,11 @@ hipError_t launch_gemm_kmajor_data(const GemmTileMap& map, const KmDataArgs& a, 
 // Grouped K: out[g][m][n] = sum over rows r in [offsets[g], offsets[g+1]) of
 // A[r][m] * B[r][n] (fp32 out, [G][N1][N2]); A [rows][lda], B [rows][ldb] bf16,
 // N1 and N2 multiples of 256.
+// rows_stream: the groups are short (gemm_n_fast), so the products are bound by
+// writing the fp32 output: tiles go out n-fastest with plain stores.
 hipError_t launch_gemm_kmajor_groupk(const int32_t* offsets, int G, const uint16_t* A, int lda,
                                      int N1, const uint16_t* B, int ldb, int N2, float* out,
-                                     hipStream_t s);
+                                     bool rows_stream, hipStream_t s);
 hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, int BM,
                                    hipStream_t s);
 hipError_t launch_gemm_down_bf16(const GemmTileMap& map, const DownArgs& a, int BM,

@@ -800,24 +800,27 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   // ---- weight gradients over each expert's rows: dW2 = dY_perm^T act,
   // dW1 = dH1^T X_perm, dW3 = dH3^T X_perm (both operands K-major)
   MOE_HIP(moe::launch_gather_rows(2, x, b.src, b.offsets, E, R, d, b.xp, strm), "x_perm");
-  MOE_HIP(moe::launch_gemm_kmajor_groupk(b.offsets, E, b.dyp, d, d, b.act, As, dff, dw2, strm),
+  const bool gk_stream = moe::gemm_n_fast(256, s.R, E);
+  MOE_HIP(moe::launch_gemm_kmajor_groupk(b.offsets, E, b.dyp, d, d, b.act, As, dff, dw2, gk_stream,
+                                         strm),
           "dW2");
-  MOE_HIP(moe::launch_gemm_kmajor_groupk(b.offsets, E, b.dH, 2 * As, dff, b.xp, d, d, dw1, strm),
+  MOE_HIP(moe::launch_gemm_kmajor_groupk(b.offsets, E, b.dH, 2 * As, dff, b.xp, d, d, dw1, gk_stream,
+                                         strm),
           "dW1");
   MOE_HIP(moe::launch_gemm_kmajor_groupk(b.offsets, E, b.dH + dff, 2 * As, dff, b.xp, d, d, dw3,
-                                         strm),
+                                         gk_stream, strm),
           "dW3");
   if (s.nsh) {
     const size_t r0 = static_cast<size_t>(R);
     MOE_HIP(moe::launch_single_group_offsets(T, b.soff, strm), "shared offsets");
     MOE_HIP(moe::launch_gemm_kmajor_groupk(b.soff, 1, b.dyb, d, d, b.act + r0 * As, As, dffs, dws2,
-                                           strm),
+                                           false, strm),
             "dWs2");
     MOE_HIP(moe::launch_gemm_kmajor_groupk(b.soff, 1, b.dH + r0 * 2 * As, 2 * As, dffs, u16(x), d,
-                                           d, dws1, strm),
+                                           d, dws1, false, strm),
             "dWs1");
     MOE_HIP(moe::launch_gemm_kmajor_groupk(b.soff, 1, b.dH + r0 * 2 * As + dffs, 2 * As, dffs,
-                                           u16(x), d, d, dws3, strm),
+                                           u16(x), d, d, dws3, false, strm),
             "dWs3");
   }
   return MOE_OK;
