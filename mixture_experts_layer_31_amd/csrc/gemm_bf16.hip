@@ -220,6 +220,12 @@ struct LdsRing {
   static constexpr int st = ST_, xb = XB_, stage = STAGE_, sl = SL_;
 };
 
+// Stages of the short ring (xs token rows, wr weight rows): four when they fit
+// in the LDS, else three.
+constexpr int short_ring_stages(int xs, int wr) {
+  return 4 * (xs + wr) * kRowBytes <= static_cast<int>(kMaxLdsBytes) ? 4 : 3;
+}
+
 template <int BM, int BN, int WM, int WN, bool GATEUP, int ST, bool HOUT = false, bool SK = false,
           bool NF = false, int XS = 0>
 __global__ __launch_bounds__(64 * WM * WN)
@@ -246,13 +252,14 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
   // by ST - 1 steps (with three stages every slice still has a full step of
   // latency to hide)
   constexpr int SL = ST == 3 ? kDmaSlices3 : kDmaSlices;
-  // XS > 0: tiles of at most XS rows run a three-stage ring whose stages hold
-  // only XS token rows (the LDS holds three of those but two full stages)
+  // XS > 0: tiles of at most XS rows run a deeper ring (three or four stages)
+  // whose stages hold only XS token rows, in the LDS of the full stages
   static_assert(XS == 0 || (XS % 32 == 0 && XS < BM && 3 * (XS + WR) * kRowBytes <= kMaxLdsBytes),
                 "three short stages must fit");
+  constexpr int XSR = XS > 0 ? XS : BM;
+  constexpr int SRS = short_ring_stages(XSR, WR);
   using FullRing = LdsRing<ST, XBYTES, STAGE, SL>;
-  using ShortRing = LdsRing<3, (XS > 0 ? XS : BM) * kRowBytes, ((XS > 0 ? XS : BM) + WR) * kRowBytes,
-                            kDmaSlices3>;
+  using ShortRing = LdsRing<SRS, XSR * kRowBytes, (XSR + WR) * kRowBytes, kDmaSlices3>;
 
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[];
 
@@ -369,16 +376,18 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
     auto kloop = [&](auto na_c, auto ring) {
       using R = decltype(ring);
       constexpr int RS = R::st;
-      if (nk > 0) dma(0, 0, ring);
-      if (RS == 3 && nk > 1) dma(1, 1, ring);
+#pragma unroll
+      for (int p = 0; p < RS - 1; ++p)
+        if (p < nk) dma(p, p, ring);
       int cur = 0;
       for (int kt = 0; kt < nk; ++kt) {
         // loads complete in issue order: stage kt has landed once no more than
-        // the next stage's nd_stage loads are outstanding
-        if (RS == 3 && kt + 1 < nk) wait_vmcnt_at_most<ND>(nd_stage);
+        // the later stages' loads (nd_stage each) are outstanding
+        const int later = min(RS - 2, nk - 1 - kt);
+        if (RS >= 3 && later > 0) wait_vmcnt_at_most<(RS >= 3 ? RS - 2 : 1) * ND>(later * nd_stage);
         else MOE_WAIT_VMCNT(0);
-        // with three stages the next stage's loads stay in flight across it
-        if constexpr (RS == 3) dma_barrier();
+        // with three or more stages the later stages' loads stay in flight across it
+        if constexpr (RS >= 3) dma_barrier();
         else __syncthreads();
         const int ahead = kt + RS - 1;
         const bool more = ahead < nk;
@@ -801,7 +810,8 @@ static hipError_t run_lds(const GemmTileMap& map, const uint16_t* xa, const int3
   constexpr int WR = GATEUP ? 2 * BN : BN;
   constexpr size_t kStage = static_cast<size_t>(BM + WR) * kRowBytes;
   constexpr int ST = 3 * kStage <= kMaxLdsBytes ? 3 : 2;
-  constexpr size_t kShort = XS > 0 ? 3 * static_cast<size_t>(XS + WR) * kRowBytes : 0;
+  constexpr size_t kShort =
+      XS > 0 ? short_ring_stages(XS, WR) * static_cast<size_t>(XS + WR) * kRowBytes : 0;
   const size_t lds = ST * kStage > kShort ? ST * kStage : kShort;
   return launch_tiled(gemm_bf16_lds_kernel<BM, BN, WM, WN, GATEUP, ST, HOUT, false, NF, XS>, NF, BM, BN,
                       64 * WM * WN, lds, map, xa, src, a_stride, a_row0, wa, wb, w_stride, out,
@@ -906,11 +916,12 @@ hipError_t launch_gemm_down_bf16(const GemmTileMap& map, const DownArgs& a, int 
   const int ys = a.out_stride > 0 ? a.out_stride : a.N;
   const auto* act = static_cast<const uint16_t*>(a.act);
   const auto* w2 = static_cast<const uint16_t*>(a.w2);
-  // weight-streaming shapes: 256 x 128 tiles (three LDS stages) in n-fastest order
+  // weight-streaming shapes: 256 x 128 tiles (three LDS stages) in n-fastest order.
+  // (A four-stage ring of 160-row stages, 4 x 36 KB, measured no faster here.)
   if (BM == 256 && map.n_fast && a.N % 128 == 0)
-    return run_lds<256, 128, 2, 4, false, false, true>(map, act, a.src, a.act_stride, a.in_row0,
-                                                       w2, nullptr, a.w_stride, a.y, ys,
-                                                       a.out_row0, a.K, a.N, s);
+    return run_lds<256, 128, 2, 4, false, false, true>(
+        map, act, a.src, a.act_stride, a.in_row0, w2, nullptr, a.w_stride, a.y, ys, a.out_row0,
+        a.K, a.N, s);
   if (BM == 256) {
     const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + BM - 1) / BM;
     if (gemm_down_cols(BM, m_tiles, a.N) == 128)
