@@ -742,13 +742,14 @@ int gemm_tile_rows(int dtype_bf16, int R_max, int groups, bool n256_ok) {
   return 256;
 }
 
-// Measured on MI355X from cold caches (DeepSeek shape, 256 groups of ~128 rows:
-// gate/up -9 %, down -10 % against the m-fastest order with stream-K; 64 groups:
-// -2 % and -11 %); with 8 groups the m-fastest order stays ahead.
-constexpr int kNFastMinGroups = 32;
+// Measured on MI355X from cold caches (DeepSeek shape, 256 experts of ~128 rows:
+// gate/up -9 %, down -10 % against the m-fastest order with stream-K; 64 experts:
+// -2 % and -11 %); with 8 experts the m-fastest order stays ahead, also when
+// their rows come as 64 groups (the expert-parallel layout of 8 ranks).
+constexpr int kNFastMinExperts = 32;
 
-bool gemm_n_fast(int BM, long long R_max, int groups) {
-  return BM == 256 && groups >= kNFastMinGroups && R_max <= 256LL * groups;
+bool gemm_n_fast(int BM, long long R_max, int experts) {
+  return BM == 256 && experts >= kNFastMinExperts && R_max <= 256LL * experts;
 }
 
 int gemm_max_tiles(int BM, int R_max, int E) {

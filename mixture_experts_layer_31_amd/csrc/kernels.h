@@ -119,10 +119,13 @@ struct GemmTileMap {
   int avg_rows = 0;       // rows per non-empty group on average (decode kernels; 0: unknown)
 };
 
-// Tile order of the 256-row kernels for R_max rows in G groups: n tiles fastest
-// (gemm_bf16.hip, xcd_tile_nfast) when there are many groups of at most one
-// tile each on average, which makes those products weight-streaming.
-bool gemm_n_fast(int BM, long long R_max, int groups);
+// Tile order of the 256-row kernels for R_max rows over `experts` weight
+// matrices: n tiles fastest (gemm_bf16.hip, xcd_tile_nfast) when there are many
+// experts of at most one tile each on average, which makes those products
+// weight-streaming. It counts experts, not row groups: groups that share an
+// expert's weights (the expert-parallel layout) want the m-fastest order, which
+// runs them side by side on one weight panel.
+bool gemm_n_fast(int BM, long long R_max, int experts);
 
 // BM of the grouped GEMMs for R_max rows in `groups` groups; n256_ok: d is a
 // multiple of 256 and d_ff (and d_ff_shared) of 128, as the large tiles need

@@ -407,7 +407,7 @@ int shared_gateup_rows(const Shape& s) {
 moe_status do_gateup(const Shape& s, const void* x, const int32_t* src, const int32_t* tiles,
                      const void* w1, const void* w3, const void* ws1, const void* ws3, void* act,
                      hipStream_t stream) {
-  moe::GemmTileMap map{tiles, s.max_tiles, 0, moe::gemm_n_fast(s.BM, s.R, s.G), avg_group_rows(s)};
+  moe::GemmTileMap map{tiles, s.max_tiles, 0, moe::gemm_n_fast(s.BM, s.R, s.E), avg_group_rows(s)};
   moe::GateUpArgs a{x, src, w1, w3, static_cast<long long>(s.dff) * s.d, act, s.act_stride, 0,
                     s.d, s.dff};
   const int bm_sh = shared_gateup_rows(s);
@@ -428,7 +428,7 @@ moe_status do_gateup(const Shape& s, const void* x, const int32_t* src, const in
 
 moe_status do_down(const Shape& s, const void* act, const int32_t* tiles, const void* w2,
                    const void* ws2, float* y_perm, float* sk_part, hipStream_t stream) {
-  moe::GemmTileMap map{tiles, s.max_tiles, 0, moe::gemm_n_fast(s.BM, s.R, s.G), avg_group_rows(s)};
+  moe::GemmTileMap map{tiles, s.max_tiles, 0, moe::gemm_n_fast(s.BM, s.R, s.E), avg_group_rows(s)};
   moe::DownArgs a{act, s.act_stride, 0, w2, static_cast<long long>(s.d) * s.dff, y_perm, 0, s.dff, s.d};
   a.sk_part = sk_part;
   const int bm_sh = moe::gemm_tile_rows(1, s.T, 1, s.n256);
