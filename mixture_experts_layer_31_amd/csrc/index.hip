@@ -17,6 +17,7 @@
 // sequential definition.
 #include "common.h"
 #include "kernels.h"
+#include "select.h"
 
 namespace moe {
 
@@ -218,12 +219,13 @@ hipError_t launch_ep_traffic(const int32_t* offsets, int n, int E, int32_t* rows
 // (every per-block base is 0). When `tiles` is set it also writes the grouped
 // GEMM tile table of BM-row tiles (group, first row, rows) from the offsets, as
 // tile_map_kernel does, and zero entries up to max_tiles.
-__global__ __launch_bounds__(1024) void index_single_kernel(
+// The workgroup's body; idx may point to global memory or to LDS.
+__device__ __forceinline__ void index_single_body(
     const int32_t* __restrict__ idx, int T, int k, int E, long long C,
     int32_t* __restrict__ offsets, int32_t* __restrict__ dest, int32_t* __restrict__ src,
     int32_t* __restrict__ counts_out, int32_t* __restrict__ kept_out,
-    int32_t* __restrict__ n_dropped, int BM, int max_tiles, int ep, int4* __restrict__ tiles) {
-  extern __shared__ uint32_t smem[];
+    int32_t* __restrict__ n_dropped, int BM, int max_tiles, int ep, int4* __restrict__ tiles,
+    uint32_t* smem) {
   const int cap = C >= 0;
   const int nkeys = cap ? E * k : E;
   uint32_t* bm = smem;                                              // [nkeys][kWords]
@@ -328,12 +330,99 @@ __global__ __launch_bounds__(1024) void index_single_kernel(
   for (int i = total + tid; i < max_tiles; i += 1024) tiles[i] = make_int4(0, 0, 0, 0);
 }
 
+// LDS words of index_single_body
+__host__ __device__ constexpr size_t index_single_words(int E, int nkeys) {
+  return static_cast<size_t>(nkeys) * (kWords + 3) + (E + 1) + 16;
+}
+
+__global__ __launch_bounds__(1024) void index_single_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int E, long long C,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ dest, int32_t* __restrict__ src,
+    int32_t* __restrict__ counts_out, int32_t* __restrict__ kept_out,
+    int32_t* __restrict__ n_dropped, int BM, int max_tiles, int ep, int4* __restrict__ tiles) {
+  extern __shared__ uint32_t smem[];
+  index_single_body(idx, T, k, E, C, offsets, dest, src, counts_out, kept_out, n_dropped, BM,
+                    max_tiles, ep, tiles, smem);
+}
+
+// Small batches in one launch: selection (as router_select_kernel, without the
+// statistics) and then the single-workgroup index. Wave w selects the tokens
+// w, w + 16, ...; their choices go to idx and gates and to LDS, from where the
+// index body reads them after a barrier. One launch instead of two for the
+// decode-sized steps of the fused forward.
+template <int NE>
+__global__ __launch_bounds__(1024) void route_index_single_kernel(
+    const float* __restrict__ z, const float* __restrict__ bias, int T, int k, int E,
+    int gate_all, int32_t* __restrict__ idx, float* __restrict__ gates, long long C,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ dest, int32_t* __restrict__ src,
+    int32_t* __restrict__ counts_out, int32_t* __restrict__ kept_out,
+    int32_t* __restrict__ n_dropped, int BM, int max_tiles, int4* __restrict__ tiles) {
+  extern __shared__ uint32_t smem[];
+  const int nkeys = C >= 0 ? E * k : E;   // as index_keys()
+  int32_t* sidx = reinterpret_cast<int32_t*>(smem + index_single_words(E, nkeys));   // [T][k]
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  float b[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const int e = lane + 64 * i;
+    b[i] = (bias != nullptr && e < E) ? bias[e] : 0.f;
+  }
+  for (int t = wv; t < T; t += 16) {
+    TokenSelect<NE> ts;
+    select_token<NE>(z + static_cast<size_t>(t) * E, b, E, k, gate_all, lane, ts);
+    if (lane < k) {
+      idx[static_cast<size_t>(t) * k + lane] = ts.e;
+      gates[static_cast<size_t>(t) * k + lane] = ts.g;
+      sidx[t * k + lane] = ts.e;
+    }
+  }
+  __syncthreads();
+  index_single_body(sidx, T, k, E, C, offsets, dest, src, counts_out, kept_out, n_dropped, BM,
+                    max_tiles, 1, tiles, smem);
+}
+
 static size_t index_single_lds(int E, int nkeys) {
-  return (static_cast<size_t>(nkeys) * (kWords + 3) + (E + 1) + 16) * sizeof(uint32_t);
+  return index_single_words(E, nkeys) * sizeof(uint32_t);
 }
 
 bool index_single_ok(int T, int E, int k, bool cap) {
   return T <= kTB && E <= 1024 && index_keys(E, k, cap) <= kIndexSingleMaxKeys;
+}
+
+bool route_index_single_ok(int T, int E, int k, bool cap) {
+  return T <= kRouteIndexMaxTokens && index_single_ok(T, E, k, cap);
+}
+
+hipError_t launch_route_index_single(const float* z, const float* bias, int T, int k, int E,
+                                     int gate_all, int32_t* idx, float* gates,
+                                     long long capacity, int32_t* offsets, int32_t* dest,
+                                     int32_t* src, int32_t* counts, int32_t* kept,
+                                     int32_t* n_dropped, int BM, int max_tiles, int32_t* tiles,
+                                     hipStream_t s) {
+  const bool cap = capacity >= 0;
+  if (!route_index_single_ok(T, E, k, cap)) return hipErrorInvalidValue;
+  if (T == 0) return hipSuccess;
+  const size_t lds = index_single_lds(E, index_keys(E, k, cap)) +
+                     static_cast<size_t>(T) * k * sizeof(int32_t);
+  const int ne = (E + 63) / 64;
+#define MOE_RIS(NE_)                                                                         \
+  do {                                                                                       \
+    auto kern = route_index_single_kernel<NE_>;                                              \
+    if (lds > 65536) {                                                                       \
+      const hipError_t e1 = allow_large_lds(reinterpret_cast<const void*>(kern), lds);       \
+      if (e1 != hipSuccess) return e1;                                                       \
+    }                                                                                        \
+    kern<<<dim3(1), dim3(1024), lds, s>>>(z, bias, T, k, E, gate_all, idx, gates,             \
+                                          cap ? capacity : -1, offsets, dest, src, counts,   \
+                                          kept, n_dropped, BM, max_tiles,                    \
+                                          reinterpret_cast<int4*>(tiles));                   \
+  } while (0)
+  if (ne <= 1) MOE_RIS(1);
+  else if (ne <= 2) MOE_RIS(2);
+  else if (ne <= 4) MOE_RIS(4);
+  else MOE_RIS(16);
+#undef MOE_RIS
+  return hipGetLastError();
 }
 
 hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capacity,

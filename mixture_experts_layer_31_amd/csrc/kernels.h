@@ -82,6 +82,18 @@ constexpr int kIndexSingleMaxKeys = 1024;
 bool index_single_ok(int T, int E, int k, bool cap);
 // With `tiles` set, also writes the grouped GEMM tile table for BM-row tiles
 // (as launch_tile_map does), in the same launch on the single-workgroup path.
+// Selection and index of a small batch in one single-workgroup launch (the
+// fused forward's decode steps; no routing statistics, no expert-parallel
+// layout): idx and gates as launch_router_select writes them, then what
+// launch_index writes, with the tile table.
+constexpr int kRouteIndexMaxTokens = 64;
+bool route_index_single_ok(int T, int E, int k, bool cap);
+hipError_t launch_route_index_single(const float* z, const float* bias, int T, int k, int E,
+                                     int gate_all, int32_t* idx, float* gates,
+                                     long long capacity, int32_t* offsets, int32_t* dest,
+                                     int32_t* src, int32_t* counts, int32_t* kept,
+                                     int32_t* n_dropped, int BM, int max_tiles, int32_t* tiles,
+                                     hipStream_t s);
 hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capacity,
                         int32_t* blk, int32_t* slot_base, int32_t* slot_keep, int32_t* offsets,
                         int32_t* dest, int32_t* src, int32_t* counts, int32_t* kept,

@@ -882,11 +882,31 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   if (idx_out) idx = idx_out;
   if (gates_out) gates = gates_out;
 
-  st = do_route(s, cfg->aux_alpha, x, w_router, sel_bias, idx, gates, stats, scratch, strm);
-  if (st != MOE_OK) return st;
   int32_t* tiles = static_cast<int32_t*>(scratch);
-  st = do_permute(s, idx, x, offsets, dest, src, nullptr, stats, scratch, tiles, strm);
-  if (st != MOE_OK) return st;
+  if (s.ep == 1 && !want_route_stats(stats) && moe::route_index_single_ok(s.T, s.E, s.k, s.C >= 0)) {
+    // small batch, no routing statistics: selection and index in one launch after
+    // the scores. The tile table is written over the logits at the start of the
+    // scratch, after the kernel's barrier, when every logit has been read.
+    Carver rc{static_cast<char*>(scratch)};
+    float* z = rc.take<float>(static_cast<size_t>(s.T) * s.E * 4);
+    rc.take<float>(static_cast<size_t>(s.nb_sel) * s.E * 4);              // p_part
+    rc.take<int32_t>(static_cast<size_t>(s.nb_sel) * s.E * 4);            // c_part
+    rc.take<float>(static_cast<size_t>(s.E) * 4);                         // fp
+    rc.take<float>(static_cast<size_t>(s.nb_sel) * moe::kScaleStats * 4); // q_part
+    float* zpart = rc.take<float>(zpart_bytes(s));
+    MOE_HIP(moe::launch_router_scores(s.bf16, x, w_router, s.T, s.d, s.E, z, zpart, strm),
+            "router_scores");
+    MOE_HIP(moe::launch_route_index_single(
+                z, sel_bias, s.T, s.k, s.E, s.gate_all, idx, gates, s.C, offsets, dest, src,
+                stats ? stats->counts : nullptr, stats ? stats->kept : nullptr,
+                stats ? stats->n_dropped : nullptr, s.BM, s.max_tiles, tiles, strm),
+            "route_index");
+  } else {
+    st = do_route(s, cfg->aux_alpha, x, w_router, sel_bias, idx, gates, stats, scratch, strm);
+    if (st != MOE_OK) return st;
+    st = do_permute(s, idx, x, offsets, dest, src, nullptr, stats, scratch, tiles, strm);
+    if (st != MOE_OK) return st;
+  }
   st = do_gateup(s, x, src, tiles, w1, w3, ws1, ws3, act, strm);
   if (st != MOE_OK) return st;
   float* sk = sk_bytes(s) ? reinterpret_cast<float*>(static_cast<char*>(scratch) + tiles_bytes(s))

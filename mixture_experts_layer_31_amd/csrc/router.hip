@@ -8,6 +8,7 @@
 #include "common.h"
 #include "gemm_common.h"
 #include "kernels.h"
+#include "select.h"
 
 namespace moe {
 
@@ -404,28 +405,15 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   }
 
   for (int t = tb0 + wv; t < tb1; t += 4) {
-    const float* zr = z + static_cast<size_t>(t) * E;
-    float zl[NE], sl[NE];
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      const int e = lane + 64 * i;
-      zl[i] = e < E ? zr[e] : -INFINITY;
-      sl[i] = e < E ? zl[i] + b[i] : -INFINITY;
-      m = fmaxf(m, zl[i]);
-    }
-    m = wave_allmax(m);
-    float ex[NE];
-    float se = 0.f;
-#pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      ex[i] = (lane + 64 * i < E) ? expf(zl[i] - m) : 0.f;
-      se += ex[i];
-    }
-    se = wave_allsum(se);
+    TokenSelect<NE> ts;
+    select_token<NE>(z + static_cast<size_t>(t) * E, b, E, k, gate_all, lane, ts);
+    const float m = ts.m, se = ts.se;
     const float inv = 1.0f / se;
 #pragma unroll
-    for (int i = 0; i < NE; ++i) pacc[i] += ex[i] * inv;
+    for (int i = 0; i < NE; ++i) {
+      pacc[i] += ts.ex[i] * inv;
+      cacc[i] += ts.chosen[i];
+    }
     if (q_part != nullptr) {
       // scale statistics of p_t = softmax(z_t): with m the max logit and
       // se = sum e^{z-m}, log sum e^z = m + ln se, max p = 1/se,
@@ -435,9 +423,9 @@ __global__ __launch_bounds__(256) void router_select_kernel(
 #pragma unroll
       for (int i = 0; i < NE; ++i) {
         if (lane + 64 * i < E) {
-          zm += ex[i] * (zl[i] - m);
-          if (zl[i] > t1) { t2 = t1; t1 = zl[i]; }
-          else if (zl[i] > t2) { t2 = zl[i]; }
+          zm += ts.ex[i] * (ts.zl[i] - m);
+          if (ts.zl[i] > t1) { t2 = t1; t1 = ts.zl[i]; }
+          else if (ts.zl[i] > t2) { t2 = ts.zl[i]; }
         }
       }
       zm = wave_allsum(zm);
@@ -454,43 +442,8 @@ __global__ __launch_bounds__(256) void router_select_kernel(
       qacc[2] += inv;
       qacc[3] += (1.0f - expf(t2 - m)) * inv;
     }
-
-    // k rounds of argmax; lane r keeps the round-r winner and its unbiased logit
-    int my_e = 0;
-    float my_z = -INFINITY;
-    for (int r = 0; r < k; ++r) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < NE; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E && (sl[i] > bv || (sl[i] == bv && e < be))) { bv = sl[i]; be = e; }
-      }
-      wave_argmax(bv, be);
-      const int owner = be & 63, slot = be >> 6;
-      float zsel = 0.f;
-#pragma unroll
-      for (int i = 0; i < NE; ++i)
-        if (i == slot) zsel = zl[i];
-      zsel = readlane_f(zsel, owner);
-      // the winner cannot win again: its score becomes -inf while at least
-      // E - r - 1 >= 1 unselected experts keep finite scores
-      if (lane == owner) {
-#pragma unroll
-        for (int i = 0; i < NE; ++i)
-          if (i == slot) { sl[i] = -INFINITY; cacc[i] += 1; }
-      }
-      if (lane == r) { my_e = be; my_z = zsel; }
-    }
-    // gates from the unbiased logits
-    float g;
-    if (gate_all) {
-      g = expf(my_z - m) / se;
-    } else {
-      const float ms = wave_allmax(lane < k ? my_z : -INFINITY);
-      const float num = lane < k ? expf(my_z - ms) : 0.f;
-      g = num / wave_allsum(num);
-    }
+    const int my_e = ts.e;
+    const float g = ts.g;
     if (lane < k) {
       idx[static_cast<size_t>(t) * k + lane] = my_e;
       gates[static_cast<size_t>(t) * k + lane] = g;

@@ -80,8 +80,10 @@ def config_of(wl: wk.Workload, T: int) -> moe.MoeConfig:
 
 
 def run_forward(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int, bias="default",
-                ep: int = 0):
-    """Fused moe_forward; returns numpy copies of y, idx, gates and the stats."""
+                ep: int = 0, stats: str = "full"):
+    """Fused moe_forward; returns numpy copies of y, idx, gates and the stats.
+    stats="counts" asks only for the expert counts, kept rows and drops; "none" for no
+    statistics (the keys of what was not asked for are absent)."""
     cfg = config_of(wl, T)
     cfg.ep_ranks = ep
     x = to_dev(x_host, wl.dtype)
@@ -91,8 +93,19 @@ def run_forward(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int, bias="d
     st = moe.Stats.alloc(wl.E, groups=wl.E * (ep if ep > 1 else 1))
     ws = moe.alloc_workspace(cfg, moe.STAGE_FORWARD)
     b = W.bias if bias == "default" else bias
+    if stats == "counts":
+        st = moe.Stats(st.counts, st.kept, st.n_dropped)
+    elif stats == "none":
+        st = None
     moe.forward(cfg, x, W.wr, b, W.w1, W.w3, W.w2, W.s1, W.s3, W.s2, y, idx, gates, st, ws)
     torch.cuda.synchronize()
+    if st is None:
+        return dict(y=y.cpu().numpy(), idx=idx.cpu().numpy().astype(np.int64),
+                    gates=gates.cpu().numpy())
+    if stats == "counts":
+        return dict(y=y.cpu().numpy(), idx=idx.cpu().numpy().astype(np.int64),
+                    gates=gates.cpu().numpy(), counts=st.counts.cpu().numpy(),
+                    kept=st.kept.cpu().numpy(), n_dropped=int(st.n_dropped.cpu()[0]))
     return dict(y=y.cpu().numpy(), idx=idx.cpu().numpy().astype(np.int64),
                 gates=gates.cpu().numpy(), counts=st.counts.cpu().numpy(),
                 kept=st.kept.cpu().numpy(), n_dropped=int(st.n_dropped.cpu()[0]),

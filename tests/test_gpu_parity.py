@@ -135,6 +135,58 @@ def test_zero_tokens_leaves_outputs():
     assert (y == 3.0).all()
 
 
+# ------------------------------------------------------------------ forward without statistics
+
+# Up to 64 tokens with no routing statistics asked for, the fused forward selects and
+# indexes in one workgroup; with statistics (or more tokens) it runs the selection and
+# index kernels apart. Both must give the same routing and the same y bit for bit.
+_NOSTAT_CASES = {
+    "toy_f32_t1": dict(T=1),
+    "toy_f32_t37": dict(T=37),
+    "toy_f32_t64": dict(T=64),
+    "toy_f32_t65": dict(T=65),
+    "dense_e1_t5": dict(T=5, wl=("ns_dense", 120, dict(d=128, E=1, k=1, d_ff=64, dtype=wk.BF16))),
+    "capacity_k2_t48": dict(T=48, wl=("ns_cap", 121, dict(d=128, E=8, k=2, d_ff=128,
+                                                          dtype=wk.BF16, capacity_factor=0.6,
+                                                          offset_var=1.5))),
+    "gate_all_cap_e64_t40": dict(T=40, wl=("ns_gall", 122, dict(d=128, E=64, k=1, d_ff=64,
+                                                               dtype=wk.BF16, gate=wk.GATE_ALL,
+                                                               capacity_factor=1.0,
+                                                               offset_var=1.5))),
+    "bias_e64_k8_t64": dict(T=64, wl=("ns_bias", 123, dict(d=256, E=64, k=8, d_ff=64,
+                                                          dtype=wk.BF16, bias_range=0.1))),
+    "e128_k4_shared_t33": dict(T=33, wl=("ns_e128", 124, dict(d=128, E=128, k=4, d_ff=64,
+                                                             n_shared=1, d_ff_shared=128,
+                                                             dtype=wk.BF16))),
+    "e1024_k16_t20": dict(T=20, wl=("ns_e1024", 125, dict(d=256, E=1024, k=16, d_ff=64,
+                                                         dtype=wk.BF16))),
+}
+
+
+@pytest.mark.parametrize("case", list(_NOSTAT_CASES))
+def test_forward_without_statistics(case):
+    c = _NOSTAT_CASES[case]
+    T = c["T"]
+    if "wl" in c:
+        name, cid, kw = c["wl"]
+        wl = _adhoc(name, cid, T=T, **kw)
+        W = Weights(wl)
+    else:
+        W = weights("toy_t64")
+        wl = W.wl
+    log(f"[case] forward without statistics: {case}")
+    g, r, p = full_check(wl, W, T)      # statistics asked for: selection and index apart
+    x = wk.make_inputs(wl, T=T).x
+    none = run_forward(wl, W, x, T, stats="none")
+    counts = run_forward(wl, W, x, T, stats="counts")
+    for other, what in ((none, "none"), (counts, "counts")):
+        for key in ("y", "idx", "gates"):
+            assert np.array_equal(other[key], g[key]), f"{case} stats={what}: {key}"
+    for key in ("counts", "kept", "n_dropped"):
+        assert np.array_equal(counts[key], g[key]), f"{case}: {key}"
+    check_permutation(wl, T, counts, counts["idx"])
+
+
 # ------------------------------------------------------------------ small special cases
 
 def _adhoc(name, cid, **kw):
@@ -626,6 +678,23 @@ def test_mixtral_decode(T):
     assert g["counts"].sum() == 2 * T
 
 
+@pytest.mark.parametrize("T", [1, 8, 32])
+def test_mixtral_decode_without_statistics(T):
+    """The one-workgroup selection + index of the fused forward against the separate kernels."""
+    W = weights("mixtral_t32")
+    _same_without_statistics(W, T)
+
+
+def _same_without_statistics(W, T):
+    wl = W.wl
+    x = wk.make_inputs(wl, T=T).x
+    log(f"[case] {wl.name} T={T} forward with and without statistics")
+    full = run_forward(wl, W, x, T)
+    none = run_forward(wl, W, x, T, stats="none")
+    for key in ("y", "idx", "gates"):
+        assert np.array_equal(none[key], full[key]), key
+
+
 def test_mixtral_prefill_512():
     W = weights("mixtral_t32")
     full_check(W.wl, W, 512, sample=48)
@@ -674,6 +743,13 @@ def test_deepseek_t1():
 def test_deepseek_t64():
     W = weights("deepseek_t64")
     full_check(W.wl, W, 64, sample=6)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("T", [1, 64])
+def test_deepseek_without_statistics(T):
+    W = weights("deepseek_t64")
+    _same_without_statistics(W, T)
 
 
 @pytest.mark.timeout(300)
