@@ -559,23 +559,67 @@ __global__ __launch_bounds__(256) void streamk_fixup_kernel(
 // consecutive output columns 4*(l/16)..+3. Items with the same n-slice and
 // consecutive token tiles run in the same workgroup (KS < 4) so they share the
 // weight rows in cache.
+//
+// An optional second segment (seg.rows > 0) is one dense group with weights,
+// widths and rows of its own (the shared expert of a decode step): its items
+// follow the grouped ones in the same launch, so both weight streams fill the
+// device together instead of one launch's ramp and tail after the other's.
+struct StreamSeg {
+  const uint16_t* xa = nullptr;   // row r reads xa[(a_row0 + r) * a_stride ...] (no src)
+  const uint16_t* wa = nullptr;   // [N][K]
+  const uint16_t* wb = nullptr;   // [N][K] (gate/up only)
+  int a_row0 = 0, rows = 0, K = 0, N = 0, out_row0 = 0;
+};
+
+static __host__ __device__ long long stream_seg_items(const StreamSeg& seg) {
+  return seg.rows > 0 ? static_cast<long long>((seg.rows + 15) >> 4) * (seg.N >> 4) : 0;
+}
+
 template <bool GATEUP, int U, int KS>
 __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
     const int32_t* __restrict__ tiles, int max_tiles, int n_single,
-    const uint16_t* __restrict__ xa, const int32_t* __restrict__ src, int a_stride, int a_row0,
-    const uint16_t* __restrict__ w_a, const uint16_t* __restrict__ w_b, long long w_stride,
-    void* __restrict__ out, int out_stride, int out_row0, int K, int N) {
+    const uint16_t* __restrict__ xa_g, const int32_t* __restrict__ src_g, int a_stride,
+    int a_row0_g, const uint16_t* __restrict__ w_a_g, const uint16_t* __restrict__ w_b_g,
+    long long w_stride, void* __restrict__ out, int out_stride, int out_row0_g, int K_g, int N,
+    StreamSeg seg) {
   typedef __attribute__((ext_vector_type(8))) __bf16 bf8;
   constexpr int IPB = 4 / KS;                  // items per workgroup
   __shared__ f32x4 red[KS > 1 ? 3 : 1][GATEUP ? 2 : 1][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kpart = wave % KS;
   const long long item = static_cast<long long>(blockIdx.x) * IPB + wave / KS;
-  const int n_slices = N >> 4;
-  const bool live = item < static_cast<long long>(max_tiles) * n_slices;
-  const int m_tile = live ? static_cast<int>(item % max_tiles) : 0;
-  const int n0 = live ? static_cast<int>(item / max_tiles) * 16 : 0;
-  const TileCoord tc = lookup_tile(tiles, n_single, 16, m_tile);
+  const long long items_g = static_cast<long long>(max_tiles) * (N >> 4);
+  // this wave's item: a tile of the grouped rows or of the second segment
+  const uint16_t* xa = xa_g;
+  const int32_t* src = src_g;
+  const uint16_t* w_a = w_a_g;
+  const uint16_t* w_b = w_b_g;
+  int a_row0 = a_row0_g, out_row0 = out_row0_g, K = K_g;
+  bool live;
+  int n0 = 0;
+  TileCoord tc{0, 0, 0};
+  if (item < items_g) {
+    live = true;
+    n0 = static_cast<int>(item / max_tiles) * 16;
+    tc = lookup_tile(tiles, n_single, 16, static_cast<int>(item % max_tiles));
+  } else {
+    const long long j = item - items_g;
+    live = j < stream_seg_items(seg);
+    if (live) {
+      const int seg_tiles = (seg.rows + 15) >> 4;
+      const int mt = static_cast<int>(j % seg_tiles);
+      n0 = static_cast<int>(j / seg_tiles) * 16;
+      tc.row0 = mt * 16;
+      tc.rows = min(16, seg.rows - mt * 16);
+      xa = seg.xa;
+      src = nullptr;
+      w_a = seg.wa;
+      w_b = seg.wb;
+      a_row0 = seg.a_row0;
+      out_row0 = seg.out_row0;
+      K = seg.K;
+    }
+  }
   const bool active = live && tc.rows > 0;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
@@ -673,21 +717,24 @@ template <bool GATEUP, int U, int KS>
 static void launch_stream(long long items, const GemmTileMap& map, int m_tiles,
                           const uint16_t* xa, const int32_t* src, int a_stride, int a_row0,
                           const uint16_t* wa, const uint16_t* wb, long long w_stride, void* out,
-                          int out_stride, int out_row0, int K, int N, hipStream_t s) {
+                          int out_stride, int out_row0, int K, int N, const StreamSeg& seg,
+                          hipStream_t s) {
   constexpr int IPB = 4 / KS;
   gemm_bf16_stream_kernel<GATEUP, U, KS>
       <<<dim3(static_cast<unsigned>((items + IPB - 1) / IPB)), dim3(256), 0, s>>>(
           map.tiles, m_tiles, map.n_single, xa, src, a_stride, a_row0, wa, wb, w_stride, out,
-          out_stride, out_row0, K, N);
+          out_stride, out_row0, K, N, seg);
 }
 
+// seg: an optional dense group launched with the grouped rows (its K may differ;
+// the launch shape follows the grouped rows' K and the total item count)
 template <bool GATEUP>
 static hipError_t run_stream(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
                              int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
                              long long w_stride, void* out, int out_stride, int out_row0, int K,
-                             int N, hipStream_t s) {
+                             int N, hipStream_t s, const StreamSeg& seg = StreamSeg{}) {
   const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + 15) / 16;
-  const long long items = static_cast<long long>(m_tiles) * (N / 16);
+  const long long items = static_cast<long long>(m_tiles) * (N / 16) + stream_seg_items(seg);
   const int avg = map.tiles ? map.avg_rows : map.n_single;
   int KS = 1;
   if (items < 1024 || (items < 8192 && avg <= 2)) KS = 4;
@@ -696,7 +743,7 @@ static hipError_t run_stream(const GemmTileMap& map, const uint16_t* xa, const i
   const bool u4 = steps < 16 || (!GATEUP && steps >= 100);
 #define MOE_STREAM(U_, KS_)                                                                  \
   launch_stream<GATEUP, U_, KS_>(items, map, m_tiles, xa, src, a_stride, a_row0, wa, wb,     \
-                                 w_stride, out, out_stride, out_row0, K, N, s)
+                                 w_stride, out, out_stride, out_row0, K, N, seg, s)
   if (KS == 4) {
     if (u4) MOE_STREAM(4, 4); else MOE_STREAM(8, 4);
   } else if (KS == 2) {
@@ -902,6 +949,42 @@ hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, 
                             a.out_row0, a.K, a.N, s);
   return run_small<32, 64, 1, 2, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
                                        a.act_stride, a.out_row0, a.K, a.N, s);
+}
+
+hipError_t launch_gemm_gateup_bf16_with_shared(const GemmTileMap& map, const GateUpArgs& a,
+                                               const GateUpArgs& sh, int sh_rows, hipStream_t s) {
+  if (a.h1 != nullptr || sh.src != nullptr || a.act_stride != sh.act_stride)
+    return hipErrorInvalidValue;
+  StreamSeg seg;
+  seg.xa = static_cast<const uint16_t*>(sh.x);
+  seg.wa = static_cast<const uint16_t*>(sh.w1);
+  seg.wb = static_cast<const uint16_t*>(sh.w3);
+  seg.rows = sh_rows;
+  seg.K = sh.K;
+  seg.N = sh.N;
+  seg.out_row0 = sh.out_row0;
+  return run_stream<true>(map, static_cast<const uint16_t*>(a.x), a.src, a.K, 0,
+                          static_cast<const uint16_t*>(a.w1), static_cast<const uint16_t*>(a.w3),
+                          a.w_stride, a.act, a.act_stride, a.out_row0, a.K, a.N, s, seg);
+}
+
+hipError_t launch_gemm_down_bf16_with_shared(const GemmTileMap& map, const DownArgs& a,
+                                             const DownArgs& sh, int sh_rows, hipStream_t s) {
+  const int ys = a.out_stride > 0 ? a.out_stride : a.N;
+  if (sh.src != nullptr || sh.act_stride != a.act_stride || sh.N != a.N ||
+      (sh.out_stride > 0 ? sh.out_stride : sh.N) != ys || sh.y != a.y)
+    return hipErrorInvalidValue;
+  StreamSeg seg;
+  seg.xa = static_cast<const uint16_t*>(sh.act);
+  seg.wa = static_cast<const uint16_t*>(sh.w2);
+  seg.a_row0 = sh.in_row0;
+  seg.rows = sh_rows;
+  seg.K = sh.K;
+  seg.N = sh.N;
+  seg.out_row0 = sh.out_row0;
+  return run_stream<false>(map, static_cast<const uint16_t*>(a.act), a.src, a.act_stride,
+                           a.in_row0, static_cast<const uint16_t*>(a.w2), nullptr, a.w_stride,
+                           a.y, ys, a.out_row0, a.K, a.N, s, seg);
 }
 
 // Output tiles of 256 columns unless that leaves fewer than two tiles per CU

@@ -210,6 +210,13 @@ hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, 
                                    hipStream_t s);
 hipError_t launch_gemm_down_bf16(const GemmTileMap& map, const DownArgs& a, int BM,
                                  hipStream_t s);
+// Decode-sized steps: the grouped rows (16-row tiles, streaming kernel) and one
+// dense group of sh_rows rows with its own weights (sh: the shared expert; no
+// src, same activation / output buffers and strides) in one launch.
+hipError_t launch_gemm_gateup_bf16_with_shared(const GemmTileMap& map, const GateUpArgs& a,
+                                               const GateUpArgs& sh, int sh_rows, hipStream_t s);
+hipError_t launch_gemm_down_bf16_with_shared(const GemmTileMap& map, const DownArgs& a,
+                                             const DownArgs& sh, int sh_rows, hipStream_t s);
 hipError_t launch_gemm_gateup_f32(const GemmTileMap& map, const GateUpArgs& a, hipStream_t s);
 hipError_t launch_gemm_down_f32(const GemmTileMap& map, const DownArgs& a, hipStream_t s);
 

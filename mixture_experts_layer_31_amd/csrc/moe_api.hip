@@ -364,11 +364,14 @@ int avg_group_rows(const Shape& s) {
   return g > 0 ? s.R / g : 0;
 }
 
-// Decode-sized layers with a shared expert over more than 16 tokens: the shared
-// expert's product (one dense group, too few tiles to fill the device alone) runs
-// on the side stream beside the routed one. Both only stream weights from HBM,
-// and side by side each fills the other's idle CUs, ramp and tail (DeepSeek
-// shape at 64 tokens: 3.34 -> 3.27 ms; at one token it only added the fork). The side stream is forked
+// Decode-sized layers with a shared expert: where both products take the 16-row
+// streaming tiles, the shared expert's items join the routed launch (DeepSeek
+// shape, one token: 0.179 -> 0.165 ms). Otherwise, over more than 16 tokens, the
+// shared expert's product (one dense group, too few tiles to fill the device
+// alone) runs on the side stream beside the routed one: both only stream weights
+// from HBM, and side by side each fills the other's idle CUs, ramp and tail
+// (DeepSeek shape at 64 tokens: 3.34 -> 3.27 ms before the joint launch took its
+// gate/up product; at one token the side stream only added the fork). It is forked
 // from the caller's stream before either launch and joined back after both, so
 // the call's work stays ordered on the caller's stream; it uses no scratch
 // (no stream-K) and writes rows of its own (the shared block).
@@ -411,6 +414,12 @@ moe_status do_gateup(const Shape& s, const void* x, const int32_t* src, const in
   moe::GateUpArgs a{x, src, w1, w3, static_cast<long long>(s.dff) * s.d, act, s.act_stride, 0,
                     s.d, s.dff};
   const int bm_sh = shared_gateup_rows(s);
+  if (s.nsh && s.bf16 && s.BM == 16 && bm_sh == 16) {
+    // both stream weights in 16-row tiles: one launch for the two
+    moe::GateUpArgs b{x, nullptr, ws1, ws3, 0, act, s.act_stride, s.R, s.d, s.dffs};
+    MOE_HIP(moe::launch_gemm_gateup_bf16_with_shared(map, a, b, s.T, stream), "gemm_gateup");
+    return MOE_OK;
+  }
   SharedOnSide sh;
   moe_status st = sh.fork(s, bm_sh, stream);
   if (st != MOE_OK) return st;
@@ -432,6 +441,11 @@ moe_status do_down(const Shape& s, const void* act, const int32_t* tiles, const 
   moe::DownArgs a{act, s.act_stride, 0, w2, static_cast<long long>(s.d) * s.dff, y_perm, 0, s.dff, s.d};
   a.sk_part = sk_part;
   const int bm_sh = moe::gemm_tile_rows(1, s.T, 1, s.n256);
+  if (s.nsh && s.bf16 && s.BM == 16 && bm_sh == 16) {
+    moe::DownArgs b{act, s.act_stride, s.R, ws2, 0, y_perm, s.R, s.dffs, s.d};
+    MOE_HIP(moe::launch_gemm_down_bf16_with_shared(map, a, b, s.T, stream), "gemm_down");
+    return MOE_OK;
+  }
   SharedOnSide sh;
   moe_status st = sh.fork(s, bm_sh, stream);
   if (st != MOE_OK) return st;

@@ -210,6 +210,19 @@ def test_shared_expert_wider_than_routed():
     full_check(wl, W, 150)
 
 
+@pytest.mark.parametrize("T,dffs", [(1, 192), (5, 64), (16, 320), (17, 192), (40, 128)])
+def test_decode_shared_expert_beside_routed(T, dffs):
+    """Decode-sized steps stream the shared expert's weights in the routed experts' launch,
+    at its own width (d_ff_shared != d_ff); the down product joins it up to 16 tokens.
+    Every token against the oracle, and the staged entry points give the same y."""
+    wl = _adhoc(f"dec_shared_{dffs}", 126, T=T, d=256, E=64, k=6, d_ff=128, n_shared=1,
+                d_ff_shared=dffs, dtype=wk.BF16)
+    W = Weights(wl)
+    g, _, _ = full_check(wl, W, T)
+    b = run_staged(wl, W, wk.make_inputs(wl, T=T).x, T)
+    assert np.array_equal(g["y"], b["y"])
+
+
 def test_single_expert_is_dense_swiglu():
     """E = 1, k = 1: the layer is the dense SwiGLU FFN (CME295 notes §B)."""
     wl = _adhoc("dense_e1", 102, T=70, d=128, E=1, k=1, d_ff=192, dtype=wk.BF16)
