@@ -481,6 +481,7 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
   if constexpr (!SK) {
     int m_tile, n_tile;
     if constexpr (NF) xcd_tile_nfast(max_tiles, N / BN, m_tile, n_tile);
+    else if (tile_order_blocked(BM, N / BN)) xcd_tile_blocked(max_tiles, N / BN, m_tile, n_tile);
     else xcd_tile(n_logical, max_tiles, m_tile, n_tile);
     if (m_tile < 0) return;
     run_tile(m_tile, n_tile, 0, nk_all, nullptr);
@@ -825,7 +826,9 @@ static hipError_t launch_tiled(Kern kern, bool n_fast, int BM, int BN, int threa
   }
   const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + BM - 1) / BM;
   const long long n_logical = static_cast<long long>(m_tiles) * (N / BN);
-  const long long grid = n_fast ? 8LL * ((m_tiles + 7) / 8) * (N / BN) : ((n_logical + 7) / 8) * 8;
+  const long long grid = n_fast                               ? 8LL * ((m_tiles + 7) / 8) * (N / BN)
+                         : tile_order_blocked(BM, N / BN) ? blocked_grid(m_tiles, N / BN)
+                                                          : ((n_logical + 7) / 8) * 8;
   kern<<<dim3(static_cast<unsigned>(grid)), dim3(threads), lds, s>>>(
       map.tiles, m_tiles, map.n_single, static_cast<int>(n_logical), xa, src, a_stride, a_row0,
       wa, wb, w_stride, out, out_stride, out_row0, K, N, extra...);

@@ -50,6 +50,37 @@ __device__ __forceinline__ void xcd_tile_nfast(int max_tiles, int n_tiles, int& 
   if (m_tile >= max_tiles) m_tile = -1;
 }
 
+// Launch index -> (m_tile, n_tile) in blocks of kTileBlockM m tiles: XCD x owns
+// the n tiles [x * n_tiles / 8, (x + 1) * n_tiles / 8) and walks one block of m
+// tiles over all of them (m fastest), then the next block. Each weight panel is
+// then read by one XCD only, and the workgroups in flight on an XCD share their
+// token rows (the block's m tiles) as well as their weight panels (a few n
+// tiles) in its L2; in m-fastest order over all m tiles they would share only
+// the weight panels and read every token row again for every n tile.
+// Grid: blocked_grid(max_tiles, n_tiles).
+constexpr int kTileBlockM = 8;
+__host__ __device__ constexpr bool tile_order_blocked(int BM, int n_tiles) {
+  return BM == 256 && n_tiles >= 16;   // enough n tiles for every XCD
+}
+__host__ __device__ constexpr long long blocked_grid(int max_tiles, int n_tiles) {
+  return 8LL * ((max_tiles + kTileBlockM - 1) / kTileBlockM) * kTileBlockM * ((n_tiles + 7) / 8);
+}
+__device__ __forceinline__ void xcd_tile_blocked(int max_tiles, int n_tiles, int& m_tile,
+                                                 int& n_tile) {
+  const int L = blockIdx.x, x = L & 7, j = L >> 3;
+  const int n_lo = x * n_tiles / 8;
+  const int nn = (x + 1) * n_tiles / 8 - n_lo;
+  m_tile = -1;
+  n_tile = 0;
+  if (nn <= 0) return;
+  const int per = kTileBlockM * nn;   // workgroups of one block on this XCD
+  const int b = j / per, r = j - b * per;
+  const int m = b * kTileBlockM + r % kTileBlockM;
+  if (m >= max_tiles) return;
+  m_tile = m;
+  n_tile = n_lo + r / kTileBlockM;
+}
+
 #if defined(__HIP_DEVICE_COMPILE__)
 // s_waitcnt with vmcnt = n and the other counters not waited on (gfx9 encoding)
 #define MOE_WAIT_VMCNT(n) \
