@@ -147,7 +147,11 @@ typedef struct {
  *   max_prob   mean_t of max_i p_{t,i} (float[1])
  *   top_gap    mean_t of p_{t,(1)} - p_{t,(2)}, the two largest probabilities
  *              (p_{(2)} = 0 when E = 1) (float[1])
- * The last four are computed by moe_route / moe_forward; all in fp32 with
+ *   margin[T]  per token, s_(k) - s_(k+1): the k-th largest selection score
+ *              s = z + b minus the largest score left out (+inf when k = E),
+ *              how far the top-k choice is from a tie ([CME295] §1.3, the
+ *              top-k step; §4.2 for b) (float)
+ * z_loss .. margin are computed by moe_route / moe_forward; all in fp32 with
  * fixed summation orders (reproducible bit for bit).                          */
 typedef struct {
   int32_t* counts;
@@ -160,6 +164,7 @@ typedef struct {
   float* entropy;
   float* max_prob;
   float* top_gap;
+  float* margin;
 } moe_stats;
 
 /* Human-readable status name; never NULL. */

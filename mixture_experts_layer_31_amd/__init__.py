@@ -41,7 +41,8 @@ class MoeStats(ctypes.Structure):
                 ("n_dropped", ctypes.c_void_p), ("f", ctypes.c_void_p),
                 ("P", ctypes.c_void_p), ("aux", ctypes.c_void_p),
                 ("z_loss", ctypes.c_void_p), ("entropy", ctypes.c_void_p),
-                ("max_prob", ctypes.c_void_p), ("top_gap", ctypes.c_void_p)]
+                ("max_prob", ctypes.c_void_p), ("top_gap", ctypes.c_void_p),
+                ("margin", ctypes.c_void_p)]
 
 
 class MoEError(RuntimeError):
@@ -157,22 +158,26 @@ class Stats:
     entropy: object = None
     max_prob: object = None
     top_gap: object = None
+    margin: object = None
 
     @staticmethod
-    def alloc(E: int, device="cuda", groups: Optional[int] = None) -> "Stats":
+    def alloc(E: int, device="cuda", groups: Optional[int] = None,
+              T: Optional[int] = None) -> "Stats":
         """counts/kept hold one entry per row group: E, or ep_ranks*E with the
-        expert-parallel layout (pass groups=ep_ranks*E then)."""
+        expert-parallel layout (pass groups=ep_ranks*E then). margin[T] is
+        allocated when T is given."""
         import torch
         z = lambda n, dt: torch.zeros(n, dtype=dt, device=device)
         f1 = lambda: z(1, torch.float32)
         G = groups or E
         return Stats(z(G, torch.int32), z(G, torch.int32), z(1, torch.int32),
-                     z(E, torch.float32), z(E, torch.float32), f1(), f1(), f1(), f1(), f1())
+                     z(E, torch.float32), z(E, torch.float32), f1(), f1(), f1(), f1(), f1(),
+                     z(T, torch.float32) if T is not None else None)
 
     def c(self) -> MoeStats:
         return MoeStats(_p(self.counts), _p(self.kept), _p(self.n_dropped), _p(self.f),
                         _p(self.P), _p(self.aux), _p(self.z_loss), _p(self.entropy),
-                        _p(self.max_prob), _p(self.top_gap))
+                        _p(self.max_prob), _p(self.top_gap), _p(self.margin))
 
 
 def _stats_ref(stats: Optional[Stats]):

@@ -59,11 +59,12 @@ size_t router_scores_part_floats(int dtype_bf16, int T, int d, int E);
 hipError_t launch_router_scores(int dtype_bf16, const void* x, const void* w, int T, int d, int E,
                                 float* z, float* part, hipStream_t s);
 // q_part (nullable): per-block sums of the four scale statistics (z-loss,
-// entropy, top probability, top-2 gap), [blocks][kScaleStats]
+// entropy, top probability, top-2 gap), [blocks][kScaleStats]; margin
+// (nullable): s_(k) - s_(k+1) per token, [T]
 constexpr int kScaleStats = 4;
 hipError_t launch_router_select(const float* z, const float* bias, int T, int E, int k,
                                 int gate_all, int32_t* idx, float* gates, float* p_part,
-                                int32_t* c_part, float* q_part, hipStream_t s);
+                                int32_t* c_part, float* q_part, float* margin, hipStream_t s);
 hipError_t launch_bias_update(const int32_t* counts, int T, int k, int E, int ep, float gamma,
                               float* bias, hipStream_t s);
 hipError_t launch_router_stats(const float* p_part, const int32_t* c_part, const float* q_part,

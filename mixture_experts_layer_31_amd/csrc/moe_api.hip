@@ -271,7 +271,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 bool want_route_stats(const moe_stats* st) {
   return st != nullptr && (st->f != nullptr || st->P != nullptr || st->aux != nullptr ||
                            st->z_loss != nullptr || st->entropy != nullptr ||
-                           st->max_prob != nullptr || st->top_gap != nullptr);
+                           st->max_prob != nullptr || st->top_gap != nullptr ||
+                           st->margin != nullptr);
 }
 
 // ---- stage bodies (arguments already validated)
@@ -291,7 +292,8 @@ moe_status do_route(const Shape& s, float alpha, const void* x, const void* wr, 
           "router_scores");
   MOE_HIP(moe::launch_router_select(z, bias, s.T, s.E, s.k, s.gate_all, idx, gates,
                                     stats ? p_part : nullptr, stats ? c_part : nullptr,
-                                    scale ? q_part : nullptr, stream),
+                                    scale ? q_part : nullptr, stats ? st->margin : nullptr,
+                                    stream),
           "router_select");
   if (stats)
     MOE_HIP(moe::launch_router_stats(p_part, c_part, scale ? q_part : nullptr, s.nb_sel, s.T, s.E,
@@ -704,7 +706,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   // ---- forward, recomputed: routing, index, pre-activations, activation
   MOE_HIP(moe::launch_router_scores(1, x, w_router, T, d, E, b.z, b.zpart, strm), "router_scores");
   MOE_HIP(moe::launch_router_select(b.z, sel_bias, T, E, k, s.gate_all, b.idx, b.gates, nullptr,
-                                    nullptr, nullptr, strm),
+                                    nullptr, nullptr, nullptr, strm),
           "router_select");
   MOE_HIP(moe::launch_index(b.idx, T, k, E, s.C, b.blk, b.slot_base, b.slot_keep, b.offsets, b.dest,
                             b.src, b.counts, b.kept, b.ndrop, s.BM, s.max_tiles, 1, b.tiles, strm),

@@ -383,7 +383,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     const float* __restrict__ z, const float* __restrict__ bias, int T, int E, int k,
     int gate_all, int tokens_per_block, int32_t* __restrict__ idx,
     float* __restrict__ gates, float* __restrict__ p_part, int32_t* __restrict__ c_part,
-    float* __restrict__ q_part) {
+    float* __restrict__ q_part, float* __restrict__ margin) {
   extern __shared__ unsigned char smem_raw[];
   __shared__ float sq[4][kScaleStats];
   float* sp = reinterpret_cast<float*>(smem_raw);             // [4][E]
@@ -407,6 +407,10 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   for (int t = tb0 + wv; t < tb1; t += 4) {
     TokenSelect<NE> ts;
     select_token<NE>(z + static_cast<size_t>(t) * E, b, E, k, gate_all, lane, ts);
+    if (margin != nullptr) {
+      const float mg = select_margin<NE>(ts, E, k);
+      if (lane == 0) margin[t] = mg;
+    }
     const float m = ts.m, se = ts.se;
     const float inv = 1.0f / se;
 #pragma unroll
@@ -688,7 +692,7 @@ int router_select_blocks(int T) {
 
 hipError_t launch_router_select(const float* z, const float* bias, int T, int E, int k,
                                 int gate_all, int32_t* idx, float* gates, float* p_part,
-                                int32_t* c_part, float* q_part, hipStream_t s) {
+                                int32_t* c_part, float* q_part, float* margin, hipStream_t s) {
   const int nb = router_select_blocks(T);
   const int tpb = router_select_tokens(T);
   const size_t lds = static_cast<size_t>(8) * E * sizeof(float);
@@ -696,7 +700,8 @@ hipError_t launch_router_select(const float* z, const float* bias, int T, int E,
 #define MOE_SEL(NE_)                                                                       \
   router_select_kernel<NE_><<<dim3(nb), dim3(256), lds, s>>>(z, bias, T, E, k, gate_all,   \
                                                              tpb, idx,                     \
-                                                             gates, p_part, c_part, q_part)
+                                                             gates, p_part, c_part, q_part, \
+                                                             margin)
   if (ne <= 1) MOE_SEL(1);
   else if (ne <= 2) MOE_SEL(2);
   else if (ne <= 4) MOE_SEL(4);

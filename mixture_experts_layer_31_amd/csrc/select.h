@@ -18,6 +18,8 @@ struct TokenSelect {
   float ex[NE];    // e^{z - m}, 0 past E
   float m, se;     // the largest logit and the wave's sum of e^{z - m}
   int chosen[NE];  // 1 where this lane's expert was chosen
+  float sl[NE];    // selection scores z + b, -inf where chosen or past E
+  float kth;       // the k-th largest selection score (the last one chosen)
   int e;           // lane r < k: the r-th choice
   float g;         // lane r < k: its gate
 };
@@ -28,7 +30,7 @@ template <int NE>
 __device__ __forceinline__ void select_token(const float* __restrict__ zr, const float (&b)[NE],
                                              int E, int k, int gate_all, int lane,
                                              TokenSelect<NE>& o) {
-  float sl[NE];
+  float* sl = o.sl;
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NE; ++i) {
@@ -61,6 +63,7 @@ __device__ __forceinline__ void select_token(const float* __restrict__ zr, const
       if (e < E && (sl[i] > bv || (sl[i] == bv && e < be))) { bv = sl[i]; be = e; }
     }
     wave_argmax(bv, be);
+    o.kth = bv;
     const int owner = be & 63, slot = be >> 6;
     float zsel = 0.f;
 #pragma unroll
@@ -87,6 +90,19 @@ __device__ __forceinline__ void select_token(const float* __restrict__ zr, const
   }
   o.e = my_e;
   o.g = g;
+}
+
+// The selection's margin s_(k) - s_(k+1) over the scores s = z + b (+inf when
+// k = E: nothing was left out), the distance of the k-th choice from the first
+// expert left out: a small margin marks a token whose choice rounding can flip.
+// Call after select_token on the same TokenSelect, with all 64 lanes active.
+template <int NE>
+__device__ __forceinline__ float select_margin(const TokenSelect<NE>& o, int E, int k) {
+  float v = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) v = fmaxf(v, o.sl[i]);
+  v = wave_allmax(v);
+  return k < E ? o.kth - v : INFINITY;
 }
 
 }  // namespace moe

@@ -353,6 +353,52 @@ def test_router_scale_statistics(std):
         f"max_prob {g['max_prob']:.4f} gap {g['top_gap']:.4f}")
 
 
+_MARGIN_CASES = {
+    "bias_e64_k8": dict(E=64, k=8, bias_range=0.1),
+    "gate_all_capacity_e64_k1": dict(E=64, k=1, gate=wk.GATE_ALL, capacity_factor=1.0),
+    "k_equals_E": dict(E=4, k=4),
+}
+
+
+@pytest.mark.parametrize("case", list(_MARGIN_CASES))
+def test_selection_margin(case):
+    """Per-token selection margin s_(k) - s_(k+1) (s = z + b) against the oracle's float64
+    margin on the same operands: within the fp32 error of the two logits it subtracts,
+    (d - 1) 2^-23 sum_i |x_i w_ei| each, plus the rounding of z + b; +inf when k = E.
+    moe_forward, asked for the margin, returns the same values bit for bit."""
+    T = 300
+    wl = _adhoc(f"margin_{case}", 127, T=T, d=256, d_ff=64, dtype=wk.BF16, **_MARGIN_CASES[case])
+    W = Weights(wl)
+    inp = wk.make_inputs(wl, T=T)
+    cfg = config_of(wl, T)
+    x = to_dev(inp.x, wl.dtype)
+    log(f"[case] selection margin {case}")
+    idx = torch.empty((T, wl.k), dtype=torch.int32, device=dev())
+    gates = torch.empty((T, wl.k), dtype=torch.float32, device=dev())
+    st = moe.Stats.alloc(wl.E, T=T)
+    moe.route(cfg, x, W.wr, W.bias, idx, gates, st, moe.alloc_workspace(cfg, moe.STAGE_ROUTE))
+    torch.cuda.synchronize()
+    mg = st.margin.cpu().numpy().astype(np.float64)
+    r, x64 = oracle_route(wl, W, inp.x)
+    if wl.k == wl.E:
+        assert np.all(np.isposinf(mg)) and np.all(np.isposinf(r["margin"]))
+    else:
+        w64 = wk.to_f64(W.wr_host, wl.dtype)
+        zb = (wl.d - 1) * 2.0 ** -23 * (np.abs(x64) @ np.abs(w64).T).max(axis=1)
+        tol = 2 * zb + 4 * 2.0 ** -24 * np.abs(r["s"]).max(axis=1)
+        err = np.abs(mg - r["margin"])
+        assert np.all(np.isfinite(mg)) and np.all(err <= tol), float((err - tol).max())
+        assert np.all(mg >= 0)
+    # the fused layer with the margin asked for (selection and index run apart)
+    y = torch.empty((T, wl.d), dtype=torch.float32, device=dev())
+    st2 = moe.Stats(margin=torch.full((T,), float("nan"), device=dev()))
+    moe.forward(cfg, x, W.wr, W.bias, W.w1, W.w3, W.w2, W.s1, W.s3, W.s2, y, None, None, st2,
+                moe.alloc_workspace(cfg, moe.STAGE_FORWARD))
+    torch.cuda.synchronize()
+    assert np.array_equal(st2.margin.cpu().numpy(), st.margin.cpu().numpy())
+    log(f"[ok] margin {case}: min {mg.min():.3g} median {np.median(mg):.3g}")
+
+
 def _route_counts(cfg, x, wr, bias, T, k, E):
     idx = torch.empty((T, k), dtype=torch.int32, device=dev())
     gates = torch.empty((T, k), dtype=torch.float32, device=dev())
