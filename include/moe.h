@@ -56,6 +56,11 @@
  *     events); calls from several host threads are safe when they use distinct
  *     workspaces and outputs.
  *   - Results are deterministic: the same inputs give bitwise-equal outputs.
+ *   - The calls enqueue kernels and events only (no allocation, memset, copy or
+ *     synchronisation), so a call may be captured into a HIP graph on `stream`
+ *     and replayed; the side stream joins the capture through its fork event.
+ *     Make one call of the same shape before capturing (it sets the kernels'
+ *     LDS limits, a host-side step).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

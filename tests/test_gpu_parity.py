@@ -817,6 +817,75 @@ def test_deepseek_t4096():
     full_check(W.wl, W, 4096, sample=3)
 
 
+def _forward_bare(wl, W, x, T, y=None, ws=None, stream=None):
+    """moe_forward as the benchmark calls it: no idx, gates or statistics outputs."""
+    cfg = config_of(wl, T)
+    if y is None:
+        y = torch.full((T, wl.d), float("nan"), dtype=torch.float32, device=dev())
+    if ws is None:
+        ws = moe.alloc_workspace(cfg, moe.STAGE_FORWARD)
+    moe.forward(cfg, x, W.wr, W.bias, W.w1, W.w3, W.w2, W.s1, W.s3, W.s2, y, None, None, None,
+                ws, stream)
+    return y
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,T", [("mixtral_t32", 4096), ("mixtral_t32", 1),
+                                    ("deepseek_t64", 1), ("deepseek_t64", 32)])
+def test_benchmark_launch_matches_checked_launch(name, T):
+    """The launch the benchmark times (no idx / gates / statistics outputs, so up to 64
+    tokens the one-workgroup selection + index) gives the y of the launch the parity
+    tests check against the oracle, bit for bit."""
+    W = weights(name)
+    wl = W.wl
+    inp = wk.make_inputs(wl, T=T)
+    log(f"[case] {wl.name} T={T} benchmark launch")
+    checked = run_forward(wl, W, inp.x, T)
+    y = _forward_bare(wl, W, to_dev(inp.x, wl.dtype), T)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), checked["y"])
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,T", [("mixtral_t32", 1), ("mixtral_t32", 512),
+                                    ("deepseek_t64", 32)])
+def test_forward_in_a_hip_graph(name, T):
+    """moe_forward captured into a HIP graph (the DeepSeek shape at 32 tokens forks the
+    shared expert's down product onto the library's side stream inside the capture) and
+    replayed three times, with eager forwards on other inputs between the replays: every
+    replay equals the eager result bit for bit."""
+    W = weights(name)
+    wl = W.wl
+    cfg = config_of(wl, T)
+    x_a = to_dev(wk.make_inputs(wl, T=T).x, wl.dtype)
+    x_b = -x_a                     # exact in bf16; other logits, other experts
+    log(f"[case] {wl.name} T={T} graph capture")
+    want = _forward_bare(wl, W, x_a, T).clone()
+    other = _forward_bare(wl, W, x_b, T).clone()
+    torch.cuda.synchronize()
+    assert not np.array_equal(want.cpu().numpy(), other.cpu().numpy())
+    ws = moe.alloc_workspace(cfg, moe.STAGE_FORWARD)
+    y = torch.full((T, wl.d), float("nan"), dtype=torch.float32, device=dev())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _forward_bare(wl, W, x_a, T, y=y, ws=ws)       # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        _forward_bare(wl, W, x_a, T, y=y, ws=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), want.cpu().numpy()), f"replay {rep}"
+        eager = _forward_bare(wl, W, x_b, T)      # eager work between the replays
+        torch.cuda.synchronize()
+        assert np.array_equal(eager.cpu().numpy(), other.cpu().numpy())
+
+
 @pytest.mark.timeout(300)
 def test_deepseek_backward_4096_sampled():
     _backward_full_sampled("deepseek_t64", 4096, n_tokens=4, n_experts=6, n_units=8, seed=12)
