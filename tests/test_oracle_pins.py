@@ -27,7 +27,7 @@ def _gold(name):
 # --------------------------------------------------------------- permutation
 
 def test_permutation_worked_examples():
-    """CMU 15-779 L21 §3.3 worked example and §10 exercise 2: dest and indptr."""
+    """CMU 15-779 Lecture 21 §3.3 worked example and §10 exercise 2: dest and indptr."""
     for ex in _gold("permutation_examples.json")["examples"]:
         idx = np.array(ex["choices"])
         p = om.assign_rows(idx, ex["E"])
