@@ -201,6 +201,35 @@ def check_permutation(wl, T, gpu, gpu_idx):
     return p
 
 
+def y_rounding_bound(wl, W: Weights, x64, idx, gates64, keep):
+    """Per-element bound on |y_gpu - y| for bf16 layers, from the kernels' rounding points:
+    the SwiGLU activation is rounded to bf16 (relative 2^-9) before the second product, so
+    an output element moves by at most 2^-9 sum_j g_j sum_f |act_jf w2_e,if| (+ the shared
+    expert's term with weight 1); the fp32 accumulations of the two products add at most
+    (d + d_ff) 2^-24 of the same magnitudes (the first product's error passes through
+    silu and the gate's product with a factor below 2). Returned doubled, [T, d]."""
+    T = x64.shape[0]
+    mag = np.zeros((T, wl.d))
+    need = {}
+    for t in range(T):
+        for j in range(wl.k):
+            if keep[t, j]:
+                need.setdefault(int(idx[t, j]), []).append((t, j))
+    for e in sorted(need):
+        w1, w3, w2 = W.expert64(e)
+        rows = need[e]
+        act = np.abs(om.swiglu_hidden(x64[[t for t, _ in rows]], w1, w3))
+        out = act @ np.abs(w2).T
+        for (t, j), o in zip(rows, out):
+            mag[t] += abs(gates64[t, j]) * o
+    sh = W.shared64()
+    dff = wl.d_ff
+    if sh is not None:
+        mag += np.abs(om.swiglu_hidden(x64, sh[0], sh[1])) @ np.abs(sh[2]).T
+        dff = max(dff, wl.d_ff_shared)
+    return 2.0 * (2.0 ** -9 + (wl.d + dff) * 2.0 ** -24) * mag
+
+
 def check_y(wl, y_gpu, y_ref, what=""):
     rms = float(np.sqrt(np.mean(y_ref ** 2)))
     err = float(np.max(np.abs(y_gpu - y_ref)))

@@ -20,6 +20,7 @@ import mixture_experts_layer_31_amd as moe
 import workloads as wk
 from oracle import moe as om
 from gpu_support import (Weights, check_gates, check_permutation, check_routing, check_y,
+                         y_rounding_bound,
                          config_of, dev, log, oracle_route, oracle_y_sampled, run_forward,
                          run_staged, to_dev)
 
@@ -185,6 +186,100 @@ def test_forward_without_statistics(case):
     for key in ("counts", "kept", "n_dropped"):
         assert np.array_equal(counts[key], g[key]), f"{case}: {key}"
     check_permutation(wl, T, counts, counts["idx"])
+
+
+# ------------------------------------------------------------------ seeded sweep of small layers
+
+def _sweep_cases(n=16, seed=2024):
+    """Seeded draws over the layer's parameters (sizes the oracle finishes in seconds)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 3, 8, 16, 40, 64, 96]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        kw = dict(T=int(rng.choice([1, 2, 5, 17, 64, 65, 129, 300])),
+                  d=int(rng.choice([64, 128, 256])), E=E, k=k,
+                  d_ff=int(rng.choice([64, 128, 192])),
+                  dtype=wk.BF16 if rng.random() < 0.75 else wk.F32,
+                  gate=wk.GATE_ALL if rng.random() < 0.3 else wk.GATE_SELECTED)
+        if rng.random() < 0.35:
+            kw.update(n_shared=1, d_ff_shared=int(rng.choice([64, 128, 256])))
+        if rng.random() < 0.35:
+            kw.update(capacity_factor=float(rng.choice([0.5, 1.0, 1.25])), offset_var=1.0)
+        if rng.random() < 0.3:
+            kw.update(bias_range=0.1)
+        cases.append(kw)
+    return cases
+
+
+_SWEEP = _sweep_cases(48)
+
+
+@pytest.mark.parametrize("i", range(len(_SWEEP)))
+def test_seeded_sweep(i):
+    """Layer i of the sweep: routing, permutation, statistics and y against the oracle,
+    and the staged entry points give the fused y bit for bit. y is held to a bound per
+    element from the kernels' rounding points (y_rounding_bound) for bf16 layers, and to
+    1e-5 rms(y) for fp32 ones: a global max/rms bar does not fit layers this small, where
+    capacity drops zero half the rows and single tokens reach 10 rms(y) (the activation's
+    bf16 rounding alone then moves y by 0.024 rms(y), CPU emulation)."""
+    kw = dict(_SWEEP[i])
+    T = kw["T"]
+    wl = _adhoc(f"sweep_{i}", 200 + i, **kw)
+    log(f"[case] sweep {i}: {kw}")
+    W = Weights(wl)
+    inp = wk.make_inputs(wl, T=T)
+    g = run_forward(wl, W, inp.x, T)
+    r, x64 = oracle_route(wl, W, inp.x)
+    check_routing(wl, g["idx"], r)
+    g64, _ = check_gates(wl, g["idx"], g["gates"], r["z"])
+    p = check_permutation(wl, T, g, g["idx"])
+    assert np.allclose(g["f"], g["counts"] / T, rtol=1e-6, atol=0)
+    check_scale_stats(g, r["z"], f"sweep {i}")
+    keep = p["dest"] >= 0
+    y_ref = oracle_y_sampled(wl, W, x64, np.arange(T), g["idx"], g64, keep)
+    assert np.isfinite(g["y"]).all()
+    if wl.dtype == wk.BF16:
+        bound = y_rounding_bound(wl, W, x64, g["idx"], g64, keep)
+        excess = np.abs(g["y"] - y_ref) - bound
+        assert excess.max() <= 1e-6 * float(np.sqrt(np.mean(y_ref ** 2))), float(excess.max())
+    else:
+        check_y(wl, g["y"], y_ref, f"sweep {i}")
+    b = run_staged(wl, W, inp.x, T)
+    assert np.array_equal(g["y"], b["y"]) and np.array_equal(g["idx"], b["idx"])
+
+
+def _bwd_sweep_cases(n=8, seed=77):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 8, 24, 64]))
+        kw = dict(T=int(rng.choice([1, 3, 40, 129, 300])), d=int(rng.choice([256, 512])), E=E,
+                  k=int(rng.integers(1, min(E, 8) + 1)), d_ff=int(rng.choice([256, 512])),
+                  gate=wk.GATE_ALL if rng.random() < 0.3 else wk.GATE_SELECTED,
+                  aux_alpha=0.01 if rng.random() < 0.5 else 0.0)
+        if rng.random() < 0.35:
+            kw.update(n_shared=1, d_ff_shared=int(rng.choice([256, 512])))
+        if rng.random() < 0.35:
+            kw.update(capacity_factor=float(rng.choice([0.5, 1.0, 1.25])), offset_var=1.0)
+        if rng.random() < 0.3:
+            kw.update(bias_range=0.1)
+        cases.append(kw)
+    return cases
+
+
+_BWD_SWEEP = _bwd_sweep_cases()
+
+
+@pytest.mark.parametrize("i", range(len(_BWD_SWEEP)))
+def test_backward_seeded_sweep(i):
+    """Backward of layer i of a seeded sweep (bf16; the backward's widths are multiples
+    of 256) against the oracle, with the bar of test_backward_matches_oracle."""
+    kw = dict(_BWD_SWEEP[i])
+    T = kw["T"]
+    wl = _adhoc(f"bwd_sweep_{i}", 300 + i, dtype=wk.BF16, **kw)
+    log(f"[case] backward sweep {i}: {kw}")
+    _check_backward(wl, T, f"sweep {i}")
 
 
 # ------------------------------------------------------------------ small special cases
@@ -541,20 +636,9 @@ _BWD_CASES = {
 }
 
 
-@pytest.mark.parametrize("case", list(_BWD_CASES))
-def test_backward_matches_oracle(case):
-    """moe_backward against the float64 oracle's gradients of <dy, y> + L_aux, evaluated
-    under the GPU's own routing: dx, dW_r, dW1/dW3/dW2 (and the shared expert's).
-
-    The GEMM operands dyp = g dy, act = silu(h1) h3 and dH are bf16 (unit roundoff
-    u = 2^-9) and every product accumulates in fp32, so each gradient carries a chain of
-    at most three bf16 roundings of independent sign: rms(got - want) is about u rms(want)
-    (measured 0.9-1.2 u) and the bar is 4 u. A weight-gradient element sums products over
-    the expert's rows, and its error scales with that row's and column's magnitude, so the
-    largest error sits 10-14 error-rms out; a 64 u rms(want) bound on the largest element
-    catches a single wrong row or element without tripping on that tail."""
-    kw, T = _BWD_CASES[case]
-    wl = _adhoc(f"bwd_{case}", 110 + list(_BWD_CASES).index(case), T=T, dtype=wk.BF16, **kw)
+def _check_backward(wl, T, case):
+    """moe_backward on layer wl at T tokens against the oracle (the bar of
+    test_backward_matches_oracle)."""
     W = Weights(wl)
     inp = wk.make_inputs(wl, T=T)
     cfg = config_of(wl, T)
@@ -587,19 +671,39 @@ def test_backward_matches_oracle(case):
     if wl.n_shared:
         pairs += [("dws1", ref["dws1"]), ("dws3", ref["dws3"]), ("dws2", ref["dws2"])]
     worst = []
+    # The bars hold per expert for the stacked weight gradients: an expert's gradient
+    # sums over its own rows, so its error scales with its own magnitude, and experts
+    # without rows (exact zeros) would otherwise shrink the rms the bar is taken of.
+    # A gradient that is exactly zero in exact arithmetic (E = 1: the gate is 1 and
+    # the balance loss constant) may carry fp32 cancellation noise: at most 2^-20 of
+    # the case's largest gradient rms.
+    # An expert with a single kept row has a rank-1 gradient (an outer product of two
+    # vectors), whose largest element over its rms is the product of the two factors'
+    # ratios (about 3.5 for a 256-wide normal dy times up to 12 for a SwiGLU activation):
+    # with two bf16 roundings (2u) its worst element sits near 84u, so 128u there.
+    scale = max(float(np.sqrt(np.mean(w ** 2))) for _, w in pairs)
     for name, want in pairs:
         got = g[name]
         assert np.all(np.isfinite(got)), f"{case}: {name} not finite"
-        rms = float(np.sqrt(np.mean(want ** 2)))
-        diff = got - want
-        err_rms = float(np.sqrt(np.mean(diff ** 2)))
-        err = float(np.max(np.abs(diff)))
-        worst.append(f"{name} rms {err_rms / max(rms, 1e-30) / _U_BF16:.2f}u "
-                     f"max {err / max(rms, 1e-30) / _U_BF16:.1f}u")
-        assert err_rms <= 4 * _U_BF16 * rms + 1e-12, \
-            f"{case}: {name} rms|d| {err_rms:.3g} vs rms {rms:.3g}"
-        assert err <= 64 * _U_BF16 * rms + 1e-12, \
-            f"{case}: {name} max|d| {err:.3g} vs rms {rms:.3g}"
+        parts = ([(got[e], want[e], f"{name}[{e}]", 128 if fw["kept"][e] == 1 else 64)
+                  for e in range(want.shape[0])]
+                 if name in ("dw1", "dw3", "dw2") else [(got, want, name, 64)])
+        w_rms, w_max = 0.0, 0.0
+        for gp, wp, what, max_bar in parts:
+            rms = float(np.sqrt(np.mean(wp ** 2)))
+            diff = gp - wp
+            if rms == 0.0:
+                assert float(np.max(np.abs(diff))) <= 2.0 ** -20 * scale, f"{case}: {what}"
+                continue
+            err_rms = float(np.sqrt(np.mean(diff ** 2)))
+            err = float(np.max(np.abs(diff)))
+            w_rms = max(w_rms, err_rms / rms / _U_BF16)
+            w_max = max(w_max, err / rms / _U_BF16)
+            assert err_rms <= 4 * _U_BF16 * rms, \
+                f"{case}: {what} rms|d| {err_rms:.3g} vs rms {rms:.3g}"
+            assert err <= max_bar * _U_BF16 * rms, \
+                f"{case}: {what} max|d| {err:.3g} vs rms {rms:.3g}"
+        worst.append(f"{name} rms {w_rms:.2f}u max {w_max:.1f}u")
     untouched = np.setdiff1d(np.arange(E), fw["idx"].ravel())
     for e in untouched:
         assert not g["dw1"][e].any() and not g["dw2"][e].any()
@@ -608,6 +712,24 @@ def test_backward_matches_oracle(case):
         # (CMU 15-779 notes, §2.5)
         assert not g["dwr"].any()
     log(f"[ok] backward {case}: " + ", ".join(worst))
+
+
+
+@pytest.mark.parametrize("case", list(_BWD_CASES))
+def test_backward_matches_oracle(case):
+    """moe_backward against the float64 oracle's gradients of <dy, y> + L_aux, evaluated
+    under the GPU's own routing: dx, dW_r, dW1/dW3/dW2 (and the shared expert's).
+
+    The GEMM operands dyp = g dy, act = silu(h1) h3 and dH are bf16 (unit roundoff
+    u = 2^-9) and every product accumulates in fp32, so each gradient carries a chain of
+    at most three bf16 roundings of independent sign: rms(got - want) is about u rms(want)
+    (measured 0.9-1.2 u) and the bar is 4 u. A weight-gradient element sums products over
+    the expert's rows, and its error scales with that row's and column's magnitude, so the
+    largest error sits 10-14 error-rms out; a 64 u rms(want) bound on the largest element
+    catches a single wrong row or element without tripping on that tail."""
+    kw, T = _BWD_CASES[case]
+    wl = _adhoc(f"bwd_{case}", 110 + list(_BWD_CASES).index(case), T=T, dtype=wk.BF16, **kw)
+    _check_backward(wl, T, case)
 
 
 def _backward_full_sampled(name, T, n_tokens, n_experts, n_units, seed):
