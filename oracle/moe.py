@@ -332,18 +332,17 @@ def silu(u: np.ndarray) -> np.ndarray:
         return u / (1.0 + np.exp(-u))
 
 
-def swiglu(X: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray) -> np.ndarray:
-    """One SwiGLU expert on rows X[n, d]: (silu(X W1^T) * (X W3^T)) W2^T,
-    with W1, W3 stored [d_ff, d] and W2 stored [d, d_ff]."""
-    X = np.asarray(X, np.float64)
-    a = silu(X @ np.asarray(w1, np.float64).T) * (X @ np.asarray(w3, np.float64).T)
-    return a @ np.asarray(w2, np.float64).T
-
-
 def swiglu_hidden(X, w1, w3) -> np.ndarray:
-    """The SwiGLU hidden activation a = silu(X W1^T) * (X W3^T)."""
+    """The SwiGLU hidden activation a = silu(X W1^T) * (X W3^T) on rows X[n, d],
+    with W1, W3 stored [d_ff, d]: silu on the W1 ("gate") branch."""
     X = np.asarray(X, np.float64)
     return silu(X @ np.asarray(w1, np.float64).T) * (X @ np.asarray(w3, np.float64).T)
+
+
+def swiglu(X: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """One SwiGLU expert on rows X[n, d]: swiglu_hidden(X) W2^T, with W2 stored
+    [d, d_ff]."""
+    return swiglu_hidden(X, w1, w3) @ np.asarray(w2, np.float64).T
 
 
 ExpertFn = Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]

@@ -332,6 +332,25 @@ def test_swiglu_triple_loop():
     assert np.allclose(om.swiglu(X, w1, w3, w2), ref, rtol=1e-13, atol=1e-13)
 
 
+def test_swiglu_hidden_triple_loop():
+    """The hidden activation on its own: silu on the W1 branch times the W3 branch,
+    against a pure-Python loop; the two branches swapped (silu on W3) is a different
+    function, so a transposed operand fails here."""
+    rng = np.random.default_rng(9)
+    n, d, f = 4, 5, 6
+    X = rng.standard_normal((n, d)); w1 = rng.standard_normal((f, d))
+    w3 = rng.standard_normal((f, d))
+    ref = np.zeros((n, f))
+    for r in range(n):
+        for i in range(f):
+            g = sum(X[r, c] * w1[i, c] for c in range(d))
+            u = sum(X[r, c] * w3[i, c] for c in range(d))
+            ref[r, i] = g / (1 + math.exp(-g)) * u
+    got = om.swiglu_hidden(X, w1, w3)
+    assert np.allclose(got, ref, rtol=1e-13, atol=1e-13)
+    assert not np.allclose(om.swiglu_hidden(X, w3, w1), ref, rtol=1e-3, atol=1e-3)
+
+
 def _toy(T=64):
     wl = wk.get("toy_t64")
     inp = wk.make_inputs(wl, T=T)
