@@ -16,8 +16,15 @@ the ceilings this device reaches on both rooflines (an MFMA loop and a
 streaming read). Steps of HBM-bound workloads start from cold caches (a 1 GiB
 read between steps, outside the timed step).
 
+After the headline workload the same line carries "configs": the fused step of
+the other workloads of the metric (Mixtral-shaped decode at 1, 8 and 32 tokens and
+prefill at 512, DeepSeek-shaped at 1, 64 and 4096 tokens, the skewed 16384-token
+load and the Switch layer at three capacity factors, with its balance loss), each
+with tokens/s, TFLOP/s, GB/s and the fractions of both rooflines; and "coverage":
+the expert coverage of decode batches under the GPU's routing against 1 - 0.75^B.
+
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--ep N]
-                  [--backward] [--no-flush] [--no-calibration]
+                  [--backward] [--no-flush] [--no-calibration] [--configs A,B,...]
   python bench.py --calibrate-copy     # plain 1 GiB copies, for counter scaling
 """
 from __future__ import annotations
@@ -40,6 +47,11 @@ METRIC = "MoE-layer tokens/s at 1 GPU + % MFMA peak (prefill) / % HBM BW (decode
 GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_31_amd", "csrc", "gemm_bf16.hip")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_gateup_mixtral_t4096_counters.md")
 CALIB_LIB = os.path.join(ROOT, "mixture_experts_layer_31_amd", "libmoe_calibrate.so")
+# the rest of the metric, timed after the headline workload: the decode rows (HBM),
+# the other prefill shapes, and the Switch layer with its balance loss
+CONFIG_SWEEP = ("mixtral_t1", "mixtral_t8", "mixtral_t32", "mixtral_t512", "deepseek_t1",
+                "deepseek_t64", "deepseek_t4096", "skew_t16384", "switch_t8192_cf1.0",
+                "switch_t8192_cf1.25", "switch_t8192_cf2.0")
 
 
 def log(msg):
@@ -63,6 +75,10 @@ def parse():
     ap.add_argument("--no-calibration", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="also time moe_backward (gradients of the layer) on the same batch")
+    ap.add_argument("--configs", default=",".join(CONFIG_SWEEP),
+                    help="comma-separated workloads timed after the headline one (their "
+                         "fused steps, from cold caches where HBM-bound); empty for none")
+    ap.add_argument("--config-steps", type=int, default=10)
     return ap.parse_args()
 
 
@@ -351,6 +367,15 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, inp, host, args.cpu_sample)
 
+    configs, coverage = None, None
+    names = [n for n in args.configs.split(",") if n]
+    if names and args.ep <= 1:
+        del x, w1, w3, w2, s1, s3, s2, y, y_perm, act, ws_f, ws_r, ws_p, ws_g, ws_d
+        if not args.no_cpu_baseline:
+            del host
+        torch.cuda.empty_cache()
+        configs, coverage = config_sweep(names, args.config_steps, args.no_flush)
+
     out = {
         "metric": METRIC,
         "value": round(T / (ms_step * 1e-3), 1),
@@ -384,8 +409,157 @@ def main():
         "cpu_baseline": cpu,
         "expert_parallel": ep_report,
         "backward": bwd_report,
+        "configs": configs,
+        "coverage": coverage,
     }
     print(json.dumps(out), flush=True)
+
+
+def config_sweep(names, K, no_flush):
+    """The fused step (one moe_forward) of each named workload, K timed steps after 3
+    warm-ups; HBM-bound workloads from cold caches (a 1 GiB read before each step,
+    outside its timing). Work and bytes are counted from each batch's own routing as
+    for the headline. Workloads of one shape share their uploaded weights. Also the
+    GPU-routing coverage of decode batches at the Mixtral shape (CME295 notes §2.3)."""
+    import numpy as np
+    import torch
+    import mixture_experts_layer_31_amd as moe
+    import workloads as wk
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    scratch = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.zeros((), dtype=torch.float32, device=dev)
+    shape = None
+    W = None
+    out = []
+    coverage = None
+
+    def up(a, dtype):
+        a = np.ascontiguousarray(a)
+        if dtype == wk.BF16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    for name in names:
+        wl = wk.get(name)
+        key = (wl.config_id, wl.d, wl.E, wl.d_ff, wl.n_shared)
+        t0 = time.time()
+        if key != shape:
+            W = None
+            torch.cuda.empty_cache()
+            inp = wk.make_inputs(wl)
+            W = {"w": tuple(up(a, wl.dtype) for a in inp.expert_stacks())}
+            sh = inp.shared()
+            W["s"] = tuple(up(a, wl.dtype) for a in sh) if sh is not None else (None,) * 3
+            W["wr"] = up(inp.w_router, wl.dtype)
+            W["bias"] = torch.from_numpy(inp.bias).to(dev) if inp.bias is not None else None
+            shape = key
+        else:
+            inp = wk.make_inputs(wl)
+        T = wl.T
+        x = up(inp.x, wl.dtype)
+        cfg = moe.make_config(T, wl.d, wl.E, wl.k, wl.d_ff, n_shared=wl.n_shared,
+                              d_ff_shared=wl.d_ff_shared, gate=wl.gate, dtype=wl.dtype,
+                              capacity_factor=wl.capacity_factor, aux_alpha=wl.aux_alpha)
+        y = torch.empty((T, wl.d), dtype=torch.float32, device=dev)
+        ws = moe.alloc_workspace(cfg, moe.STAGE_FORWARD)
+        st = moe.Stats.alloc(wl.E)
+
+        def fused(stats=None):
+            moe.forward(cfg, x, W["wr"], W["bias"], *W["w"], *W["s"], y, None, None, stats, ws,
+                        stream)
+
+        fused(st)
+        torch.cuda.synchronize()
+        kept = st.kept.cpu().numpy().astype(np.int64)
+        R_kept, touched = int(kept.sum()), int((kept > 0).sum())
+        elt = 2 if wl.dtype == wk.BF16 else 4
+        d, dff, dffs, nsh = wl.d, wl.d_ff, wl.d_ff_shared, wl.n_shared
+        F = 2.0 * T * d * wl.E + 6.0 * d * dff * R_kept + 6.0 * d * dffs * T * nsh
+        B = (touched * 3.0 * d * dff * elt + nsh * 3.0 * d * dffs * elt + wl.E * d * elt
+             + T * d * elt + T * d * 4.0)
+        peak_f = PEAK_BF16_TFLOPS if wl.dtype == wk.BF16 else PEAK_F32_TFLOPS
+        bound = "mfma" if F / (peak_f * 1e12) >= B / (PEAK_HBM_GBPS * 1e9) else "hbm"
+        flush = bound == "hbm" and not no_flush
+        for _ in range(3):
+            fused()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(K)]
+        for i in range(K):
+            if flush:
+                torch.sum(scratch, dim=0, out=sink)
+            evs[i][0].record(stream)
+            fused()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms_all = np.array([a.elapsed_time(b) for a, b in evs])
+        ms = float(ms_all.mean())
+        tf = F / (ms * 1e-3) / 1e12
+        gb = B / (ms * 1e-3) / 1e9
+        rec = {"workload": name, "T": T, "ms": round(ms, 4),
+               "ms_median": round(float(np.median(ms_all)), 4),
+               "tokens_per_s": round(T / (ms * 1e-3), 1), "tflops": round(tf, 2),
+               "gbps": round(gb, 1), "bound": bound, "frac_mfma": round(tf / peak_f, 4),
+               "frac_hbm": round(gb / PEAK_HBM_GBPS, 4),
+               "frac_bound": round((tf / peak_f) if bound == "mfma" else (gb / PEAK_HBM_GBPS), 4),
+               "cold_caches": flush, "kept_rows": R_kept, "touched_experts": touched,
+               "algorithmic_flops": F, "algorithmic_bytes": B}
+        if wl.capacity_factor > 0:
+            rec["capacity_factor"] = wl.capacity_factor
+            rec["n_dropped"] = int(st.n_dropped.cpu()[0])
+        if wl.aux_alpha > 0:
+            rec["aux_loss"] = round(float(st.aux.cpu()[0]), 6)
+            rec["aux_alpha"] = wl.aux_alpha
+        counts = st.counts.cpu().numpy().astype(np.int64)
+        rec["max_over_mean_load"] = round(float(counts.max() / (T * wl.k / wl.E)), 3)
+        out.append(rec)
+        log(f"[bench] {name}: {ms:.4f} ms/step, {rec['frac_bound']:.3f} of the {bound} roofline "
+            f"({time.time() - t0:.1f}s)")
+        if wl.config_id == 2 and coverage is None:
+            coverage = gpu_coverage(wl, W, stream)
+        del x, y, ws, st
+    del scratch, sink, W
+    torch.cuda.empty_cache()
+    return out, coverage
+
+
+def gpu_coverage(wl, W, stream, n=2000, Bs=(1, 2, 4, 8, 16, 32)):
+    """Fraction of the experts a batch of B tokens touches under the GPU's routing
+    (moe_route on n * 32 seeded tokens, batches of consecutive tokens), against
+    1 - (1 - k/E)^B, with the standard error of the mean from the exact variance of the
+    untouched-expert count under uniform top-k choices."""
+    import math
+    import numpy as np
+    import torch
+    import mixture_experts_layer_31_amd as moe
+    import workloads as wk
+
+    dev = torch.device("cuda:0")
+    T = n * max(Bs)
+    cfg = moe.make_config(T, wl.d, wl.E, wl.k, wl.d_ff, gate=wl.gate, dtype=wl.dtype)
+    a = np.ascontiguousarray(wk.make_inputs(wl, T=T).x)
+    x = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    idx = torch.empty((T, wl.k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, wl.k), dtype=torch.float32, device=dev)
+    moe.route(cfg, x, W["wr"], None, idx, gates, None, moe.alloc_workspace(cfg, moe.STAGE_ROUTE),
+              stream)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    E, k = wl.E, wl.k
+    res = {"batches": n, "B": [], "gpu": [], "closed_form": [], "se": [], "within_3se": True}
+    for B in Bs:
+        cov = np.array([np.unique(gi[i * B:(i + 1) * B]).size / E for i in range(n)])
+        q = (1 - k / E) ** B
+        q2 = (math.comb(E - 2, k) / math.comb(E, k)) ** B
+        se = math.sqrt(max(E * q * (1 - q) + E * (E - 1) * (q2 - q * q), 0.0) / E ** 2 / n)
+        res["B"].append(B)
+        res["gpu"].append(round(float(cov.mean()), 5))
+        res["closed_form"].append(round(1 - q, 5))
+        res["se"].append(float(f"{se:.2e}"))
+        res["within_3se"] &= bool(abs(cov.mean() - (1 - q)) <= 3 * se + 1e-12)
+    return res
 
 
 def time_backward(args, cfg, wl, x, wr, bias, experts, shared, R_kept, stream, peak_f):

@@ -349,14 +349,16 @@ __global__ __launch_bounds__(1024) void index_single_kernel(
 // statistics) and then the single-workgroup index. Wave w selects the tokens
 // w, w + 16, ...; their choices go to idx and gates and to LDS, from where the
 // index body reads them after a barrier. One launch instead of two for the
-// decode-sized steps of the fused forward.
+// decode-sized steps of the fused forward. The caller may place the tile table
+// over the logits (z and tiles may alias, hence no __restrict__ on either): every
+// logit is read before the barrier that precedes the first tile store.
 template <int NE>
 __global__ __launch_bounds__(1024) void route_index_single_kernel(
-    const float* __restrict__ z, const float* __restrict__ bias, int T, int k, int E,
+    const float* z, const float* __restrict__ bias, int T, int k, int E,
     int gate_all, int32_t* __restrict__ idx, float* __restrict__ gates, long long C,
     int32_t* __restrict__ offsets, int32_t* __restrict__ dest, int32_t* __restrict__ src,
     int32_t* __restrict__ counts_out, int32_t* __restrict__ kept_out,
-    int32_t* __restrict__ n_dropped, int BM, int max_tiles, int4* __restrict__ tiles) {
+    int32_t* __restrict__ n_dropped, int BM, int max_tiles, int4* tiles) {
   extern __shared__ uint32_t smem[];
   const int nkeys = C >= 0 ? E * k : E;   // as index_keys()
   int32_t* sidx = reinterpret_cast<int32_t*>(smem + index_single_words(E, nkeys));   // [T][k]

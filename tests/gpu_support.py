@@ -14,6 +14,7 @@ import torch
 import mixture_experts_layer_31_amd as moe
 import workloads as wk
 from oracle import moe as om
+from rounding_model import y_bound
 
 NEAR_TIE = 1e-3          # tokens whose k-th/(k+1)-th score margin is below this are flagged
 Y_TOL_F32 = 1e-5         # max|dy| <= 1e-5 * rms(y) for fp32 inputs
@@ -114,10 +115,12 @@ def run_forward(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int, bias="d
                 max_prob=float(st.max_prob.cpu()[0]), top_gap=float(st.top_gap.cpu()[0]))
 
 
-def run_staged(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int, ep: int = 0):
+def run_staged(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int, ep: int = 0,
+               keep_perm: bool = True):
     """route -> permute -> expert_ffn -> combine through the staged entry points; ep > 1
     lays the rows out as ep simulated expert-parallel ranks (and returns the send-row
-    matrix as "traffic")."""
+    matrix as "traffic"). keep_perm=False skips the gathered rows x_perm (permute with
+    no gather) and does not copy y_perm back (full-size layers)."""
     cfg = config_of(wl, T)
     cfg.ep_ranks = ep
     G = wl.E * (ep if ep > 1 else 1)
@@ -131,7 +134,7 @@ def run_staged(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int, ep: int 
     rows = R + wl.n_shared * T
     y_perm = torch.zeros((rows, wl.d), dtype=torch.float32, device=dev())
     y = torch.empty((T, wl.d), dtype=torch.float32, device=dev())
-    x_perm = torch.zeros((R, wl.d), dtype=x.dtype, device=dev())
+    x_perm = torch.zeros((R, wl.d), dtype=x.dtype, device=dev()) if keep_perm else None
     st = moe.Stats.alloc(wl.E, groups=G)
     moe.route(cfg, x, W.wr, W.bias, idx, gates, st, moe.alloc_workspace(cfg, moe.STAGE_ROUTE))
     moe.permute(cfg, idx, x, offsets, dest, src, x_perm, st,
@@ -147,8 +150,11 @@ def run_staged(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int, ep: int 
     out = dict(y=y.cpu().numpy(), idx=idx.cpu().numpy().astype(np.int64), gates=gates.cpu().numpy(),
                offsets=offsets.cpu().numpy(), dest=dest.cpu().numpy(), src=src.cpu().numpy(),
                counts=st.counts.cpu().numpy(), kept=st.kept.cpu().numpy(),
-               n_dropped=int(st.n_dropped.cpu()[0]), y_perm=y_perm.cpu().numpy(),
+               n_dropped=int(st.n_dropped.cpu()[0]),
                traffic=None if traffic is None else traffic.cpu().numpy().reshape(ep, ep))
+    if not keep_perm:
+        return out
+    out["y_perm"] = y_perm.cpu().numpy()
     if wl.dtype == wk.BF16:
         out["x_perm"] = x_perm.view(torch.int16).cpu().numpy().view(np.uint16)
     else:
@@ -202,32 +208,11 @@ def check_permutation(wl, T, gpu, gpu_idx):
 
 
 def y_rounding_bound(wl, W: Weights, x64, idx, gates64, keep):
-    """Per-element bound on |y_gpu - y| for bf16 layers, from the kernels' rounding points:
-    the SwiGLU activation is rounded to bf16 (relative 2^-9) before the second product, so
-    an output element moves by at most 2^-9 sum_j g_j sum_f |act_jf w2_e,if| (+ the shared
-    expert's term with weight 1); the fp32 accumulations of the two products add at most
-    (d + d_ff) 2^-24 of the same magnitudes (the first product's error passes through
-    silu and the gate's product with a factor below 2). Returned doubled, [T, d]."""
-    T = x64.shape[0]
-    mag = np.zeros((T, wl.d))
-    need = {}
-    for t in range(T):
-        for j in range(wl.k):
-            if keep[t, j]:
-                need.setdefault(int(idx[t, j]), []).append((t, j))
-    for e in sorted(need):
-        w1, w3, w2 = W.expert64(e)
-        rows = need[e]
-        act = np.abs(om.swiglu_hidden(x64[[t for t, _ in rows]], w1, w3))
-        out = act @ np.abs(w2).T
-        for (t, j), o in zip(rows, out):
-            mag[t] += abs(gates64[t, j]) * o
-    sh = W.shared64()
-    dff = wl.d_ff
-    if sh is not None:
-        mag += np.abs(om.swiglu_hidden(x64, sh[0], sh[1])) @ np.abs(sh[2]).T
-        dff = max(dff, wl.d_ff_shared)
-    return 2.0 * (2.0 ** -9 + (wl.d + dff) * 2.0 ** -24) * mag
+    """Per-element bound on |y_gpu - y| for bf16 layers from the kernels' rounding points
+    (rounding_model.y_bound: the activation's bf16 rounding before the second product
+    plus the fp32 accumulation of both products), [T, d]."""
+    return y_bound(wl.d, wl.d_ff, x64, idx, gates64, keep, W.expert64, W.shared64(),
+                   wl.d_ff_shared)
 
 
 def check_y(wl, y_gpu, y_ref, what=""):
