@@ -220,7 +220,9 @@ def main():
     offsets = torch.empty(G + 1, dtype=i32, device=dev)
     dest = torch.empty((T, wl.k), dtype=i32, device=dev)
     src = torch.empty(R, dtype=i32, device=dev)
-    act = torch.empty((rows, moe.act_stride(cfg)), dtype=x.dtype, device=dev)
+    # the SwiGLU activation between the two entry points: IEEE half for bf16 layers
+    act = torch.empty((rows, moe.act_stride(cfg)),
+                      dtype=torch.float16 if wl.dtype == wk.BF16 else torch.float32, device=dev)
     y_perm = torch.empty((rows, wl.d), dtype=torch.float32, device=dev)
     y = torch.empty((T, wl.d), dtype=torch.float32, device=dev)
     ws_r = moe.alloc_workspace(cfg, moe.STAGE_ROUTE)

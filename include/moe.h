@@ -215,7 +215,11 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* idx, const void* x,
  *   (x then holds T*k pre-permuted rows; n_shared must be 0).
  *   -> y_perm fp32 [T*k + n_shared*T, d]; rows outside the groups and the
  *   shared block are left untouched.
- *   The SwiGLU hidden activation is rounded to elt before the W2 product.   */
+ *   The SwiGLU hidden activation is rounded before the W2 product: to IEEE
+ *   half (11-bit significand, round to nearest even) for bf16 layers, whose W2
+ *   is then widened to half inside the product (exact for |w| >= 2^-17; smaller
+ *   weights move by at most 2^-25); to fp32 for fp32 layers. Half overflows
+ *   above 65504, an activation magnitude the layer's inputs never approach.  */
 moe_status moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* src,
                           const int32_t* offsets, const void* w1, const void* w3,
                           const void* w2, const void* ws1, const void* ws3,
@@ -223,17 +227,19 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* s
                           void* stream);
 
 /* First half of moe_expert_ffn: the SwiGLU hidden activation
- * act[r] = silu(W1_e u) * (W3_e u) (rounded to elt) for every grouped row r,
- * data rows as in moe_expert_ffn, and for the shared expert act[T*k + t] from
- * x[t] with ws1, ws3. act is elt [T*k + n_shared*T, moe_act_stride(cfg)];
- * routed rows use the first d_ff columns, shared rows the first d_ff_shared.  */
+ * act[r] = silu(W1_e u) * (W3_e u) for every grouped row r, data rows as in
+ * moe_expert_ffn, and for the shared expert act[T*k + t] from x[t] with ws1,
+ * ws3. act is [T*k + n_shared*T, moe_act_stride(cfg)] of IEEE half (bf16
+ * layers) or fp32 (fp32 layers), 2 or 4 bytes per element; routed rows use the
+ * first d_ff columns, shared rows the first d_ff_shared.                      */
 moe_status moe_expert_gateup(const moe_config* cfg, const void* x, const int32_t* src,
                              const int32_t* offsets, const void* w1, const void* w3,
                              const void* ws1, const void* ws3, void* act,
                              void* ws, size_t ws_bytes, void* stream);
 
 /* Second half: y_perm[r] = W2_e act[r] in fp32 for every grouped row, and
- * y_perm[T*k + t] = Ws2 act[T*k + t] for the shared expert.                  */
+ * y_perm[T*k + t] = Ws2 act[T*k + t] for the shared expert; act as written by
+ * moe_expert_gateup (half for bf16 layers).                                  */
 moe_status moe_expert_down(const moe_config* cfg, const void* act, const int32_t* offsets,
                            const void* w2, const void* ws2, float* y_perm,
                            void* ws, size_t ws_bytes, void* stream);

@@ -30,6 +30,48 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+
+// Two fp32 -> IEEE half (round to nearest even; v_cvt_pk_f16_f32), lo in bits 0-15.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+}
+
+// Eight bf16 -> eight IEEE half, in place of a fragment. Exact for |v| >= 2^-17
+// (bf16's 8-bit significand fits half's 11 bits down to half's subnormals of step
+// 2^-24); smaller magnitudes round to that step (error <= 2^-25); |v| > 65504
+// overflows (not a weight or activation magnitude this layer meets).
+__device__ __forceinline__ bf16x8 bf16x8_to_f16(bf16x8 v) {
+  const u32x4 u = __builtin_bit_cast(u32x4, v);
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = pack_f16x2(__uint_as_float(u[i] << 16), __uint_as_float(u[i] & 0xFFFF0000u));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// v_mfma_f32_32x32x16 on bf16 operands, or (H16) on half operands held in the
+// same 16-byte registers
+template <bool H16>
+__device__ __forceinline__ f32x16 mfma32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (H16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <bool H16>
+__device__ __forceinline__ f32x4 mfma16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  if constexpr (H16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // Element loaders: 8 consecutive elements widened to fp32.
 template <typename T> struct Elt;
 template <> struct Elt<float> {

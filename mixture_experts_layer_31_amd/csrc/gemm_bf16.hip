@@ -35,7 +35,10 @@
 
 namespace moe {
 
-template <int BM, int BN, int WM, int WN, bool GATEUP>
+// H16: gate/up writes the activation as IEEE half; down takes half activation
+// rows, widens its bf16 weights to half as they are staged, and multiplies on half
+// MFMAs.
+template <int BM, int BN, int WM, int WN, bool GATEUP, bool H16>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(
     const int32_t* __restrict__ tiles, int max_tiles, int n_single, int n_logical,
     const uint16_t* __restrict__ xa,      // A rows: x (gate/up) or act (down)
@@ -117,7 +120,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < XC; ++i) *reinterpret_cast<u32x4*>(xs + xoff[i]) = xr[i];
 #pragma unroll
-    for (int i = 0; i < WC; ++i) *reinterpret_cast<u32x4*>(ws + woff[i]) = wr[i];
+    for (int i = 0; i < WC; ++i) {
+      u32x4 w = wr[i];
+      if constexpr (H16 && !GATEUP)
+        w = __builtin_bit_cast(u32x4, bf16x8_to_f16(__builtin_bit_cast(bf16x8, w)));
+      *reinterpret_cast<u32x4*>(ws + woff[i]) = w;
+    }
   };
 
   const int nk = K / kBK;
@@ -150,7 +158,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(
       for (int a = 0; a < MT; ++a)
 #pragma unroll
         for (int b = 0; b < NTW; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[b], bfr[a], acc[a][b], 0, 0, 0);
+          acc[a][b] = mfma32x16<H16 && !GATEUP>(afr[b], bfr[a], acc[a][b]);
     }
     if (kt + 1 < nk) lstore(cur ^ 1);
     __syncthreads();
@@ -173,8 +181,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(
           for (int q = 0; q < 4; ++q)
             h[q] = silu(acc[a][b][4 * rq + q]) * acc[a][NT + b][4 * rq + q];
           u32x2 pk;
-          pk[0] = pack_bf16x2(h[0], h[1]);
-          pk[1] = pack_bf16x2(h[2], h[3]);
+          pk[0] = H16 ? pack_f16x2(h[0], h[1]) : pack_bf16x2(h[0], h[1]);
+          pk[1] = H16 ? pack_f16x2(h[2], h[3]) : pack_bf16x2(h[2], h[3]);
           *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow * out_stride + n) = pk;
         } else {
           f32x4 v;
@@ -226,8 +234,9 @@ constexpr int short_ring_stages(int xs, int wr) {
   return 4 * (xs + wr) * kRowBytes <= static_cast<int>(kMaxLdsBytes) ? 4 : 3;
 }
 
+// H16: as gemm_bf16_kernel (half activations; down widens its weight fragments).
 template <int BM, int BN, int WM, int WN, bool GATEUP, int ST, bool HOUT = false, bool SK = false,
-          bool NF = false, int XS = 0>
+          bool NF = false, int XS = 0, bool H16 = false>
 __global__ __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_lds_kernel(
     const int32_t* __restrict__ tiles, int max_tiles, int n_single, int n_logical,
@@ -236,7 +245,9 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
     void* __restrict__ out, int out_stride, int out_row0, int K, int N,
     float* __restrict__ h1o, float* __restrict__ h3o, float* __restrict__ sk_part) {
   static_assert(!HOUT || GATEUP, "pre-activations come from the gate/up product");
+  static_assert(!HOUT || !H16, "the backward's activation stays bf16");
   static_assert(!SK || !GATEUP, "stream-K splits plain fp32 products");
+  constexpr bool WIDEN = H16 && !GATEUP;   // half activation rows x widened weights
   constexpr int NW = WM * WN;
   constexpr int WR = GATEUP ? 2 * BN : BN;     // weight rows per tile
   constexpr int XD = BM / 8 / NW;              // LDS-DMA instructions per wave per stage
@@ -350,6 +361,7 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
       for (int b = 0; b < NTW; ++b) {
         const int wrow = (b < NT) ? wn * (BN / WN) + b * 32 : BN + wn * (BN / WN) + (b - NT) * 32;
         fa[kk][b] = *reinterpret_cast<const bf16x8*>(ws + wrow * kRowBytes + koff[kk]);
+        if constexpr (WIDEN) fa[kk][b] = bf16x8_to_f16(fa[kk][b]);
       }
 #pragma unroll
       for (int a = 0; a < NA; ++a)
@@ -361,7 +373,7 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
       for (int a = 0; a < NA; ++a)
 #pragma unroll
         for (int b = 0; b < NTW; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][b], fb[kk][a], acc[a][b], 0, 0, 0);
+          acc[a][b] = mfma32x16<WIDEN>(fa[kk][b], fb[kk][a], acc[a][b]);
     };
 
     // one barrier per K-step: it publishes stage kt (every thread waited for its
@@ -454,8 +466,8 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
             for (int q = 0; q < 4; ++q)
               h[q] = silu(acc[a][b][4 * rq + q]) * acc[a][NT + b][4 * rq + q];
             u32x2 pk;
-            pk[0] = pack_bf16x2(h[0], h[1]);
-            pk[1] = pack_bf16x2(h[2], h[3]);
+            pk[0] = H16 ? pack_f16x2(h[0], h[1]) : pack_bf16x2(h[0], h[1]);
+            pk[1] = H16 ? pack_f16x2(h[2], h[3]) : pack_bf16x2(h[2], h[3]);
             *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow * out_stride + n) = pk;
             if constexpr (HOUT) {
               f32x4 v1, v3;
@@ -518,13 +530,13 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
 // between shares p and p + 1, recomputed as in the GEMM, q the q-th quarter of
 // the tile's rows. One fp32 addition per element, so the result does not depend
 // on which part finished first.
-template <int BM, int BN>
+template <int BM, int BN, int BK>
 __global__ __launch_bounds__(256) void streamk_fixup_kernel(
     const int32_t* __restrict__ tiles, int max_tiles, int n_single, int K, int N, int P,
     const float* __restrict__ sk_part, float* __restrict__ out, int out_stride, int out_row0) {
   __shared__ int s_real;
   const int n_real = real_tiles<BM>(tiles, max_tiles, n_single, &s_real);
-  const int nk_all = K / kBK;
+  const int nk_all = K / BK;   // the GEMM's K-steps
   const long long U = static_cast<long long>(n_real) * (N / BN) * nk_all;
   if (U < static_cast<long long>(P) * nk_all) return;   // nothing was split
   const int p = blockIdx.x;
@@ -545,6 +557,250 @@ __global__ __launch_bounds__(256) void streamk_fixup_kernel(
     *y = *y + v;
   }
 }
+// ---------------------------------------------------------------- large tiles, one wave per SIMD
+//
+// 256 x 256 tiles (256 token rows x 256 weight rows: gate/up 128 gate + 128 up
+// columns, down 256 columns), four waves of 128 x 128 each (one per SIMD), so a
+// wave reads 8 fragments per 16 MFMAs (two waves of 128 x 64 read 12 per 16).
+// K-steps of 32: a stage is 256 token + 256 weight rows of 64 bytes (32 KB),
+// filled by LDS-DMA (16 rows per instruction; the four 16-byte chunks of a row
+// XOR-swizzled by (row >> 1) & 3, so the fragment reads of eight consecutive rows
+// hit distinct banks) in a ring of ST stages, so ST - 1 stages of loads are in
+// flight while a stage is multiplied. One barrier per K-step; the fragments of a
+// step's second k-slice are read before the next barrier and its MFMAs issued
+// after it, so the matrix pipe stays busy across the barrier while the next
+// step's first fragments are read.
+constexpr int kW4BK = 32;          // K per step
+constexpr int kW4Row = 64;         // LDS row bytes (32 bf16)
+constexpr int kW4Stage = 512 * kW4Row;   // 256 token + 256 weight rows
+
+// H16: as gemm_bf16_kernel (half activations; down widens its weight fragments).
+template <bool GATEUP, int ST, bool SK, bool NF, bool H16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+gemm_bf16_w4_kernel(const int32_t* __restrict__ tiles, int max_tiles, int n_single,
+                    int n_logical, const uint16_t* __restrict__ xa,
+                    const int32_t* __restrict__ src, int a_stride, int a_row0,
+                    const uint16_t* __restrict__ w_a, const uint16_t* __restrict__ w_b,
+                    long long w_stride, void* __restrict__ out, int out_stride, int out_row0,
+                    int K, int N, float* __restrict__ sk_part) {
+  static_assert(!SK || !GATEUP, "stream-K splits plain fp32 products");
+  static_assert(ST >= 3 && ST * kW4Stage <= static_cast<int>(kMaxLdsBytes), "ring must fit");
+  constexpr int BM = 256, BN = GATEUP ? 128 : 256;
+  constexpr int ND = 8;   // LDS-DMA instructions per wave per stage (4 token, 4 weight)
+  constexpr bool WIDEN = H16 && !GATEUP;   // half activation rows x widened weights
+  extern __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nk_all = K / kW4BK;
+
+  auto run_tile = [&](int m_tile, int n_tile, int kt0, int kt1, float* part) {
+    if constexpr (SK) __syncthreads();   // the previous tile's reads of the ring are done
+    const TileCoord tc = lookup_tile(tiles, n_single, BM, m_tile);
+    if (tc.rows <= 0) return;
+    const int nk = kt1 - kt0;
+    const int n0 = n_tile * BN;
+
+    // DMA instruction j of this wave fills rows 16 * (4 * (j % 4) + wave) .. + 15
+    // of the token (j < 4) or weight (j >= 4) half of a stage; lane l writes row
+    // + l / 4, physical chunk l % 4, which holds logical chunk (l % 4) ^ ((l >> 3) & 3)
+    const int lrow = lane >> 2;
+    const int lchunk = (lane & 3) ^ ((lane >> 3) & 3);
+    const uint16_t* gp[ND];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * (4 * j + wave) + lrow;
+      int grow = tc.row0 + min(r, tc.rows - 1);
+      if (src != nullptr) grow = src[grow];
+      gp[j] = xa + (static_cast<size_t>(a_row0) + grow) * a_stride + lchunk * 8 +
+              static_cast<size_t>(kt0) * kW4BK;
+    }
+    const size_t wbase = static_cast<size_t>(tc.group) * w_stride;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * (4 * j + wave) + lrow;
+      const uint16_t* wsrc = (!GATEUP || r < BN) ? w_a : w_b;
+      const int n = n0 + ((GATEUP && r >= BN) ? r - BN : r);
+      gp[4 + j] = wsrc + wbase + static_cast<size_t>(n) * K + lchunk * 8 +
+                  static_cast<size_t>(kt0) * kW4BK;
+    }
+    // instructions [J0, J1) of stage kt into ring slot buf; every wave issues all
+    // eight (rows past a ragged tile's end load its last row again and are never
+    // stored), so the count of loads in flight is the same on every wave
+    auto dma = [&](int kt, int buf, auto j0_c, auto j1_c) {
+      constexpr int J0 = decltype(j0_c)::value, J1 = decltype(j1_c)::value;
+      unsigned char* st = lds_raw + buf * kW4Stage;
+#pragma unroll
+      for (int j = J0; j < J1; ++j) {
+        unsigned char* dst = st + (j >= 4 ? BM * kW4Row : 0) + (4 * (j & 3) + wave) * 16 * kW4Row;
+        MOE_LDS_DMA16(gp[j] + kt * kW4BK, dst);
+      }
+    };
+
+    // fragment of 32-row block `blk` of a stage's token (tok) or weight half at
+    // k-slice kk: row lane % 32, logical chunk 2 kk + lane / 32
+    const int frow = lane & 31;
+    const int fsw = (frow >> 1) & 3;
+    const int foff0 = frow * kW4Row + (((0 + (lane >> 5)) ^ fsw) << 4);
+    const int foff1 = frow * kW4Row + (((2 + (lane >> 5)) ^ fsw) << 4);
+    // this wave's weight blocks: gate/up the gate and up rows of its 64 columns
+    int wblk[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      wblk[b] = GATEUP ? (b < 2 ? wn * 2 + b : 4 + wn * 2 + (b - 2)) : wn * 4 + b;
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+    // token block a of this wave is the tile's 32-row block 2 a + wm
+    auto rfrag = [&](int buf, int kk, bf16x8 (&fa)[4], bf16x8 (&fb)[4], auto na_c) {
+      constexpr int NA = decltype(na_c)::value;
+      const unsigned char* st = lds_raw + buf * kW4Stage;
+      const int fo = kk ? foff1 : foff0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        fa[b] = *reinterpret_cast<const bf16x8*>(st + BM * kW4Row + wblk[b] * 32 * kW4Row + fo);
+        if constexpr (WIDEN) fa[b] = bf16x8_to_f16(fa[b]);
+      }
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+        fb[a] = *reinterpret_cast<const bf16x8*>(st + (2 * a + wm) * 32 * kW4Row + fo);
+    };
+    auto mfmas = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4], auto na_c) {
+      constexpr int NA = decltype(na_c)::value;
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[a][b] = mfma32x16<WIDEN>(fa[b], fb[a], acc[a][b]);
+    };
+
+    auto kloop = [&](auto na_c) {
+      using I0 = std::integral_constant<int, 0>;
+      using I4 = std::integral_constant<int, 4>;
+      using I8 = std::integral_constant<int, 8>;
+#pragma unroll
+      for (int p = 0; p < ST - 1; ++p)
+        if (p < nk) dma(p, p, I0{}, I8{});
+      bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+      int cur = 0;
+      for (int kt = 0; kt < nk; ++kt) {
+        // stage kt has landed once no more than the later stages' loads are outstanding
+        const int later = min(ST - 2, nk - 1 - kt);
+        if (later == ST - 2) MOE_WAIT_VMCNT((ST - 2) * ND);
+        else wait_vmcnt_at_most<(ST - 2) * ND>(later * ND);
+        dma_barrier();   // publishes stage kt; every read of slot (kt - 1) % ST is done
+        const int ahead = kt + ST - 1;
+        const int nbuf = cur == 0 ? ST - 1 : cur - 1;
+        if (ahead < nk) dma(ahead, nbuf, I0{}, I4{});
+        MOE_SCHED_FENCE();
+        rfrag(cur, 0, fa0, fb0, na_c);
+        if (kt > 0) mfmas(fa1, fb1, na_c);       // second slice of the previous step
+        if (ahead < nk) dma(ahead, nbuf, I4{}, I8{});
+        MOE_SCHED_FENCE();
+        rfrag(cur, 1, fa1, fb1, na_c);
+        mfmas(fa0, fb0, na_c);
+        cur = cur + 1 == ST ? 0 : cur + 1;
+      }
+      mfmas(fa1, fb1, na_c);
+    };
+    const int nb = (min(tc.rows, BM) + 31) / 32;
+    const int na_count = (nb - wm + 1) / 2;
+    with_count<4>(na_count, [&](auto na_c) { kloop(na_c); });
+
+    if constexpr (SK) {
+      if (part != nullptr) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int m = (2 * a + wm) * 32 + frow;
+          if (m >= tc.rows) continue;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+              f32x4 v;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[q] = acc[a][b][4 * rq + q];
+              *reinterpret_cast<f32x4*>(part + static_cast<size_t>(m) * BN + wblk[b] * 32 +
+                                        8 * rq + 4 * (lane >> 5)) = v;
+            }
+        }
+        return;
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int m = (2 * a + wm) * 32 + frow;
+      if (m >= tc.rows) continue;
+      const size_t orow = static_cast<size_t>(out_row0) + tc.row0 + m;
+      if constexpr (GATEUP) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const int n = n0 + wn * 64 + b * 32 + 8 * rq + 4 * (lane >> 5);
+            float h[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              h[q] = silu(acc[a][b][4 * rq + q]) * acc[a][b + 2][4 * rq + q];
+            u32x2 pk;
+            pk[0] = H16 ? pack_f16x2(h[0], h[1]) : pack_bf16x2(h[0], h[1]);
+            pk[1] = H16 ? pack_f16x2(h[2], h[3]) : pack_bf16x2(h[2], h[3]);
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow * out_stride + n) = pk;
+          }
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const int n = n0 + wblk[b] * 32 + 8 * rq + 4 * (lane >> 5);
+            f32x4 v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = acc[a][b][4 * rq + q];
+            *reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow * out_stride + n) = v;
+          }
+      }
+    }
+  };
+
+  if constexpr (!SK) {
+    int m_tile, n_tile;
+    if constexpr (NF) xcd_tile_nfast(max_tiles, N / BN, m_tile, n_tile);
+    else if (tile_order_blocked(BM, N / BN)) xcd_tile_blocked(max_tiles, N / BN, m_tile, n_tile);
+    else xcd_tile(n_logical, max_tiles, m_tile, n_tile);
+    if (m_tile < 0) return;
+    run_tile(m_tile, n_tile, 0, nk_all, nullptr);
+  } else {
+    __shared__ int s_real;
+    const int n_real = real_tiles<BM>(tiles, max_tiles, n_single, &s_real);
+    const long long n_tiles = static_cast<long long>(n_real) * (N / BN);
+    const long long U = n_tiles * nk_all;
+    const int P = gridDim.x;
+    const int L = blockIdx.x;
+    const int p = (L & 7) * (P >> 3) + (L >> 3);
+    if (U < static_cast<long long>(P) * nk_all) {
+      for (long long t = p; t < n_tiles; t += P)
+        run_tile(static_cast<int>(t % n_real), static_cast<int>(t / n_real), 0, nk_all, nullptr);
+      return;
+    }
+    const long long u1 = U * (p + 1) / P;
+    for (long long u = U * p / P; u < u1;) {
+      const long long t = u / nk_all;
+      const int kt0 = static_cast<int>(u - t * nk_all);
+      const int kt1 = static_cast<int>(min(static_cast<long long>(nk_all), kt0 + (u1 - u)));
+      float* part = kt1 < nk_all ? sk_part + static_cast<size_t>(p) * BM * BN : nullptr;
+      run_tile(static_cast<int>(t % n_real), static_cast<int>(t / n_real), kt0, kt1, part);
+      u += kt1 - kt0;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- decode tiles
 //
 // Groups of at most a few rows (decode): the time is reading the experts'
@@ -576,7 +832,8 @@ static __host__ __device__ long long stream_seg_items(const StreamSeg& seg) {
   return seg.rows > 0 ? static_cast<long long>((seg.rows + 15) >> 4) * (seg.N >> 4) : 0;
 }
 
-template <bool GATEUP, int U, int KS>
+// H16: as gemm_bf16_kernel (half activations; down widens its weight fragments).
+template <bool GATEUP, int U, int KS, bool H16>
 __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
     const int32_t* __restrict__ tiles, int max_tiles, int n_single,
     const uint16_t* __restrict__ xa_g, const int32_t* __restrict__ src_g, int a_stride,
@@ -585,6 +842,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
     StreamSeg seg) {
   typedef __attribute__((ext_vector_type(8))) __bf16 bf8;
   constexpr int IPB = 4 / KS;                  // items per workgroup
+  constexpr bool WIDEN = H16 && !GATEUP;       // half activation rows x widened weights
+  auto wfrag = [](bf8 w) { if constexpr (WIDEN) return bf16x8_to_f16(w); else return w; };
   __shared__ f32x4 red[KS > 1 ? 3 : 1][GATEUP ? 2 : 1][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kpart = wave % KS;
@@ -648,7 +907,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
     auto comp = [&](int b) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[b][u], xv[b][u], acc, 0, 0, 0);
+        acc = mfma16x32<WIDEN>(wfrag(wv[b][u]), xv[b][u], acc);
         if (GATEUP) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qv[b][u], xv[b][u], acc2, 0, 0, 0);
       }
     };
@@ -668,7 +927,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
       const int k = st << 5;
       const bf8 w1v = *reinterpret_cast<const bf8*>(wp + k);
       const bf8 x1v = *reinterpret_cast<const bf8*>(xp + k);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1v, x1v, acc, 0, 0, 0);
+      acc = mfma16x32<WIDEN>(wfrag(w1v), x1v, acc);
       if (GATEUP) {
         const bf8 q1v = *reinterpret_cast<const bf8*>(wq + k);
         acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q1v, x1v, acc2, 0, 0, 0);
@@ -698,9 +957,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
   const size_t orow = static_cast<size_t>(out_row0) + tc.row0 + r16;
   const int n = n0 + (lane >> 4) * 4;
   if (GATEUP) {
+    auto pack = [](float lo, float hi) { return H16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi); };
     u32x2 pk;
-    pk[0] = pack_bf16x2(silu(acc[0]) * acc2[0], silu(acc[1]) * acc2[1]);
-    pk[1] = pack_bf16x2(silu(acc[2]) * acc2[2], silu(acc[3]) * acc2[3]);
+    pk[0] = pack(silu(acc[0]) * acc2[0], silu(acc[1]) * acc2[1]);
+    pk[1] = pack(silu(acc[2]) * acc2[2], silu(acc[3]) * acc2[3]);
     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow * out_stride + n) = pk;
   } else {
     *reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow * out_stride + n) = acc;
@@ -714,14 +974,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
 // either grows; batches of U = 8 steps,
 // or 4 when a wave's K range is short (one batch) or, in the down product,
 // very long (more waves per SIMD in place of deeper batches).
-template <bool GATEUP, int U, int KS>
+template <bool GATEUP, int U, int KS, bool H16>
 static void launch_stream(long long items, const GemmTileMap& map, int m_tiles,
                           const uint16_t* xa, const int32_t* src, int a_stride, int a_row0,
                           const uint16_t* wa, const uint16_t* wb, long long w_stride, void* out,
                           int out_stride, int out_row0, int K, int N, const StreamSeg& seg,
                           hipStream_t s) {
   constexpr int IPB = 4 / KS;
-  gemm_bf16_stream_kernel<GATEUP, U, KS>
+  gemm_bf16_stream_kernel<GATEUP, U, KS, H16>
       <<<dim3(static_cast<unsigned>((items + IPB - 1) / IPB)), dim3(256), 0, s>>>(
           map.tiles, m_tiles, map.n_single, xa, src, a_stride, a_row0, wa, wb, w_stride, out,
           out_stride, out_row0, K, N, seg);
@@ -729,7 +989,7 @@ static void launch_stream(long long items, const GemmTileMap& map, int m_tiles,
 
 // seg: an optional dense group launched with the grouped rows (its K may differ;
 // the launch shape follows the grouped rows' K and the total item count)
-template <bool GATEUP>
+template <bool GATEUP, bool H16>
 static hipError_t run_stream(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
                              int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
                              long long w_stride, void* out, int out_stride, int out_row0, int K,
@@ -743,7 +1003,7 @@ static hipError_t run_stream(const GemmTileMap& map, const uint16_t* xa, const i
   const int steps = K / 32 / KS;
   const bool u4 = steps < 16 || (!GATEUP && steps >= 100);
 #define MOE_STREAM(U_, KS_)                                                                  \
-  launch_stream<GATEUP, U_, KS_>(items, map, m_tiles, xa, src, a_stride, a_row0, wa, wb,     \
+  launch_stream<GATEUP, U_, KS_, H16>(items, map, m_tiles, xa, src, a_stride, a_row0, wa, wb,\
                                  w_stride, out, out_stride, out_row0, K, N, seg, s)
   if (KS == 4) {
     if (u4) MOE_STREAM(4, 4); else MOE_STREAM(8, 4);
@@ -836,14 +1096,14 @@ static hipError_t launch_tiled(Kern kern, bool n_fast, int BM, int BN, int threa
 }
 
 // register-staged small tiles
-template <int BM, int BN, int WM, int WN, bool GATEUP>
+template <int BM, int BN, int WM, int WN, bool GATEUP, bool H16>
 static hipError_t run_small(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
                             int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
                             long long w_stride, void* out, int out_stride, int out_row0, int K,
                             int N, hipStream_t s) {
   constexpr int WR = GATEUP ? 2 * BN : BN;
   const size_t lds = static_cast<size_t>(2) * (BM + WR) * kPitch * sizeof(uint16_t);
-  return launch_tiled(gemm_bf16_kernel<BM, BN, WM, WN, GATEUP>, false, BM, BN, 64 * WM * WN, lds, map,
+  return launch_tiled(gemm_bf16_kernel<BM, BN, WM, WN, GATEUP, H16>, false, BM, BN, 64 * WM * WN, lds, map,
                       xa, src, a_stride, a_row0, wa, wb, w_stride, out, out_stride, out_row0, K,
                       N, s);
 }
@@ -852,8 +1112,8 @@ static hipError_t run_small(const GemmTileMap& map, const uint16_t* xa, const in
 // Three LDS stages where they fit (256 x 128 down tiles: 3 x 48 KB), which
 // keeps two stages of loads in flight per CU; those tiles serve short groups,
 // where the weights stream from HBM and load latency matters most.
-template <int BM, int BN, int WM, int WN, bool GATEUP, bool HOUT = false, bool NF = false,
-          int XS = 0>
+template <int BM, int BN, int WM, int WN, bool GATEUP, bool H16, bool HOUT = false,
+          bool NF = false, int XS = 0>
 static hipError_t run_lds(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
                           int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
                           long long w_stride, void* out, int out_stride, int out_row0, int K,
@@ -864,7 +1124,7 @@ static hipError_t run_lds(const GemmTileMap& map, const uint16_t* xa, const int3
   constexpr size_t kShort =
       XS > 0 ? short_ring_stages(XS, WR) * static_cast<size_t>(XS + WR) * kRowBytes : 0;
   const size_t lds = ST * kStage > kShort ? ST * kStage : kShort;
-  return launch_tiled(gemm_bf16_lds_kernel<BM, BN, WM, WN, GATEUP, ST, HOUT, false, NF, XS>, NF, BM, BN,
+  return launch_tiled(gemm_bf16_lds_kernel<BM, BN, WM, WN, GATEUP, ST, HOUT, false, NF, XS, H16>, NF, BM, BN,
                       64 * WM * WN, lds, map, xa, src, a_stride, a_row0, wa, wb, w_stride, out,
                       out_stride, out_row0, K, N, s, h1o, h3o, static_cast<float*>(nullptr));
 }
@@ -885,6 +1145,7 @@ static int streamk_workgroups() { return persistent_workgroups(kStreamKMaxWorkgr
 // Plain 256 x 256 products as stream-K (see gemm_bf16_lds_kernel) when the
 // launch has at least one tile per workgroup: the fix-up kernel follows.
 // Returns hipErrorNotSupported when stream-K does not apply.
+template <bool H16>
 static hipError_t run_lds_streamk(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
                                   int a_stride, int a_row0, const uint16_t* wa, long long w_stride,
                                   float* out, int out_stride, int out_row0, int K, int N,
@@ -894,7 +1155,7 @@ static hipError_t run_lds_streamk(const GemmTileMap& map, const uint16_t* xa, co
   const int P = streamk_workgroups();
   const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + BM - 1) / BM;
   if (P < 8 || static_cast<long long>(m_tiles) * (N / BN) < P) return hipErrorNotSupported;
-  auto kern = gemm_bf16_lds_kernel<BM, BN, 2, 4, false, 2, false, true>;
+  auto kern = gemm_bf16_lds_kernel<BM, BN, 2, 4, false, 2, false, true, false, 0, H16>;
   hipError_t e = allow_large_lds(reinterpret_cast<const void*>(kern), lds);
   if (e != hipSuccess) return e;
   kern<<<dim3(P), dim3(512), lds, s>>>(map.tiles, m_tiles, map.n_single, 0, xa, src, a_stride,
@@ -902,10 +1163,56 @@ static hipError_t run_lds_streamk(const GemmTileMap& map, const uint16_t* xa, co
                                        K, N, nullptr, nullptr, sk_part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  streamk_fixup_kernel<BM, BN><<<dim3(P - 1, 4), dim3(256), 0, s>>>(
+  streamk_fixup_kernel<BM, BN, kBK><<<dim3(P - 1, 4), dim3(256), 0, s>>>(
       map.tiles, m_tiles, map.n_single, K, N, P, sk_part, out, out_stride, out_row0);
   return hipGetLastError();
 }
+
+// One wave per SIMD, 256 x 256 weight-row tiles, BK = 32 in an ST-stage ring.
+#ifndef MOE_W4_STAGES
+#define MOE_W4_STAGES 4
+#endif
+constexpr int kW4Stages = MOE_W4_STAGES;
+
+template <bool GATEUP, bool NF, bool H16>
+static hipError_t run_w4(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
+                         int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
+                         long long w_stride, void* out, int out_stride, int out_row0, int K,
+                         int N, hipStream_t s) {
+  constexpr int BN = GATEUP ? 128 : 256;
+  constexpr size_t lds = static_cast<size_t>(kW4Stages) * kW4Stage;
+  return launch_tiled(gemm_bf16_w4_kernel<GATEUP, kW4Stages, false, NF, H16>, NF, 256, BN, 256, lds,
+                      map, xa, src, a_stride, a_row0, wa, wb, w_stride, out, out_stride,
+                      out_row0, K, N, s, static_cast<float*>(nullptr));
+}
+
+// stream-K form of run_w4 for plain products (see gemm_bf16_lds_kernel)
+template <bool H16>
+static hipError_t run_w4_streamk(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
+                                 int a_stride, int a_row0, const uint16_t* wa, long long w_stride,
+                                 float* out, int out_stride, int out_row0, int K, int N,
+                                 float* sk_part, hipStream_t s) {
+  constexpr int BM = 256, BN = 256, ST = kW4Stages < 4 ? kW4Stages : 4;
+  constexpr size_t lds = static_cast<size_t>(ST) * kW4Stage;
+  const int P = streamk_workgroups();
+  const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + BM - 1) / BM;
+  if (P < 8 || static_cast<long long>(m_tiles) * (N / BN) < P) return hipErrorNotSupported;
+  auto kern = gemm_bf16_w4_kernel<false, ST, true, false, H16>;
+  hipError_t e = allow_large_lds(reinterpret_cast<const void*>(kern), lds);
+  if (e != hipSuccess) return e;
+  kern<<<dim3(P), dim3(256), lds, s>>>(map.tiles, m_tiles, map.n_single, 0, xa, src, a_stride,
+                                       a_row0, wa, nullptr, w_stride, out, out_stride, out_row0,
+                                       K, N, sk_part);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  streamk_fixup_kernel<BM, BN, kW4BK><<<dim3(P - 1, 4), dim3(256), 0, s>>>(
+      map.tiles, m_tiles, map.n_single, K, N, P, sk_part, out, out_stride, out_row0);
+  return hipGetLastError();
+}
+
+#ifndef MOE_W4
+#define MOE_W4 0
+#endif
 
 // Token rows of the short three-stage ring of the 256 x 128 gate/up tiles:
 // 3 x (160 + 256) x 128 B = 156 KB of LDS. Measured from cold caches: gate/up
@@ -916,6 +1223,8 @@ constexpr int kShortRingRows = 160;
 
 // BM = 256 needs N % 256 == 0 (down) / N % 128 == 0 (gate/up); the
 // caller picks BM with gemm_tile_rows(), which checks that.
+// The forward's gate/up products write the activation as IEEE half (its down
+// product reads it so); the backward's recompute (h1 set) keeps bf16.
 hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, int BM,
                                    hipStream_t s) {
   const auto* x = static_cast<const uint16_t*>(a.x);
@@ -927,31 +1236,34 @@ hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, 
   if (a.h1 != nullptr) {   // pre-activations too: 256-row tiles only
     if (BM != 256 || a.h3 == nullptr) return hipErrorInvalidValue;
     if (map.n_fast)
-      return run_lds<256, 128, 2, 4, true, true, true, kShortRingRows>(
+      return run_lds<256, 128, 2, 4, true, false, true, true, kShortRingRows>(
           map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act, a.act_stride, a.out_row0, a.K, a.N, s,
           a.h1, a.h3);
     if (short_ring)
-      return run_lds<256, 128, 2, 4, true, true, false, kShortRingRows>(
+      return run_lds<256, 128, 2, 4, true, false, true, false, kShortRingRows>(
           map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act, a.act_stride, a.out_row0, a.K, a.N, s,
           a.h1, a.h3);
-    return run_lds<256, 128, 2, 4, true, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
-                                               a.act_stride, a.out_row0, a.K, a.N, s, a.h1,
-                                               a.h3);
+    return run_lds<256, 128, 2, 4, true, false, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride,
+                                                      a.act, a.act_stride, a.out_row0, a.K, a.N,
+                                                      s, a.h1, a.h3);
   }
   if (BM == 256 && map.n_fast)
-    return run_lds<256, 128, 2, 4, true, false, true, kShortRingRows>(
+    return run_lds<256, 128, 2, 4, true, true, false, true, kShortRingRows>(
         map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act, a.act_stride, a.out_row0, a.K, a.N, s);
   if (BM == 256 && short_ring)
-    return run_lds<256, 128, 2, 4, true, false, false, kShortRingRows>(
+    return run_lds<256, 128, 2, 4, true, true, false, false, kShortRingRows>(
         map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act, a.act_stride, a.out_row0, a.K, a.N, s);
+  if (BM == 256 && MOE_W4)
+    return run_w4<true, false, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
+                                     a.act_stride, a.out_row0, a.K, a.N, s);
   if (BM == 256)
-    return run_lds<256, 128, 2, 4, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
-                                         a.act_stride, a.out_row0, a.K, a.N, s);
+    return run_lds<256, 128, 2, 4, true, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
+                                               a.act_stride, a.out_row0, a.K, a.N, s);
   if (BM == 16)
-    return run_stream<true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act, a.act_stride,
-                            a.out_row0, a.K, a.N, s);
-  return run_small<32, 64, 1, 2, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
-                                       a.act_stride, a.out_row0, a.K, a.N, s);
+    return run_stream<true, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act, a.act_stride,
+                                  a.out_row0, a.K, a.N, s);
+  return run_small<32, 64, 1, 2, true, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
+                                             a.act_stride, a.out_row0, a.K, a.N, s);
 }
 
 hipError_t launch_gemm_gateup_bf16_with_shared(const GemmTileMap& map, const GateUpArgs& a,
@@ -966,16 +1278,18 @@ hipError_t launch_gemm_gateup_bf16_with_shared(const GemmTileMap& map, const Gat
   seg.K = sh.K;
   seg.N = sh.N;
   seg.out_row0 = sh.out_row0;
-  return run_stream<true>(map, static_cast<const uint16_t*>(a.x), a.src, a.K, 0,
-                          static_cast<const uint16_t*>(a.w1), static_cast<const uint16_t*>(a.w3),
-                          a.w_stride, a.act, a.act_stride, a.out_row0, a.K, a.N, s, seg);
+  return run_stream<true, true>(map, static_cast<const uint16_t*>(a.x), a.src, a.K, 0,
+                                static_cast<const uint16_t*>(a.w1),
+                                static_cast<const uint16_t*>(a.w3), a.w_stride, a.act,
+                                a.act_stride, a.out_row0, a.K, a.N, s, seg);
 }
 
 hipError_t launch_gemm_down_bf16_with_shared(const GemmTileMap& map, const DownArgs& a,
                                              const DownArgs& sh, int sh_rows, hipStream_t s) {
   const int ys = a.out_stride > 0 ? a.out_stride : a.N;
   if (sh.src != nullptr || sh.act_stride != a.act_stride || sh.N != a.N ||
-      (sh.out_stride > 0 ? sh.out_stride : sh.N) != ys || sh.y != a.y)
+      (sh.out_stride > 0 ? sh.out_stride : sh.N) != ys || sh.y != a.y ||
+      sh.act_f16 != a.act_f16)
     return hipErrorInvalidValue;
   StreamSeg seg;
   seg.xa = static_cast<const uint16_t*>(sh.act);
@@ -985,9 +1299,13 @@ hipError_t launch_gemm_down_bf16_with_shared(const GemmTileMap& map, const DownA
   seg.K = sh.K;
   seg.N = sh.N;
   seg.out_row0 = sh.out_row0;
-  return run_stream<false>(map, static_cast<const uint16_t*>(a.act), a.src, a.act_stride,
-                           a.in_row0, static_cast<const uint16_t*>(a.w2), nullptr, a.w_stride,
-                           a.y, ys, a.out_row0, a.K, a.N, s, seg);
+  if (a.act_f16)
+    return run_stream<false, true>(map, static_cast<const uint16_t*>(a.act), a.src, a.act_stride,
+                                   a.in_row0, static_cast<const uint16_t*>(a.w2), nullptr,
+                                   a.w_stride, a.y, ys, a.out_row0, a.K, a.N, s, seg);
+  return run_stream<false, false>(map, static_cast<const uint16_t*>(a.act), a.src, a.act_stride,
+                                  a.in_row0, static_cast<const uint16_t*>(a.w2), nullptr,
+                                  a.w_stride, a.y, ys, a.out_row0, a.K, a.N, s, seg);
 }
 
 // Output tiles of 256 columns unless that leaves fewer than two tiles per CU
@@ -998,37 +1316,46 @@ static int gemm_down_cols(int BM, int m_tiles, int N) {
   return static_cast<long long>(m_tiles) * (N / 256) < 2 * kNumCUs ? 128 : 256;
 }
 
-hipError_t launch_gemm_down_bf16(const GemmTileMap& map, const DownArgs& a, int BM,
-                                 hipStream_t s) {
+template <bool H16>
+static hipError_t launch_down(const GemmTileMap& map, const DownArgs& a, int BM, hipStream_t s) {
   const int ys = a.out_stride > 0 ? a.out_stride : a.N;
   const auto* act = static_cast<const uint16_t*>(a.act);
   const auto* w2 = static_cast<const uint16_t*>(a.w2);
   // weight-streaming shapes: 256 x 128 tiles (three LDS stages) in n-fastest order.
   // (A four-stage ring of 160-row stages, 4 x 36 KB, measured no faster here.)
   if (BM == 256 && map.n_fast && a.N % 128 == 0)
-    return run_lds<256, 128, 2, 4, false, false, true>(
+    return run_lds<256, 128, 2, 4, false, H16, false, true>(
         map, act, a.src, a.act_stride, a.in_row0, w2, nullptr, a.w_stride, a.y, ys, a.out_row0,
         a.K, a.N, s);
   if (BM == 256) {
     const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + BM - 1) / BM;
     if (gemm_down_cols(BM, m_tiles, a.N) == 128)
-      return run_lds<256, 128, 2, 4, false>(map, act, a.src, a.act_stride, a.in_row0, w2,
-                                            nullptr, a.w_stride, a.y, ys, a.out_row0, a.K,
-                                            a.N, s);
+      return run_lds<256, 128, 2, 4, false, H16>(map, act, a.src, a.act_stride, a.in_row0, w2,
+                                                 nullptr, a.w_stride, a.y, ys, a.out_row0, a.K,
+                                                 a.N, s);
     if (a.sk_part != nullptr) {
-      const hipError_t e = run_lds_streamk(map, act, a.src, a.act_stride, a.in_row0, w2,
-                                           a.w_stride, a.y, ys, a.out_row0, a.K, a.N, a.sk_part, s);
+      const hipError_t e =
+          MOE_W4 ? run_w4_streamk<H16>(map, act, a.src, a.act_stride, a.in_row0, w2, a.w_stride,
+                                       a.y, ys, a.out_row0, a.K, a.N, a.sk_part, s)
+                 : run_lds_streamk<H16>(map, act, a.src, a.act_stride, a.in_row0, w2,
+                                        a.w_stride, a.y, ys, a.out_row0, a.K, a.N, a.sk_part, s);
       if (e != hipErrorNotSupported) return e;
     }
-    return run_lds<256, 256, 2, 4, false>(map, act, a.src, a.act_stride, a.in_row0, w2,
-                                          nullptr, a.w_stride, a.y, ys, a.out_row0, a.K, a.N,
-                                          s);
+    return run_lds<256, 256, 2, 4, false, H16>(map, act, a.src, a.act_stride, a.in_row0, w2,
+                                               nullptr, a.w_stride, a.y, ys, a.out_row0, a.K,
+                                               a.N, s);
   }
   if (BM == 16)
-    return run_stream<false>(map, act, a.src, a.act_stride, a.in_row0, w2, nullptr, a.w_stride,
-                             a.y, ys, a.out_row0, a.K, a.N, s);
-  return run_small<32, 64, 1, 2, false>(map, act, a.src, a.act_stride, a.in_row0, w2, nullptr,
-                                        a.w_stride, a.y, ys, a.out_row0, a.K, a.N, s);
+    return run_stream<false, H16>(map, act, a.src, a.act_stride, a.in_row0, w2, nullptr,
+                                  a.w_stride, a.y, ys, a.out_row0, a.K, a.N, s);
+  return run_small<32, 64, 1, 2, false, H16>(map, act, a.src, a.act_stride, a.in_row0, w2,
+                                             nullptr, a.w_stride, a.y, ys, a.out_row0, a.K,
+                                             a.N, s);
+}
+
+hipError_t launch_gemm_down_bf16(const GemmTileMap& map, const DownArgs& a, int BM,
+                                 hipStream_t s) {
+  return a.act_f16 ? launch_down<true>(map, a, BM, s) : launch_down<false>(map, a, BM, s);
 }
 
 }  // namespace moe

@@ -153,7 +153,7 @@ struct GateUpArgs {
   const void* w1;         // [G][N][K]
   const void* w3;
   long long w_stride;     // elements between groups' weight matrices
-  void* act;              // [rows][act_stride]
+  void* act;              // [rows][act_stride]: IEEE half, or bf16 when h1 is set
   int act_stride;
   int out_row0;           // output row = out_row0 + grouped row
   int K, N;               // K = d, N = d_ff
@@ -172,6 +172,9 @@ struct DownArgs {
   const int32_t* src = nullptr;   // grouped row -> input row (nullable: identity)
   int out_stride = 0;             // y row stride in floats (0: N)
   float* sk_part = nullptr;       // stream-K partial tiles (streamk_part_bytes), nullable
+  bool act_f16 = false;           // act rows are IEEE half (the forward's SwiGLU
+                                  // activation): the bf16 weights are widened to half
+                                  // and the product runs on half MFMAs
 };
 // Workgroups of a persistent launch: one per CU (a multiple of 8), at most cap; 0 if
 // the CU count is unavailable.

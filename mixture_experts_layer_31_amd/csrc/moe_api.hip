@@ -442,9 +442,11 @@ moe_status do_down(const Shape& s, const void* act, const int32_t* tiles, const 
   moe::GemmTileMap map{tiles, s.max_tiles, 0, moe::gemm_n_fast(s.BM, s.R, s.E), avg_group_rows(s)};
   moe::DownArgs a{act, s.act_stride, 0, w2, static_cast<long long>(s.d) * s.dff, y_perm, 0, s.dff, s.d};
   a.sk_part = sk_part;
+  a.act_f16 = true;   // the gate/up products wrote the activation as IEEE half
   const int bm_sh = moe::gemm_tile_rows(1, s.T, 1, s.n256);
   if (s.nsh && s.bf16 && s.BM == 16 && bm_sh == 16) {
     moe::DownArgs b{act, s.act_stride, s.R, ws2, 0, y_perm, s.R, s.dffs, s.d};
+    b.act_f16 = true;
     MOE_HIP(moe::launch_gemm_down_bf16_with_shared(map, a, b, s.T, stream), "gemm_down");
     return MOE_OK;
   }
@@ -455,6 +457,7 @@ moe_status do_down(const Shape& s, const void* act, const int32_t* tiles, const 
     const hipStream_t ss = sh.stream_for_shared(stream);
     moe::GemmTileMap m1{nullptr, 0, s.T};
     moe::DownArgs b{act, s.act_stride, s.R, ws2, 0, y_perm, s.R, s.dffs, s.d};
+    b.act_f16 = true;
     // the stream-K partials are shared scratch: only on the caller's stream
     b.sk_part = sh.side ? nullptr : sk_part;
     if (s.bf16) MOE_HIP(moe::launch_gemm_down_bf16(m1, b, bm_sh, ss), "gemm_down_shared");
