@@ -324,6 +324,25 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
                        float* y, int32_t* idx_out, float* gates_out,
                        const moe_stats* stats, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * call and results, with no workspace argument. Its scratch is a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until
+ * the process ends; the array's address on a device is looked up on the first
+ * call there (make that call before any capture). Enough for decode-sized
+ * batches and prefills of a few hundred tokens (moe_workspace_size(cfg,
+ * MOE_STAGE_FORWARD) tells); a layer that needs more returns MOE_ERR_WORKSPACE
+ * before anything is launched. Calls on one GPU share its array: calls that
+ * overlap on one GPU (other streams, other host threads) race and must not be
+ * issued; calls ordered on one stream are safe. The array keeps the last call's
+ * contents; nothing in it needs to start at zero. Other errors as moe_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+moe_status moe_forward_noalloc(const moe_config* cfg, const void* x, const void* w_router,
+                               const float* sel_bias, const void* w1, const void* w3,
+                               const void* w2, const void* ws1, const void* ws3,
+                               const void* ws2, float* y, int32_t* idx_out, float* gates_out,
+                               const moe_stats* stats, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

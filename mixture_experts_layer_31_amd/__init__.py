@@ -24,7 +24,9 @@ GATE_SELECTED, GATE_ALL = 0, 1
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_workspace_size", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_expert_gateup", "moe_expert_down",
            "moe_act_stride", "moe_combine", "moe_forward", "moe_update_bias", "moe_ep_traffic",
-           "moe_backward")
+           "moe_backward", "moe_forward_noalloc")
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 
 
 class MoeConfig(ctypes.Structure):
@@ -82,6 +84,8 @@ def load(path: str = LIB_PATH):
         "moe_update_bias": (ctypes.c_int, [cfgp, vp, ctypes.c_float, vp, vp]),
         "moe_ep_traffic": (ctypes.c_int, [cfgp, vp, vp, vp]),
         "moe_backward": (ctypes.c_int, [cfgp] + [vp] * 19 + [sz, vp]),
+        "moe_forward_noalloc": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               vp, stp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -258,3 +262,12 @@ def forward(cfg, x, w_router, sel_bias, w1, w3, w2, ws1, ws3, ws2, y, idx=None, 
                               _p(w3), _p(w2), _p(ws1), _p(ws3), _p(ws2), _p(y), _p(idx),
                               _p(gates), _stats_ref(stats), wp, wb, _stream(stream)),
            "moe_forward")
+
+
+def forward_noalloc(cfg, x, w_router, sel_bias, w1, w3, w2, ws1, ws3, ws2, y, idx=None,
+                    gates=None, stats: Optional[Stats] = None, stream=None):
+    """moe_forward with the library's fixed per-GPU scratch instead of a workspace."""
+    _check(load().moe_forward_noalloc(ctypes.byref(cfg), _p(x), _p(w_router), _p(sel_bias),
+                                      _p(w1), _p(w3), _p(w2), _p(ws1), _p(ws3), _p(ws2), _p(y),
+                                      _p(idx), _p(gates), _stats_ref(stats), _stream(stream)),
+           "moe_forward_noalloc")

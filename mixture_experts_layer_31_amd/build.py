@@ -21,7 +21,7 @@ LIB_NAME = "libmoe_mi355x.so"
 LIB = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["moe_api.hip", "router.hip", "index.hip", "rows.hip", "gemm_bf16.hip", "gemm_f32.hip",
-           "backward.hip", "gemm_kmajor.hip"]
+           "backward.hip", "gemm_kmajor.hip", "noalloc.hip"]
 CALIB_SOURCE = "calibrate.hip"
 CALIB_LIB = os.path.join(PKG, "libmoe_calibrate.so")
 

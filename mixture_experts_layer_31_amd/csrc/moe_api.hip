@@ -474,6 +474,8 @@ moe_status do_down(const Shape& s, const void* act, const int32_t* tiles, const 
 
 namespace moe {
 
+moe_status report_error(moe_status s, const char* msg) { return fail(s, "%s", msg); }
+
 hipError_t allow_large_lds(const void* kernel, size_t bytes) {
   static std::mutex mu;
   static std::set<std::tuple<const void*, int, size_t>> done;
