@@ -224,7 +224,13 @@ __device__ __forceinline__ int wave_allsum_int(int v) {
   return v;
 }
 
-// silu(v) = v / (1 + e^-v)
-__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+// silu(v) = v / (1 + e^-v), the quotient through the hardware reciprocal (v_rcp_f32,
+// within 1 ulp) instead of an IEEE division (about ten instructions more per
+// element in the GEMM epilogues); the result is rounded to half or bf16 next, or
+// carries fp32 accumulation error of the same order. Limits: v -> -inf gives -0
+// (e^-v = inf, rcp(inf) = 0), v -> +inf gives v.
+__device__ __forceinline__ float silu(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+}
 
 }  // namespace moe

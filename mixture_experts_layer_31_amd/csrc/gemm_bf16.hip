@@ -565,28 +565,31 @@ __global__ __launch_bounds__(256) void streamk_fixup_kernel(
 // K-steps of 32: a stage is 256 token + 256 weight rows of 64 bytes (32 KB),
 // filled by LDS-DMA (16 rows per instruction; the four 16-byte chunks of a row
 // XOR-swizzled by (row >> 1) & 3, so the fragment reads of eight consecutive rows
-// hit distinct banks) in a ring of ST stages, so ST - 1 stages of loads are in
-// flight while a stage is multiplied. One barrier per K-step; the fragments of a
-// step's second k-slice are read before the next barrier and its MFMAs issued
-// after it, so the matrix pipe stays busy across the barrier while the next
-// step's first fragments are read.
+// hit distinct banks) in a ring of ST slots. The load issued at step kt is stage
+// kt + LA (LA = ST - 2 stages ahead), into the slot of stage kt - 2: every wave
+// has consumed that stage's fragments before it reaches step kt - 1's MFMAs, so
+// the step's barrier waits only for the wave's own loads of stage kt, not for
+// LDS reads still in flight. One barrier per K-step; the fragments of a step's
+// second k-slice are read before the next barrier and multiplied after it, so
+// the matrix pipe stays busy across the barrier while the next step's first
+// fragments are read.
 constexpr int kW4BK = 32;          // K per step
 constexpr int kW4Row = 64;         // LDS row bytes (32 bf16)
 constexpr int kW4Stage = 512 * kW4Row;   // 256 token + 256 weight rows
 
 // H16: as gemm_bf16_kernel (half activations; down widens its weight fragments).
-template <bool GATEUP, int ST, bool SK, bool NF, bool H16>
+template <bool GATEUP, int ST, bool NF, bool H16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 gemm_bf16_w4_kernel(const int32_t* __restrict__ tiles, int max_tiles, int n_single,
                     int n_logical, const uint16_t* __restrict__ xa,
                     const int32_t* __restrict__ src, int a_stride, int a_row0,
                     const uint16_t* __restrict__ w_a, const uint16_t* __restrict__ w_b,
                     long long w_stride, void* __restrict__ out, int out_stride, int out_row0,
-                    int K, int N, float* __restrict__ sk_part) {
-  static_assert(!SK || !GATEUP, "stream-K splits plain fp32 products");
-  static_assert(ST >= 3 && ST * kW4Stage <= static_cast<int>(kMaxLdsBytes), "ring must fit");
+                    int K, int N) {
+  static_assert(ST >= 4 && ST * kW4Stage <= static_cast<int>(kMaxLdsBytes), "ring must fit");
   constexpr int BM = 256, BN = GATEUP ? 128 : 256;
-  constexpr int ND = 8;   // LDS-DMA instructions per wave per stage (4 token, 4 weight)
+  constexpr int ND = 8;        // LDS-DMA instructions per wave per stage (4 token, 4 weight)
+  constexpr int LA = ST - 2;   // stages loaded ahead
   constexpr bool WIDEN = H16 && !GATEUP;   // half activation rows x widened weights
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[];
 
@@ -595,12 +598,16 @@ gemm_bf16_w4_kernel(const int32_t* __restrict__ tiles, int max_tiles, int n_sing
   const int wm = wave >> 1, wn = wave & 1;
   const int nk_all = K / kW4BK;
 
-  auto run_tile = [&](int m_tile, int n_tile, int kt0, int kt1, float* part) {
-    if constexpr (SK) __syncthreads();   // the previous tile's reads of the ring are done
-    const TileCoord tc = lookup_tile(tiles, n_single, BM, m_tile);
-    if (tc.rows <= 0) return;
-    const int nk = kt1 - kt0;
-    const int n0 = n_tile * BN;
+  int m_tile, n_tile;
+  if constexpr (NF) xcd_tile_nfast(max_tiles, N / BN, m_tile, n_tile);
+  else if (tile_order_blocked(BM, N / BN)) xcd_tile_blocked(max_tiles, N / BN, m_tile, n_tile);
+  else xcd_tile(n_logical, max_tiles, m_tile, n_tile);
+  if (m_tile < 0) return;
+  const TileCoord tc = lookup_tile(tiles, n_single, BM, m_tile);
+  if (tc.rows <= 0) return;
+  const int nk = nk_all;
+  const int n0 = n_tile * BN;
+  {
 
     // DMA instruction j of this wave fills rows 16 * (4 * (j % 4) + wave) .. + 15
     // of the token (j < 4) or weight (j >= 4) half of a stage; lane l writes row
@@ -613,8 +620,7 @@ gemm_bf16_w4_kernel(const int32_t* __restrict__ tiles, int max_tiles, int n_sing
       const int r = 16 * (4 * j + wave) + lrow;
       int grow = tc.row0 + min(r, tc.rows - 1);
       if (src != nullptr) grow = src[grow];
-      gp[j] = xa + (static_cast<size_t>(a_row0) + grow) * a_stride + lchunk * 8 +
-              static_cast<size_t>(kt0) * kW4BK;
+      gp[j] = xa + (static_cast<size_t>(a_row0) + grow) * a_stride + lchunk * 8;
     }
     const size_t wbase = static_cast<size_t>(tc.group) * w_stride;
 #pragma unroll
@@ -622,24 +628,22 @@ gemm_bf16_w4_kernel(const int32_t* __restrict__ tiles, int max_tiles, int n_sing
       const int r = 16 * (4 * j + wave) + lrow;
       const uint16_t* wsrc = (!GATEUP || r < BN) ? w_a : w_b;
       const int n = n0 + ((GATEUP && r >= BN) ? r - BN : r);
-      gp[4 + j] = wsrc + wbase + static_cast<size_t>(n) * K + lchunk * 8 +
-                  static_cast<size_t>(kt0) * kW4BK;
+      gp[4 + j] = wsrc + wbase + static_cast<size_t>(n) * K + lchunk * 8;
     }
-    // instructions [J0, J1) of stage kt into ring slot buf; every wave issues all
-    // eight (rows past a ragged tile's end load its last row again and are never
+    // the eight loads of stage kt into ring slot buf; every wave issues all eight
+    // (rows past a ragged tile's end load its last row again and are never
     // stored), so the count of loads in flight is the same on every wave
-    auto dma = [&](int kt, int buf, auto j0_c, auto j1_c) {
-      constexpr int J0 = decltype(j0_c)::value, J1 = decltype(j1_c)::value;
+    auto dma = [&](int kt, int buf) {
       unsigned char* st = lds_raw + buf * kW4Stage;
 #pragma unroll
-      for (int j = J0; j < J1; ++j) {
+      for (int j = 0; j < ND; ++j) {
         unsigned char* dst = st + (j >= 4 ? BM * kW4Row : 0) + (4 * (j & 3) + wave) * 16 * kW4Row;
         MOE_LDS_DMA16(gp[j] + kt * kW4BK, dst);
       }
     };
 
-    // fragment of 32-row block `blk` of a stage's token (tok) or weight half at
-    // k-slice kk: row lane % 32, logical chunk 2 kk + lane / 32
+    // fragment of a 32-row block at k-slice kk: row lane % 32, logical chunk
+    // 2 kk + lane / 32
     const int frow = lane & 31;
     const int fsw = (frow >> 1) & 3;
     const int foff0 = frow * kW4Row + (((0 + (lane >> 5)) ^ fsw) << 4);
@@ -681,59 +685,92 @@ gemm_bf16_w4_kernel(const int32_t* __restrict__ tiles, int max_tiles, int n_sing
           acc[a][b] = mfma32x16<WIDEN>(fa[b], fb[a], acc[a][b]);
     };
 
-    auto kloop = [&](auto na_c) {
-      using I0 = std::integral_constant<int, 0>;
-      using I4 = std::integral_constant<int, 4>;
-      using I8 = std::integral_constant<int, 8>;
+    bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+    // One K-step (any step; conditions at run time): publish stage kt, load stage
+    // kt + LA, read this stage's first k-slice while the previous step's second
+    // slice is multiplied, then its second slice while the first is multiplied.
+    auto step = [&](int kt, auto na_c) {
+      const int later = min(LA - 1, nk - 1 - kt);   // stages after kt already issued
+      if (later == LA - 1) MOE_WAIT_VMCNT((LA - 1) * ND);
+      else wait_vmcnt_at_most<(LA - 1) * ND>(later * ND);
+      dma_barrier();   // publishes stage kt
+      const int cur = kt % ST;
+      if (kt + LA < nk) dma(kt + LA, (kt + LA) % ST);
+      MOE_SCHED_FENCE();
+      rfrag(cur, 0, fa0, fb0, na_c);
+      if (kt > 0) mfmas(fa1, fb1, na_c);       // second slice of the previous step
+      rfrag(cur, 1, fa1, fb1, na_c);
+      mfmas(fa0, fb0, na_c);
+    };
+    // The same step in the steady state of a full tile: ring slot S known at
+    // compile time (LDS offsets and the DMA's M0 values become immediates), a
+    // step before it and the load ahead of it always present, no branches. With
+    // one wave per SIMD the wave issues in order, so every other instruction is
+    // placed in the shadow of an MFMA (32 cycles each): the 16 MFMAs of the
+    // previous step's second slice alternate with this step's first-slice reads
+    // and its eight LDS-DMA loads, the first 8 MFMAs of its first slice with the
+    // second-slice reads.
+    auto main_step = [&](int kt, auto slot_c) {
+      constexpr int S = decltype(slot_c)::value;
+      constexpr int DS = (S + LA) % ST;
+      using N4 = std::integral_constant<int, 4>;
+      MOE_WAIT_VMCNT((LA - 1) * ND);
+      lds_barrier();
+#if defined(__HIP_DEVICE_COMPILE__)
+      __builtin_amdgcn_sched_barrier(0);   // nothing crosses the barrier
+#endif
+      rfrag(S, 0, fa0, fb0, N4{});
+      mfmas(fa1, fb1, N4{});
+      dma(kt + LA, DS);
+      rfrag(S, 1, fa1, fb1, N4{});
+      mfmas(fa0, fb0, N4{});
+#if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
-      for (int p = 0; p < ST - 1; ++p)
-        if (p < nk) dma(p, p, I0{}, I8{});
-      bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-      int cur = 0;
-      for (int kt = 0; kt < nk; ++kt) {
-        // stage kt has landed once no more than the later stages' loads are outstanding
-        const int later = min(ST - 2, nk - 1 - kt);
-        if (later == ST - 2) MOE_WAIT_VMCNT((ST - 2) * ND);
-        else wait_vmcnt_at_most<(ST - 2) * ND>(later * ND);
-        dma_barrier();   // publishes stage kt; every read of slot (kt - 1) % ST is done
-        const int ahead = kt + ST - 1;
-        const int nbuf = cur == 0 ? ST - 1 : cur - 1;
-        if (ahead < nk) dma(ahead, nbuf, I0{}, I4{});
-        MOE_SCHED_FENCE();
-        rfrag(cur, 0, fa0, fb0, na_c);
-        if (kt > 0) mfmas(fa1, fb1, na_c);       // second slice of the previous step
-        if (ahead < nk) dma(ahead, nbuf, I4{}, I8{});
-        MOE_SCHED_FENCE();
-        rfrag(cur, 1, fa1, fb1, na_c);
-        mfmas(fa0, fb0, na_c);
-        cur = cur + 1 == ST ? 0 : cur + 1;
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
       }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // LDS-DMA load
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#endif
+    };
+
+    auto kloop = [&](auto na_c) {
+      constexpr int NA = decltype(na_c)::value;
+#pragma unroll
+      for (int p = 0; p < LA; ++p)
+        if (p < nk) dma(p, p);
+      int kt = 0;
+      if constexpr (NA == 4) {
+        // the first ST steps, then whole turns of the ring while every load of the
+        // turn is before the tile's end, then the rest
+        for (; kt < ST && kt < nk; ++kt) step(kt, na_c);
+        for (; kt + ST - 1 + LA < nk; kt += ST) {
+          main_step(kt, std::integral_constant<int, 0>{});
+          main_step(kt + 1, std::integral_constant<int, 1>{});
+          main_step(kt + 2, std::integral_constant<int, 2>{});
+          main_step(kt + 3, std::integral_constant<int, 3>{});
+          if constexpr (ST > 4) main_step(kt + 4, std::integral_constant<int, 4 % ST>{});
+          if constexpr (ST > 5) main_step(kt + 5, std::integral_constant<int, 5 % ST>{});
+        }
+      }
+      for (; kt < nk; ++kt) step(kt, na_c);
       mfmas(fa1, fb1, na_c);
     };
     const int nb = (min(tc.rows, BM) + 31) / 32;
     const int na_count = (nb - wm + 1) / 2;
     with_count<4>(na_count, [&](auto na_c) { kloop(na_c); });
 
-    if constexpr (SK) {
-      if (part != nullptr) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int m = (2 * a + wm) * 32 + frow;
-          if (m >= tc.rows) continue;
-#pragma unroll
-          for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-              f32x4 v;
-#pragma unroll
-              for (int q = 0; q < 4; ++q) v[q] = acc[a][b][4 * rq + q];
-              *reinterpret_cast<f32x4*>(part + static_cast<size_t>(m) * BN + wblk[b] * 32 +
-                                        8 * rq + 4 * (lane >> 5)) = v;
-            }
-        }
-        return;
-      }
-    }
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int m = (2 * a + wm) * 32 + frow;
@@ -766,37 +803,6 @@ gemm_bf16_w4_kernel(const int32_t* __restrict__ tiles, int max_tiles, int n_sing
             *reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow * out_stride + n) = v;
           }
       }
-    }
-  };
-
-  if constexpr (!SK) {
-    int m_tile, n_tile;
-    if constexpr (NF) xcd_tile_nfast(max_tiles, N / BN, m_tile, n_tile);
-    else if (tile_order_blocked(BM, N / BN)) xcd_tile_blocked(max_tiles, N / BN, m_tile, n_tile);
-    else xcd_tile(n_logical, max_tiles, m_tile, n_tile);
-    if (m_tile < 0) return;
-    run_tile(m_tile, n_tile, 0, nk_all, nullptr);
-  } else {
-    __shared__ int s_real;
-    const int n_real = real_tiles<BM>(tiles, max_tiles, n_single, &s_real);
-    const long long n_tiles = static_cast<long long>(n_real) * (N / BN);
-    const long long U = n_tiles * nk_all;
-    const int P = gridDim.x;
-    const int L = blockIdx.x;
-    const int p = (L & 7) * (P >> 3) + (L >> 3);
-    if (U < static_cast<long long>(P) * nk_all) {
-      for (long long t = p; t < n_tiles; t += P)
-        run_tile(static_cast<int>(t % n_real), static_cast<int>(t / n_real), 0, nk_all, nullptr);
-      return;
-    }
-    const long long u1 = U * (p + 1) / P;
-    for (long long u = U * p / P; u < u1;) {
-      const long long t = u / nk_all;
-      const int kt0 = static_cast<int>(u - t * nk_all);
-      const int kt1 = static_cast<int>(min(static_cast<long long>(nk_all), kt0 + (u1 - u)));
-      float* part = kt1 < nk_all ? sk_part + static_cast<size_t>(p) * BM * BN : nullptr;
-      run_tile(static_cast<int>(t % n_real), static_cast<int>(t / n_real), kt0, kt1, part);
-      u += kt1 - kt0;
     }
   }
 }
@@ -1170,7 +1176,7 @@ static hipError_t run_lds_streamk(const GemmTileMap& map, const uint16_t* xa, co
 
 // One wave per SIMD, 256 x 256 weight-row tiles, BK = 32 in an ST-stage ring.
 #ifndef MOE_W4_STAGES
-#define MOE_W4_STAGES 4
+#define MOE_W4_STAGES 5
 #endif
 constexpr int kW4Stages = MOE_W4_STAGES;
 
@@ -1181,38 +1187,10 @@ static hipError_t run_w4(const GemmTileMap& map, const uint16_t* xa, const int32
                          int N, hipStream_t s) {
   constexpr int BN = GATEUP ? 128 : 256;
   constexpr size_t lds = static_cast<size_t>(kW4Stages) * kW4Stage;
-  return launch_tiled(gemm_bf16_w4_kernel<GATEUP, kW4Stages, false, NF, H16>, NF, 256, BN, 256, lds,
+  return launch_tiled(gemm_bf16_w4_kernel<GATEUP, kW4Stages, NF, H16>, NF, 256, BN, 256, lds,
                       map, xa, src, a_stride, a_row0, wa, wb, w_stride, out, out_stride,
-                      out_row0, K, N, s, static_cast<float*>(nullptr));
+                      out_row0, K, N, s);
 }
-
-// stream-K form of run_w4 for plain products (see gemm_bf16_lds_kernel)
-template <bool H16>
-static hipError_t run_w4_streamk(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
-                                 int a_stride, int a_row0, const uint16_t* wa, long long w_stride,
-                                 float* out, int out_stride, int out_row0, int K, int N,
-                                 float* sk_part, hipStream_t s) {
-  constexpr int BM = 256, BN = 256, ST = kW4Stages < 4 ? kW4Stages : 4;
-  constexpr size_t lds = static_cast<size_t>(ST) * kW4Stage;
-  const int P = streamk_workgroups();
-  const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + BM - 1) / BM;
-  if (P < 8 || static_cast<long long>(m_tiles) * (N / BN) < P) return hipErrorNotSupported;
-  auto kern = gemm_bf16_w4_kernel<false, ST, true, false, H16>;
-  hipError_t e = allow_large_lds(reinterpret_cast<const void*>(kern), lds);
-  if (e != hipSuccess) return e;
-  kern<<<dim3(P), dim3(256), lds, s>>>(map.tiles, m_tiles, map.n_single, 0, xa, src, a_stride,
-                                       a_row0, wa, nullptr, w_stride, out, out_stride, out_row0,
-                                       K, N, sk_part);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  streamk_fixup_kernel<BM, BN, kW4BK><<<dim3(P - 1, 4), dim3(256), 0, s>>>(
-      map.tiles, m_tiles, map.n_single, K, N, P, sk_part, out, out_stride, out_row0);
-  return hipGetLastError();
-}
-
-#ifndef MOE_W4
-#define MOE_W4 0
-#endif
 
 // Token rows of the short three-stage ring of the 256 x 128 gate/up tiles:
 // 3 x (160 + 256) x 128 B = 156 KB of LDS. Measured from cold caches: gate/up
@@ -1253,12 +1231,10 @@ hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, 
   if (BM == 256 && short_ring)
     return run_lds<256, 128, 2, 4, true, true, false, false, kShortRingRows>(
         map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act, a.act_stride, a.out_row0, a.K, a.N, s);
-  if (BM == 256 && MOE_W4)
+  // full 256-row tiles: one wave per SIMD (gemm_bf16_w4_kernel)
+  if (BM == 256)
     return run_w4<true, false, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
                                      a.act_stride, a.out_row0, a.K, a.N, s);
-  if (BM == 256)
-    return run_lds<256, 128, 2, 4, true, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
-                                               a.act_stride, a.out_row0, a.K, a.N, s);
   if (BM == 16)
     return run_stream<true, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act, a.act_stride,
                                   a.out_row0, a.K, a.N, s);
@@ -1334,11 +1310,9 @@ static hipError_t launch_down(const GemmTileMap& map, const DownArgs& a, int BM,
                                                  nullptr, a.w_stride, a.y, ys, a.out_row0, a.K,
                                                  a.N, s);
     if (a.sk_part != nullptr) {
-      const hipError_t e =
-          MOE_W4 ? run_w4_streamk<H16>(map, act, a.src, a.act_stride, a.in_row0, w2, a.w_stride,
-                                       a.y, ys, a.out_row0, a.K, a.N, a.sk_part, s)
-                 : run_lds_streamk<H16>(map, act, a.src, a.act_stride, a.in_row0, w2,
-                                        a.w_stride, a.y, ys, a.out_row0, a.K, a.N, a.sk_part, s);
+      const hipError_t e = run_lds_streamk<H16>(map, act, a.src, a.act_stride, a.in_row0, w2,
+                                                a.w_stride, a.y, ys, a.out_row0, a.K, a.N,
+                                                a.sk_part, s);
       if (e != hipErrorNotSupported) return e;
     }
     return run_lds<256, 256, 2, 4, false, H16>(map, act, a.src, a.act_stride, a.in_row0, w2,

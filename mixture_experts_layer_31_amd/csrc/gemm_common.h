@@ -114,9 +114,20 @@ __device__ __forceinline__ void dma_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+// Workgroup barrier that waits for no memory counter at all: for rings whose
+// stages are published by each wave's own s_waitcnt vmcnt and whose slot reuse
+// is ordered by the MFMAs that consumed the slot's fragments (those MFMAs waited
+// for their LDS reads). The empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 #else
 #define MOE_SCHED_FENCE() ((void)0)
 __device__ __forceinline__ void dma_barrier() {}
+__device__ __forceinline__ void lds_barrier() {}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_at_most(int) {}
 #define MOE_WAIT_VMCNT(n) ((void)0)

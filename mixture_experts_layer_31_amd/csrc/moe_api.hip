@@ -671,8 +671,19 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   const int sh_row0 = s.nsh ? R : -1;
   auto u16 = [](const void* p) { return static_cast<const uint16_t*>(p); };
 
+  // ---- forward, recomputed: routing, index, pre-activations, activation
+  MOE_HIP(moe::launch_router_scores(1, x, w_router, T, d, E, b.z, b.zpart, strm), "router_scores");
+  MOE_HIP(moe::launch_router_select(b.z, sel_bias, T, E, k, s.gate_all, b.idx, b.gates, nullptr,
+                                    nullptr, nullptr, nullptr, strm),
+          "router_select");
+  MOE_HIP(moe::launch_index(b.idx, T, k, E, s.C, b.blk, b.slot_base, b.slot_keep, b.offsets, b.dest,
+                            b.src, b.counts, b.kept, b.ndrop, s.BM, s.max_tiles, 1, b.tiles, strm),
+          "index");
   // ---- weight transposes (experts of >= kTransposeMinRows rows): on the side
-  // stream, beside the recomputed forward; joined before the first product
+  // stream, beside the recomputed gate/up product; joined before the first
+  // product that reads them. Forked after the routing and index kernels: a
+  // transpose workgroup beside the single-workgroup scan of the index slowed it
+  // from 5 to 205 us.
   std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
   SideStream* side = nullptr;
   if (b.tr_routed || b.tr_shared) {
@@ -708,14 +719,6 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
     if (side != nullptr) MOE_HIP(hipEventRecord(side->join, side->s), "join");
   }
 
-  // ---- forward, recomputed: routing, index, pre-activations, activation
-  MOE_HIP(moe::launch_router_scores(1, x, w_router, T, d, E, b.z, b.zpart, strm), "router_scores");
-  MOE_HIP(moe::launch_router_select(b.z, sel_bias, T, E, k, s.gate_all, b.idx, b.gates, nullptr,
-                                    nullptr, nullptr, nullptr, strm),
-          "router_select");
-  MOE_HIP(moe::launch_index(b.idx, T, k, E, s.C, b.blk, b.slot_base, b.slot_keep, b.offsets, b.dest,
-                            b.src, b.counts, b.kept, b.ndrop, s.BM, s.max_tiles, 1, b.tiles, strm),
-          "index");
   const moe::GemmTileMap map{b.tiles, s.max_tiles, 0, moe::gemm_n_fast(s.BM, s.R, E),
                             avg_group_rows(s)};
   const moe::GemmTileMap map1{nullptr, 0, T};
