@@ -156,8 +156,18 @@ typedef struct {
  *              s = z + b minus the largest score left out (+inf when k = E),
  *              how far the top-k choice is from a tie ([CME295] §1.3, the
  *              top-k step; §4.2 for b) (float)
+ *   touched    experts that keep at least one assignment after capacity, i.e.
+ *              whose weights the expert products read ([15-779] §3.1 and
+ *              §4.2: experts a batch touches) (int32[1])
+ *   max_over_mean  max_e load_e / (T*k/E), load_e = assignments before drops:
+ *              the busiest expert's load over the mean ([CME295] §3.3 and
+ *              §4.2; [15-779] §3.4), computed in double and rounded once to
+ *              float (float[1])
  * z_loss .. margin are computed by moe_route / moe_forward; all in fp32 with
- * fixed summation orders (reproducible bit for bit).                          */
+ * fixed summation orders (reproducible bit for bit). counts, kept, n_dropped,
+ * touched and max_over_mean are computed by moe_permute / moe_forward; with
+ * ep_ranks = n > 1, touched and max_over_mean are per expert, summed over its
+ * n groups.                                                                   */
 typedef struct {
   int32_t* counts;
   int32_t* kept;
@@ -170,6 +180,8 @@ typedef struct {
   float* max_prob;
   float* top_gap;
   float* margin;
+  int32_t* touched;
+  float* max_over_mean;
 } moe_stats;
 
 /* Human-readable status name; never NULL. */
@@ -202,7 +214,8 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
  *   checked on the device) -> offsets[E+1], dest[T,k], src[T*k] int32
  *   (required). x_perm (nullable, elt [T*k, d]): when set, also gathers
  *   x_perm[r] = x[src[r]] (x then required).
- *   stats (nullable): fills counts, kept and n_dropped when set.             */
+ *   stats (nullable): fills counts, kept, n_dropped, touched and
+ *   max_over_mean when set.                                                  */
 moe_status moe_permute(const moe_config* cfg, const int32_t* idx, const void* x,
                        int32_t* offsets, int32_t* dest, int32_t* src, void* x_perm,
                        const moe_stats* stats, void* ws, size_t ws_bytes, void* stream);
@@ -314,10 +327,15 @@ moe_status moe_ep_traffic(const moe_config* cfg, const int32_t* offsets, int32_t
 moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float gamma, float* bias,
                            void* stream);
 
-/* The whole layer in one call: route -> permute -> grouped experts (+shared)
- * -> combine, on one stream, with every intermediate in `ws`.
+/* The whole layer in one call: y_t = sum_{i in TopK} g_{t,i} f_i(x_t) (+ the
+ * shared expert) ([CME295] §1.3), batched as the four steps route -> permute
+ * -> grouped experts (+shared) -> combine ([15-779] §3.2), on one stream, with
+ * every intermediate in `ws`.
  *   idx_out[T,k], gates_out[T,k] (nullable) receive the routing; stats as in
- *   moe_route + moe_permute.                                                 */
+ *   moe_route + moe_permute.
+ *   y[T,d] fp32 is written in full (dropped assignments add 0).
+ * Errors: INVALID_ARG / UNSUPPORTED / WORKSPACE before anything is launched;
+ * HIP when a launch fails (moe_last_error names the kernel).               */
 moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_router,
                        const float* sel_bias, const void* w1, const void* w3,
                        const void* w2, const void* ws1, const void* ws3, const void* ws2,

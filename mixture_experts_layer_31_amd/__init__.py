@@ -44,7 +44,8 @@ class MoeStats(ctypes.Structure):
                 ("P", ctypes.c_void_p), ("aux", ctypes.c_void_p),
                 ("z_loss", ctypes.c_void_p), ("entropy", ctypes.c_void_p),
                 ("max_prob", ctypes.c_void_p), ("top_gap", ctypes.c_void_p),
-                ("margin", ctypes.c_void_p)]
+                ("margin", ctypes.c_void_p), ("touched", ctypes.c_void_p),
+                ("max_over_mean", ctypes.c_void_p)]
 
 
 class MoEError(RuntimeError):
@@ -163,6 +164,8 @@ class Stats:
     max_prob: object = None
     top_gap: object = None
     margin: object = None
+    touched: object = None
+    max_over_mean: object = None
 
     @staticmethod
     def alloc(E: int, device="cuda", groups: Optional[int] = None,
@@ -176,12 +179,14 @@ class Stats:
         G = groups or E
         return Stats(z(G, torch.int32), z(G, torch.int32), z(1, torch.int32),
                      z(E, torch.float32), z(E, torch.float32), f1(), f1(), f1(), f1(), f1(),
-                     z(T, torch.float32) if T is not None else None)
+                     z(T, torch.float32) if T is not None else None,
+                     z(1, torch.int32), f1())
 
     def c(self) -> MoeStats:
         return MoeStats(_p(self.counts), _p(self.kept), _p(self.n_dropped), _p(self.f),
                         _p(self.P), _p(self.aux), _p(self.z_loss), _p(self.entropy),
-                        _p(self.max_prob), _p(self.top_gap), _p(self.margin))
+                        _p(self.max_prob), _p(self.top_gap), _p(self.margin),
+                        _p(self.touched), _p(self.max_over_mean))
 
 
 def _stats_ref(stats: Optional[Stats]):

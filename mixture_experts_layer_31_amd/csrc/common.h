@@ -218,6 +218,21 @@ __device__ __forceinline__ int block_scan_1024(int v, int* wtot, int* total) {
   return v + add;
 }
 
+// Largest v over a 1024-thread workgroup, returned to every thread; wtot holds
+// 16 ints of LDS and is free again on return.
+__device__ __forceinline__ int block_max_1024(int v, int* wtot) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m, kWave));
+  if (lane == 0) wtot[wv] = v;
+  __syncthreads();
+  int all = wtot[0];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) all = max(all, wtot[w]);
+  __syncthreads();
+  return all;
+}
+
 __device__ __forceinline__ int wave_allsum_int(int v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);

@@ -1297,8 +1297,17 @@ static hipError_t launch_down(const GemmTileMap& map, const DownArgs& a, int BM,
   const int ys = a.out_stride > 0 ? a.out_stride : a.N;
   const auto* act = static_cast<const uint16_t*>(a.act);
   const auto* w2 = static_cast<const uint16_t*>(a.w2);
-  // weight-streaming shapes: 256 x 128 tiles (three LDS stages) in n-fastest order.
-  // (A four-stage ring of 160-row stages, 4 x 36 KB, measured no faster here.)
+  // weight-streaming shapes, n-fastest order: 256 x 256 tiles whose groups of at
+  // most kShortRingRows rows run three stages of that many token rows and 256
+  // weight rows (3 x 52 KB), so two stages of 32 KB of weights are in flight per
+  // CU. Measured at the DeepSeek shape (4096 tokens, ~128 rows per expert): 2.22
+  // -> 2.00 ms against 256 x 128 tiles with three full stages (16 KB of weights
+  // per stage); Switch shape even. (A four-stage ring of 160-row stages at 128
+  // columns, 4 x 36 KB, measured no faster than the three full stages.)
+  if (BM == 256 && map.n_fast && a.N % 256 == 0)
+    return run_lds<256, 256, 2, 4, false, H16, false, true, kShortRingRows>(
+        map, act, a.src, a.act_stride, a.in_row0, w2, nullptr, a.w_stride, a.y, ys, a.out_row0,
+        a.K, a.N, s);
   if (BM == 256 && map.n_fast && a.N % 128 == 0)
     return run_lds<256, 128, 2, 4, false, H16, false, true>(
         map, act, a.src, a.act_stride, a.in_row0, w2, nullptr, a.w_stride, a.y, ys, a.out_row0,

@@ -53,6 +53,41 @@ __device__ __forceinline__ int bits_below(const uint32_t* bm, int key, int p) {
   return r + __popc(b[w] & ((1u << (p & 31)) - 1u));
 }
 
+// Expert load summary, called by every thread of a 1024-thread workgroup once the
+// per-key totals are final. With ep == 1 thread e holds expert e's assignments
+// before drops (cnt) and after capacity (keep). With ep = n > 1 the G keys are
+// the groups of the expert-parallel layout, with no capacity (kept = counts),
+// and expert e of the E = G / n sums its n groups (r*n + s)*(E/n) + l, r = e div
+// (E/n), l = e mod (E/n), over the source ranks s, read from tot. touched counts
+// the experts with a kept assignment; max_over_mean is max_e load_e * E / (T*k),
+// the quotient taken in double and rounded once to float.
+__device__ __forceinline__ void load_summary(int cnt, int keep, const int32_t* tot, int G, int ep,
+                                             int T, int k, const LoadOut& o, int* part) {
+  if (o.touched == nullptr && o.max_over_mean == nullptr) return;   // uniform
+  const int e = threadIdx.x;
+  const int E = G / ep;
+  int load = 0, used = 0;
+  if (ep > 1) {
+    if (e < E) {
+      const int per = E / ep, r = e / per, l = e - r * per;
+      for (int src_rank = 0; src_rank < ep; ++src_rank) load += tot[(r * ep + src_rank) * per + l];
+      used = load > 0;
+    }
+  } else if (e < G) {
+    load = cnt;
+    used = keep > 0;
+  }
+  int n_used = 0;
+  block_scan_1024(used, part, &n_used);
+  const int mx = block_max_1024(load, part);
+  if (threadIdx.x == 0) {
+    if (o.touched) o.touched[0] = n_used;
+    if (o.max_over_mean)
+      o.max_over_mean[0] = static_cast<float>(static_cast<double>(mx) * E /
+                                              (static_cast<double>(T) * k));
+  }
+}
+
 __global__ __launch_bounds__(kTB) void index_count_kernel(const int32_t* __restrict__ idx, int T,
                                                           int k, int E, int cap,
                                                           int32_t* __restrict__ blk) {
@@ -70,8 +105,7 @@ __global__ __launch_bounds__(kTB) void index_count_kernel(const int32_t* __restr
 __global__ __launch_bounds__(1024) void index_scan_kernel(
     int32_t* __restrict__ blk, int nb, int T, int k, int E, long long C,
     int32_t* __restrict__ slot_base, int32_t* __restrict__ slot_keep,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ counts_out,
-    int32_t* __restrict__ kept_out, int32_t* __restrict__ n_dropped) {
+    int32_t* __restrict__ offsets, LoadOut o, int ep) {
   __shared__ int32_t part[16];
   const int cap = C >= 0;
   const int nkeys = cap ? E * k : E;
@@ -90,9 +124,8 @@ __global__ __launch_bounds__(1024) void index_scan_kernel(
   __syncthreads();
   // per expert: count before drops and kept after capacity
   const int e = threadIdx.x;
-  int keep_e = 0;
+  int keep_e = 0, cnt = 0;
   if (e < E) {
-    int cnt = 0;
     if (cap) {
       // all j-th choices are served before any (j+1)-th choice
       for (int j = 0; j < k; ++j) {
@@ -109,8 +142,8 @@ __global__ __launch_bounds__(1024) void index_scan_kernel(
       cnt = tot[e];
       keep_e = cnt;
     }
-    if (counts_out) counts_out[e] = cnt;
-    if (kept_out) kept_out[e] = keep_e;
+    if (o.counts) o.counts[e] = cnt;
+    if (o.kept) o.kept[e] = keep_e;
   }
   // scan of kept over experts (E <= 1024 = blockDim.x)
   int kept_total = 0;
@@ -118,8 +151,9 @@ __global__ __launch_bounds__(1024) void index_scan_kernel(
   if (e < E) offsets[e + 1] = incl;
   if (threadIdx.x == 0) {
     offsets[0] = 0;
-    if (n_dropped) n_dropped[0] = T * k - kept_total;
+    if (o.n_dropped) o.n_dropped[0] = T * k - kept_total;
   }
+  load_summary(cnt, keep_e, tot, E, ep, T, k, o, part);
 }
 
 __global__ __launch_bounds__(kTB) void index_rank_kernel(
@@ -223,9 +257,7 @@ hipError_t launch_ep_traffic(const int32_t* offsets, int n, int E, int32_t* rows
 __device__ __forceinline__ void index_single_body(
     const int32_t* __restrict__ idx, int T, int k, int E, long long C,
     int32_t* __restrict__ offsets, int32_t* __restrict__ dest, int32_t* __restrict__ src,
-    int32_t* __restrict__ counts_out, int32_t* __restrict__ kept_out,
-    int32_t* __restrict__ n_dropped, int BM, int max_tiles, int ep, int4* __restrict__ tiles,
-    uint32_t* smem) {
+    const LoadOut& o, int BM, int max_tiles, int ep, int4* __restrict__ tiles, uint32_t* smem) {
   const int cap = C >= 0;
   const int nkeys = cap ? E * k : E;
   uint32_t* bm = smem;                                              // [nkeys][kWords]
@@ -254,9 +286,8 @@ __device__ __forceinline__ void index_single_body(
   }
   __syncthreads();
   const int e = tid;
-  int keep_e = 0;
+  int keep_e = 0, cnt = 0;
   if (e < E) {
-    int cnt = 0;
     if (cap) {
       for (int j = 0; j < k; ++j) {
         const int tj = tot[j * E + e];
@@ -272,8 +303,8 @@ __device__ __forceinline__ void index_single_body(
       cnt = tot[e];
       keep_e = cnt;
     }
-    if (counts_out) counts_out[e] = cnt;
-    if (kept_out) kept_out[e] = keep_e;
+    if (o.counts) o.counts[e] = cnt;
+    if (o.kept) o.kept[e] = keep_e;
   }
   int kept_total = 0;
   const int incl = block_scan_1024((e < E) ? keep_e : 0, part, &kept_total);
@@ -281,8 +312,9 @@ __device__ __forceinline__ void index_single_body(
   if (tid == 0) {
     off[0] = 0;
     offsets[0] = 0;
-    if (n_dropped) n_dropped[0] = T * k - kept_total;
+    if (o.n_dropped) o.n_dropped[0] = T * k - kept_total;
   }
+  load_summary(cnt, keep_e, tot, E, ep, T, k, o, part);
   __syncthreads();
 
   if (tid < T) {
@@ -338,11 +370,9 @@ __host__ __device__ constexpr size_t index_single_words(int E, int nkeys) {
 __global__ __launch_bounds__(1024) void index_single_kernel(
     const int32_t* __restrict__ idx, int T, int k, int E, long long C,
     int32_t* __restrict__ offsets, int32_t* __restrict__ dest, int32_t* __restrict__ src,
-    int32_t* __restrict__ counts_out, int32_t* __restrict__ kept_out,
-    int32_t* __restrict__ n_dropped, int BM, int max_tiles, int ep, int4* __restrict__ tiles) {
+    LoadOut o, int BM, int max_tiles, int ep, int4* __restrict__ tiles) {
   extern __shared__ uint32_t smem[];
-  index_single_body(idx, T, k, E, C, offsets, dest, src, counts_out, kept_out, n_dropped, BM,
-                    max_tiles, ep, tiles, smem);
+  index_single_body(idx, T, k, E, C, offsets, dest, src, o, BM, max_tiles, ep, tiles, smem);
 }
 
 // Small batches in one launch: selection (as router_select_kernel, without the
@@ -357,8 +387,7 @@ __global__ __launch_bounds__(1024) void route_index_single_kernel(
     const float* z, const float* __restrict__ bias, int T, int k, int E,
     int gate_all, int32_t* __restrict__ idx, float* __restrict__ gates, long long C,
     int32_t* __restrict__ offsets, int32_t* __restrict__ dest, int32_t* __restrict__ src,
-    int32_t* __restrict__ counts_out, int32_t* __restrict__ kept_out,
-    int32_t* __restrict__ n_dropped, int BM, int max_tiles, int4* tiles) {
+    LoadOut o, int BM, int max_tiles, int4* tiles) {
   extern __shared__ uint32_t smem[];
   const int nkeys = C >= 0 ? E * k : E;   // as index_keys()
   int32_t* sidx = reinterpret_cast<int32_t*>(smem + index_single_words(E, nkeys));   // [T][k]
@@ -379,8 +408,7 @@ __global__ __launch_bounds__(1024) void route_index_single_kernel(
     }
   }
   __syncthreads();
-  index_single_body(sidx, T, k, E, C, offsets, dest, src, counts_out, kept_out, n_dropped, BM,
-                    max_tiles, 1, tiles, smem);
+  index_single_body(sidx, T, k, E, C, offsets, dest, src, o, BM, max_tiles, 1, tiles, smem);
 }
 
 static size_t index_single_lds(int E, int nkeys) {
@@ -398,9 +426,8 @@ bool route_index_single_ok(int T, int E, int k, bool cap) {
 hipError_t launch_route_index_single(const float* z, const float* bias, int T, int k, int E,
                                      int gate_all, int32_t* idx, float* gates,
                                      long long capacity, int32_t* offsets, int32_t* dest,
-                                     int32_t* src, int32_t* counts, int32_t* kept,
-                                     int32_t* n_dropped, int BM, int max_tiles, int32_t* tiles,
-                                     hipStream_t s) {
+                                     int32_t* src, const LoadOut& load, int BM, int max_tiles,
+                                     int32_t* tiles, hipStream_t s) {
   const bool cap = capacity >= 0;
   if (!route_index_single_ok(T, E, k, cap)) return hipErrorInvalidValue;
   if (T == 0) return hipSuccess;
@@ -415,9 +442,8 @@ hipError_t launch_route_index_single(const float* z, const float* bias, int T, i
       if (e1 != hipSuccess) return e1;                                                       \
     }                                                                                        \
     kern<<<dim3(1), dim3(1024), lds, s>>>(z, bias, T, k, E, gate_all, idx, gates,             \
-                                          cap ? capacity : -1, offsets, dest, src, counts,   \
-                                          kept, n_dropped, BM, max_tiles,                    \
-                                          reinterpret_cast<int4*>(tiles));                   \
+                                          cap ? capacity : -1, offsets, dest, src, load, BM, \
+                                          max_tiles, reinterpret_cast<int4*>(tiles));        \
   } while (0)
   if (ne <= 1) MOE_RIS(1);
   else if (ne <= 2) MOE_RIS(2);
@@ -429,9 +455,8 @@ hipError_t launch_route_index_single(const float* z, const float* bias, int T, i
 
 hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capacity,
                         int32_t* blk, int32_t* slot_base, int32_t* slot_keep, int32_t* offsets,
-                        int32_t* dest, int32_t* src, int32_t* counts, int32_t* kept,
-                        int32_t* n_dropped, int BM, int max_tiles, int ep, int32_t* tiles,
-                        hipStream_t s) {
+                        int32_t* dest, int32_t* src, const LoadOut& load, int BM, int max_tiles,
+                        int ep, int32_t* tiles, hipStream_t s) {
   const bool cap = capacity >= 0;
   if (index_single_ok(T, E, k, cap)) {
     const size_t lds = index_single_lds(E, index_keys(E, k, cap));
@@ -440,8 +465,8 @@ hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capac
       if (e1 != hipSuccess) return e1;
     }
     index_single_kernel<<<dim3(1), dim3(1024), lds, s>>>(
-        idx, T, k, E, cap ? capacity : -1, offsets, dest, src, counts, kept, n_dropped, BM,
-        max_tiles, ep, reinterpret_cast<int4*>(tiles));
+        idx, T, k, E, cap ? capacity : -1, offsets, dest, src, load, BM, max_tiles, ep,
+        reinterpret_cast<int4*>(tiles));
     return hipGetLastError();
   }
   const int nb = index_blocks(T);
@@ -457,8 +482,7 @@ hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capac
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   index_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(blk, nb, T, k, E, cap ? capacity : -1,
-                                                   slot_base, slot_keep, offsets, counts, kept,
-                                                   n_dropped);
+                                                   slot_base, slot_keep, offsets, load, ep);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   index_rank_kernel<<<dim3(nb), dim3(kTB), lds, s>>>(idx, T, k, E, cap ? capacity : -1, blk,

@@ -89,17 +89,26 @@ bool index_single_ok(int T, int E, int k, bool cap);
 // launch_index writes, with the tile table.
 constexpr int kRouteIndexMaxTokens = 64;
 bool route_index_single_ok(int T, int E, int k, bool cap);
+// Load statistics the index writes where a pointer is set (each nullable):
+// per key the assignments before drops (counts) and after capacity (kept), the
+// dropped total, the number of experts that keep at least one assignment
+// (touched) and the largest expert load over the mean T*k/E (max_over_mean).
+struct LoadOut {
+  int32_t* counts = nullptr;
+  int32_t* kept = nullptr;
+  int32_t* n_dropped = nullptr;
+  int32_t* touched = nullptr;
+  float* max_over_mean = nullptr;
+};
 hipError_t launch_route_index_single(const float* z, const float* bias, int T, int k, int E,
                                      int gate_all, int32_t* idx, float* gates,
                                      long long capacity, int32_t* offsets, int32_t* dest,
-                                     int32_t* src, int32_t* counts, int32_t* kept,
-                                     int32_t* n_dropped, int BM, int max_tiles, int32_t* tiles,
-                                     hipStream_t s);
+                                     int32_t* src, const LoadOut& load, int BM, int max_tiles,
+                                     int32_t* tiles, hipStream_t s);
 hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capacity,
                         int32_t* blk, int32_t* slot_base, int32_t* slot_keep, int32_t* offsets,
-                        int32_t* dest, int32_t* src, int32_t* counts, int32_t* kept,
-                        int32_t* n_dropped, int BM, int max_tiles, int ep, int32_t* tiles,
-                        hipStream_t s);
+                        int32_t* dest, int32_t* src, const LoadOut& load, int BM, int max_tiles,
+                        int ep, int32_t* tiles, hipStream_t s);
 // Simulated expert parallelism (ep > 1 ranks): row-group ids and send-row matrix.
 hipError_t launch_ep_group_ids(const int32_t* idx, int T, int k, int E, int n, int32_t* gid,
                                hipStream_t s);

@@ -303,6 +303,19 @@ moe_status do_route(const Shape& s, float alpha, const void* x, const void* wr, 
   return MOE_OK;
 }
 
+// the load statistics of `st` (nullable) that the index kernels write
+moe::LoadOut load_out(const moe_stats* st) {
+  moe::LoadOut o;
+  if (st != nullptr) {
+    o.counts = st->counts;
+    o.kept = st->kept;
+    o.n_dropped = st->n_dropped;
+    o.touched = st->touched;
+    o.max_over_mean = st->max_over_mean;
+  }
+  return o;
+}
+
 // tiles (nullable): also build the grouped GEMM tile table there; it may alias
 // the workspace (written after the index kernels are done with it)
 moe_status do_permute(const Shape& s, const int32_t* idx, const void* x, int32_t* offsets,
@@ -320,8 +333,7 @@ moe_status do_permute(const Shape& s, const int32_t* idx, const void* x, int32_t
     keys = gid;
   }
   MOE_HIP(moe::launch_index(keys, s.T, s.k, s.G, s.C, blk, slot_base, slot_keep, offsets, dest,
-                            src, st ? st->counts : nullptr, st ? st->kept : nullptr,
-                            st ? st->n_dropped : nullptr, s.BM, s.max_tiles, s.ep, tiles, stream),
+                            src, load_out(st), s.BM, s.max_tiles, s.ep, tiles, stream),
           "index");
   if (x_perm != nullptr)
     MOE_HIP(moe::launch_gather_rows(s.elt, x, src, offsets, s.G, s.R, s.d, x_perm, stream),
@@ -676,8 +688,12 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   MOE_HIP(moe::launch_router_select(b.z, sel_bias, T, E, k, s.gate_all, b.idx, b.gates, nullptr,
                                     nullptr, nullptr, nullptr, strm),
           "router_select");
+  moe::LoadOut load;
+  load.counts = b.counts;
+  load.kept = b.kept;
+  load.n_dropped = b.ndrop;
   MOE_HIP(moe::launch_index(b.idx, T, k, E, s.C, b.blk, b.slot_base, b.slot_keep, b.offsets, b.dest,
-                            b.src, b.counts, b.kept, b.ndrop, s.BM, s.max_tiles, 1, b.tiles, strm),
+                            b.src, load, s.BM, s.max_tiles, 1, b.tiles, strm),
           "index");
   // ---- weight transposes (experts of >= kTransposeMinRows rows): on the side
   // stream, beside the recomputed gate/up product; joined before the first
@@ -922,8 +938,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
             "router_scores");
     MOE_HIP(moe::launch_route_index_single(
                 z, sel_bias, s.T, s.k, s.E, s.gate_all, idx, gates, s.C, offsets, dest, src,
-                stats ? stats->counts : nullptr, stats ? stats->kept : nullptr,
-                stats ? stats->n_dropped : nullptr, s.BM, s.max_tiles, tiles, strm),
+                load_out(stats), s.BM, s.max_tiles, tiles, strm),
             "route_index");
   } else {
     st = do_route(s, cfg->aux_alpha, x, w_router, sel_bias, idx, gates, stats, scratch, strm);

@@ -200,6 +200,13 @@ def touched_experts(idx: np.ndarray, E: int) -> int:
     return int(np.count_nonzero(np.bincount(np.asarray(idx).ravel(), minlength=E)))
 
 
+def max_over_mean_load(counts: np.ndarray, T: int, k: int) -> float:
+    """The busiest expert's load over the mean load T·k/E ([CME295] §3.3 and
+    §4.2; [15-779] §3.4); counts[e] are expert e's assignments before drops."""
+    counts = np.asarray(counts)
+    return float(np.max(counts)) / (T * k / counts.size)
+
+
 # ------------------------------------------------------------------ permutation
 
 def capacity(cf: float, T: int, k: int, E: int) -> Optional[int]:

@@ -83,7 +83,8 @@ def config_of(wl: wk.Workload, T: int) -> moe.MoeConfig:
 def run_forward(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int, bias="default",
                 ep: int = 0, stats: str = "full"):
     """Fused moe_forward; returns numpy copies of y, idx, gates and the stats.
-    stats="counts" asks only for the expert counts, kept rows and drops; "none" for no
+    stats="counts" asks only for what the index writes (expert counts, kept rows, drops,
+    touched experts, busiest load over the mean); "none" for no
     statistics (the keys of what was not asked for are absent)."""
     cfg = config_of(wl, T)
     cfg.ep_ranks = ep
@@ -95,7 +96,8 @@ def run_forward(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int, bias="d
     ws = moe.alloc_workspace(cfg, moe.STAGE_FORWARD)
     b = W.bias if bias == "default" else bias
     if stats == "counts":
-        st = moe.Stats(st.counts, st.kept, st.n_dropped)
+        st = moe.Stats(st.counts, st.kept, st.n_dropped, touched=st.touched,
+                       max_over_mean=st.max_over_mean)
     elif stats == "none":
         st = None
     moe.forward(cfg, x, W.wr, b, W.w1, W.w3, W.w2, W.s1, W.s3, W.s2, y, idx, gates, st, ws)
@@ -106,10 +108,14 @@ def run_forward(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int, bias="d
     if stats == "counts":
         return dict(y=y.cpu().numpy(), idx=idx.cpu().numpy().astype(np.int64),
                     gates=gates.cpu().numpy(), counts=st.counts.cpu().numpy(),
-                    kept=st.kept.cpu().numpy(), n_dropped=int(st.n_dropped.cpu()[0]))
+                    kept=st.kept.cpu().numpy(), n_dropped=int(st.n_dropped.cpu()[0]),
+                    touched=int(st.touched.cpu()[0]),
+                    max_over_mean=float(st.max_over_mean.cpu()[0]))
     return dict(y=y.cpu().numpy(), idx=idx.cpu().numpy().astype(np.int64),
                 gates=gates.cpu().numpy(), counts=st.counts.cpu().numpy(),
                 kept=st.kept.cpu().numpy(), n_dropped=int(st.n_dropped.cpu()[0]),
+                touched=int(st.touched.cpu()[0]),
+                max_over_mean=float(st.max_over_mean.cpu()[0]),
                 f=st.f.cpu().numpy(), P=st.P.cpu().numpy(), aux=float(st.aux.cpu()[0]),
                 z_loss=float(st.z_loss.cpu()[0]), entropy=float(st.entropy.cpu()[0]),
                 max_prob=float(st.max_prob.cpu()[0]), top_gap=float(st.top_gap.cpu()[0]))
@@ -150,7 +156,8 @@ def run_staged(wl: wk.Workload, W: Weights, x_host: np.ndarray, T: int, ep: int 
     out = dict(y=y.cpu().numpy(), idx=idx.cpu().numpy().astype(np.int64), gates=gates.cpu().numpy(),
                offsets=offsets.cpu().numpy(), dest=dest.cpu().numpy(), src=src.cpu().numpy(),
                counts=st.counts.cpu().numpy(), kept=st.kept.cpu().numpy(),
-               n_dropped=int(st.n_dropped.cpu()[0]),
+               n_dropped=int(st.n_dropped.cpu()[0]), touched=int(st.touched.cpu()[0]),
+               max_over_mean=float(st.max_over_mean.cpu()[0]),
                traffic=None if traffic is None else traffic.cpu().numpy().reshape(ep, ep))
     if not keep_perm:
         return out
@@ -193,12 +200,24 @@ def check_gates(wl, gpu_idx, gpu_gates, z64):
     return g64, err
 
 
+def check_load_summary(gpu, gpu_idx, E, counts, kept):
+    """touched (experts keeping an assignment) exact; the busiest expert's load over the
+    mean to fp32 rounding (the GPU divides in double and rounds once to float)."""
+    T, k = gpu_idx.shape
+    assert gpu["touched"] == int(np.count_nonzero(kept)), "touched"
+    ref = om.max_over_mean_load(counts, T, k)
+    assert abs(gpu["max_over_mean"] - ref) <= 2.0 ** -23 * ref, ("max_over_mean",
+                                                                  gpu["max_over_mean"], ref)
+
+
 def check_permutation(wl, T, gpu, gpu_idx):
     """Bit-exact against the oracle's histogram/capacity/permutation run on the GPU's idx."""
     p = om.assign_rows(gpu_idx, wl.E, wl.capacity_factor)
     assert np.array_equal(gpu["counts"], p["counts"]), "counts"
     assert np.array_equal(gpu["kept"], p["kept"]), "kept"
     assert gpu["n_dropped"] == p["n_dropped"], "n_dropped"
+    if "touched" in gpu:
+        check_load_summary(gpu, gpu_idx, wl.E, p["counts"], p["kept"])
     if "offsets" in gpu:
         assert np.array_equal(gpu["offsets"], p["offsets"]), "offsets"
         assert np.array_equal(gpu["dest"], p["dest"]), "dest"

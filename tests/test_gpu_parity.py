@@ -19,10 +19,9 @@ import torch
 import mixture_experts_layer_31_amd as moe
 import workloads as wk
 from oracle import moe as om
-from gpu_support import (Weights, check_gates, check_permutation, check_routing, check_y,
-                         y_rounding_bound,
-                         config_of, dev, log, oracle_route, oracle_y_sampled, run_forward,
-                         run_staged, to_dev)
+from gpu_support import (Weights, check_gates, check_load_summary, check_permutation,
+                         check_routing, check_y, config_of, dev, log, oracle_route,
+                         oracle_y_sampled, run_forward, run_staged, to_dev, y_rounding_bound)
 from sweep_cases import bwd_sweep_cases, sweep_cases
 
 pytestmark = pytest.mark.gpu
@@ -204,7 +203,7 @@ def test_forward_without_statistics(case):
     for other, what in ((none, "none"), (counts, "counts")):
         for key in ("y", "idx", "gates"):
             assert np.array_equal(other[key], g[key]), f"{case} stats={what}: {key}"
-    for key in ("counts", "kept", "n_dropped"):
+    for key in ("counts", "kept", "n_dropped", "touched", "max_over_mean"):
         assert np.array_equal(counts[key], g[key]), f"{case}: {key}"
     check_permutation(wl, T, counts, counts["idx"])
 
@@ -551,6 +550,9 @@ def test_expert_parallel_layout(ep):
     assert np.array_equal(a["dest"], dest)
     assert np.array_equal(a["src"], src)
     assert np.array_equal(a["counts"], np.diff(offsets))
+    per_expert = om.assign_rows(a["idx"], E)     # touched / busiest load are per expert
+    check_load_summary(a, a["idx"], E, per_expert["counts"], per_expert["kept"])
+    assert a["touched"] == b["touched"] and a["max_over_mean"] == b["max_over_mean"]
     assert np.array_equal(a["traffic"], om.ep_send_rows(offsets, E, ep))
     assert np.array_equal(a["x_perm"], inp.x[src])
     r, x64 = oracle_route(wl, W, inp.x)

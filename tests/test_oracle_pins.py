@@ -811,3 +811,16 @@ def test_sampled_backward_equals_full_backward(case):
         assert np.allclose(d1, full["dws1"], rtol=1e-12, atol=1e-12)
         assert np.allclose(d3, full["dws3"], rtol=1e-12, atol=1e-12)
         assert np.allclose(d2, full["dws2"], rtol=1e-12, atol=1e-12)
+
+
+def test_max_over_mean_load_cases():
+    """Balanced load gives 1; every assignment on one expert gives E; a hand-counted
+    case: 2 tokens x top-2 over 2 experts with loads 3 and 1 (mean 2) gives 1.5."""
+    assert om.max_over_mean_load(np.full(8, 16), T=64, k=2) == 1.0
+    assert om.max_over_mean_load(np.array([128, 0, 0, 0, 0, 0, 0, 0]), T=64, k=2) == 8.0
+    assert om.max_over_mean_load(np.array([3, 1]), T=2, k=2) == 1.5
+    # from a routing: the per-expert histogram of idx, brute force
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.choice(8, 2, replace=False) for _ in range(37)])
+    loads = [sum(int(e == x) for row in idx for x in row) for e in range(8)]
+    assert om.max_over_mean_load(om.assign_rows(idx, 8)["counts"], 37, 2) == max(loads) / (37 * 2 / 8)
