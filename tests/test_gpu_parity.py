@@ -272,6 +272,35 @@ def test_k_equals_E_is_full_softmax():
     assert np.allclose(np.take_along_axis(p, g["idx"], 1), g["gates"], atol=1e-6)
 
 
+_PS_CASES = {
+    # one expert takes most first choices: a group of 1600 rows = seven 256-row
+    # tiles (six full ones through the full ring), beside groups of ~50 (short ring);
+    # a two-step K loop in the down product (d_ff = 128)
+    "one_hot_expert": dict(T=1600, d=256, E=32, k=2, d_ff=128,
+                           offsets=(6.0,) + (0.0,) * 31),
+    # groups of every size (logit offsets of variance 1) over 48 experts: short and
+    # full rings, empty experts, six K-steps
+    "varied_groups": dict(T=2400, d=512, E=48, k=2, d_ff=384, offset_var=1.0),
+    # top-1 over 32 experts, three 256-column output panels per group
+    "k1_three_panels": dict(T=3200, d=768, E=32, k=1, d_ff=256, offset_var=0.5),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_PS_CASES))
+def test_weight_streaming_products(case):
+    """Layers with many short groups (at least 32 experts, ~100 rows on average): their
+    products take 256-row tiles in n-fastest order, groups of at most 160 rows through
+    the deeper ring of short stages and longer ones through the full ring. y at every
+    token against the oracle, the staged entry points equal to the fused forward bit
+    for bit."""
+    wl = _adhoc(f"ps_{case}", 120 + sorted(_PS_CASES).index(case), dtype=wk.BF16,
+                **_PS_CASES[case])
+    W = Weights(wl)
+    g, _, _ = full_check(wl, W, wl.T, staged=True)
+    if case == "one_hot_expert":
+        assert g["counts"].max() > 1024, "the skew must give a group of several tiles"
+
+
 def test_shared_expert_wider_than_routed():
     """d_ff_shared != d_ff: the shared rows of the activation buffer are wider than the
     routed ones, so every row sits at the common act stride."""
