@@ -44,7 +44,10 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 METRIC = "MoE-layer tokens/s at 1 GPU + % MFMA peak (prefill) / % HBM BW (decode)"
-GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_31_amd", "csrc", "gemm_bf16.hip")
+# sources of the gate/up kernel (its code, tile order and helpers): the committed
+# counter summary is used only while their hash matches
+GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_31_amd", "csrc", f)
+                for f in ("gemm_bf16.hip", "gemm_common.h", "common.h")]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_gateup_mixtral_t4096_counters.md")
 CALIB_LIB = os.path.join(ROOT, "mixture_experts_layer_31_amd", "libmoe_calibrate.so")
 # the rest of the metric, timed after the headline workload: the decode rows (HBM),
@@ -145,8 +148,11 @@ def device_ceilings():
 
 
 def kernel_source_hash():
-    with open(GEMM_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in GEMM_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def counters_traffic(workload):
