@@ -853,8 +853,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
   __shared__ f32x4 red[KS > 1 ? 3 : 1][GATEUP ? 2 : 1][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kpart = wave % KS;
-  const long long item = static_cast<long long>(blockIdx.x) * IPB + wave / KS;
-  const long long items_g = static_cast<long long>(max_tiles) * (N >> 4);
+  // Workgroup L of the grouped rows: n-slice L % ncol of token tiles
+  // (L / ncol) * IPB .. + IPB - 1 (one per item of the workgroup, so items of a
+  // group's consecutive tiles share the weight rows in cache). n-slices run
+  // fastest, so the empty tiles at the end of the table (the table holds an upper
+  // bound of tiles) are the last workgroups of the grid. With token tiles fastest,
+  // a table of 4 tiles of which 2 were empty made every other workgroup empty, and
+  // that pattern of active workgroups kept half of the CUs' slots idle (2 tokens,
+  // Mixtral shape: gate/up 92 -> 134 us).
+  const int ncol = N >> 4;
+  const long long wg_g = static_cast<long long>((max_tiles + IPB - 1) / IPB) * ncol;
+  const long long L = blockIdx.x;
   // this wave's item: a tile of the grouped rows or of the second segment
   const uint16_t* xa = xa_g;
   const int32_t* src = src_g;
@@ -864,12 +873,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
   bool live;
   int n0 = 0;
   TileCoord tc{0, 0, 0};
-  if (item < items_g) {
-    live = true;
-    n0 = static_cast<int>(item / max_tiles) * 16;
-    tc = lookup_tile(tiles, n_single, 16, static_cast<int>(item % max_tiles));
+  if (L < wg_g) {
+    const int mt = static_cast<int>(L / ncol) * IPB + wave / KS;
+    live = mt < max_tiles;
+    n0 = static_cast<int>(L % ncol) * 16;
+    if (live) tc = lookup_tile(tiles, n_single, 16, mt);
   } else {
-    const long long j = item - items_g;
+    const long long j = (L - wg_g) * IPB + wave / KS;
     live = j < stream_seg_items(seg);
     if (live) {
       const int seg_tiles = (seg.rows + 15) >> 4;
@@ -981,14 +991,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
 // or 4 when a wave's K range is short (one batch) or, in the down product,
 // very long (more waves per SIMD in place of deeper batches).
 template <bool GATEUP, int U, int KS, bool H16>
-static void launch_stream(long long items, const GemmTileMap& map, int m_tiles,
+static void launch_stream(const GemmTileMap& map, int m_tiles,
                           const uint16_t* xa, const int32_t* src, int a_stride, int a_row0,
                           const uint16_t* wa, const uint16_t* wb, long long w_stride, void* out,
                           int out_stride, int out_row0, int K, int N, const StreamSeg& seg,
                           hipStream_t s) {
   constexpr int IPB = 4 / KS;
+  const long long wgs = static_cast<long long>((m_tiles + IPB - 1) / IPB) * (N >> 4) +
+                        (stream_seg_items(seg) + IPB - 1) / IPB;
   gemm_bf16_stream_kernel<GATEUP, U, KS, H16>
-      <<<dim3(static_cast<unsigned>((items + IPB - 1) / IPB)), dim3(256), 0, s>>>(
+      <<<dim3(static_cast<unsigned>(wgs)), dim3(256), 0, s>>>(
           map.tiles, m_tiles, map.n_single, xa, src, a_stride, a_row0, wa, wb, w_stride, out,
           out_stride, out_row0, K, N, seg);
 }
@@ -1009,7 +1021,7 @@ static hipError_t run_stream(const GemmTileMap& map, const uint16_t* xa, const i
   const int steps = K / 32 / KS;
   const bool u4 = steps < 16 || (!GATEUP && steps >= 100);
 #define MOE_STREAM(U_, KS_)                                                                  \
-  launch_stream<GATEUP, U_, KS_, H16>(items, map, m_tiles, xa, src, a_stride, a_row0, wa, wb,\
+  launch_stream<GATEUP, U_, KS_, H16>(map, m_tiles, xa, src, a_stride, a_row0, wa, wb,       \
                                  w_stride, out, out_stride, out_row0, K, N, seg, s)
   if (KS == 4) {
     if (u4) MOE_STREAM(4, 4); else MOE_STREAM(8, 4);
@@ -1067,8 +1079,12 @@ bool gemm_n_fast(int BM, long long R_max, int experts) {
 }
 
 int gemm_max_tiles(int BM, int R_max, int E) {
-  // sum_e ceil(n_e / BM) <= ceil(R / BM) + (number of non-empty groups)
-  return (R_max + BM - 1) / BM + (E < R_max ? E : R_max);
+  // sum_e ceil(n_e / BM) <= sum_e floor(n_e / BM) + (non-empty groups)
+  //                      <= floor(R / BM) + min(E, R)
+  // (ceil(n / BM) <= floor(n / BM) + 1 for n > 0). Tight for a decode step of
+  // one token: k groups of one row, k tiles, so its streaming launches hold no
+  // empty tile rows.
+  return R_max / BM + (E < R_max ? E : R_max);
 }
 
 hipError_t launch_tile_map(const int32_t* offsets, int E, int BM, int max_tiles, int ep,
