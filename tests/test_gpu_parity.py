@@ -181,6 +181,15 @@ _NOSTAT_CASES = {
                                                              dtype=wk.BF16))),
     "e1024_k16_t20": dict(T=20, wl=("ns_e1024", 125, dict(d=256, E=1024, k=16, d_ff=64,
                                                          dtype=wk.BF16))),
+    # decode steps whose scores come from the vector-unit score kernel with 1, 2 and
+    # 4 chunks per thread (d <= 2048, <= 4096, <= 8192)
+    "scores_j1_t2": dict(T=2, wl=("ns_sj1", 150, dict(d=1024, E=8, k=2, d_ff=128,
+                                                      dtype=wk.BF16, router="orthonormal"))),
+    "scores_j2_e4_t3": dict(T=3, wl=("ns_sj2", 151, dict(d=4096, E=4, k=2, d_ff=128,
+                                                         dtype=wk.BF16))),
+    "scores_j4_shared_t1": dict(T=1, wl=("ns_sj4", 152, dict(d=6144, E=16, k=2, d_ff=128,
+                                                             n_shared=1, d_ff_shared=128,
+                                                             dtype=wk.BF16, bias_range=0.1))),
 }
 
 
@@ -293,7 +302,7 @@ def test_weight_streaming_products(case):
     the deeper ring of short stages and longer ones through the full ring. y at every
     token against the oracle, the staged entry points equal to the fused forward bit
     for bit."""
-    wl = _adhoc(f"ps_{case}", 120 + sorted(_PS_CASES).index(case), dtype=wk.BF16,
+    wl = _adhoc(f"ps_{case}", 160 + sorted(_PS_CASES).index(case), dtype=wk.BF16,
                 **_PS_CASES[case])
     W = Weights(wl)
     g, _, _ = full_check(wl, W, wl.T, staged=True)
@@ -897,7 +906,7 @@ def test_coverage_law_with_gpu_routing():
         assert abs(cov.mean() - want) <= 3 * se + 1e-12, B
 
 
-@pytest.mark.parametrize("T", [1, 8, 32])
+@pytest.mark.parametrize("T", [1, 2, 8, 32])
 def test_mixtral_decode_without_statistics(T):
     """The one-workgroup selection + index of the fused forward against the separate kernels."""
     W = weights("mixtral_t32")
