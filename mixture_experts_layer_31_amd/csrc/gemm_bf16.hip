@@ -1007,17 +1007,36 @@ static void launch_stream(const GemmTileMap& map, int m_tiles,
 
 // seg: an optional dense group launched with the grouped rows (its K may differ;
 // the launch shape follows the grouped rows' K and the total item count)
+static int stream_split_rule(long long items, int avg) {
+  if (items < 1024 || (items < 8192 && avg <= 2)) return 4;
+  if (items < 16384 && avg <= 4) return 2;
+  return 1;
+}
+
+static int stream_split(const GemmTileMap& map, int N, const StreamSeg& seg) {
+  const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + 15) / 16;
+  const long long items = static_cast<long long>(m_tiles) * (N / 16) + stream_seg_items(seg);
+  return stream_split_rule(items, map.tiles ? map.avg_rows : map.n_single);
+}
+
+int stream_gateup_split(int max_tiles, int avg_rows, int N, int seg_rows, int seg_N) {
+  StreamSeg seg;
+  seg.rows = seg_rows;
+  seg.N = seg_N;
+  return stream_split_rule(static_cast<long long>(max_tiles) * (N / 16) + stream_seg_items(seg),
+                           avg_rows);
+}
+
+// ks_force > 0: that K split instead of the rule's (4, 2 or 1)
 template <bool GATEUP, bool H16>
 static hipError_t run_stream(const GemmTileMap& map, const uint16_t* xa, const int32_t* src,
                              int a_stride, int a_row0, const uint16_t* wa, const uint16_t* wb,
                              long long w_stride, void* out, int out_stride, int out_row0, int K,
-                             int N, hipStream_t s, const StreamSeg& seg = StreamSeg{}) {
+                             int N, hipStream_t s, const StreamSeg& seg = StreamSeg{},
+                             int ks_force = 0) {
   const int m_tiles = map.tiles ? map.max_tiles : (map.n_single + 15) / 16;
-  const long long items = static_cast<long long>(m_tiles) * (N / 16) + stream_seg_items(seg);
-  const int avg = map.tiles ? map.avg_rows : map.n_single;
-  int KS = 1;
-  if (items < 1024 || (items < 8192 && avg <= 2)) KS = 4;
-  else if (items < 16384 && avg <= 4) KS = 2;
+  const int KS = ks_force > 0 ? ks_force : stream_split(map, N, seg);
+  if (KS != 1 && KS != 2 && KS != 4) return hipErrorInvalidValue;
   const int steps = K / 32 / KS;
   const bool u4 = steps < 16 || (!GATEUP && steps >= 100);
 #define MOE_STREAM(U_, KS_)                                                                  \
@@ -1253,7 +1272,7 @@ hipError_t launch_gemm_gateup_bf16(const GemmTileMap& map, const GateUpArgs& a, 
                                      a.act_stride, a.out_row0, a.K, a.N, s);
   if (BM == 16)
     return run_stream<true, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act, a.act_stride,
-                                  a.out_row0, a.K, a.N, s);
+                                  a.out_row0, a.K, a.N, s, StreamSeg{}, a.stream_ks);
   return run_small<32, 64, 1, 2, true, true>(map, x, a.src, a.K, 0, w1, w3, a.w_stride, a.act,
                                              a.act_stride, a.out_row0, a.K, a.N, s);
 }

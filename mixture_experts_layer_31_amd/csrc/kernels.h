@@ -168,7 +168,14 @@ struct GateUpArgs {
   int K, N;               // K = d, N = d_ff
   float* h1 = nullptr;    // optional fp32 pre-activations X W1^T, X W3^T at the
   float* h3 = nullptr;    // activation's rows and stride (256-row tiles only)
+  int stream_ks = 0;      // 16-row streaming tiles: the K split to use (0: the
+                          // launch's own rule; stream_gateup_split() gives another's)
 };
+// The K split that a 16-row streaming launch of a tile table (max_tiles tiles,
+// avg_rows rows per group, N columns) plus a dense segment of seg_rows rows and
+// seg_N columns chooses: a product run on its own gets this value in
+// GateUpArgs::stream_ks to compute bit for bit as it would in that joint launch.
+int stream_gateup_split(int max_tiles, int avg_rows, int N, int seg_rows, int seg_N);
 struct DownArgs {
   const void* act;        // [rows][act_stride]
   int act_stride;

@@ -322,8 +322,10 @@ def test_shared_expert_wider_than_routed():
 @pytest.mark.parametrize("T,dffs", [(1, 192), (5, 64), (16, 320), (17, 192), (40, 128)])
 def test_decode_shared_expert_beside_routed(T, dffs):
     """Decode-sized steps stream the shared expert's weights in the routed experts' launch,
-    at its own width (d_ff_shared != d_ff); the down product joins it up to 16 tokens.
-    Every token against the oracle, and the staged entry points give the same y."""
+    at its own width (d_ff_shared != d_ff); the down product joins it up to 16 tokens, and
+    above 16 the fused forward starts the shared gate/up product on the side stream before
+    the router (with the joint launch's K split). Every token against the oracle, and the
+    staged entry points give the same y bit for bit."""
     wl = _adhoc(f"dec_shared_{dffs}", 126, T=T, d=256, E=64, k=6, d_ff=128, n_shared=1,
                 d_ff_shared=dffs, dtype=wk.BF16)
     W = Weights(wl)
