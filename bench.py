@@ -44,10 +44,17 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 METRIC = "MoE-layer tokens/s at 1 GPU + % MFMA peak (prefill) / % HBM BW (decode)"
-# sources of the gate/up kernel (its code, tile order and helpers): the committed
-# counter summary is used only while their hash matches
-GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_31_amd", "csrc", f)
-                for f in ("gemm_bf16.hip", "gemm_common.h", "common.h")]
+# sources of the prefill gate/up kernel: its part of gemm_bf16.hip (the one-wave-per-
+# SIMD kernel, its launcher and the gate/up dispatch) and the headers with its tile
+# order and helpers; the committed counter summary is used only while their hash matches
+_CSRC = os.path.join(ROOT, "mixture_experts_layer_31_amd", "csrc")
+GEMM_SOURCE_PARTS = [
+    ("gemm_bf16.hip", "// ---------------------------------------------------------------- large tiles, one wave per SIMD",
+     "// ---------------------------------------------------------------- decode tiles"),
+    ("gemm_bf16.hip", "// One wave per SIMD, 256 x 256 weight-row tiles", "hipError_t launch_gemm_gateup_bf16_with_shared("),
+    ("gemm_common.h", None, None),
+    ("common.h", None, None),
+]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_gateup_mixtral_t4096_counters.md")
 CALIB_LIB = os.path.join(ROOT, "mixture_experts_layer_31_amd", "libmoe_calibrate.so")
 # the rest of the metric, timed after the headline workload: the decode rows (HBM),
@@ -149,9 +156,13 @@ def device_ceilings():
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for path in GEMM_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+    for name, start, end in GEMM_SOURCE_PARTS:
+        with open(os.path.join(_CSRC, name), encoding="utf-8") as f:
+            text = f.read()
+        if start is not None:
+            a = text.index(start)
+            text = text[a:text.index(end, a)]
+        h.update(text.encode("utf-8"))
     return h.hexdigest()[:16]
 
 

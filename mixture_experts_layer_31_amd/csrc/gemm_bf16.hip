@@ -853,7 +853,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
   __shared__ f32x4 red[KS > 1 ? 3 : 1][GATEUP ? 2 : 1][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kpart = wave % KS;
-  // Workgroup L of the grouped rows: n-slice L % ncol of token tiles
+  // The second segment's workgroups come first (all of their items are real, and
+  // at 64 rows a shared expert's workgroups hold its whole K: started last, they
+  // formed a tail; DeepSeek shape at 64 tokens, joint gate/up launch 2.47 ms).
+  // Then workgroup L of the grouped rows: n-slice L % ncol of token tiles
   // (L / ncol) * IPB .. + IPB - 1 (one per item of the workgroup, so items of a
   // group's consecutive tiles share the weight rows in cache). n-slices run
   // fastest, so the empty tiles at the end of the table (the table holds an upper
@@ -862,8 +865,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
   // that pattern of active workgroups kept half of the CUs' slots idle (2 tokens,
   // Mixtral shape: gate/up 92 -> 134 us).
   const int ncol = N >> 4;
-  const long long wg_g = static_cast<long long>((max_tiles + IPB - 1) / IPB) * ncol;
-  const long long L = blockIdx.x;
+  const long long wg_s = (stream_seg_items(seg) + IPB - 1) / IPB;
+  const long long L0 = blockIdx.x;
   // this wave's item: a tile of the grouped rows or of the second segment
   const uint16_t* xa = xa_g;
   const int32_t* src = src_g;
@@ -873,13 +876,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
   bool live;
   int n0 = 0;
   TileCoord tc{0, 0, 0};
-  if (L < wg_g) {
+  if (L0 >= wg_s) {
+    const long long L = L0 - wg_s;
     const int mt = static_cast<int>(L / ncol) * IPB + wave / KS;
     live = mt < max_tiles;
     n0 = static_cast<int>(L % ncol) * 16;
     if (live) tc = lookup_tile(tiles, n_single, 16, mt);
   } else {
-    const long long j = (L - wg_g) * IPB + wave / KS;
+    const long long j = L0 * IPB + wave / KS;
     live = j < stream_seg_items(seg);
     if (live) {
       const int seg_tiles = (seg.rows + 15) >> 4;
