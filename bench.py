@@ -88,7 +88,7 @@ def parse():
     ap.add_argument("--configs", default=",".join(CONFIG_SWEEP),
                     help="comma-separated workloads timed after the headline one (their "
                          "fused steps, from cold caches where HBM-bound); empty for none")
-    ap.add_argument("--config-steps", type=int, default=10)
+    ap.add_argument("--config-steps", type=int, default=20)
     return ap.parse_args()
 
 
@@ -436,7 +436,7 @@ def main():
 
 def config_sweep(names, K, no_flush):
     """The fused step (one moe_forward) of each named workload, K timed steps after 3
-    warm-ups; HBM-bound workloads from cold caches (a 1 GiB read before each step,
+    warm-ups (mean, median, minimum and maximum reported); HBM-bound workloads from cold caches (a 1 GiB read before each step,
     outside its timing). Work and bytes are counted from each batch's own routing as
     for the headline. Workloads of one shape share their uploaded weights. Also the
     GPU-routing coverage of decode batches at the Mixtral shape (CME295 notes §2.3)."""
@@ -519,6 +519,7 @@ def config_sweep(names, K, no_flush):
         gb = B / (ms * 1e-3) / 1e9
         rec = {"workload": name, "T": T, "ms": round(ms, 4),
                "ms_median": round(float(np.median(ms_all)), 4),
+               "ms_min": round(float(ms_all.min()), 4), "ms_max": round(float(ms_all.max()), 4),
                "tokens_per_s": round(T / (ms * 1e-3), 1), "tflops": round(tf, 2),
                "gbps": round(gb, 1), "bound": bound, "frac_mfma": round(tf / peak_f, 4),
                "frac_hbm": round(gb / PEAK_HBM_GBPS, 4),
