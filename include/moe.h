@@ -41,9 +41,9 @@
  *     scratch and accepts ws == NULL.
  *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *     asynchronously; the call never synchronises the host and never reads
- *     device data back. moe_backward, and the expert entry points (moe_expert_*,
- *     moe_forward) for decode-sized batches with a shared expert, run part of
- *     their work on a side stream the library keeps per device, forked from
+ *     device data back. The expert entry points (moe_expert_*, moe_forward)
+ *     for decode-sized batches with a shared expert run part of their work
+ *     on a side stream the library keeps per device, forked from
  *     `stream` by an event and joined back into it, so every effect of the call
  *     is still ordered on `stream`.
  *   - Arguments are validated before anything is enqueued. On any error the
@@ -287,12 +287,9 @@ moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t
  *   that receive no row get zero gradients.
  *   ws: moe_workspace_size(cfg, MOE_STAGE_BACKWARD). T == 0 leaves the
  *   outputs untouched.
- * Streams: all work is ordered after what precedes the call on `stream`, and
- * everything after it on `stream` sees the results. When experts average at
- * least 512 rows, the weights are transposed once per call on a second stream
- * that the library keeps per device (default priority), forked from and joined
- * back into `stream` through events; calls from several host threads take turns
- * on it. Two calls that share a workspace must be ordered on one stream.
+ * Streams: all work runs on `stream`, ordered after what precedes the call;
+ * everything after it on `stream` sees the results. Two calls that share a
+ * workspace must be ordered on one stream.
  * Errors: INVALID_ARG (bad config, NULL or misaligned pointer), WORKSPACE,
  * UNSUPPORTED (fp32, ep_ranks > 1, or d, d_ff, d_ff_shared not multiples of
  * 256).                                                                       */

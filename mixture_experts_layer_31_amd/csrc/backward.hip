@@ -7,83 +7,12 @@
 // loss adds (alpha E / T) p_i (f_i - sum_j p_j f_j) to the logits' gradient
 // (same notes, §3.2). The expert products are the transposed GEMMs of the
 // forward ones (CMU 15-779 Lecture 21 notes, §7: dW2 = H^T dY and so on); the
-// GEMMs themselves run in gemm_bf16.hip. Every reduction here sums in a fixed
+// GEMMs themselves run in gemm_bf16.hip and gemm_kmajor.hip. Every reduction here sums in a fixed
 // order, so the gradients are reproducible bit for bit.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
-
-// A TM-row x 128-column tile of 16-bit values, transposed through LDS: in_row(rr)
-// gives row rr's first column (nullptr: a zero row), out_row(n) the TM-value
-// output row that receives column n. LDS holds 32-bit words pairing rows 2i and
-// 2i+1 of one column (low half = row 2i), so every output row is TM/2 contiguous
-// words. Every wave-wide global access is coalesced: a load instruction covers 4
-// rows x 256 contiguous bytes (16 lanes a row), a store instruction 8 output rows
-// x 128 contiguous bytes. The odd word pitch TM/2 + 1 keeps the LDS stores at
-// most 2-way bank conflicted.
-template <int TM>
-struct TrTile {
-  static constexpr int kPitch = TM / 2 + 1;
-  static constexpr int kWords = 128 * kPitch;
-};
-
-template <int TM, class InRow, class OutRow>
-__device__ __forceinline__ void transpose_tile(InRow in_row, OutRow out_row, uint32_t* lds) {
-  constexpr int S = TrTile<TM>::kPitch;
-  const int tid = threadIdx.x;
-  {
-    const int c8 = tid & 15, rs = tid >> 4;   // columns 8 c8 .. 8 c8 + 7; pairs rs + 16 pp
-#pragma unroll
-    for (int pp = 0; pp < TM / 32; ++pp) {
-      const int i = rs + 16 * pp;
-      const uint16_t* pa = in_row(2 * i);
-      const uint16_t* pb = in_row(2 * i + 1);
-      u32x4 a = {0u, 0u, 0u, 0u}, b = a;
-      if (pa != nullptr) a = *reinterpret_cast<const u32x4*>(pa + c8 * 8);
-      if (pb != nullptr) b = *reinterpret_cast<const u32x4*>(pb + c8 * 8);
-      uint32_t* w = lds + c8 * 8 * S + i;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        w[(2 * q) * S] = (a[q] & 0xFFFFu) | (b[q] << 16);
-        w[(2 * q + 1) * S] = (a[q] >> 16) | (b[q] & 0xFFFF0000u);
-      }
-    }
-  }
-  __syncthreads();
-  {
-    constexpr int kChunks = TM / 8;           // 16-byte chunks per output row
-#pragma unroll
-    for (int pass = 0; pass < TM / 16; ++pass) {
-      const int id = tid + 256 * pass;
-      const int n = id / kChunks, q = id % kChunks;
-      const uint32_t* w = lds + n * S + 4 * q;
-      u32x4 o;
-      o[0] = w[0];
-      o[1] = w[1];
-      o[2] = w[2];
-      o[3] = w[3];
-      *reinterpret_cast<u32x4*>(out_row(n) + q * 8) = o;
-    }
-  }
-}
-
-// out[b][n][col0 + m] = in[b][m][n] for in [B][M][N]; M a multiple of TM, N of 128.
-// grid (M/TM, N/128, B): consecutive workgroups fill consecutive 256-byte pieces
-// of the same output rows.
-template <int TM>
-__global__ __launch_bounds__(256) void transpose_mat_kernel(const uint16_t* __restrict__ in, int M,
-                                                            int N, uint16_t* __restrict__ out,
-                                                            int out_stride, int col0,
-                                                            long long out_batch) {
-  __shared__ uint32_t lds[TrTile<TM>::kWords];
-  const int m0 = blockIdx.x * TM, n0 = blockIdx.y * 128;
-  const uint16_t* ib = in + static_cast<size_t>(blockIdx.z) * M * N;
-  uint16_t* ob = out + static_cast<size_t>(blockIdx.z) * out_batch;
-  transpose_tile<TM>(
-      [&](int rr) -> const uint16_t* { return ib + static_cast<size_t>(m0 + rr) * N + n0; },
-      [&](int n) { return ob + static_cast<size_t>(n0 + n) * out_stride + col0 + m0; }, lds);
-}
 
 // act = silu(h1) * h3 rounded to bf16, rows [row0, row0 + rows), n columns.
 __global__ __launch_bounds__(256) void swiglu_fwd_kernel(const float* __restrict__ h1,
@@ -263,11 +192,13 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
 }
 
 // dx_t = sum_j dXp[dest[t,j]] (slot order) + dXp[shared_row0 + t]
-// + sum_e dz[t,e] W_r[e] (expert order), fp32. A workgroup takes TT tokens and
+// + sum_e dz[t,e] W_r[e] (expert order), fp32. With dXp2 set, a routed row's
+// dXp is the sum of two halves, dXp[r] + dXp2[r] (the W1 and W3 parts). A workgroup takes TT tokens and
 // 1024 columns (4 per thread), so each W_r row segment is loaded once for TT
 // tokens; the TT tokens' dz rows sit in LDS. grid (d / 1024, ceil(T / TT)).
 template <typename Tw, int TT>
 __global__ __launch_bounds__(256) void unpermute_dx_kernel(const float* __restrict__ dxp,
+                                                           const float* __restrict__ dxp2,
                                                            const int32_t* __restrict__ dest,
                                                            const float* __restrict__ dz,
                                                            const Tw* __restrict__ wr, int T,
@@ -290,7 +221,9 @@ __global__ __launch_bounds__(256) void unpermute_dx_kernel(const float* __restri
       for (int j = 0; j < k; ++j) {
         const int r = dest[static_cast<size_t>(t) * k + j];
         if (r < 0) continue;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(dxp + static_cast<size_t>(r) * d + i);
+        f32x4 v = *reinterpret_cast<const f32x4*>(dxp + static_cast<size_t>(r) * d + i);
+        if (dxp2 != nullptr)
+          v = v + *reinterpret_cast<const f32x4*>(dxp2 + static_cast<size_t>(r) * d + i);
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[tt][q] += v[q];
       }
@@ -392,22 +325,6 @@ hipError_t launch_single_group_offsets(int rows, int32_t* off, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_transpose_mat(const uint16_t* in, int B, int M, int N, uint16_t* out,
-                                int out_stride, int col0, long long out_batch, hipStream_t s,
-                                bool narrow) {
-  if (M % 128 || N % 128 || out_stride % 8 || col0 % 8) return hipErrorInvalidValue;
-  // measured: 128-row tiles are 2-3 % faster for wide inputs (N > M), 64-row tiles
-  // 7-9 % faster for tall ones; `narrow` asks for 64-row tiles (17 KB of LDS), which
-  // fit on a CU beside a 128 KB GEMM workgroup
-  if (narrow || M > N)
-    transpose_mat_kernel<64><<<dim3(M / 64, N / 128, B), dim3(256), 0, s>>>(
-        in, M, N, out, out_stride, col0, out_batch);
-  else
-    transpose_mat_kernel<128><<<dim3(M / 128, N / 128, B), dim3(256), 0, s>>>(
-        in, M, N, out, out_stride, col0, out_batch);
-  return hipGetLastError();
-}
-
 hipError_t launch_swiglu_fwd(const float* h1, const float* h3, int stride, int row0, int rows,
                              int n, uint16_t* act, hipStream_t s) {
   const long long cnt = static_cast<long long>(rows) * n;
@@ -442,24 +359,25 @@ hipError_t launch_gate_bwd(const float* z, const int32_t* idx, const float* gate
 }
 
 template <typename Tw, int TT>
-static void unpermute_dx_as(const float* dxp, const int32_t* dest, const float* dz, const void* wr,
-                            int T, int k, int E, int d, int shared_row0, float* dx, hipStream_t s) {
+static void unpermute_dx_as(const float* dxp, const float* dxp2, const int32_t* dest,
+                            const float* dz, const void* wr, int T, int k, int E, int d,
+                            int shared_row0, float* dx, hipStream_t s) {
   const dim3 grid(d / 1024 + (d % 1024 ? 1 : 0), (T + TT - 1) / TT);
   unpermute_dx_kernel<Tw, TT><<<grid, dim3(256), TT * E * sizeof(float), s>>>(
-      dxp, dest, dz, static_cast<const Tw*>(wr), T, k, E, d, shared_row0, dx);
+      dxp, dxp2, dest, dz, static_cast<const Tw*>(wr), T, k, E, d, shared_row0, dx);
 }
 
-hipError_t launch_unpermute_dx(int dtype_bf16, const float* dxp, const int32_t* dest,
-                               const float* dz, const void* wr, int T, int k, int E, int d,
-                               int shared_row0, float* dx, hipStream_t s) {
+hipError_t launch_unpermute_dx(int dtype_bf16, const float* dxp, const float* dxp2,
+                               const int32_t* dest, const float* dz, const void* wr, int T, int k,
+                               int E, int d, int shared_row0, float* dx, hipStream_t s) {
   if (d % 4) return hipErrorInvalidValue;
   const bool wide = E > 32;   // more W_r rows per token: share each load among more tokens
   if (dtype_bf16) {
-    if (wide) unpermute_dx_as<uint16_t, 16>(dxp, dest, dz, wr, T, k, E, d, shared_row0, dx, s);
-    else unpermute_dx_as<uint16_t, 8>(dxp, dest, dz, wr, T, k, E, d, shared_row0, dx, s);
+    if (wide) unpermute_dx_as<uint16_t, 16>(dxp, dxp2, dest, dz, wr, T, k, E, d, shared_row0, dx, s);
+    else unpermute_dx_as<uint16_t, 8>(dxp, dxp2, dest, dz, wr, T, k, E, d, shared_row0, dx, s);
   } else {
-    if (wide) unpermute_dx_as<float, 16>(dxp, dest, dz, wr, T, k, E, d, shared_row0, dx, s);
-    else unpermute_dx_as<float, 8>(dxp, dest, dz, wr, T, k, E, d, shared_row0, dx, s);
+    if (wide) unpermute_dx_as<float, 16>(dxp, dxp2, dest, dz, wr, T, k, E, d, shared_row0, dx, s);
+    else unpermute_dx_as<float, 8>(dxp, dxp2, dest, dz, wr, T, k, E, d, shared_row0, dx, s);
   }
   return hipGetLastError();
 }

@@ -27,13 +27,18 @@ __device__ __forceinline__ TileCoord lookup_tile(const int32_t* tiles, int n_sin
 
 // Launch index -> (m_tile, n_tile), XCD-contiguous (see the file comment):
 // m fastest over a contiguous range of (n, m) pairs per XCD.
-__device__ __forceinline__ void xcd_tile(int n_logical, int max_tiles, int& m_tile, int& n_tile) {
-  const int L = blockIdx.x;
+// L: the launch index (a multiple of 8 apart from blockIdx.x when a launch runs
+// several copies of the tile grid, so the XCD is the same).
+__device__ __forceinline__ void xcd_tile_at(int L, int n_logical, int max_tiles, int& m_tile,
+                                            int& n_tile) {
   const int per = (n_logical + 7) >> 3;
   const int logical = (L & 7) * per + (L >> 3);
   if (logical >= n_logical) { m_tile = -1; n_tile = 0; return; }
   m_tile = logical % max_tiles;
   n_tile = logical / max_tiles;
+}
+__device__ __forceinline__ void xcd_tile(int n_logical, int max_tiles, int& m_tile, int& n_tile) {
+  xcd_tile_at(blockIdx.x, n_logical, max_tiles, m_tile, n_tile);
 }
 
 // Launch index -> (m_tile, n_tile) with the n tiles of one m tile in a row on
@@ -41,13 +46,16 @@ __device__ __forceinline__ void xcd_tile(int n_logical, int max_tiles, int& m_ti
 // workgroups that share its token rows share an L2 and stream neighbouring
 // panels of one weight matrix at the same time; the empty m tiles at the end of
 // the table fall evenly on all XCDs. Grid: 8 * ceil(max_tiles / 8) * n_tiles.
-__device__ __forceinline__ void xcd_tile_nfast(int max_tiles, int n_tiles, int& m_tile,
-                                               int& n_tile) {
-  const int L = blockIdx.x;
+__device__ __forceinline__ void xcd_tile_nfast_at(int L, int max_tiles, int n_tiles, int& m_tile,
+                                                  int& n_tile) {
   const int j = L >> 3;
   m_tile = (j / n_tiles) * 8 + (L & 7);
   n_tile = j % n_tiles;
   if (m_tile >= max_tiles) m_tile = -1;
+}
+__device__ __forceinline__ void xcd_tile_nfast(int max_tiles, int n_tiles, int& m_tile,
+                                               int& n_tile) {
+  xcd_tile_nfast_at(blockIdx.x, max_tiles, n_tiles, m_tile, n_tile);
 }
 
 // Launch index -> (m_tile, n_tile) in blocks of kTileBlockM m tiles: XCD x owns

@@ -14,9 +14,6 @@ hipError_t allow_large_lds(const void* kernel, size_t bytes);
 
 // ---- backward (backward.hip)
 hipError_t launch_single_group_offsets(int rows, int32_t* off, hipStream_t s);
-hipError_t launch_transpose_mat(const uint16_t* in, int B, int M, int N, uint16_t* out,
-                                int out_stride, int col0, long long out_batch, hipStream_t s,
-                                bool narrow = false);
 hipError_t launch_swiglu_fwd(const float* h1, const float* h3, int stride, int row0, int rows,
                              int n, uint16_t* act, hipStream_t s);
 hipError_t launch_swiglu_bwd(const float* u, const float* h1, const float* h3,
@@ -27,9 +24,9 @@ hipError_t launch_dy_rows(const float* dy, const int32_t* dest, const float* gat
 hipError_t launch_gate_bwd(const float* z, const int32_t* idx, const float* gates,
                            const int32_t* dest, const float* dg_row, const int32_t* counts, int T,
                            int E, int k, int gate_all, float alpha, float* dz, hipStream_t s);
-hipError_t launch_unpermute_dx(int dtype_bf16, const float* dxp, const int32_t* dest,
-                               const float* dz, const void* wr, int T, int k, int E, int d,
-                               int shared_row0, float* dx, hipStream_t s);
+hipError_t launch_unpermute_dx(int dtype_bf16, const float* dxp, const float* dxp2,
+                               const int32_t* dest, const float* dz, const void* wr, int T, int k,
+                               int E, int d, int shared_row0, float* dx, hipStream_t s);
 // dW_r = dz^T x in token chunks (part: chunks * E * d floats of scratch), then the
 // chunks summed in order.
 struct RouterWgradPlan {
@@ -203,7 +200,9 @@ constexpr size_t kStreamKPartBytes = static_cast<size_t>(kStreamKMaxWorkgroups) 
 // Data mode: y[y_row0 + row][n] = sum_k x[x_row0 + row(r)][k] * W_g[k][n] for the
 // rows of a 256-row tile table (row(r) = src[r] when src is set), with
 // W_g[k] = wa + g w_stride + k ldw for k < ksplit, wb + g w_stride + (k - ksplit) ldw
-// after; K and ksplit multiples of 64, N of 256.
+// after; K and ksplit multiples of 32, N of 256. With y2 set (0 < ksplit < K)
+// the sum is split at ksplit: y gets the k < ksplit part, y2 (same stride and
+// rows) the rest, each from its own half of a doubled grid.
 struct KmDataArgs {
   const uint16_t* x;
   int lda;
@@ -216,6 +215,7 @@ struct KmDataArgs {
   float* y;
   int y_stride, y_row0;
   int K, N;
+  float* y2 = nullptr;
 };
 hipError_t launch_gemm_kmajor_data(const GemmTileMap& map, const KmDataArgs& a, hipStream_t s);
 // Grouped K: out[g][m][n] = sum over rows r in [offsets[g], offsets[g+1]) of

@@ -160,29 +160,37 @@ struct Carver {
 // Workspace of moe_backward: every buffer of the recomputed forward and of the
 // backward, carved in this order (a null base only measures the size).
 struct BwdBufs {
-  float *z, *zpart, *gates, *h1, *h3, *row_gate, *dg_row, *dz, *u, *dxp, *wpart, *sk;
+  float *z, *zpart, *gates, *h1, *h3, *row_gate, *dg_row, *dz, *u, *dxp, *dxp2, *wpart;
   int32_t *idx, *dest, *src, *offsets, *counts, *kept, *ndrop, *soff, *tiles, *tiles256;
   int32_t *blk, *slot_base, *slot_keep;
-  uint16_t *act, *dyb, *dyp, *dH, *xp, *w2t, *w13t, *w2st, *w13st;
+  uint16_t *act, *dyb, *dyp, *dH, *xp;
   int max_tiles256;
-  bool tr_routed, tr_shared;   // weights transposed once per call (else read K-major)
+  bool split_dx;    // routed dX_perm in two halves (W1 part, W3 part), summed by unpermute_dx
 };
 
-// The activation products (u = dy W2, dX = dH [W1; W3]) either transpose the
-// weights once per call (5.5 TB/s read + write) and run the forward's
-// K-contiguous kernel, or read the weights K-major: the transposes cost 2 bytes
-// moved per weight byte, the K-major kernel runs these shapes at about 0.6 of
-// the K-contiguous one's rate, so the transposes pay off from about 650 rows per
-// expert (measured on the Mixtral and DeepSeek layer shapes).
-constexpr int kTransposeMinRows = 512;
+// The activation products (u = dy W2, dX = dH [W1; W3]) read the experts' weights
+// K-major (gemm_kmajor_w4_kernel, through the LDS transpose read). Measured
+// against transposing the weights in memory once per call (on a side stream,
+// beside the recomputed gate/up product) and running the forward's K-contiguous
+// kernel: Mixtral layer at 4096 tokens 10.45 -> 9.21 ms with 2.9 GB less
+// workspace; the shared expert of the DeepSeek layer u 140 + dX 321 us
+// transposed (plus three transposes of 0.2 ms each) against 186 + 231 us.
+
+// The routed dX_perm product (N = d) has few output tiles per CU when the groups
+// are long: at the Mixtral shape (4096 tokens) 35 x 16 tiles, 2.2 per CU, so its
+// last round of workgroups ran a fifth full. Below four tiles per CU the grid
+// runs twice, each copy over half of K (W1, then W3), into two buffers that
+// unpermute_dx adds.
+constexpr int kSplitDxTilesPerCU = 4;
 
 size_t backward_layout(const Shape& s, char* base, BwdBufs* b) {
   Carver cv{base};
   const size_t T = s.T, E = s.E, k = s.k, R = s.R, d = s.d, As = s.act_stride;
   const size_t rows = s.rows_total;
   b->max_tiles256 = moe::gemm_max_tiles(256, s.R, s.E);
-  b->tr_routed = s.R >= static_cast<long long>(kTransposeMinRows) * s.E;
-  b->tr_shared = s.nsh && s.T >= kTransposeMinRows;
+  const long long dx_tiles =
+      static_cast<long long>(s.BM == 256 ? s.max_tiles : b->max_tiles256) * (s.d / 256);
+  b->split_dx = dx_tiles < static_cast<long long>(kSplitDxTilesPerCU) * 256;
   const size_t dff = s.dff, dffs = s.dffs;
   b->z = cv.take<float>(T * E * 4);
   b->zpart = cv.take<float>(zpart_bytes(s));
@@ -212,13 +220,9 @@ size_t backward_layout(const Shape& s, char* base, BwdBufs* b) {
   b->u = cv.take<float>(rows * As * 4);
   b->dH = cv.take<uint16_t>(rows * 2 * As * 2);
   b->dxp = cv.take<float>(rows * d * 4);
+  b->dxp2 = cv.take<float>(b->split_dx ? R * d * 4 : 0);
   b->wpart = cv.take<float>(static_cast<size_t>(moe::router_wgrad_plan(s.T, s.E, s.d).chunks) *
                             E * d * 4);
-  b->w2t = cv.take<uint16_t>(b->tr_routed ? E * dff * d * 2 : 0);
-  b->w13t = cv.take<uint16_t>(b->tr_routed ? E * d * 2 * dff * 2 : 0);
-  b->w2st = cv.take<uint16_t>(b->tr_shared ? dffs * d * 2 : 0);
-  b->w13st = cv.take<uint16_t>(b->tr_shared ? d * 2 * dffs * 2 : 0);
-  b->sk = cv.take<float>(b->tr_routed || b->tr_shared ? moe::kStreamKPartBytes : 0);
   return static_cast<size_t>(cv.p - base);
 }
 
@@ -656,14 +660,6 @@ moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t
   return MOE_OK;
 }
 
-// A second stream per device for the part of a call that reads only the call's
-// inputs (the backward's weight transposes): it forks from the caller's stream
-// and joins back into it through events, so that part runs beside the caller
-// stream's kernels (they leave LDS and vector registers for a transpose
-// workgroup on every CU). Default priority, non-blocking, created on first use.
-namespace {
-}  // namespace
-
 moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_router,
                         const float* sel_bias, const void* w1, const void* w3, const void* w2,
                         const void* ws1, const void* ws3, const void* ws2, const float* dy,
@@ -705,53 +701,13 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   MOE_HIP(moe::launch_index(b.idx, T, k, E, s.C, b.blk, b.slot_base, b.slot_keep, b.offsets, b.dest,
                             b.src, load, s.BM, s.max_tiles, 1, b.tiles, strm),
           "index");
-  // ---- weight transposes (experts of >= kTransposeMinRows rows): on the side
-  // stream, beside the recomputed gate/up product; joined before the first
-  // product that reads them. Forked after the routing and index kernels: a
-  // transpose workgroup beside the single-workgroup scan of the index slowed it
-  // from 5 to 205 us.
-  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
-  SideStream* side = nullptr;
-  if (b.tr_routed || b.tr_shared) {
-    side_lock.lock();
-    side = side_stream();
-    hipStream_t ts = strm;
-    if (side != nullptr) {
-      MOE_HIP(hipEventRecord(side->fork, strm), "fork");
-      MOE_HIP(hipStreamWaitEvent(side->s, side->fork, 0), "fork");
-      ts = side->s;
-    }
-    const bool narrow = side != nullptr;
-    if (b.tr_routed) {
-      MOE_HIP(moe::launch_transpose_mat(u16(w2), E, d, dff, b.w2t, d, 0,
-                                        static_cast<long long>(dff) * d, ts, narrow),
-              "transpose w2");
-      MOE_HIP(moe::launch_transpose_mat(u16(w1), E, dff, d, b.w13t, 2 * dff, 0,
-                                        static_cast<long long>(d) * 2 * dff, ts, narrow),
-              "transpose w1");
-      MOE_HIP(moe::launch_transpose_mat(u16(w3), E, dff, d, b.w13t, 2 * dff, dff,
-                                        static_cast<long long>(d) * 2 * dff, ts, narrow),
-              "transpose w3");
-    }
-    if (b.tr_shared) {
-      MOE_HIP(moe::launch_transpose_mat(u16(ws2), 1, d, dffs, b.w2st, d, 0, 0, ts, narrow),
-              "transpose ws2");
-      MOE_HIP(moe::launch_transpose_mat(u16(ws1), 1, dffs, d, b.w13st, 2 * dffs, 0, 0, ts, narrow),
-              "transpose ws1");
-      MOE_HIP(moe::launch_transpose_mat(u16(ws3), 1, dffs, d, b.w13st, 2 * dffs, dffs, 0, ts,
-                                        narrow),
-              "transpose ws3");
-    }
-    if (side != nullptr) MOE_HIP(hipEventRecord(side->join, side->s), "join");
-  }
-
   const moe::GemmTileMap map{b.tiles, s.max_tiles, 0, moe::gemm_n_fast(s.BM, s.R, E),
                             avg_group_rows(s)};
   const moe::GemmTileMap map1{nullptr, 0, T};
   const int bm1 = moe::gemm_tile_rows(1, T, 1, s.n256);
   // the K-major products run 256-row tiles
   moe::GemmTileMap map256 = map;
-  if (s.BM != 256 && !b.tr_routed) {
+  if (s.BM != 256) {
     MOE_HIP(moe::launch_tile_map(b.offsets, E, 256, b.max_tiles256, 1, b.tiles256, strm),
             "tile_map 256");
     map256 = moe::GemmTileMap{b.tiles256, b.max_tiles256, 0};
@@ -788,15 +744,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   // <act_r, u_r>; then the logits' gradient.
   MOE_HIP(moe::launch_dy_rows(dy, b.dest, b.gates, T, k, d, b.dyb, b.dyp, b.row_gate, strm),
           "dy_rows");
-  if (side != nullptr) {
-    MOE_HIP(hipStreamWaitEvent(strm, side->join, 0), "join");
-    side_lock.unlock();
-  }
-  if (b.tr_routed) {
-    moe::DownArgs a{b.dyb, d, 0, b.w2t, static_cast<long long>(dff) * d, b.u, 0, d, dff, b.src, As};
-    a.sk_part = b.sk;
-    MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "u");
-  } else {
+  {
     moe::KmDataArgs a{b.dyb, d, b.src, 0, u16(w2), nullptr, d, dff,
                       static_cast<long long>(d) * dff, b.u, As, 0, d, dff};
     MOE_HIP(moe::launch_gemm_kmajor_data(map256, a, strm), "u");
@@ -805,11 +753,7 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
                                  b.dg_row, strm),
           "swiglu_bwd");
   if (s.nsh) {
-    if (b.tr_shared) {
-      moe::DownArgs a{b.dyb, d, 0, b.w2st, 0, b.u, R, d, dffs, nullptr, As};
-      a.sk_part = b.sk;
-      MOE_HIP(moe::launch_gemm_down_bf16(map1, a, bm1, strm), "u shared");
-    } else {
+    {
       moe::KmDataArgs a{b.dyb, d, nullptr, 0, u16(ws2), nullptr, d, dffs, 0, b.u, As, R, d, dffs};
       MOE_HIP(moe::launch_gemm_kmajor_data(map1, a, strm), "u shared");
     }
@@ -822,28 +766,19 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
           "gate_bwd");
 
   // ---- gate/up: dX_perm = [dh1 dh3] [W1; W3], K = 2 d_ff over W1 then W3 (K-major)
-  if (b.tr_routed) {
-    moe::DownArgs a{b.dH, 2 * As, 0, b.w13t, static_cast<long long>(d) * 2 * dff, b.dxp, 0,
-                    2 * dff, d};
-    a.sk_part = b.sk;
-    MOE_HIP(moe::launch_gemm_down_bf16(map, a, s.BM, strm), "dx_perm");
-  } else {
+  {
     moe::KmDataArgs a{b.dH, 2 * As, nullptr, 0, u16(w1), u16(w3), dff, d,
                       static_cast<long long>(dff) * d, b.dxp, d, 0, 2 * dff, d};
+    if (b.split_dx) a.y2 = b.dxp2;
     MOE_HIP(moe::launch_gemm_kmajor_data(map256, a, strm), "dx_perm");
   }
   if (s.nsh) {
-    if (b.tr_shared) {
-      moe::DownArgs a{b.dH, 2 * As, R, b.w13st, 0, b.dxp, R, 2 * dffs, d};
-      a.sk_part = b.sk;
-      MOE_HIP(moe::launch_gemm_down_bf16(map1, a, bm1, strm), "dx_perm shared");
-    } else {
-      moe::KmDataArgs a{b.dH, 2 * As, nullptr, R, u16(ws1), u16(ws3), dffs, d, 0, b.dxp, d, R,
-                        2 * dffs, d};
-      MOE_HIP(moe::launch_gemm_kmajor_data(map1, a, strm), "dx_perm shared");
-    }
+    moe::KmDataArgs a{b.dH, 2 * As, nullptr, R, u16(ws1), u16(ws3), dffs, d, 0, b.dxp, d, R,
+                      2 * dffs, d};
+    MOE_HIP(moe::launch_gemm_kmajor_data(map1, a, strm), "dx_perm shared");
   }
-  MOE_HIP(moe::launch_unpermute_dx(1, b.dxp, b.dest, b.dz, w_router, T, k, E, d, sh_row0, dx, strm),
+  MOE_HIP(moe::launch_unpermute_dx(1, b.dxp, b.split_dx ? b.dxp2 : nullptr, b.dest, b.dz,
+                                   w_router, T, k, E, d, sh_row0, dx, strm),
           "unpermute_dx");
   MOE_HIP(moe::launch_router_wgrad(1, b.dz, x, T, E, d, b.wpart, dw_router, strm), "router_wgrad");
 

@@ -641,9 +641,9 @@ _BWD_CASES = {
     "decode": (dict(d=256, E=8, k=2, d_ff=256), 8),
     # a shared expert wider than the routed ones: rows of act, h and u at act_stride
     "shared_wide": (dict(d=256, E=8, k=2, d_ff=256, n_shared=1, d_ff_shared=512), 160),
-    # 512 tokens: the shared expert's weights are transposed once, the routed ones
-    # (128 rows per expert) read K-major
-    "shared_transposed": (dict(d=256, E=8, k=2, d_ff=256, n_shared=1, d_ff_shared=512), 512),
+    # 512 tokens: the shared expert's dense group spans two 256-row tiles of the
+    # K-major products, the routed groups (128 rows each) one ragged tile each
+    "shared_512_rows": (dict(d=256, E=8, k=2, d_ff=256, n_shared=1, d_ff_shared=512), 512),
     # E = 1, k = 1: a dense SwiGLU layer; the selected gate is identically 1
     "dense_e1": (dict(d=256, E=1, k=1, d_ff=256), 96),
     # fine-grained: > 32 experts (wide router-gradient and dx kernels), 32-row tiles
