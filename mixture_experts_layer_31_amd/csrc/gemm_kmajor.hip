@@ -62,6 +62,33 @@ __device__ __forceinline__ int km_frag_off(int lane, int col) {
   return kr * kKmRowBytes + ((chunk ^ (4 * (s >> 2))) << 4) + 8 * (s & 1);
 }
 
+// Grouped K, long groups: launch index -> (m_tile, n_tile) in blocks of
+// kGkBlockM x kGkBlockN tiles of one group, one block per XCD at a time (block b
+// on XCD b % 8), so the 32 workgroups an XCD holds share their A and B K-slices in
+// its L2 (4 A and 8 B slices per K-step) instead of 32 A slices and one B slice in
+// m-fastest order. Workgroups past a partial block's edge return.
+constexpr int kGkBlockM = 4, kGkBlockN = 8;   // kGkBlockM * kGkBlockN workgroups per XCD
+__host__ __device__ constexpr long long gk_blocks(int G, int n_single, int n_tiles) {
+  return static_cast<long long>(G) * ((n_single + kGkBlockM - 1) / kGkBlockM) *
+         ((n_tiles + kGkBlockN - 1) / kGkBlockN);
+}
+__device__ __forceinline__ void gk_tile_blocked(int max_tiles, int n_single, int n_tiles,
+                                                int& m_tile, int& n_tile) {
+  const int L = blockIdx.x, j = L >> 3;
+  constexpr int per = kGkBlockM * kGkBlockN;
+  const int b = (j / per) * 8 + (L & 7), r = j % per;
+  const int mb = (n_single + kGkBlockM - 1) / kGkBlockM;
+  const int nb = (n_tiles + kGkBlockN - 1) / kGkBlockN;
+  const int g = b / (mb * nb), q = b % (mb * nb);
+  const int mi = (q % mb) * kGkBlockM + r % kGkBlockM;
+  const int ni = (q / mb) * kGkBlockN + r / kGkBlockM;
+  m_tile = -1;
+  n_tile = 0;
+  if (mi >= n_single || ni >= n_tiles || g * n_single >= max_tiles) return;
+  m_tile = g * n_single + mi;
+  n_tile = ni;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- the kernel
@@ -139,6 +166,7 @@ gemm_kmajor_w4_kernel(const int32_t* __restrict__ tiles, int max_tiles, int n_si
   }
   int m_tile, n_tile;
   if constexpr (NF) xcd_tile_nfast_at(L, max_tiles, n_logical / max_tiles, m_tile, n_tile);
+  else if constexpr (GK) gk_tile_blocked(max_tiles, n_single, n_logical / max_tiles, m_tile, n_tile);
   else xcd_tile_at(L, n_logical, max_tiles, m_tile, n_tile);
   if (m_tile < 0) return;
   const int n0 = n_tile * BN;
@@ -471,8 +499,9 @@ hipError_t launch_gemm_kmajor_groupk(const int32_t* offsets, int G, const uint16
   const int m_tiles = G * n_single;
   const long long n_logical = static_cast<long long>(m_tiles) * (N2 / kKmBN);
   if (n_logical == 0) return hipSuccess;
-  const long long grid = rows_stream ? 8LL * ((m_tiles + 7) / 8) * (N2 / kKmBN)
-                                     : ((n_logical + 7) / 8) * 8;
+  const long long grid = rows_stream
+                             ? 8LL * ((m_tiles + 7) / 8) * (N2 / kKmBN)
+                             : (gk_blocks(G, n_single, N2 / kKmBN) + 7) / 8 * 8 * kGkBlockM * kGkBlockN;
   kern<<<dim3(static_cast<unsigned>(grid)), block, lds, s>>>(
       offsets, m_tiles, n_single, static_cast<int>(n_logical), A, lda, nullptr, 0, B, nullptr, 0,
       ldb, static_cast<long long>(N1) * N2, out, N2, 0, 0, nullptr);
