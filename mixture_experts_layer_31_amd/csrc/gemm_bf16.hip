@@ -493,7 +493,7 @@ __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_ld
   if constexpr (!SK) {
     int m_tile, n_tile;
     if constexpr (NF) xcd_tile_nfast(max_tiles, N / BN, m_tile, n_tile);
-    else if (tile_order_blocked(BM, N / BN)) xcd_tile_blocked(max_tiles, N / BN, m_tile, n_tile);
+    else if (tile_order_blocked(BM, N / BN)) xcd_tile_blocked(tiles, max_tiles, N / BN, m_tile, n_tile);
     else xcd_tile(n_logical, max_tiles, m_tile, n_tile);
     if (m_tile < 0) return;
     run_tile(m_tile, n_tile, 0, nk_all, nullptr);
@@ -600,7 +600,7 @@ gemm_bf16_w4_kernel(const int32_t* __restrict__ tiles, int max_tiles, int n_sing
 
   int m_tile, n_tile;
   if constexpr (NF) xcd_tile_nfast(max_tiles, N / BN, m_tile, n_tile);
-  else if (tile_order_blocked(BM, N / BN)) xcd_tile_blocked(max_tiles, N / BN, m_tile, n_tile);
+  else if (tile_order_blocked(BM, N / BN)) xcd_tile_blocked(tiles, max_tiles, N / BN, m_tile, n_tile);
   else xcd_tile(n_logical, max_tiles, m_tile, n_tile);
   if (m_tile < 0) return;
   const TileCoord tc = lookup_tile(tiles, n_single, BM, m_tile);
@@ -1074,7 +1074,8 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
   const int start = block_scan_1024(nt, part, &total) - nt;
   const int w = tile_group_weights(e, E, ep);
   for (int i = 0; i < nt && start + i < max_tiles; ++i)
-    tiles[start + i] = make_int4(w, lo + i * BM, min(BM, n - i * BM), 0);
+    tiles[start + i] =
+        make_int4(w, lo + i * BM, min(BM, n - i * BM), tile_block_word(start, nt, i));
   for (int i = total + e; i < max_tiles; i += 1024) tiles[i] = make_int4(0, 0, 0, 0);
 }
 

@@ -58,18 +58,22 @@ __device__ __forceinline__ void xcd_tile_nfast(int max_tiles, int n_tiles, int& 
   xcd_tile_nfast_at(blockIdx.x, max_tiles, n_tiles, m_tile, n_tile);
 }
 
-// Launch index -> (m_tile, n_tile) in blocks of kTileBlockM m tiles: XCD x owns
-// the n tiles [x * n_tiles / 8, (x + 1) * n_tiles / 8) and walks one block of m
-// tiles over all of them (m fastest), then the next block. Each weight panel is
-// then read by one XCD only, and the workgroups in flight on an XCD share their
-// token rows (the block's m tiles) as well as their weight panels (a few n
-// tiles) in its L2; in m-fastest order over all m tiles they would share only
-// the weight panels and read every token row again for every n tile.
-// Blocks of two m tiles: the 32 workgroups of an XCD then hold one block of 2 m x
-// 14 n tiles and the start of the next (gate/up of the Mixtral shape at 4096
-// tokens: 112 n tiles, four 256-row tiles per expert), mostly within one expert. Measured there against blocks of eight (two experts' weight panels in
-// flight per n tile): gate/up kernel L2-to-fabric reads 8.6 -> 6.3 GB, layer
-// 3.17 -> 3.11 ms; blocks of four read 6.0 GB but ran no faster.
+// Launch index -> (m_tile, n_tile) in blocks of m tiles: XCD x owns the n tiles
+// [x * n_tiles / 8, (x + 1) * n_tiles / 8) and walks one block of m tiles over all
+// of them (m fastest), then the next block. Each weight panel is then read by one
+// XCD only, and the workgroups in flight on an XCD share their token rows (the
+// block's m tiles) as well as their weight panels (a few n tiles) in its L2; in
+// m-fastest order over all m tiles they would share only the weight panels and
+// read every token row again for every n tile.
+// With a tile table the blocks are the table's order blocks (tile_block_word):
+// all tiles of a group of up to eight, so the workgroups in flight on an XCD work
+// on one expert's weights at a time. Slot j of XCD x lies in the block of tile
+// j / nn (nn: the XCD's n tiles), which spans slots [nn * start, nn * (start +
+// tiles)), so the grid is the same as for fixed blocks and no slot is wasted.
+// Measured on the gate/up product of the Mixtral shape at 4096 tokens (groups of
+// four or five 256-row tiles): 1.98 -> 1.90 ms against fixed blocks of two m
+// tiles, which straddle the experts (fixed blocks of five: 1.97 ms). Without a
+// table (one dense group), fixed blocks of kTileBlockM m tiles.
 // Grid: blocked_grid(max_tiles, n_tiles).
 #ifndef MOE_TILE_BLOCK_M
 #define MOE_TILE_BLOCK_M 2
@@ -81,14 +85,25 @@ __host__ __device__ constexpr bool tile_order_blocked(int BM, int n_tiles) {
 __host__ __device__ constexpr long long blocked_grid(int max_tiles, int n_tiles) {
   return 8LL * ((max_tiles + kTileBlockM - 1) / kTileBlockM) * kTileBlockM * ((n_tiles + 7) / 8);
 }
-__device__ __forceinline__ void xcd_tile_blocked(int max_tiles, int n_tiles, int& m_tile,
-                                                 int& n_tile) {
+__device__ __forceinline__ void xcd_tile_blocked(const int32_t* tiles, int max_tiles, int n_tiles,
+                                                 int& m_tile, int& n_tile) {
   const int L = blockIdx.x, x = L & 7, j = L >> 3;
   const int n_lo = x * n_tiles / 8;
   const int nn = (x + 1) * n_tiles / 8 - n_lo;
   m_tile = -1;
   n_tile = 0;
   if (nn <= 0) return;
+  if (tiles != nullptr) {
+    const int t = j / nn;
+    if (t >= max_tiles) return;
+    const int4 e = reinterpret_cast<const int4*>(tiles)[t];
+    if (e.z <= 0) return;   // past the last real tile
+    const int s0 = e.w >> 8, c = e.w & 255;
+    const int r = j - nn * s0;
+    m_tile = s0 + r % c;
+    n_tile = n_lo + r / c;
+    return;
+  }
   const int per = kTileBlockM * nn;   // workgroups of one block on this XCD
   const int b = j / per, r = j - b * per;
   const int m = b * kTileBlockM + r % kTileBlockM;

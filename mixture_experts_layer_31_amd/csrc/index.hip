@@ -367,7 +367,8 @@ __device__ __forceinline__ void index_single_body(
   const int start = block_scan_1024(nt, part, &total) - nt;
   const int w = tile_group_weights(e, E, ep);
   for (int i = 0; i < nt && start + i < max_tiles; ++i)
-    tiles[start + i] = make_int4(w, lo + i * BM, min(BM, n - i * BM), 0);
+    tiles[start + i] =
+        make_int4(w, lo + i * BM, min(BM, n - i * BM), tile_block_word(start, nt, i));
   for (int i = total + tid; i < max_tiles; i += 1024) tiles[i] = make_int4(0, 0, 0, 0);
 }
 

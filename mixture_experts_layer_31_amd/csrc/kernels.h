@@ -110,6 +110,19 @@ hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capac
 hipError_t launch_ep_group_ids(const int32_t* idx, int T, int k, int E, int n, int32_t* gid,
                                hipStream_t s);
 hipError_t launch_ep_traffic(const int32_t* offsets, int n, int E, int32_t* rows, hipStream_t s);
+// Tile table entries are int4 (weights group, first row, rows, order block). The
+// fourth field packs the tile's block of the blocked launch order (first tile of
+// the block << 8 | tiles in it): a group of nt tiles forms ceil(nt / 8) blocks of
+// ceil(nt / blocks) consecutive tiles (the last one shorter), so a group of up to
+// eight tiles is one block and is walked as a whole.
+constexpr int kTileOrderBlock = 8;
+__host__ __device__ inline int tile_block_word(int start, int nt, int i) {
+  const int nb = (nt + kTileOrderBlock - 1) / kTileOrderBlock;
+  const int c = (nt + nb - 1) / nb;
+  const int lo = (i / c) * c;
+  return ((start + lo) << 8) | (nt - lo < c ? nt - lo : c);
+}
+
 // Weights index of row group g of G groups: g itself, or with ep > 1 ranks the
 // expert of group (r*ep + s)*El + l, namely r*El + l with El = G / ep^2.
 __host__ __device__ inline int tile_group_weights(int g, int G, int ep) {

@@ -191,7 +191,6 @@ size_t backward_layout(const Shape& s, char* base, BwdBufs* b) {
   const long long dx_tiles =
       static_cast<long long>(s.BM == 256 ? s.max_tiles : b->max_tiles256) * (s.d / 256);
   b->split_dx = dx_tiles < static_cast<long long>(kSplitDxTilesPerCU) * 256;
-  const size_t dff = s.dff, dffs = s.dffs;
   b->z = cv.take<float>(T * E * 4);
   b->zpart = cv.take<float>(zpart_bytes(s));
   b->idx = cv.take<int32_t>(T * k * 4);
