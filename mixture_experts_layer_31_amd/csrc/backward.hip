@@ -193,7 +193,8 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
 
 // dx_t = sum_j dXp[dest[t,j]] (slot order) + dXp[shared_row0 + t]
 // + sum_e dz[t,e] W_r[e] (expert order), fp32. With dXp2 set, a routed row's
-// dXp is the sum of two halves, dXp[r] + dXp2[r] (the W1 and W3 parts). A workgroup takes TT tokens and
+// dXp is the sum of two halves, dXp[r] + dXp2[r] (the W1 and W3 parts). With W_r
+// null, dx holds dz W_r on entry (an MFMA product) and is read as that term. A workgroup takes TT tokens and
 // 1024 columns (4 per thread), so each W_r row segment is loaded once for TT
 // tokens; the TT tokens' dz rows sit in LDS. grid (d / 1024, ceil(T / TT)).
 template <typename Tw, int TT>
@@ -207,7 +208,8 @@ __global__ __launch_bounds__(256) void unpermute_dx_kernel(const float* __restri
   extern __shared__ float sdz[];   // [TT][E]
   const int t0 = blockIdx.y * TT;
   const int nt = min(TT, T - t0);
-  for (int q = threadIdx.x; q < nt * E; q += 256) sdz[q] = dz[static_cast<size_t>(t0) * E + q];
+  if (wr != nullptr)
+    for (int q = threadIdx.x; q < nt * E; q += 256) sdz[q] = dz[static_cast<size_t>(t0) * E + q];
   __syncthreads();
   const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= d) return;
@@ -235,7 +237,17 @@ __global__ __launch_bounds__(256) void unpermute_dx_kernel(const float* __restri
       }
     }
   }
-  for (int e = 0; e < E; ++e) {
+  if (wr == nullptr) {
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      if (tt < nt) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(dx + static_cast<size_t>(t0 + tt) * d + i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ra[tt][q] = v[q];
+      }
+    }
+  }
+  for (int e = 0; wr != nullptr && e < E; ++e) {
     float w[4];
     Elt<Tw>::load4(wr + static_cast<size_t>(e) * d + i, w);
 #pragma unroll
@@ -312,6 +324,41 @@ __global__ __launch_bounds__(256) void router_wgrad_sum_kernel(const float* __re
   dwr[i] = acc;
 }
 
+// The router's gradients as MFMA products (wide routers, E a multiple of 128):
+// dz (fp32 [T][E]) in two bf16 halves, dzs[t][e] = hi = bf16(dz) and
+// dzs[t][E + e] = lo = bf16(dz - hi) (dz - hi is exact in fp32), so hi + lo is
+// dz to within 2^-18 of |dz|; then dz W_r = [hi | lo] [W_r; W_r] and
+// dz^T x = hi^T x + lo^T x with bf16 operands and fp32 sums. The same launch
+// writes the token chunks of dW_r, chunk_off[c] = c T / C for c = 0..C.
+__global__ __launch_bounds__(256) void dz_split_kernel(const float* __restrict__ dz, int T, int E,
+                                                       int C, uint16_t* __restrict__ dzs,
+                                                       int32_t* __restrict__ chunk_off) {
+  const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i <= C) chunk_off[i] = static_cast<int32_t>(static_cast<long long>(i) * T / C);
+  if (i >= static_cast<long long>(T) * E) return;
+  const long long t = i / E, e = i - t * E;
+  const float v = dz[i];
+  const uint16_t hi = f32_to_bf16(v);
+  dzs[t * 2 * E + e] = hi;
+  dzs[t * 2 * E + E + e] = f32_to_bf16(v - bf16_to_f32(hi));
+}
+
+// dW_r[e][i] = sum over the chunks c in order of part[c][e][i] + part[c][E + e][i]
+// (the hi and lo products of chunk c; part is [C][2E][d]).
+__global__ __launch_bounds__(256) void router_wgrad_pairs_kernel(const float* __restrict__ part,
+                                                                 int C, int E, int d,
+                                                                 float* __restrict__ dwr) {
+  const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  const long long n = static_cast<long long>(E) * d;
+  if (i >= n) return;
+  float acc = 0.f;
+  for (int c = 0; c < C; ++c) {
+    const float* pc = part + static_cast<size_t>(c) * 2 * n;
+    acc += pc[i] + pc[n + i];
+  }
+  dwr[i] = acc;
+}
+
 __global__ void single_group_offsets_kernel(int rows, int32_t* __restrict__ off) {
   if (threadIdx.x == 0) { off[0] = 0; off[1] = rows; }
 }
@@ -319,6 +366,21 @@ __global__ void single_group_offsets_kernel(int rows, int32_t* __restrict__ off)
 // ---------------------------------------------------------------- launchers
 
 static unsigned blocks_for(long long n) { return static_cast<unsigned>((n + 255) / 256); }
+
+hipError_t launch_dz_split(const float* dz, int T, int E, int C, uint16_t* dzs, int32_t* chunk_off,
+                           hipStream_t s) {
+  const long long n = static_cast<long long>(T) * E;
+  dz_split_kernel<<<dim3(blocks_for(n > C ? n : C + 1)), dim3(256), 0, s>>>(dz, T, E, C, dzs,
+                                                                          chunk_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_wgrad_pairs(const float* part, int C, int E, int d, float* dwr,
+                                     hipStream_t s) {
+  const long long n = static_cast<long long>(E) * d;
+  router_wgrad_pairs_kernel<<<dim3(blocks_for(n)), dim3(256), 0, s>>>(part, C, E, d, dwr);
+  return hipGetLastError();
+}
 
 hipError_t launch_single_group_offsets(int rows, int32_t* off, hipStream_t s) {
   single_group_offsets_kernel<<<dim3(1), dim3(64), 0, s>>>(rows, off);

@@ -14,6 +14,16 @@ hipError_t allow_large_lds(const void* kernel, size_t bytes);
 
 // ---- backward (backward.hip)
 hipError_t launch_single_group_offsets(int rows, int32_t* off, hipStream_t s);
+// Router gradients as MFMA products (E a multiple of 128): dz split into bf16
+// halves dzs [T][2E] (hi | lo) and the C + 1 token-chunk offsets c T / C; then,
+// after the grouped-K product part [C][2E][d] = per chunk [hi | lo]^T x, dW_r as
+// the chunk-ordered sum of its hi and lo rows.
+constexpr int kRouterMfmaExperts = 128;
+inline bool router_grad_mfma(int E) { return E >= kRouterMfmaExperts && E % kRouterMfmaExperts == 0; }
+hipError_t launch_dz_split(const float* dz, int T, int E, int C, uint16_t* dzs, int32_t* chunk_off,
+                           hipStream_t s);
+hipError_t launch_router_wgrad_pairs(const float* part, int C, int E, int d, float* dwr,
+                                     hipStream_t s);
 hipError_t launch_swiglu_fwd(const float* h1, const float* h3, int stride, int row0, int rows,
                              int n, uint16_t* act, hipStream_t s);
 hipError_t launch_swiglu_bwd(const float* u, const float* h1, const float* h3,

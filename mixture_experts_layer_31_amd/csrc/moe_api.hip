@@ -160,11 +160,12 @@ struct Carver {
 // Workspace of moe_backward: every buffer of the recomputed forward and of the
 // backward, carved in this order (a null base only measures the size).
 struct BwdBufs {
-  float *z, *zpart, *gates, *h1, *h3, *row_gate, *dg_row, *dz, *u, *dxp, *dxp2, *wpart;
+  float *z, *zpart, *gates, *h1, *h3, *row_gate, *dg_row, *dz, *u, *dxp, *dxp2, *wpart, *rpart;
   int32_t *idx, *dest, *src, *offsets, *counts, *kept, *ndrop, *soff, *tiles, *tiles256;
-  int32_t *blk, *slot_base, *slot_keep;
-  uint16_t *act, *dyb, *dyp, *dH, *xp;
+  int32_t *blk, *slot_base, *slot_keep, *chunk_off;
+  uint16_t *act, *dyb, *dyp, *dH, *xp, *dzs;
   int max_tiles256;
+  int rchunks;      // > 0: the router's gradients as MFMA products over this many token chunks
   bool split_dx;    // routed dX_perm in two halves (W1 part, W3 part), summed by unpermute_dx
 };
 
@@ -220,7 +221,20 @@ size_t backward_layout(const Shape& s, char* base, BwdBufs* b) {
   b->dH = cv.take<uint16_t>(rows * 2 * As * 2);
   b->dxp = cv.take<float>(rows * d * 4);
   b->dxp2 = cv.take<float>(b->split_dx ? R * d * 4 : 0);
-  b->wpart = cv.take<float>(static_cast<size_t>(moe::router_wgrad_plan(s.T, s.E, s.d).chunks) *
+  // wide routers: dz W_r and dz^T x on the MFMA kernels, the token chunks of dW_r
+  // sized so the grouped-K product has about one tile per CU
+  b->rchunks = 0;
+  if (moe::router_grad_mfma(s.E)) {
+    const int per_chunk = (2 * s.E / 256) * (s.d / 256);
+    const int want = per_chunk < 256 ? 256 / per_chunk : 1;
+    const int most = (s.T + 255) / 256;
+    b->rchunks = want < most ? want : most;
+  }
+  b->dzs = cv.take<uint16_t>(b->rchunks ? T * 2 * E * 2 : 0);
+  b->chunk_off = cv.take<int32_t>(b->rchunks ? (static_cast<size_t>(b->rchunks) + 1) * 4 : 0);
+  b->rpart = cv.take<float>(static_cast<size_t>(b->rchunks) * 2 * E * d * 4);
+  b->wpart = cv.take<float>(b->rchunks ? 0 :
+                            static_cast<size_t>(moe::router_wgrad_plan(s.T, s.E, s.d).chunks) *
                             E * d * 4);
   return static_cast<size_t>(cv.p - base);
 }
@@ -763,6 +777,8 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
   MOE_HIP(moe::launch_gate_bwd(b.z, b.idx, b.gates, b.dest, b.dg_row, b.counts, T, E, k,
                                s.gate_all, cfg->aux_alpha, b.dz, strm),
           "gate_bwd");
+  if (b.rchunks > 0)
+    MOE_HIP(moe::launch_dz_split(b.dz, T, E, b.rchunks, b.dzs, b.chunk_off, strm), "dz_split");
 
   // ---- gate/up: dX_perm = [dh1 dh3] [W1; W3], K = 2 d_ff over W1 then W3 (K-major)
   {
@@ -776,10 +792,26 @@ moe_status moe_backward(const moe_config* cfg, const void* x, const void* w_rout
                       2 * dffs, d};
     MOE_HIP(moe::launch_gemm_kmajor_data(map1, a, strm), "dx_perm shared");
   }
+  // dx = the rows' dX_perm in slot order (+ shared) + dz W_r; a wide router's
+  // dz W_r = [hi | lo] [W_r; W_r] is written into dx first and read back there
+  if (b.rchunks > 0) {
+    moe::KmDataArgs a{b.dzs, 2 * E, nullptr, 0, u16(w_router), u16(w_router), E, d, 0, dx, d, 0,
+                      2 * E, d};
+    MOE_HIP(moe::launch_gemm_kmajor_data(map1, a, strm), "dz W_r");
+  }
   MOE_HIP(moe::launch_unpermute_dx(1, b.dxp, b.split_dx ? b.dxp2 : nullptr, b.dest, b.dz,
-                                   w_router, T, k, E, d, sh_row0, dx, strm),
+                                   b.rchunks > 0 ? nullptr : w_router, T, k, E, d, sh_row0, dx,
+                                   strm),
           "unpermute_dx");
-  MOE_HIP(moe::launch_router_wgrad(1, b.dz, x, T, E, d, b.wpart, dw_router, strm), "router_wgrad");
+  if (b.rchunks > 0) {
+    MOE_HIP(moe::launch_gemm_kmajor_groupk(b.chunk_off, b.rchunks, b.dzs, 2 * E, 2 * E, u16(x), d,
+                                           d, b.rpart, false, strm),
+            "dz^T x");
+    MOE_HIP(moe::launch_router_wgrad_pairs(b.rpart, b.rchunks, E, d, dw_router, strm), "dW_r");
+  } else {
+    MOE_HIP(moe::launch_router_wgrad(1, b.dz, x, T, E, d, b.wpart, dw_router, strm),
+            "router_wgrad");
+  }
 
   // ---- weight gradients over each expert's rows: dW2 = dY_perm^T act,
   // dW1 = dH1^T X_perm, dW3 = dH3^T X_perm (both operands K-major)

@@ -652,6 +652,10 @@ _BWD_CASES = {
                           bias_range=0.1), 256),
     # 32 groups of ~128 rows: the 256-row gate/up recompute in n-fastest tile order
     "weight_streaming": (dict(d=256, E=32, k=2, d_ff=256), 2048),
+    # a router of 128 experts: its gradients as MFMA products (dz split into bf16
+    # halves), dW_r over two token chunks
+    "wide_router": (dict(d=256, E=128, k=4, d_ff=256, n_shared=1, d_ff_shared=256,
+                         bias_range=0.1, aux_alpha=0.01), 384),
 }
 
 
