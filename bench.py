@@ -22,9 +22,11 @@ prefill at 512, DeepSeek-shaped at 1, 64 and 4096 tokens, the skewed 16384-token
 load and the Switch layer at three capacity factors, with its balance loss), each
 with tokens/s, TFLOP/s, GB/s and the fractions of both rooflines; and "coverage":
 the expert coverage of decode batches under the GPU's routing against 1 - 0.75^B.
+The headline workload's moe_backward (the layer's gradients on the same batch) is
+timed too and reported as "backward" (--no-backward leaves it out).
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--ep N]
-                  [--backward] [--no-flush] [--no-calibration] [--configs A,B,...]
+                  [--no-backward] [--no-flush] [--no-calibration] [--configs A,B,...]
   python bench.py --calibrate-copy     # plain 1 GiB copies, for counter scaling
 """
 from __future__ import annotations
@@ -84,7 +86,9 @@ def parse():
                     help="HBM-bound workloads: time steps back to back (warm MALL/L2)")
     ap.add_argument("--no-calibration", action="store_true")
     ap.add_argument("--backward", action="store_true",
-                    help="also time moe_backward (gradients of the layer) on the same batch")
+                    help="time moe_backward on the same batch (the default)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="leave out the timing of moe_backward")
     ap.add_argument("--configs", default=",".join(CONFIG_SWEEP),
                     help="comma-separated workloads timed after the headline one (their "
                          "fused steps, from cold caches where HBM-bound); empty for none")
@@ -378,7 +382,10 @@ def main():
                      "rows_per_rank_max": int(rows.sum(axis=0).max())}
 
     bwd_report = None
-    if args.backward:
+    # moe_backward takes bf16 layers with d, d_ff and d_ff_shared multiples of 256
+    bwd_ok = (wl.dtype == "bf16" and wl.d % 256 == 0 and wl.d_ff % 256 == 0
+              and wl.d_ff_shared % 256 == 0)
+    if not args.no_backward and args.ep <= 1 and bwd_ok:
         bwd_report = time_backward(args, cfg, wl, x, wr, bias, (w1, w3, w2), (s1, s3, s2),
                                    R_kept, stream, peak_f)
 
