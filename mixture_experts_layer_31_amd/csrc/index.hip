@@ -392,9 +392,15 @@ __global__ __launch_bounds__(1024) void index_single_kernel(
 // decode-sized steps of the fused forward. The caller may place the tile table
 // over the logits (z and tiles may alias, hence no __restrict__ on either): every
 // logit is read before the barrier that precedes the first tile store.
-template <int NE>
+// J > 0 (a small bf16 router, T * E <= kRouteScoresMaxPairs): the logits are
+// computed here first, into LDS, each by four waves exactly as
+// router_scores_gemv_kernel<1, J> does (256 threads, chunk c on thread c % 256,
+// J chunks each in order, a wave butterfly, the four wave sums in order), so z is
+// the same bit for bit and the scores' launch is saved.
+template <int NE, int J>
 __global__ __launch_bounds__(1024) void route_index_single_kernel(
-    const float* z, const float* __restrict__ bias, int T, int k, int E,
+    const float* z, const uint16_t* __restrict__ xr, const uint16_t* __restrict__ wr, int d,
+    const float* __restrict__ bias, int T, int k, int E,
     int gate_all, int32_t* __restrict__ idx, float* __restrict__ gates, long long C,
     int32_t* __restrict__ offsets, int32_t* __restrict__ dest, int32_t* __restrict__ src,
     LoadOut o, int BM, int max_tiles, int4* tiles) {
@@ -402,6 +408,55 @@ __global__ __launch_bounds__(1024) void route_index_single_kernel(
   const int nkeys = C >= 0 ? E * k : E;   // as index_keys()
   int32_t* sidx = reinterpret_cast<int32_t*>(smem + index_single_words(E, nkeys));   // [T][k]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if constexpr (J > 0) {
+    static_assert(kRouteScoresMaxPairs <= 8, "two rounds of four pairs");
+    float* zl = reinterpret_cast<float*>(sidx + T * k);   // [T][E]
+    float* red = zl + T * E;                                // [2][16] wave sums
+    const int g = wv >> 2, wg = wv & 3, vt = threadIdx.x & 255;
+    const int npairs = T * E, nchunk = d >> 3;
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    u32x4 wc[2][J], xc[2][J];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int p = 4 * r + g;
+      const int t = p < npairs ? p / E : 0, e = p < npairs ? p % E : 0;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int c = vt + 256 * j;
+        const bool in = p < npairs && c < nchunk;
+        wc[r][j] = in ? *reinterpret_cast<const u32x4*>(wr + static_cast<size_t>(e) * d + c * 8)
+                      : zero4;
+        xc[r][j] = in ? *reinterpret_cast<const u32x4*>(xr + static_cast<size_t>(t) * d + c * 8)
+                      : zero4;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float w0 = __uint_as_float(wc[r][j][q] << 16);
+          const float w1 = __uint_as_float(wc[r][j][q] & 0xFFFF0000u);
+          acc = fmaf(__uint_as_float(xc[r][j][q] << 16), w0, acc);
+          acc = fmaf(__uint_as_float(xc[r][j][q] & 0xFFFF0000u), w1, acc);
+        }
+      acc = wave_allsum(acc);
+      if (lane == 0) red[16 * r + 4 * g + wg] = acc;
+    }
+    __syncthreads();
+    if (vt == 0) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int p = 4 * r + g;
+        const float* rr = red + 16 * r + 4 * g;
+        if (p < npairs) zl[p] = ((rr[0] + rr[1]) + rr[2]) + rr[3];
+      }
+    }
+    __syncthreads();
+    z = zl;
+  }
   float b[NE];
 #pragma unroll
   for (int i = 0; i < NE; ++i) {
@@ -421,6 +476,11 @@ __global__ __launch_bounds__(1024) void route_index_single_kernel(
   index_single_body(sidx, T, k, E, C, offsets, dest, src, o, BM, max_tiles, 1, tiles, smem);
 }
 
+bool route_scores_in_index_ok(int dtype_bf16, int T, int d, int E) {
+  return dtype_bf16 && T * E <= kRouteScoresMaxPairs && d % 8 == 0 && d / 8 <= 512 &&
+         router_score_plan(T, d, E).gemv;
+}
+
 static size_t index_single_lds(int E, int nkeys) {
   return index_single_words(E, nkeys) * sizeof(uint32_t);
 }
@@ -437,28 +497,42 @@ hipError_t launch_route_index_single(const float* z, const float* bias, int T, i
                                      int gate_all, int32_t* idx, float* gates,
                                      long long capacity, int32_t* offsets, int32_t* dest,
                                      int32_t* src, const LoadOut& load, int BM, int max_tiles,
-                                     int32_t* tiles, hipStream_t s) {
+                                     int32_t* tiles, hipStream_t s, const void* x,
+                                     const void* w_router, int d) {
   const bool cap = capacity >= 0;
   if (!route_index_single_ok(T, E, k, cap)) return hipErrorInvalidValue;
+  const bool scores = x != nullptr;
+  if (scores && !route_scores_in_index_ok(1, T, d, E)) return hipErrorInvalidValue;
   if (T == 0) return hipSuccess;
   const size_t lds = index_single_lds(E, index_keys(E, k, cap)) +
-                     static_cast<size_t>(T) * k * sizeof(int32_t);
+                     static_cast<size_t>(T) * k * sizeof(int32_t) +
+                     (scores ? (static_cast<size_t>(T) * E + 32) * sizeof(float) : 0);
   const int ne = (E + 63) / 64;
-#define MOE_RIS(NE_)                                                                         \
+  const auto* xr = static_cast<const uint16_t*>(x);
+  const auto* wr = static_cast<const uint16_t*>(w_router);
+#define MOE_RIS(NE_, J_)                                                                     \
   do {                                                                                       \
-    auto kern = route_index_single_kernel<NE_>;                                              \
+    auto kern = route_index_single_kernel<NE_, J_>;                                          \
     if (lds > 65536) {                                                                       \
       const hipError_t e1 = allow_large_lds(reinterpret_cast<const void*>(kern), lds);       \
       if (e1 != hipSuccess) return e1;                                                       \
     }                                                                                        \
-    kern<<<dim3(1), dim3(1024), lds, s>>>(z, bias, T, k, E, gate_all, idx, gates,             \
+    kern<<<dim3(1), dim3(1024), lds, s>>>(z, xr, wr, d, bias, T, k, E, gate_all, idx, gates, \
                                           cap ? capacity : -1, offsets, dest, src, load, BM, \
                                           max_tiles, reinterpret_cast<int4*>(tiles));        \
   } while (0)
-  if (ne <= 1) MOE_RIS(1);
-  else if (ne <= 2) MOE_RIS(2);
-  else if (ne <= 4) MOE_RIS(4);
-  else MOE_RIS(16);
+  if (scores) {   // E <= kRouteScoresMaxPairs: one selection chunk per lane
+    if (d / 8 <= 256) MOE_RIS(1, 1);
+    else MOE_RIS(1, 2);
+  } else if (ne <= 1) {
+    MOE_RIS(1, 0);
+  } else if (ne <= 2) {
+    MOE_RIS(2, 0);
+  } else if (ne <= 4) {
+    MOE_RIS(4, 0);
+  } else {
+    MOE_RIS(16, 0);
+  }
 #undef MOE_RIS
   return hipGetLastError();
 }

@@ -107,11 +107,18 @@ struct LoadOut {
   int32_t* touched = nullptr;
   float* max_over_mean = nullptr;
 };
+// With x set (bf16 [T][d], and w_router [E][d]) the logits are computed in the
+// same launch, bit for bit as launch_router_scores computes them, where
+// route_scores_in_index_ok holds (a small router: T * E <= kRouteScoresMaxPairs,
+// the scores' single-token vector plan); z is then unused.
+constexpr int kRouteScoresMaxPairs = 8;
+bool route_scores_in_index_ok(int dtype_bf16, int T, int d, int E);
 hipError_t launch_route_index_single(const float* z, const float* bias, int T, int k, int E,
                                      int gate_all, int32_t* idx, float* gates,
                                      long long capacity, int32_t* offsets, int32_t* dest,
                                      int32_t* src, const LoadOut& load, int BM, int max_tiles,
-                                     int32_t* tiles, hipStream_t s);
+                                     int32_t* tiles, hipStream_t s, const void* x = nullptr,
+                                     const void* w_router = nullptr, int d = 0);
 hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capacity,
                         int32_t* blk, int32_t* slot_base, int32_t* slot_keep, int32_t* offsets,
                         int32_t* dest, int32_t* src, const LoadOut& load, int BM, int max_tiles,

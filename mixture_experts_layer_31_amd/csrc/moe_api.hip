@@ -935,11 +935,15 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
     rc.take<float>(static_cast<size_t>(s.E) * 4);                         // fp
     rc.take<float>(static_cast<size_t>(s.nb_sel) * moe::kScaleStats * 4); // q_part
     float* zpart = rc.take<float>(zpart_bytes(s));
-    MOE_HIP(moe::launch_router_scores(s.bf16, x, w_router, s.T, s.d, s.E, z, zpart, strm),
-            "router_scores");
+    // a small router's scores in the same launch (Mixtral shape, one token)
+    const bool scores_here = moe::route_scores_in_index_ok(s.bf16, s.T, s.d, s.E);
+    if (!scores_here)
+      MOE_HIP(moe::launch_router_scores(s.bf16, x, w_router, s.T, s.d, s.E, z, zpart, strm),
+              "router_scores");
     MOE_HIP(moe::launch_route_index_single(
                 z, sel_bias, s.T, s.k, s.E, s.gate_all, idx, gates, s.C, offsets, dest, src,
-                load_out(stats), s.BM, s.max_tiles, tiles, strm),
+                load_out(stats), s.BM, s.max_tiles, tiles, strm, scores_here ? x : nullptr,
+                scores_here ? w_router : nullptr, s.d),
             "route_index");
   } else {
     st = do_route(s, cfg->aux_alpha, x, w_router, sel_bias, idx, gates, stats, scratch, strm);

@@ -190,6 +190,12 @@ _NOSTAT_CASES = {
     "scores_j4_shared_t1": dict(T=1, wl=("ns_sj4", 152, dict(d=6144, E=16, k=2, d_ff=128,
                                                              n_shared=1, d_ff_shared=128,
                                                              dtype=wk.BF16, bias_range=0.1))),
+    # small routers (T * E <= 8): the scores computed inside the selection-and-index
+    # workgroup, with 2 and 1 chunks per thread
+    "scores_here_j2_t1": dict(T=1, wl=("ns_sh2", 153, dict(d=4096, E=8, k=2, d_ff=128,
+                                                           dtype=wk.BF16))),
+    "scores_here_j1_e4_t2": dict(T=2, wl=("ns_sh1", 154, dict(d=1024, E=4, k=2, d_ff=128,
+                                                              dtype=wk.BF16, bias_range=0.1))),
 }
 
 
