@@ -25,6 +25,10 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restric
 
 // y[t] = sum_{j: dest[t,j] >= 0} gates[t,j] * y_perm[dest[t,j]] (+ y_perm[shared_row0 + t]),
 // summed in slot order. Workgroup (t, c) covers 1024 columns of token t, 4 per lane.
+// KM > 0 (k <= KM): every slot's index and gate, then every slot's row, are loaded
+// before the first sum, so a lane waits for two memory round trips instead of two
+// per slot; the sums are the same fused multiply-adds in the same order.
+template <int KM>
 __global__ __launch_bounds__(256) void combine_kernel(const f32x4* __restrict__ yp,
                                                       const int32_t* __restrict__ dest,
                                                       const float* __restrict__ gates, int k,
@@ -36,20 +40,38 @@ __global__ __launch_bounds__(256) void combine_kernel(const f32x4* __restrict__ 
   const int32_t* dt = dest + static_cast<size_t>(t) * k;
   const float* gt = gates + static_cast<size_t>(t) * k;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int r = dt[j];
-    if (r >= 0) {
-      const float g = gt[j];
-      const f32x4 a = yp[static_cast<size_t>(r) * row_vecs + v];
-      acc[0] = fmaf(g, a[0], acc[0]);
-      acc[1] = fmaf(g, a[1], acc[1]);
-      acc[2] = fmaf(g, a[2], acc[2]);
-      acc[3] = fmaf(g, a[3], acc[3]);
+  auto fma4 = [&](float g, const f32x4& a) {
+    acc[0] = fmaf(g, a[0], acc[0]);
+    acc[1] = fmaf(g, a[1], acc[1]);
+    acc[2] = fmaf(g, a[2], acc[2]);
+    acc[3] = fmaf(g, a[3], acc[3]);
+  };
+  f32x4 sh = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (KM > 0) {
+    int r[KM];
+    float g[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      r[j] = j < k ? dt[j] : -1;
+      g[j] = j < k ? gt[j] : 0.f;
     }
+    f32x4 a[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (r[j] >= 0) a[j] = yp[static_cast<size_t>(r[j]) * row_vecs + v];
+    if (shared_row0 >= 0) sh = yp[static_cast<size_t>(shared_row0 + t) * row_vecs + v];
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (r[j] >= 0) fma4(g[j], a[j]);
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const int r = dt[j];
+      if (r >= 0) fma4(gt[j], yp[static_cast<size_t>(r) * row_vecs + v]);
+    }
+    if (shared_row0 >= 0) sh = yp[static_cast<size_t>(shared_row0 + t) * row_vecs + v];
   }
   if (shared_row0 >= 0) {
-    const f32x4 a = yp[static_cast<size_t>(shared_row0 + t) * row_vecs + v];
-    acc[0] += a[0]; acc[1] += a[1]; acc[2] += a[2]; acc[3] += a[3];
+    acc[0] += sh[0]; acc[1] += sh[1]; acc[2] += sh[2]; acc[3] += sh[3];
   }
   y[static_cast<size_t>(t) * row_vecs + v] = acc;
 }
@@ -67,9 +89,17 @@ hipError_t launch_gather_rows(int elt_bytes, const void* x, const int32_t* src,
 hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* gates, int T,
                           int k, int d, int shared_row0, float* y, hipStream_t s) {
   const int row_vecs = d / 4;
-  combine_kernel<<<dim3(T, (row_vecs + 255) / 256), dim3(256), 0, s>>>(reinterpret_cast<const f32x4*>(y_perm), dest,
-                                               gates, k, row_vecs, shared_row0,
-                                               reinterpret_cast<f32x4*>(y));
+  const dim3 grid(T, (row_vecs + 255) / 256);
+  const f32x4* yp = reinterpret_cast<const f32x4*>(y_perm);
+  f32x4* yo = reinterpret_cast<f32x4*>(y);
+#define MOE_COMBINE(KM_) \
+  combine_kernel<KM_><<<grid, dim3(256), 0, s>>>(yp, dest, gates, k, row_vecs, shared_row0, yo)
+  if (k <= 1) MOE_COMBINE(1);
+  else if (k <= 2) MOE_COMBINE(2);
+  else if (k <= 4) MOE_COMBINE(4);
+  else if (k <= 8) MOE_COMBINE(8);
+  else MOE_COMBINE(0);
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 
