@@ -158,27 +158,42 @@ __device__ __forceinline__ float wave_allsum(float v) {
   return ((readlane_f(v, 0) + readlane_f(v, 16)) + readlane_f(v, 32)) + readlane_f(v, 48);
 }
 
-// Wave-wide argmax of (v, e): the largest v, ties to the smallest e, by the
-// same DPP steps and the four rows' winners in scalar registers; both results
-// are wave-uniform.
-__device__ __forceinline__ void wave_argmax(float& v, int& e) {
-  auto take = [&](float ov, int oe) {
-    if (ov > v || (ov == v && oe < e)) { v = ov; e = oe; }
-  };
-  { const float ov = dpp_f<kDppQuadXor1>(v); const int oe = dpp_i<kDppQuadXor1>(e); take(ov, oe); }
-  { const float ov = dpp_f<kDppQuadXor2>(v); const int oe = dpp_i<kDppQuadXor2>(e); take(ov, oe); }
-  { const float ov = dpp_f<kDppRowRor4>(v); const int oe = dpp_i<kDppRowRor4>(e); take(ov, oe); }
-  { const float ov = dpp_f<kDppRowRor8>(v); const int oe = dpp_i<kDppRowRor8>(e); take(ov, oe); }
-  float bv = readlane_f(v, 0);
-  int be = __builtin_amdgcn_readlane(e, 0);
-#pragma unroll
-  for (int r = 1; r < 4; ++r) {
-    const float ov = readlane_f(v, 16 * r);
-    const int oe = __builtin_amdgcn_readlane(e, 16 * r);
-    if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-  }
-  v = bv;
-  e = be;
+// Key of a selection candidate (score s, expert e) whose unsigned order is the
+// selection order: a higher score first, equal scores (-0 equal to +0) to the
+// lower expert. The high word is s's sign-magnitude bits made monotonic, the low
+// word ~e; a NaN score gets key 0, below every candidate.
+__device__ __forceinline__ uint64_t select_key(float s, int e) {
+  if (!(s == s)) return 0ull;
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(u) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(e));
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_max_key(uint64_t key) {
+  const int lo = static_cast<int>(static_cast<uint32_t>(key));
+  const int hi = static_cast<int>(static_cast<uint32_t>(key >> 32));
+  const uint32_t olo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xF, false));
+  const uint32_t ohi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xF, false));
+  const uint64_t o = (static_cast<uint64_t>(ohi) << 32) | olo;
+  return o > key ? o : key;
+}
+
+// Wave-wide maximum of a 64-bit key (all 64 lanes active), without branches:
+// DPP steps give every lane its 16-lane row's maximum, row_bcast:15 (into rows 1
+// and 3) and row_bcast:31 (into rows 2 and 3) carry the rows' maxima up to lane
+// 63, whose key every lane gets.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t key) {
+  key = dpp_max_key<kDppQuadXor1, 0xF>(key);
+  key = dpp_max_key<kDppQuadXor2, 0xF>(key);
+  key = dpp_max_key<kDppRowRor4, 0xF>(key);
+  key = dpp_max_key<kDppRowRor8, 0xF>(key);
+  key = dpp_max_key<0x142, 0xA>(key);   // row_bcast:15
+  key = dpp_max_key<0x143, 0xC>(key);   // row_bcast:31
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(key)), 63));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(key >> 32)), 63));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 // Inclusive prefix sum of an int over the wave's 64 lanes (all active): DPP

@@ -45,8 +45,8 @@ __device__ __forceinline__ void build_bitmaps(uint32_t* bm, const int32_t* idx, 
 }
 
 // number of set bits of key's bitmap strictly below local token position p
-__device__ __forceinline__ int bits_below(const uint32_t* bm, int key, int p) {
-  const uint32_t* b = bm + key * kWords;
+__device__ __forceinline__ int bits_below(const uint32_t* bm, int key, int p, int stride = kWords) {
+  const uint32_t* b = bm + key * stride;
   int r = 0;
   const int w = p >> 5;
   for (int i = 0; i < w; ++i) r += __popc(b[i]);
@@ -269,7 +269,8 @@ __device__ __forceinline__ void index_single_body(
     const LoadOut& o, int BM, int max_tiles, int ep, int4* __restrict__ tiles, uint32_t* smem) {
   const int cap = C >= 0;
   const int nkeys = cap ? E * k : E;
-  uint32_t* bm = smem;                                              // [nkeys][kWords]
+  const int nw = (T + 31) >> 5;                                     // bitmap words per key
+  uint32_t* bm = smem;                                              // [nkeys][nw]
   int32_t* tot = reinterpret_cast<int32_t*>(bm + nkeys * kWords);   // [nkeys]
   int32_t* sbase = tot + nkeys;                                     // [nkeys]
   int32_t* skeep = sbase + nkeys;                                   // [nkeys]
@@ -277,20 +278,20 @@ __device__ __forceinline__ void index_single_body(
   int32_t* part = off + (E + 1);                                    // [16]
   const int tid = threadIdx.x;
 
-  for (int i = tid; i < nkeys * kWords; i += 1024) bm[i] = 0u;
+  for (int i = tid; i < nkeys * nw; i += 1024) bm[i] = 0u;
   __syncthreads();
   if (tid < T) {
     const uint32_t bit = 1u << (tid & 31);
     for (int j = 0; j < k; ++j) {
       const int e = idx[static_cast<size_t>(tid) * k + j];
       if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) continue;
-      atomicOr(&bm[(cap ? j * E + e : e) * kWords + (tid >> 5)], bit);
+      atomicOr(&bm[(cap ? j * E + e : e) * nw + (tid >> 5)], bit);
     }
   }
   __syncthreads();
   for (int key = tid; key < nkeys; key += 1024) {
     int c = 0;
-    for (int w = 0; w < kWords; ++w) c += __popc(bm[key * kWords + w]);
+    for (int w = 0; w < nw; ++w) c += __popc(bm[key * nw + w]);
     tot[key] = c;
   }
   __syncthreads();
@@ -333,17 +334,17 @@ __device__ __forceinline__ void index_single_body(
       if (static_cast<unsigned>(ej) >= static_cast<unsigned>(E)) {
         row = -1;
       } else if (!cap) {
-        row = off[ej] + bits_below(bm, ej, tid);
+        row = off[ej] + bits_below(bm, ej, tid, nw);
       } else {
         const int key = j * E + ej;
-        const int rank_j = bits_below(bm, key, tid);
+        const int rank_j = bits_below(bm, key, tid, nw);
         if (static_cast<long long>(sbase[key]) + rank_j >= C) {
           row = -1;
         } else {
           int before = 0;
           for (int j2 = 0; j2 < k; ++j2) {
             const int key2 = j2 * E + ej;
-            const int r2 = bits_below(bm, key2, tid);
+            const int r2 = bits_below(bm, key2, tid, nw);
             const int kk = skeep[key2];
             before += r2 < kk ? r2 : kk;
           }

@@ -51,31 +51,41 @@ __device__ __forceinline__ void select_token(const float* __restrict__ zr, const
   o.m = m;
   o.se = se;
 
-  // k rounds of argmax; lane r keeps the round-r winner and its unbiased logit
+  // k rounds of argmax over the keys of (z + b, e); lane r keeps the round-r
+  // winner and its unbiased logit. The starting key, (-inf, INT_MAX), is what
+  // every lane holds before its first candidate.
+  uint64_t key[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? select_key(sl[i], e) : 0ull;
+  }
+  const uint64_t floor_key = select_key(-INFINITY, 0x7fffffff);
   int my_e = 0;
   float my_z = -INFINITY;
   for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
+    uint64_t best = floor_key;
 #pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && (sl[i] > bv || (sl[i] == bv && e < be))) { bv = sl[i]; be = e; }
-    }
-    wave_argmax(bv, be);
-    o.kth = bv;
+    for (int i = 0; i < NE; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_key(best);
+    const int be = static_cast<int>(~static_cast<uint32_t>(best));
     const int owner = be & 63, slot = be >> 6;
-    float zsel = 0.f;
+    float zsel = 0.f, ssel = 0.f;
 #pragma unroll
     for (int i = 0; i < NE; ++i)
-      if (i == slot) zsel = o.zl[i];
+      if (i == slot) { zsel = o.zl[i]; ssel = sl[i]; }
     zsel = readlane_f(zsel, owner);
+    o.kth = best == floor_key ? -INFINITY : readlane_f(ssel, owner);
     // the winner cannot win again: its score becomes -inf while at least
     // E - r - 1 >= 1 unselected experts keep finite scores
     if (lane == owner) {
 #pragma unroll
       for (int i = 0; i < NE; ++i)
-        if (i == slot) { sl[i] = -INFINITY; o.chosen[i] = 1; }
+        if (i == slot) {
+          sl[i] = -INFINITY;
+          o.chosen[i] = 1;
+          key[i] = select_key(-INFINITY, be);
+        }
     }
     if (lane == r) { my_e = be; my_z = zsel; }
   }
