@@ -316,61 +316,70 @@ __device__ __forceinline__ void index_single_body(
     if (o.counts) o.counts[e] = cnt;
     if (o.kept) o.kept[e] = keep_e;
   }
-  int kept_total = 0;
-  const int incl = block_scan_1024((e < E) ? keep_e : 0, part, &kept_total);
+  // offsets: inclusive scan of the kept counts; tile table: exclusive scan of
+  // ceil(kept / BM). Both in one scan of (kept | tiles << 16) while every partial
+  // sum fits in 15 bits (tiles <= kept <= T k), else in two.
+  const int keep_v = (e < E) ? keep_e : 0;
+  const int nt = (tiles != nullptr && e < E) ? (keep_e + BM - 1) / BM : 0;
+  int kept_total = 0, incl, tiles_total = 0, tiles_incl = 0;
+  if (T * k < 32768) {
+    int tot2 = 0;
+    const int v2 = block_scan_1024(keep_v | (nt << 16), part, &tot2);
+    incl = v2 & 0xFFFF;
+    kept_total = tot2 & 0xFFFF;
+    tiles_incl = v2 >> 16;
+    tiles_total = tot2 >> 16;
+  } else {
+    incl = block_scan_1024(keep_v, part, &kept_total);
+    if (tiles != nullptr) tiles_incl = block_scan_1024(nt, part, &tiles_total);
+  }
   if (e < E) { off[e + 1] = incl; offsets[e + 1] = incl; }
   if (tid == 0) {
     off[0] = 0;
     offsets[0] = 0;
     if (o.n_dropped) o.n_dropped[0] = T * k - kept_total;
   }
+  if (tiles != nullptr) {
+    const int start = tiles_incl - nt, lo = incl - keep_v;
+    const int w = tile_group_weights(e, E, ep);
+    for (int i = 0; i < nt && start + i < max_tiles; ++i)
+      tiles[start + i] =
+          make_int4(w, lo + i * BM, min(BM, keep_v - i * BM), tile_block_word(start, nt, i));
+    for (int i = tiles_total + tid; i < max_tiles; i += 1024) tiles[i] = make_int4(0, 0, 0, 0);
+  }
   load_summary(cnt, keep_e, tot, E, ep, T, k, o, part);
   __syncthreads();
 
-  if (tid < T) {
-    for (int j = 0; j < k; ++j) {
-      const int ej = idx[static_cast<size_t>(tid) * k + j];
-      int row;
-      if (static_cast<unsigned>(ej) >= static_cast<unsigned>(E)) {
+  // one thread per (token, slot): every slot's row depends only on the bitmaps,
+  // the offsets and (with capacity) the slot bases
+  for (int p = tid; p < T * k; p += 1024) {
+    const int t = p / k, j = p - t * k;
+    const int ej = idx[p];
+    int row;
+    if (static_cast<unsigned>(ej) >= static_cast<unsigned>(E)) {
+      row = -1;
+    } else if (!cap) {
+      row = off[ej] + bits_below(bm, ej, t, nw);
+    } else {
+      const int key = j * E + ej;
+      const int rank_j = bits_below(bm, key, t, nw);
+      if (static_cast<long long>(sbase[key]) + rank_j >= C) {
         row = -1;
-      } else if (!cap) {
-        row = off[ej] + bits_below(bm, ej, tid, nw);
       } else {
-        const int key = j * E + ej;
-        const int rank_j = bits_below(bm, key, tid, nw);
-        if (static_cast<long long>(sbase[key]) + rank_j >= C) {
-          row = -1;
-        } else {
-          int before = 0;
-          for (int j2 = 0; j2 < k; ++j2) {
-            const int key2 = j2 * E + ej;
-            const int r2 = bits_below(bm, key2, tid, nw);
-            const int kk = skeep[key2];
-            before += r2 < kk ? r2 : kk;
-          }
-          row = off[ej] + before;
+        int before = 0;
+        for (int j2 = 0; j2 < k; ++j2) {
+          const int key2 = j2 * E + ej;
+          const int r2 = bits_below(bm, key2, t, nw);
+          const int kk = skeep[key2];
+          before += r2 < kk ? r2 : kk;
         }
+        row = off[ej] + before;
       }
-      dest[static_cast<size_t>(tid) * k + j] = row;
-      if (row >= 0) src[row] = tid;
     }
+    dest[p] = row;
+    if (row >= 0) src[row] = t;
   }
 
-  if (tiles == nullptr) return;
-  // tile table: exclusive scan of ceil(n_e / BM) over the experts
-  int lo = 0, n = 0, nt = 0;
-  if (e < E) {
-    lo = off[e];
-    n = off[e + 1] - lo;
-    nt = (n + BM - 1) / BM;
-  }
-  int total = 0;
-  const int start = block_scan_1024(nt, part, &total) - nt;
-  const int w = tile_group_weights(e, E, ep);
-  for (int i = 0; i < nt && start + i < max_tiles; ++i)
-    tiles[start + i] =
-        make_int4(w, lo + i * BM, min(BM, n - i * BM), tile_block_word(start, nt, i));
-  for (int i = total + tid; i < max_tiles; i += 1024) tiles[i] = make_int4(0, 0, 0, 0);
 }
 
 // LDS words of index_single_body
