@@ -838,6 +838,59 @@ static __host__ __device__ long long stream_seg_items(const StreamSeg& seg) {
   return seg.rows > 0 ? static_cast<long long>((seg.rows + 15) >> 4) * (seg.N >> 4) : 0;
 }
 
+// One wave's share of a streamed item: K-steps [s_lo, s_hi) of 16 weight rows
+// (wp; gate/up also wq) against 16 token rows (xp), lane l holding 16 bytes of
+// row l % 16 at K-chunk l / 16 of each 32-wide step. Batches of U steps are
+// double-buffered in registers: the next batch's loads are issued before the
+// current batch is multiplied. WIDEN: the weights are bf16 and the token rows
+// IEEE half (each weight fragment widened to half before its MFMA).
+template <bool GATEUP, int U, bool WIDEN>
+__device__ __forceinline__ void stream_wave(const uint16_t* wp, const uint16_t* wq,
+                                            const uint16_t* xp, int s_lo, int s_hi, f32x4& acc,
+                                            f32x4& acc2) {
+  typedef __attribute__((ext_vector_type(8))) __bf16 bf8;
+  auto wfrag = [](bf8 w) { if constexpr (WIDEN) return bf16x8_to_f16(w); else return w; };
+  bf8 wv[2][U], xv[2][U], qv[2][U];
+  auto load = [&](int s0, int b) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (s0 + u) << 5;
+      wv[b][u] = *reinterpret_cast<const bf8*>(wp + k);
+      if (GATEUP) qv[b][u] = *reinterpret_cast<const bf8*>(wq + k);
+      xv[b][u] = *reinterpret_cast<const bf8*>(xp + k);
+    }
+  };
+  auto comp = [&](int b) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc = mfma16x32<WIDEN>(wfrag(wv[b][u]), xv[b][u], acc);
+      if (GATEUP) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qv[b][u], xv[b][u], acc2, 0, 0, 0);
+    }
+  };
+  const int nb = (s_hi - s_lo) / U;
+  if (nb > 0) {
+    load(s_lo, 0);
+    int i = 0;
+    for (; i + 2 <= nb; i += 2) {
+      load(s_lo + (i + 1) * U, 1);
+      comp(0);
+      if (i + 2 < nb) load(s_lo + (i + 2) * U, 0);
+      comp(1);
+    }
+    if (i < nb) comp(0);
+  }
+  for (int st = s_lo + nb * U; st < s_hi; ++st) {
+    const int k = st << 5;
+    const bf8 w1v = *reinterpret_cast<const bf8*>(wp + k);
+    const bf8 x1v = *reinterpret_cast<const bf8*>(xp + k);
+    acc = mfma16x32<WIDEN>(wfrag(w1v), x1v, acc);
+    if (GATEUP) {
+      const bf8 q1v = *reinterpret_cast<const bf8*>(wq + k);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q1v, x1v, acc2, 0, 0, 0);
+    }
+  }
+}
+
 // H16: as gemm_bf16_kernel (half activations; down widens its weight fragments).
 template <bool GATEUP, int U, int KS, bool H16>
 __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
@@ -846,10 +899,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
     int a_row0_g, const uint16_t* __restrict__ w_a_g, const uint16_t* __restrict__ w_b_g,
     long long w_stride, void* __restrict__ out, int out_stride, int out_row0_g, int K_g, int N,
     StreamSeg seg) {
-  typedef __attribute__((ext_vector_type(8))) __bf16 bf8;
   constexpr int IPB = 4 / KS;                  // items per workgroup
   constexpr bool WIDEN = H16 && !GATEUP;       // half activation rows x widened weights
-  auto wfrag = [](bf8 w) { if constexpr (WIDEN) return bf16x8_to_f16(w); else return w; };
   __shared__ f32x4 red[KS > 1 ? 3 : 1][GATEUP ? 2 : 1][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kpart = wave % KS;
@@ -913,46 +964,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
     const uint16_t* wq = GATEUP ? w_b + wrow : nullptr;
     // this wave's K range: whole 32-wide steps, split as evenly as possible
     const int steps = K >> 5;
-    const int s_lo = steps * kpart / KS, s_hi = steps * (kpart + 1) / KS;
-    bf8 wv[2][U], xv[2][U], qv[2][U];
-    auto load = [&](int s0, int b) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = (s0 + u) << 5;
-        wv[b][u] = *reinterpret_cast<const bf8*>(wp + k);
-        if (GATEUP) qv[b][u] = *reinterpret_cast<const bf8*>(wq + k);
-        xv[b][u] = *reinterpret_cast<const bf8*>(xp + k);
-      }
-    };
-    auto comp = [&](int b) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        acc = mfma16x32<WIDEN>(wfrag(wv[b][u]), xv[b][u], acc);
-        if (GATEUP) acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qv[b][u], xv[b][u], acc2, 0, 0, 0);
-      }
-    };
-    const int nb = (s_hi - s_lo) / U;
-    if (nb > 0) {
-      load(s_lo, 0);
-      int i = 0;
-      for (; i + 2 <= nb; i += 2) {
-        load(s_lo + (i + 1) * U, 1);
-        comp(0);
-        if (i + 2 < nb) load(s_lo + (i + 2) * U, 0);
-        comp(1);
-      }
-      if (i < nb) comp(0);
-    }
-    for (int st = s_lo + nb * U; st < s_hi; ++st) {
-      const int k = st << 5;
-      const bf8 w1v = *reinterpret_cast<const bf8*>(wp + k);
-      const bf8 x1v = *reinterpret_cast<const bf8*>(xp + k);
-      acc = mfma16x32<WIDEN>(wfrag(w1v), x1v, acc);
-      if (GATEUP) {
-        const bf8 q1v = *reinterpret_cast<const bf8*>(wq + k);
-        acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q1v, x1v, acc2, 0, 0, 0);
-      }
-    }
+    stream_wave<GATEUP, U, WIDEN>(wp, wq, xp, steps * kpart / KS, steps * (kpart + 1) / KS, acc,
+                                  acc2);
   }
   if (KS > 1) {
     // partial sums of waves 1..KS-1 of this item, added by wave 0 in wave order
@@ -984,6 +997,76 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream_kernel(
     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow * out_stride + n) = pk;
   } else {
     *reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow * out_stride + n) = acc;
+  }
+}
+
+// Down product and combine in one launch, for decode steps whose groups each fit
+// one 16-row tile and whose tiles times the K split fit one workgroup (a layer of
+// few experts per token at one or two tokens): workgroup j owns output columns
+// 16 j .. 16 j + 15 of every tile, so it holds all k rows of each token's slice.
+// Wave w streams tile w / KS over the K range of wave w % KS exactly as
+// gemm_bf16_stream_kernel does, and the KS partial sums of a tile are added in the
+// same wave order, so each y_perm value is the same bit for bit; the values stay
+// in LDS (indexed by y_perm row). Then y[t][slice] is the gate-weighted sum of
+// the token's kept rows as combine_kernel computes it: fused multiply-adds from
+// zero in slot order. The layer output is the routed experts' weighted sum (no
+// shared expert here).
+constexpr int kCombineMaxK = 8;   // slots per token the fused combine holds in registers
+template <int U, int KS, int NTL, bool H16>
+__global__ __launch_bounds__(64 * KS * NTL) void gemm_down_combine_kernel(
+    const int32_t* __restrict__ tiles, int max_tiles, const uint16_t* __restrict__ act,
+    int a_stride, const uint16_t* __restrict__ w2, long long w_stride, int K, int N,
+    const int32_t* __restrict__ dest, const float* __restrict__ gates, int T, int k,
+    float* __restrict__ y) {
+  __shared__ f32x4 red[NTL][KS > 1 ? KS - 1 : 1][64];
+  __shared__ float yl[16 * NTL][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ti = wave / KS, kpart = wave % KS;
+  const int n0 = blockIdx.x * 16;
+  TileCoord tc{0, 0, 0};
+  if (ti < max_tiles) tc = lookup_tile(tiles, 0, 16, ti);
+  const bool active = tc.rows > 0;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+  const int r16 = lane & 15, ck = (lane >> 4) * 8;
+  // this thread's combine item (token t, column c of the slice): its slots' rows
+  // and gates are loaded now, so their latency passes while the weights stream
+  const int t = threadIdx.x >> 4, c = threadIdx.x & 15;
+  const bool has_item = t < T;
+  int rj[kCombineMaxK];
+  float gj[kCombineMaxK];
+#pragma unroll
+  for (int j = 0; j < kCombineMaxK; ++j) {
+    rj[j] = has_item && j < k ? dest[t * k + j] : -1;
+    gj[j] = has_item && j < k ? gates[t * k + j] : 0.f;
+  }
+  if (active) {
+    const uint16_t* xp = act + static_cast<size_t>(tc.row0 + min(r16, tc.rows - 1)) * a_stride + ck;
+    const uint16_t* wp = w2 + static_cast<size_t>(tc.group) * w_stride +
+                         static_cast<size_t>(n0 + r16) * K + ck;
+    const int steps = K >> 5;
+    stream_wave<false, U, H16>(wp, nullptr, xp, steps * kpart / KS, steps * (kpart + 1) / KS, acc,
+                               acc2);
+  }
+  if (KS > 1 && kpart > 0) red[ti][kpart - 1][lane] = acc;
+  __syncthreads();
+  if (kpart == 0 && active) {
+#pragma unroll
+    for (int p = 0; p < KS - 1; ++p) {
+      const f32x4 v = red[ti][p][lane];
+      acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
+    }
+    if (r16 < tc.rows) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) yl[tc.row0 + r16][(lane >> 4) * 4 + q] = acc[q];
+    }
+  }
+  __syncthreads();
+  if (has_item) {
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < kCombineMaxK; ++j)
+      if (rj[j] >= 0) sum = fmaf(gj[j], yl[rj[j]][c], sum);
+    y[static_cast<size_t>(t) * N + n0 + c] = sum;
   }
 }
 
@@ -1325,6 +1408,37 @@ hipError_t launch_gemm_down_bf16_with_shared(const GemmTileMap& map, const DownA
   return run_stream<false, false>(map, static_cast<const uint16_t*>(a.act), a.src, a.act_stride,
                                   a.in_row0, static_cast<const uint16_t*>(a.w2), nullptr,
                                   a.w_stride, a.y, ys, a.out_row0, a.K, a.N, s, seg);
+}
+
+// The fused down product and combine (gemm_down_combine_kernel) where it applies:
+// half activation rows in y_perm order (no src, no row offsets), at most 16 tokens
+// (so each group is one tile), and the K split and batch depth that the streaming
+// launch's own rule picks, with that split times the tile bound within one
+// workgroup, and at most kCombineMaxK slots per token. Otherwise
+// hipErrorNotSupported, and nothing is launched.
+hipError_t launch_gemm_down_combine_bf16(const GemmTileMap& map, const DownArgs& a,
+                                         const int32_t* dest, const float* gates, int T, int k,
+                                         float* y, hipStream_t s) {
+  if (map.tiles == nullptr || !a.act_f16 || a.src != nullptr || a.in_row0 != 0 ||
+      T <= 0 || T > 16 || k <= 0 || k > kCombineMaxK || a.N % 16 != 0 || a.K % 32 != 0 ||
+      map.max_tiles > 4)
+    return hipErrorNotSupported;
+  const int KS = stream_split(map, a.N, StreamSeg{});
+  const int steps = a.K / 32 / KS;
+  const bool u4 = steps < 16 || steps >= 100;   // as run_stream for the down product
+  const auto* act = static_cast<const uint16_t*>(a.act);
+  const auto* w2 = static_cast<const uint16_t*>(a.w2);
+  const dim3 grid(a.N / 16);
+#define MOE_DOWN_COMBINE(U_, KS_, NTL_)                                                        \
+  gemm_down_combine_kernel<U_, KS_, NTL_, true><<<grid, dim3(64 * KS_ * NTL_), 0, s>>>(      \
+      map.tiles, map.max_tiles, act, a.act_stride, w2, a.w_stride, a.K, a.N, dest, gates, T, \
+      k, y)
+  if (KS == 4 && u4 && map.max_tiles <= 2) MOE_DOWN_COMBINE(4, 4, 2);
+  else if (KS == 4 && u4) MOE_DOWN_COMBINE(4, 4, 4);
+  else if (KS == 4 && map.max_tiles <= 2) MOE_DOWN_COMBINE(8, 4, 2);
+  else return hipErrorNotSupported;
+#undef MOE_DOWN_COMBINE
+  return hipGetLastError();
 }
 
 // Output tiles of 256 columns unless that leaves fewer than two tiles per CU

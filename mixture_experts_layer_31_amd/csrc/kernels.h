@@ -267,6 +267,13 @@ hipError_t launch_gemm_gateup_bf16_with_shared(const GemmTileMap& map, const Gat
                                                const GateUpArgs& sh, int sh_rows, hipStream_t s);
 hipError_t launch_gemm_down_bf16_with_shared(const GemmTileMap& map, const DownArgs& a,
                                              const DownArgs& sh, int sh_rows, hipStream_t s);
+// Decode steps of at most 16 tokens whose tile bound times the streaming K split
+// fits one workgroup: the down product and the gate-weighted combine in one launch,
+// y written directly (bit for bit the streaming down product then combine); y_perm
+// is not written. hipErrorNotSupported (nothing launched) where it does not apply.
+hipError_t launch_gemm_down_combine_bf16(const GemmTileMap& map, const DownArgs& a,
+                                         const int32_t* dest, const float* gates, int T, int k,
+                                         float* y, hipStream_t s);
 hipError_t launch_gemm_gateup_f32(const GemmTileMap& map, const GateUpArgs& a, hipStream_t s);
 hipError_t launch_gemm_down_f32(const GemmTileMap& map, const DownArgs& a, hipStream_t s);
 

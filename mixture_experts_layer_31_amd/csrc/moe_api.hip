@@ -957,6 +957,17 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
     st = early.join(strm);
     if (st != MOE_OK) return st;
   }
+  if (!s.nsh && s.bf16 && s.BM == 16 && s.ep == 1) {
+    // one or two tokens of a layer with few experts per token: the down product
+    // and the combine in one launch (the same y bit for bit, no y_perm round trip)
+    moe::GemmTileMap map{tiles, s.max_tiles, 0, false, avg_group_rows(s)};
+    moe::DownArgs a{act, s.act_stride, 0, w2, static_cast<long long>(s.d) * s.dff, y_perm, 0,
+                    s.dff, s.d};
+    a.act_f16 = true;
+    const hipError_t e = moe::launch_gemm_down_combine_bf16(map, a, dest, gates, s.T, s.k, y, strm);
+    if (e == hipSuccess) return MOE_OK;
+    if (e != hipErrorNotSupported) return hip_fail(e, "gemm_down_combine");
+  }
   float* sk = sk_bytes(s) ? reinterpret_cast<float*>(static_cast<char*>(scratch) + tiles_bytes(s))
                          : nullptr;
   st = do_down(s, act, tiles, w2, ws2, y_perm, sk, strm);
