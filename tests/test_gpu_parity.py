@@ -888,6 +888,22 @@ def test_mixtral_decode(T):
     assert g["counts"].sum() == 2 * T
 
 
+@pytest.mark.parametrize("cid,T,cf", [(110, 1, 0.0), (110, 2, 0.5), (115, 2, 0.5), (115, 2, 0.0)])
+def test_decode_down_with_combine_in_one_launch(cid, T, cf):
+    """One and two tokens of an 8-expert top-2 layer, the shape at which the fused forward
+    runs the down product and the combine as one launch (one workgroup holds every expert
+    tile of a 16-column slice). Seed 110 routes both tokens to expert 3 first, seed 115 both
+    to experts 4 and 6. With a capacity of one row per expert (GShard priority, 15-779 notes
+    §3.5) the later token's slots drop, so dest holds -1 there. y is checked against the
+    oracle and bit for bit against the staged entry points (down product, then combine)."""
+    wl = _adhoc("decode_down_combine", cid, T=T, d=256, E=8, k=2, d_ff=512, dtype=wk.BF16,
+                capacity_factor=cf, offset_var=1.5)
+    W = Weights(wl)
+    g, _, p = full_check(wl, W, T, staged=True)
+    if cf > 0:
+        assert p["n_dropped"] > 0
+
+
 def test_coverage_law_with_gpu_routing():
     """Expert coverage of decode batches under the GPU's own routing (CME295 notes
     §2.3): with the near-uniform Mixtral-shaped router, a batch of B tokens touches
