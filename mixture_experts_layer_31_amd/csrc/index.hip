@@ -102,10 +102,13 @@ __global__ __launch_bounds__(kTB) void index_count_kernel(const int32_t* __restr
 }
 
 // One workgroup. blk[b][key] (counts) becomes the exclusive prefix over blocks.
+// With a tile table (tiles != nullptr) it also writes the GEMM tiles of BM rows
+// from the kept counts, as tile_map_kernel does from the offsets (one launch less).
 __global__ __launch_bounds__(1024) void index_scan_kernel(
     int32_t* __restrict__ blk, int nb, int T, int k, int E, long long C,
     int32_t* __restrict__ slot_base, int32_t* __restrict__ slot_keep,
-    int32_t* __restrict__ offsets, LoadOut o, int ep) {
+    int32_t* __restrict__ offsets, LoadOut o, int ep, int BM, int max_tiles,
+    int4* __restrict__ tiles) {
   __shared__ int32_t part[16];
   const int cap = C >= 0;
   const int nkeys = cap ? E * k : E;
@@ -161,6 +164,17 @@ __global__ __launch_bounds__(1024) void index_scan_kernel(
   if (threadIdx.x == 0) {
     offsets[0] = 0;
     if (o.n_dropped) o.n_dropped[0] = T * k - kept_total;
+  }
+  if (tiles != nullptr) {
+    const int nt = (e < E) ? (keep_e + BM - 1) / BM : 0;
+    int tiles_total = 0;
+    const int start = block_scan_1024(nt, part, &tiles_total) - nt;
+    const int lo = incl - keep_e;
+    const int w = tile_group_weights(e, E, ep);
+    for (int i = 0; i < nt && start + i < max_tiles; ++i)
+      tiles[start + i] =
+          make_int4(w, lo + i * BM, min(BM, keep_e - i * BM), tile_block_word(start, nt, i));
+    for (int i = tiles_total + threadIdx.x; i < max_tiles; i += 1024) tiles[i] = make_int4(0, 0, 0, 0);
   }
   load_summary(cnt, keep_e, tot, E, ep, T, k, o, part);
 }
@@ -576,14 +590,13 @@ hipError_t launch_index(const int32_t* idx, int T, int k, int E, long long capac
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   index_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(blk, nb, T, k, E, cap ? capacity : -1,
-                                                   slot_base, slot_keep, offsets, load, ep);
+                                                   slot_base, slot_keep, offsets, load, ep, BM,
+                                                   max_tiles, reinterpret_cast<int4*>(tiles));
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   index_rank_kernel<<<dim3(nb), dim3(kTB), lds, s>>>(idx, T, k, E, cap ? capacity : -1, blk,
                                                      slot_base, slot_keep, offsets, dest, src);
-  err = hipGetLastError();
-  if (err != hipSuccess || tiles == nullptr) return err;
-  return launch_tile_map(offsets, E, BM, max_tiles, ep, tiles, s);
+  return hipGetLastError();
 }
 
 }  // namespace moe

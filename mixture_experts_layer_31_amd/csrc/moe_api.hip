@@ -250,7 +250,9 @@ size_t stage_bytes(const Shape& s, moe_stage st) {
     case MOE_STAGE_COMBINE: b = 0; break;
     case MOE_STAGE_FORWARD: {
       size_t scratch = route_bytes(s);
-      if (permute_bytes(s) > scratch) scratch = permute_bytes(s);
+      // the index writes the tile table at the start of the scratch while its own
+      // buffers (after the table) are still in use
+      if (tiles_bytes(s) + permute_bytes(s) > scratch) scratch = tiles_bytes(s) + permute_bytes(s);
       if (tiles_bytes(s) + sk_bytes(s) > scratch) scratch = tiles_bytes(s) + sk_bytes(s);
       b = forward_fixed_bytes(s) + scratch;
       break;
@@ -948,7 +950,8 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* w_route
   } else {
     st = do_route(s, cfg->aux_alpha, x, w_router, sel_bias, idx, gates, stats, scratch, strm);
     if (st != MOE_OK) return st;
-    st = do_permute(s, idx, x, offsets, dest, src, nullptr, stats, scratch, tiles, strm);
+    st = do_permute(s, idx, x, offsets, dest, src, nullptr, stats,
+                    static_cast<char*>(scratch) + tiles_bytes(s), tiles, strm);
     if (st != MOE_OK) return st;
   }
   st = do_gateup(s, x, src, tiles, w1, w3, ws1, ws3, act, strm, shared_done);
